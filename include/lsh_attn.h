@@ -1,0 +1,160 @@
+/*
+ * lsh_attn.h -- C ABI of the LSH-sampled decode-attention library (gfx950).
+ *
+ * MagicPIG replaces the attention of a decode query by an estimate built from
+ * keys sampled with locality-sensitive hashing ("MagicPIG: LSH Sampling for
+ * Efficient LLM Generation", GrooveSquid summary; MagicPIG project summary on
+ * sourcepulse, "How It Works"), behind an LSH library that exposes an LSH
+ * kernel through an interface header ("How infini-ai-lab/magicpig works",
+ * Components: "LSH Sampling").  This header is that interface for MI355X.
+ * The library has two operations:
+ *
+ *   lsh_build_tables      at prefill: SimHash every key into L codes of K bits
+ *                         and bucket the keys of every table (the hash-table
+ *                         construction the sourcepulse summary lists under
+ *                         "Highlighted Details").
+ *   lsh_decode_attention  at a decode step: hash each query head, probe its L
+ *                         buckets, count per-key collisions, keep keys that
+ *                         collide in >= T tables, and return the 1/u-weighted
+ *                         softmax estimate and its log-sum-exp.
+ *
+ * Definitions (d = head dim, N = keys per sequence, G = Hq / Hkv):
+ *   proj      = k @ W, W of shape [d, L*K]; column l*K + b is bit b of table l.
+ *   code_l(k) = sum_b [proj[l*K + b] > 0] << b        (bit 0 = LSB, 0 -> bit 0)
+ *   c(n)      = #{ l : code_l(k_n) == code_l(q) }      (collision count)
+ *   S         = { n : c(n) >= T }                       (selected keys)
+ *   P(n)      = (1 - theta_n / pi)^K, theta_n the angle between q and k_n
+ *               (cos := 0 when a norm is 0)
+ *   u(n)      = P[Binomial(L, P(n)) >= T], clamped to >= 1e-30
+ *   l(n)      = sm_scale * q.k_n - ln u(n)
+ *   out       = sum_{n in S} softmax(l)_n v_n,  lse = ln sum_{n in S} exp l(n)
+ *               (S empty: out = 0, lse = -inf)
+ *   Query head h reads kv head h / G.
+ *
+ * Conventions for every entry point:
+ *   - Every pointer argument is DEVICE memory owned by the caller, except
+ *     `stream`, which is a hipStream_t handle (NULL = the null stream).  The
+ *     library allocates nothing and keeps no state between calls; calls on
+ *     different streams may run concurrently if they use separate outputs and
+ *     workspaces.
+ *   - All arrays are dense, row-major (last index fastest), 16-byte aligned.
+ *   - Work is enqueued on `stream` and the call returns without waiting.
+ *     The returned status covers argument checks (made before anything is
+ *     enqueued; on error nothing is launched and no output is touched) and
+ *     launch errors; a fault during execution shows at the caller's next
+ *     synchronisation.
+ *   - Required outputs are fully written.  Optional outputs (may be NULL) are
+ *     written only when non-NULL.
+ *   - dtype: LSH_BF16 or LSH_F32, the element type of keys, values, q and W.
+ *     Projections and dot products accumulate in fp32; outputs are fp32.
+ */
+#ifndef LSH_ATTN_H
+#define LSH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LSH_OK = 0,
+  LSH_ERR_INVALID_ARG = 1,  /* null required pointer, bad size or parameter */
+  LSH_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. d != 128)   */
+  LSH_ERR_WORKSPACE = 3,    /* workspace_bytes below the size query        */
+  LSH_ERR_HIP = 4           /* a HIP runtime call or launch failed          */
+} lsh_status;
+
+typedef enum { LSH_F32 = 0, LSH_BF16 = 1 } lsh_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* lsh_status_string(int status);
+
+/* Number of key chunks of a table: ceil(N / stride). */
+int lsh_num_chunks(int N, int stride);
+
+/* A chunk stride for N keys and K bits: the smallest power of two >= 256
+ * giving at most 8 chunks, doubled while the chunk bounds would exceed about
+ * a tenth of the index array ((nchunks + 1) * 2^K * 10 > N, with nchunks > 1)
+ * or the build's limit (nchunks * 2^K > 32768), capped at 65536.  Any valid
+ * stride gives the same offsets and indices; the stride only sets the bounds
+ * array and the decode's work split.  Returns 0 for N < 1 or K outside 0..15. */
+int lsh_default_stride(int N, int K);
+
+/* ------------------------------------------------------------------------
+ * Table build
+ *
+ * Size limits: B, Hkv, N >= 1; d == 128 (else LSH_ERR_UNSUPPORTED);
+ * 0 <= K <= 15; 1 <= L <= 255; stride a power of two in [256, 65536] with
+ * ceil(N / stride) * 2^K <= 32768 (else LSH_ERR_UNSUPPORTED);
+ * B*Hkv*L*N < 2^40 and N < 2^31.
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of device workspace lsh_build_tables needs (0 on invalid sizes). */
+size_t lsh_build_workspace_size(int B, int Hkv, int N, int d, int K, int L,
+                                int stride, int dtype);
+
+/*
+ * keys     [B, Hkv, N, d]  dtype        key cache of every (sequence, kv head)
+ * W        [d, L*K]        dtype        SimHash projection, shared by all heads
+ * offsets  [B, Hkv, L, 2^K + 1] int32   out: bucket c of table l of unit (b,g) is
+ *                                       indices[b,g,l, offsets[c] : offsets[c+1]]
+ * indices  [B, Hkv, L, N]  int32        out: key indices grouped by bucket,
+ *                                       ascending inside each bucket
+ * bounds   [B, Hkv, L, 2^K, nchunks + 1] int32
+ *                                       out: bounds[..,c,j] = position of the first
+ *                                       entry of bucket c with key index
+ *                                       >= j*stride (bucket end if none), so the
+ *                                       keys of chunk j in bucket c are
+ *                                       indices[.., bounds[c,j] : bounds[c,j+1]];
+ *                                       nchunks = lsh_num_chunks(N, stride)
+ * key_codes [B, Hkv, L, N] uint16       optional out: code_l(k_n)
+ * workspace                             device scratch of the queried size
+ */
+lsh_status lsh_build_tables(const void* keys, const void* W,
+                            int B, int Hkv, int N, int d, int K, int L,
+                            int stride, int dtype,
+                            int32_t* offsets, int32_t* indices, int32_t* bounds,
+                            uint16_t* key_codes,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode
+ *
+ * Size limits: those of the build, plus Hq >= 1, Hq % Hkv == 0,
+ * G = Hq / Hkv <= 16, 1 <= T <= L and a finite sm_scale.
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of device workspace lsh_decode_attention needs (0 on invalid sizes). */
+size_t lsh_decode_workspace_size(int B, int Hq, int Hkv, int N, int d, int K,
+                                 int L, int stride);
+
+/*
+ * q        [B, Hq, d]      dtype        one decode query per head
+ * keys, values [B, Hkv, N, d] dtype     the cache the tables were built from
+ * W        [d, L*K]        dtype        the build's projection
+ * indices, bounds                       the build's outputs (same stride)
+ * out      [B, Hq, d]      float        out: the estimate
+ * lse      [B, Hq]         float        optional out: natural-log log-sum-exp
+ * nsel     [B, Hq]         int32        optional out: |S|
+ * q_codes  [B, Hq, L]      uint16       optional out: code_l(q)
+ * counts   [B, Hq, N]      uint8        optional out: collision counts c(n)
+ */
+lsh_status lsh_decode_attention(const void* q, const void* keys,
+                                const void* values, const void* W,
+                                const int32_t* indices, const int32_t* bounds,
+                                int B, int Hq, int Hkv, int N, int d, int K,
+                                int L, int T, int stride, float sm_scale,
+                                int dtype,
+                                float* out, float* lse, int32_t* nsel,
+                                uint16_t* q_codes, uint8_t* counts,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSH_ATTN_H */

@@ -1,0 +1,212 @@
+"""Python binding of liblsh_attn.so (LSH-sampled decode attention, gfx950).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels; this module checks tensor shapes and dtypes, allocates outputs and
+workspaces with PyTorch, and passes raw device pointers and the current HIP
+stream across the C ABI declared in ``include/lsh_attn.h``.  If the shared
+library is missing, every call raises: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblsh_attn.so")
+
+LSH_OK, LSH_ERR_INVALID_ARG, LSH_ERR_UNSUPPORTED, LSH_ERR_WORKSPACE, LSH_ERR_HIP = range(5)
+LSH_F32, LSH_BF16 = 0, 1
+
+EXPORTS = (
+    "lsh_status_string",
+    "lsh_num_chunks",
+    "lsh_default_stride",
+    "lsh_build_workspace_size",
+    "lsh_build_tables",
+    "lsh_decode_workspace_size",
+    "lsh_decode_attention",
+)
+
+_lib = None
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+
+def lib():
+    """Load the shared library once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m lsh_sampled_sparse_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.lsh_status_string.restype = ctypes.c_char_p
+        L.lsh_status_string.argtypes = [_i]
+        L.lsh_num_chunks.restype = _i
+        L.lsh_num_chunks.argtypes = [_i, _i]
+        L.lsh_default_stride.restype = _i
+        L.lsh_default_stride.argtypes = [_i, _i]
+        L.lsh_build_workspace_size.restype = _sz
+        L.lsh_build_workspace_size.argtypes = [_i] * 8
+        L.lsh_build_tables.restype = _i
+        L.lsh_build_tables.argtypes = [_p, _p] + [_i] * 8 + [_p, _p, _p, _p, _p, _sz, _p]
+        L.lsh_decode_workspace_size.restype = _sz
+        L.lsh_decode_workspace_size.argtypes = [_i] * 8
+        L.lsh_decode_attention.restype = _i
+        L.lsh_decode_attention.argtypes = ([_p] * 6 + [_i] * 9 + [ctypes.c_float, _i]
+                                           + [_p] * 6 + [_sz, _p])
+        _lib = L
+    return _lib
+
+
+class LshError(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__(lsh_status_string(status))
+
+
+def _check(status):
+    if status != LSH_OK:
+        raise LshError(status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return LSH_BF16
+    if dt == torch.float32:
+        return LSH_F32
+    raise TypeError(f"unsupported dtype {dt}; use bfloat16 or float32")
+
+
+# ------------------------------------------------------------------ C-ABI names
+
+def lsh_status_string(status: int) -> str:
+    return lib().lsh_status_string(int(status)).decode()
+
+
+def lsh_num_chunks(N: int, stride: int) -> int:
+    return lib().lsh_num_chunks(int(N), int(stride))
+
+
+def lsh_default_stride(N: int, K: int) -> int:
+    return lib().lsh_default_stride(int(N), int(K))
+
+
+def lsh_build_workspace_size(B, Hkv, N, d, K, L, stride, dtype) -> int:
+    return lib().lsh_build_workspace_size(B, Hkv, N, d, K, L, stride, dtype)
+
+
+def lsh_decode_workspace_size(B, Hq, Hkv, N, d, K, L, stride) -> int:
+    return lib().lsh_decode_workspace_size(B, Hq, Hkv, N, d, K, L, stride)
+
+
+def lsh_build_tables(keys, W, K, L, stride, offsets, indices, bounds, key_codes=None,
+                     workspace=None):
+    """Marshal tensors to ``lsh_build_tables``; outputs are filled in place.
+
+    keys [B, Hkv, N, d], W [d, L*K] (bf16 or fp32, contiguous, on the GPU).
+    """
+    B, Hkv, N, d = keys.shape
+    dt = _dtype_code(keys.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(1, lsh_build_workspace_size(B, Hkv, N, d, K, L, stride, dt)),
+                                dtype=torch.uint8, device=keys.device)
+    _check(lib().lsh_build_tables(
+        _ptr(keys), _ptr(W), B, Hkv, N, d, K, L, stride, dt,
+        _ptr(offsets), _ptr(indices), _ptr(bounds), _ptr(key_codes),
+        _ptr(workspace), workspace.numel(), _stream(keys.device)))
+
+
+def lsh_decode_attention(q, keys, values, W, indices, bounds, K, L, T, stride, sm_scale, out,
+                         lse=None, nsel=None, q_codes=None, counts=None, workspace=None):
+    """Marshal tensors to ``lsh_decode_attention``; outputs are filled in place."""
+    B, Hq, d = q.shape
+    _, Hkv, N, _ = keys.shape
+    dt = _dtype_code(keys.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(1, lsh_decode_workspace_size(B, Hq, Hkv, N, d, K, L, stride)),
+                                dtype=torch.uint8, device=keys.device)
+    _check(lib().lsh_decode_attention(
+        _ptr(q), _ptr(keys), _ptr(values), _ptr(W), _ptr(indices), _ptr(bounds),
+        B, Hq, Hkv, N, d, K, L, T, stride, ctypes.c_float(sm_scale), dt,
+        _ptr(out), _ptr(lse), _ptr(nsel), _ptr(q_codes), _ptr(counts),
+        _ptr(workspace), workspace.numel(), _stream(keys.device)))
+
+
+# ------------------------------------------------------------------ convenience
+
+def _require(t, name, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def build_tables(keys, W, K, L, stride=None, return_codes=False):
+    """Build the bucket tables of every (sequence, kv head).
+
+    Returns dict: offsets [B,Hkv,L,2^K+1], indices [B,Hkv,L,N],
+    bounds [B,Hkv,L,2^K,nchunks+1] (int32), stride, and codes [B,Hkv,L,N]
+    (int16 view of uint16) when ``return_codes``.
+    """
+    _require(keys, "keys")
+    _require(W, "W", keys.dtype)
+    B, Hkv, N, d = keys.shape
+    if tuple(W.shape) != (d, L * K):
+        raise ValueError(f"W must be [{d}, {L * K}], got {tuple(W.shape)}")
+    if stride is None:
+        stride = lsh_default_stride(N, K)
+    nch = lsh_num_chunks(N, stride)
+    dev = keys.device
+    offsets = torch.empty(B, Hkv, L, (1 << K) + 1, dtype=torch.int32, device=dev)
+    indices = torch.empty(B, Hkv, L, N, dtype=torch.int32, device=dev)
+    bounds = torch.empty(B, Hkv, L, 1 << K, nch + 1, dtype=torch.int32, device=dev)
+    codes = torch.empty(B, Hkv, L, N, dtype=torch.int16, device=dev) if return_codes else None
+    lsh_build_tables(keys, W, K, L, stride, offsets, indices, bounds, codes)
+    res = {"offsets": offsets, "indices": indices, "bounds": bounds, "stride": stride}
+    if return_codes:
+        res["codes"] = codes
+    return res
+
+
+def decode_attention(q, keys, values, W, tables, K, L, T, sm_scale=None, return_codes=False,
+                     return_counts=False, workspace=None):
+    """One decode step.  Returns dict: out [B,Hq,d] fp32, lse [B,Hq], nsel [B,Hq],
+    and q_codes [B,Hq,L] / counts [B,Hq,N] (uint8) when requested."""
+    for name, t in (("q", q), ("keys", keys), ("values", values)):
+        _require(t, name, keys.dtype)
+    B, Hq, d = q.shape
+    _, Hkv, N, _ = keys.shape
+    if tuple(values.shape) != tuple(keys.shape) or keys.shape[0] != B or keys.shape[3] != d:
+        raise ValueError("q [B,Hq,d] and keys/values [B,Hkv,N,d] disagree")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    dev = keys.device
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    nsel = torch.empty(B, Hq, dtype=torch.int32, device=dev)
+    qc = torch.empty(B, Hq, L, dtype=torch.int16, device=dev) if return_codes else None
+    cnt = torch.empty(B, Hq, N, dtype=torch.uint8, device=dev) if return_counts else None
+    lsh_decode_attention(q, keys, values, W, tables["indices"], tables["bounds"], K, L, T,
+                         tables["stride"], sm_scale, out, lse, nsel, qc, cnt, workspace)
+    res = {"out": out, "lse": lse, "nsel": nsel}
+    if return_codes:
+        res["q_codes"] = qc
+    if return_counts:
+        res["counts"] = cnt
+    return res

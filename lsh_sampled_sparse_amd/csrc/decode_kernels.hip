@@ -1,0 +1,569 @@
+// Decode-side kernels for gfx950.
+//
+// One decode step of MagicPIG's LSH sampling ("MagicPIG: LSH Sampling for
+// Efficient LLM Generation", GrooveSquid summary; MagicPIG project summary on
+// sourcepulse, "How It Works") runs as four launches on one stream:
+//   qhash          SimHash codes of every query head (same W and sign rule as
+//                  the keys); extra workgroups fill the ln-u correction table
+//   count_select   per (query head, key chunk): probe the head's L buckets,
+//                  restricted to the chunk through the build's chunk bounds,
+//                  count collisions in LDS byte counters, and emit the
+//                  selection bitmask (count >= T)
+//   attend         per (sequence, kv head, context split): union of the
+//                  group's selections, ballot compaction, gathered K rows,
+//                  q.k on MFMA, 1/u weights, online softmax and P.V in fp32,
+//                  partial state (m, l, acc) per query head
+//   merge          log-sum-exp merge of the split partials (the stable merge
+//                  MAC-Attention also uses, "MAC-Attention" README,
+//                  "How It Works")
+#include <math.h>
+
+#include "lsh_device.h"
+#include "lsh_kernels.h"
+
+namespace lsh {
+
+constexpr float kPi = 3.14159265358979323846f;
+constexpr float kLnUFloor = -69.07755278982137f;   // ln(1e-30)
+
+// ---------------------------------------------------------------------------
+// ln u correction table.
+//
+// u(theta) = P[Binomial(L, P) >= T] with P = (1 - theta/pi)^K.  Writing
+// ln u = T ln P + g(P),  g(P) = ln sum_{i>=T} C(L,i) P^(i-T) (1-P)^(L-i),
+// g is smooth on [0, 1] (g(0) = ln C(L,T), g(1) = 0), so it is tabulated in
+// fp64 at theta_j = j pi / kLnuTable and interpolated linearly; T ln P is
+// evaluated exactly from ln p = log1p(-theta/pi).
+// ---------------------------------------------------------------------------
+__device__ double lnu_correction(double theta, int K, int L, int T) {
+  const double p = 1.0 - theta / 3.14159265358979323846;
+  const double P = (K == 0) ? 1.0 : pow(p, static_cast<double>(K));
+  const double lP = log(P), lQ = log1p(-P);
+  const double lgL = lgamma(static_cast<double>(L) + 1.0);
+  // streaming log-sum-exp over the terms i = T..L
+  double m = -INFINITY, s = 0.0;
+  for (int i = T; i <= L; ++i) {
+    double t = lgL - lgamma(static_cast<double>(i) + 1.0) - lgamma(static_cast<double>(L - i) + 1.0);
+    if (i > T) t += (i - T) * lP;
+    if (L > i) t += (L - i) * lQ;
+    if (t == -INFINITY) continue;
+    if (t > m) {
+      s = s * exp(m - t) + 1.0;
+      m = t;
+    } else {
+      s += exp(t - m);
+    }
+  }
+  return m + log(s);
+}
+
+__device__ __forceinline__ float log_inclusion(float cosv, const float* tab, float TK) {
+  const float c = fminf(1.f, fmaxf(-1.f, cosv));
+  const float th = acosf(c);
+  const float x = th * (static_cast<float>(kLnuTable) / kPi);
+  const int j = min(static_cast<int>(x), kLnuTable - 1);
+  const float fr = x - static_cast<float>(j);
+  const float g = fmaf(fr, tab[j + 1] - tab[j], tab[j]);
+  const float lnp = log1pf(-th * (1.0f / kPi));
+  return fmaxf(fmaf(TK, lnp, g), kLnUFloor);
+}
+
+// ---------------------------------------------------------------------------
+// qhash: codes of up to 4 query heads x a block of whole tables per workgroup.
+// Workgroups with blockIdx.y >= head_blocks fill the ln-u table instead.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void qhash_kernel(const typename T::storage* __restrict__ q,
+                                                    const typename T::storage* __restrict__ W,
+                                                    uint16_t* __restrict__ qcodes, float* __restrict__ lnu_tab,
+                                                    int BH, int K, int L, int Tth, int head_blocks) {
+  __shared__ float qs[4][kHeadDim];
+  __shared__ uint8_t sgn[4][256];
+  const int tid = threadIdx.x;
+  if (static_cast<int>(blockIdx.y) >= head_blocks) {
+    const int j = ((blockIdx.y - head_blocks) * gridDim.x + blockIdx.x) * 256 + tid;
+    if (j <= kLnuTable && K > 0)
+      lnu_tab[j] = static_cast<float>(lnu_correction(j * (3.14159265358979323846 / kLnuTable), K, L, Tth));
+    return;
+  }
+  const int h0 = blockIdx.y * 4;
+  if (K == 0) {
+    for (int e = blockIdx.x * 256 + tid; e < 4 * L; e += gridDim.x * 256) {
+      const int h = h0 + e / L;
+      if (h < BH) qcodes[static_cast<size_t>(h) * L + e % L] = 0;
+    }
+    return;
+  }
+  const int tpw = 256 / K;              // whole tables per workgroup
+  const int l0 = blockIdx.x * tpw;
+  for (int e = tid; e < 4 * kHeadDim; e += 256) {
+    const int h = h0 + e / kHeadDim;
+    float v = 0.f;
+    if (h < BH) {
+      if constexpr (sizeof(typename T::storage) == 2)
+        v = bf16_to_f32(q[static_cast<size_t>(h) * kHeadDim + e % kHeadDim]);
+      else
+        v = q[static_cast<size_t>(h) * kHeadDim + e % kHeadDim];
+    }
+    qs[e / kHeadDim][e % kHeadDim] = v;
+  }
+  __syncthreads();
+  const int LK = L * K;
+  const int col = l0 * K + tid;
+  if (tid < tpw * K && col < LK) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kHeadDim; ++i) {
+      float w;
+      if constexpr (sizeof(typename T::storage) == 2)
+        w = bf16_to_f32(W[static_cast<size_t>(i) * LK + col]);
+      else
+        w = W[static_cast<size_t>(i) * LK + col];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = fmaf(qs[j][i], w, acc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sgn[j][tid] = acc[j] > 0.f ? 1 : 0;
+  }
+  __syncthreads();
+  if (tid < 4 * tpw) {
+    const int j = tid / tpw, t = tid % tpw;
+    const int l = l0 + t, h = h0 + j;
+    if (h < BH && l < L) {
+      uint32_t code = 0;
+      for (int b = 0; b < K; ++b) code |= static_cast<uint32_t>(sgn[j][t * K + b]) << b;
+      qcodes[static_cast<size_t>(h) * L + l] = static_cast<uint16_t>(code);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// count_select: one workgroup per (query head, key chunk).
+// ---------------------------------------------------------------------------
+constexpr int kCountThreads = 256;
+
+__global__ __launch_bounds__(kCountThreads) void count_select_kernel(
+    const uint16_t* __restrict__ qcodes,   // [BH][L]
+    const int32_t* __restrict__ indices,   // [U][L][N]
+    const int32_t* __restrict__ bounds,    // [U][L][2^K][nJ + 1]
+    int Hq, int Hkv, int N, int K, int L, int T, int stride_log2, int nJ,
+    uint32_t* __restrict__ bitmask,        // [BH][Nw]
+    int32_t* __restrict__ chunk_nsel,      // [BH][nJ]
+    uint8_t* __restrict__ counts) {        // optional [BH][N]
+  extern __shared__ __attribute__((aligned(16))) uint32_t cnt[];   // one byte per key of the chunk
+  __shared__ int seg_start[256];
+  __shared__ int seg_v[257];
+  __shared__ int wave_tot[kCountThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int J = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / Hq, h = bh % Hq, G = Hq / Hkv;
+  const int u = b * Hkv + h / G;
+  const int nb = 1 << K;
+  const int cbeg = J << stride_log2;
+  const int clen = min(1 << stride_log2, N - cbeg);
+  const int cwords = (clen + 3) >> 2;
+
+  for (int i = tid; i < cwords; i += kCountThreads) cnt[i] = 0;
+
+  // segment of bucket qcode_l restricted to this chunk, for every table l
+  int len = 0;
+  if (tid < L) {
+    const int qc = qcodes[static_cast<size_t>(bh) * L + tid];
+    const int32_t* bp = bounds + ((static_cast<size_t>(u) * L + tid) * nb + qc) * (nJ + 1) + J;
+    const int s = bp[0];
+    len = bp[1] - s;
+    seg_start[tid] = s;
+  }
+  int incl = len;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int w = 0; w < wave; ++w) wbase += wave_tot[w];
+  seg_v[tid + 1] = wbase + incl;
+  if (tid == 0) seg_v[0] = 0;
+  __syncthreads();
+
+  const int total = seg_v[L];
+  const int32_t* ib = indices + static_cast<size_t>(u) * L * N;
+  int l = 0;
+  for (int v = tid; v < total; v += kCountThreads) {
+    while (v >= seg_v[l + 1]) ++l;
+    const int n = ib[static_cast<size_t>(l) * N + seg_start[l] + (v - seg_v[l])];
+    const int loc = n - cbeg;
+    atomicAdd(&cnt[loc >> 2], 1u << ((loc & 3) * 8));
+  }
+  __syncthreads();
+
+  const int Nw = (N + 31) >> 5;
+  const int nwords = (clen + 31) >> 5;
+  int mysel = 0;
+  for (int w = tid; w < nwords; w += kCountThreads) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int wi = w * 8 + j;
+      const uint32_t c4 = wi < cwords ? cnt[wi] : 0u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int key = w * 32 + j * 4 + k;
+        if (key < clen && static_cast<int>((c4 >> (8 * k)) & 0xffu) >= T) m |= 1u << (j * 4 + k);
+      }
+    }
+    bitmask[static_cast<size_t>(bh) * Nw + (cbeg >> 5) + w] = m;
+    mysel += __builtin_popcount(m);
+  }
+  if (counts) {
+    const uint8_t* c8 = reinterpret_cast<const uint8_t*>(cnt);
+    uint8_t* dst = counts + static_cast<size_t>(bh) * N + cbeg;
+    for (int i = tid; i < clen; i += kCountThreads) dst[i] = c8[i];
+  }
+  mysel = wave_sum_int(mysel);
+  __syncthreads();
+  if (lane == 0) wave_tot[wave] = mysel;
+  __syncthreads();
+  if (tid == 0) {
+    int s = 0;
+    for (int w = 0; w < kCountThreads / 64; ++w) s += wave_tot[w];
+    chunk_nsel[static_cast<size_t>(bh) * nJ + J] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attend: one workgroup (4 waves) per (sequence, kv head, context split).
+// ---------------------------------------------------------------------------
+constexpr int kAttThreads = 256;
+constexpr int kRing = 128;              // per-wave ring of selected keys
+
+template <typename T>
+struct VRow;
+template <>
+struct VRow<BF16> {   // 8 consecutive dims of one value row
+  u32x4_t w;
+  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const u32x4_t*>(p); }
+  __device__ __forceinline__ float get(int k) const {
+    const uint32_t x = w[k >> 1];
+    return (k & 1) ? bf16_hi(x) : bf16_lo(x);
+  }
+};
+template <>
+struct VRow<F32> {
+  floatx4_t a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const floatx4_t*>(p)[0];
+    b = reinterpret_cast<const floatx4_t*>(p)[1];
+  }
+  __device__ __forceinline__ float get(int k) const { return k < 4 ? a[k & 3] : b[k & 3]; }
+};
+
+template <typename T>
+__device__ __forceinline__ float frag_sumsq(const Frag<T>& f);
+template <>
+__device__ __forceinline__ float frag_sumsq<BF16>(const Frag<BF16>& f) {
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = static_cast<float>(f.v[k][j]);
+      s = fmaf(x, x, s);
+    }
+  return s;
+}
+template <>
+__device__ __forceinline__ float frag_sumsq<F32>(const Frag<F32>& f) {
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) s = fmaf(f.v[k], f.v[k], s);
+  return s;
+}
+
+__device__ __forceinline__ void wave_lds_fence() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <typename T, int GM>
+__global__ __launch_bounds__(kAttThreads) void attend_kernel(
+    const typename T::storage* __restrict__ q,       // [B][Hq][128]
+    const typename T::storage* __restrict__ keys,    // [U][N][128]
+    const typename T::storage* __restrict__ values,  // [U][N][128]
+    const uint32_t* __restrict__ bitmask,            // [BH][Nw]
+    const float* __restrict__ lnu_tab,               // [kLnuTable + 1]
+    int Hq, int Hkv, int N, int K, int Tth, float scale, int split_len, int nsplit,
+    float* __restrict__ partials) {                  // [BH][nsplit][130]
+  using S = typename T::storage;
+  __shared__ float tab[kLnuTable + 1];
+  __shared__ float qn[16];
+  __shared__ int sidx[4][kRing];
+  __shared__ uint16_t shm[4][kRing];
+  __shared__ float pbuf[4][16][16];     // [wave][key slot][head]
+  __shared__ float abuf[4][16];         // [wave][head]
+  __shared__ float wm[4][16], wl[4][16];
+  __shared__ float wacc[4][GM][kHeadDim];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s = blockIdx.x, u = blockIdx.y;
+  const int G = Hq / Hkv;
+  const int b = u / Hkv, g = u % Hkv;
+  const int bh0 = b * Hq + g * G;
+  const int Nw = (N + 31) >> 5;
+  const S* kb = keys + static_cast<size_t>(u) * N * kHeadDim;
+  const S* vb = values + static_cast<size_t>(u) * N * kHeadDim;
+  const bool k0 = (K == 0);
+  const float TK = static_cast<float>(Tth * K);
+
+  for (int i = tid; i <= kLnuTable; i += kAttThreads) tab[i] = k0 ? 0.f : lnu_tab[i];
+  // query fragments: lane holds head (lane & 15), dims [32 (lane >> 4), +32)
+  const int qh = lane & 15;
+  Frag<T> Qf;
+  Qf.load(q + static_cast<size_t>(bh0 + (qh < G ? qh : 0)) * kHeadDim + (lane >> 4) * 32, qh < G);
+  if (wave == 0) {
+    float ss = frag_sumsq<T>(Qf);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    if (lane < 16) qn[lane] = sqrtf(ss);
+  }
+  __syncthreads();
+
+  const int sb = s * split_len;
+  const int se = min(N, sb + split_len);
+  const int wq = split_len / 4;
+  const int wb = min(se, sb + wave * wq), we = min(se, sb + (wave + 1) * wq);
+
+  const int grp = lane >> 4, slot = lane & 15;
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.f; }
+  float acc[GM][8];
+#pragma unroll
+  for (int hh = 0; hh < GM; ++hh)
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[hh][d] = 0.f;
+
+  int head = 0, cnt = 0;    // ring state (wave-uniform)
+
+  auto process_tile = [&](int ntile) {
+    const bool has = slot < ntile;
+    const int e = (head + (has ? slot : 0)) & (kRing - 1);
+    const int idx = sidx[wave][e];
+    const int hmk = has ? static_cast<int>(shm[wave][e]) : 0;
+    Frag<T> Kf;
+    Kf.load(kb + static_cast<size_t>(idx) * kHeadDim + grp * 32, true);
+    VRow<T> vr[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int vidx = __shfl(idx, grp + 4 * t);
+      vr[t].load(vb + static_cast<size_t>(vidx) * kHeadDim + slot * 8);
+    }
+    floatx4_t sc = {0.f, 0.f, 0.f, 0.f};
+    sc = Qf.mma(Kf, sc);     // sc[i] = q[head 4 grp + i] . k[slot]
+    float kss = frag_sumsq<T>(Kf);
+    kss += __shfl_xor(kss, 16);
+    kss += __shfl_xor(kss, 32);
+    const float kn = sqrtf(kss);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 4 * grp + i;
+      const bool valid = hh < G && ((hmk >> hh) & 1);
+      float logit = -INFINITY;
+      if (valid) {
+        const float x = sc[i];
+        const float nn = qn[hh] * kn;
+        const float cs = nn > 0.f ? x / nn : 0.f;
+        logit = scale * x - (k0 ? 0.f : log_inclusion(cs, tab, TK));
+      }
+      const float mt = row16_max(logit);
+      const float mnew = fmaxf(m_run[i], mt);
+      const float alpha = (mnew == -INFINITY) ? 1.f : __expf(m_run[i] - mnew);
+      p[i] = (logit == -INFINITY) ? 0.f : __expf(logit - mnew);
+      l_run[i] = l_run[i] * alpha + row16_sum(p[i]);
+      m_run[i] = mnew;
+      if (slot == 0) abuf[wave][hh] = alpha;
+      pbuf[wave][slot][hh] = p[i];
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int hh = 0; hh < GM; ++hh) {
+      if (hh < G) {
+        const float a = abuf[wave][hh];
+        if (a != 1.f) {
+#pragma unroll
+          for (int d = 0; d < 8; ++d) acc[hh][d] *= a;
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int j = grp + 4 * t;
+#pragma unroll
+      for (int hh = 0; hh < GM; ++hh) {
+        const float pj = pbuf[wave][j][hh];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc[hh][d] = fmaf(pj, vr[t].get(d), acc[hh][d]);
+      }
+    }
+    wave_lds_fence();
+  };
+
+  for (int blk = wb; blk < we; blk += 64) {
+    const int n = blk + lane;
+    const int w0 = blk >> 5;
+    int hm = 0;
+    for (int hh = 0; hh < G; ++hh) {
+      const uint32_t* bm = bitmask + static_cast<size_t>(bh0 + hh) * Nw;
+      const uint32_t lo = bm[w0];
+      const uint32_t hi = (w0 + 1 < Nw) ? bm[w0 + 1] : 0u;
+      const uint32_t word = lane < 32 ? lo : hi;
+      hm |= static_cast<int>((word >> (lane & 31)) & 1u) << hh;
+    }
+    const bool any = (n < we) && hm != 0;
+    const uint64_t bal = ballot(any);
+    if (any) {
+      const int e = (head + cnt + mbcnt(bal)) & (kRing - 1);
+      sidx[wave][e] = n;
+      shm[wave][e] = static_cast<uint16_t>(hm);
+    }
+    cnt += __builtin_popcountll(bal);
+    wave_lds_fence();
+    while (cnt >= 16) {
+      process_tile(16);
+      head = (head + 16) & (kRing - 1);
+      cnt -= 16;
+    }
+  }
+  if (cnt > 0) {
+    process_tile(cnt);
+    head = (head + cnt) & (kRing - 1);
+    cnt = 0;
+  }
+
+  // combine the four lane groups (each summed a quarter of every tile's keys)
+#pragma unroll
+  for (int hh = 0; hh < GM; ++hh)
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      acc[hh][d] += __shfl_xor(acc[hh][d], 16);
+      acc[hh][d] += __shfl_xor(acc[hh][d], 32);
+    }
+  if (slot == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wm[wave][4 * grp + i] = m_run[i];
+      wl[wave][4 * grp + i] = l_run[i];
+    }
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int hh = 0; hh < GM; ++hh)
+#pragma unroll
+      for (int d = 0; d < 8; ++d) wacc[wave][hh][slot * 8 + d] = acc[hh][d];
+  }
+  __syncthreads();
+  for (int e = tid; e < G * kHeadDim; e += kAttThreads) {
+    const int hh = e / kHeadDim, d = e % kHeadDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][hh]);
+    float A = 0.f, Lm = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (wm[w][hh] == -INFINITY) continue;
+        const float f = __expf(wm[w][hh] - M);
+        A = fmaf(wacc[w][hh][d], f, A);
+        Lm = fmaf(wl[w][hh], f, Lm);
+      }
+    }
+    float* dst = partials + (static_cast<size_t>(bh0 + hh) * nsplit + s) * kPartialStride;
+    dst[d] = A;
+    if (d == 0) {
+      dst[kHeadDim] = M;
+      dst[kHeadDim + 1] = Lm;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge: one workgroup per query head.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kHeadDim) void merge_kernel(const float* __restrict__ partials,
+                                                         const int32_t* __restrict__ chunk_nsel,
+                                                         int nsplit, int nJ, float* __restrict__ out,
+                                                         float* __restrict__ lse, int32_t* __restrict__ nsel) {
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const float* P = partials + static_cast<size_t>(bh) * nsplit * kPartialStride;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, P[s * kPartialStride + kHeadDim]);
+  float A = 0.f, Lm = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < nsplit; ++s) {
+      const float ms = P[s * kPartialStride + kHeadDim];
+      if (ms == -INFINITY) continue;
+      const float f = __expf(ms - M);
+      A = fmaf(P[s * kPartialStride + d], f, A);
+      Lm = fmaf(P[s * kPartialStride + kHeadDim + 1], f, Lm);
+    }
+  }
+  out[static_cast<size_t>(bh) * kHeadDim + d] = (M == -INFINITY) ? 0.f : A / Lm;
+  if (d == 0) {
+    if (lse) lse[bh] = (M == -INFINITY) ? -INFINITY : M + logf(Lm);
+    if (nsel) {
+      int t = 0;
+      for (int j = 0; j < nJ; ++j) t += chunk_nsel[static_cast<size_t>(bh) * nJ + j];
+      nsel[bh] = t;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launcher
+// ---------------------------------------------------------------------------
+template <typename T, int GM>
+static void launch_attend(const DecodeArgs& a, hipStream_t stream) {
+  using S = typename T::storage;
+  hipLaunchKernelGGL((attend_kernel<T, GM>), dim3(a.nsplit, a.B * a.Hkv), dim3(kAttThreads), 0, stream,
+                     static_cast<const S*>(a.q), static_cast<const S*>(a.keys),
+                     static_cast<const S*>(a.values), a.bitmask, a.lnu_table, a.Hq, a.Hkv, a.N, a.K,
+                     a.T, a.scale, a.split_len, a.nsplit, a.partials);
+}
+
+template <typename T>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  using S = typename T::storage;
+  const int BH = a.B * a.Hq;
+  const int head_blocks = (BH + 3) / 4;
+  const int tpw = a.K > 0 ? 256 / a.K : 256;
+  const int xblocks = (a.L + tpw - 1) / tpw;
+  const int tab_blocks = (kLnuTable + 1 + xblocks * 256 - 1) / (xblocks * 256);
+  hipLaunchKernelGGL(qhash_kernel<T>, dim3(xblocks, head_blocks + tab_blocks), dim3(256), 0, stream,
+                     static_cast<const S*>(a.q), static_cast<const S*>(a.W), a.qcodes, a.lnu_table, BH,
+                     a.K, a.L, a.T, head_blocks);
+  const size_t lds = ((static_cast<size_t>(1) << a.stride_log2) + 3) & ~static_cast<size_t>(3);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(count_select_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(count_select_kernel, dim3(a.nJ, BH), dim3(kCountThreads), lds, stream, a.qcodes,
+                     a.indices, a.bounds, a.Hq, a.Hkv, a.N, a.K, a.L, a.T, a.stride_log2, a.nJ, a.bitmask,
+                     a.chunk_nsel, a.counts);
+  const int G = a.Hq / a.Hkv;
+  if (G <= 4)
+    launch_attend<T, 4>(a, stream);
+  else if (G <= 8)
+    launch_attend<T, 8>(a, stream);
+  else
+    launch_attend<T, 16>(a, stream);
+  hipLaunchKernelGGL(merge_kernel, dim3(BH), dim3(kHeadDim), 0, stream, a.partials, a.chunk_nsel,
+                     a.nsplit, a.nJ, a.out, a.lse, a.nsel);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  return a.dtype == 1 ? launch_decode_t<BF16>(a, stream) : launch_decode_t<F32>(a, stream);
+}
+
+}  // namespace lsh

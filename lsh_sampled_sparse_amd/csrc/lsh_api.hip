@@ -1,0 +1,225 @@
+// C ABI of the LSH-sampled decode-attention library: argument checks,
+// workspace layout and launch order.  Declarations and the definitions of
+// every operation are in include/lsh_attn.h.
+#include <stdint.h>
+
+#include <cmath>
+
+#include "../../include/lsh_attn.h"
+#include "lsh_kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxStrideLog2 = 16;
+constexpr int kMinStrideLog2 = 8;
+constexpr int kMaxDirEntries = 32768;   // nchunks * 2^K held in LDS by the bucket build
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+int ilog2_exact(int x) {
+  if (x <= 0 || (x & (x - 1))) return -1;
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+struct Geometry {
+  int stride_log2 = 0, nJ = 0, spc_log2 = 0, LKpad = 0;
+};
+
+// Checks shared by build and decode.  Returns LSH_OK and fills `g`.
+lsh_status check_common(int B, int Hkv, int N, int d, int K, int L, int stride, int dtype, Geometry* g) {
+  if (B < 1 || Hkv < 1 || N < 1 || d < 1 || L < 1 || L > 255 || K < 0 || K > 15)
+    return LSH_ERR_INVALID_ARG;
+  if (dtype != LSH_F32 && dtype != LSH_BF16) return LSH_ERR_INVALID_ARG;
+  const int sl = ilog2_exact(stride);
+  if (sl < 0) return LSH_ERR_INVALID_ARG;
+  if (d != 128) return LSH_ERR_UNSUPPORTED;
+  if (sl < kMinStrideLog2 || sl > kMaxStrideLog2) return LSH_ERR_UNSUPPORTED;
+  const long long units = static_cast<long long>(B) * Hkv;
+  if (units * L * static_cast<long long>(N) >= (1ll << 40)) return LSH_ERR_UNSUPPORTED;
+  const int nJ = lsh_num_chunks(N, stride);
+  if (static_cast<long long>(nJ) << K > kMaxDirEntries) return LSH_ERR_UNSUPPORTED;
+  g->stride_log2 = sl;
+  g->nJ = nJ;
+  // sub-chunks per chunk for the bucket build: aim for >= 16 sub-chunks (one
+  // per wave), each >= 64 keys, within the LDS budget
+  int spc = 0;
+  while ((nJ << (spc + 1)) <= 16 && (sl - spc - 1) >= 6 &&
+         (static_cast<long long>(nJ) << (spc + 1 + K)) <= kMaxDirEntries)
+    ++spc;
+  g->spc_log2 = spc;
+  const int LK = L * K;
+  g->LKpad = (LK + 63) / 64 * 64;
+  return LSH_OK;
+}
+
+int elem_bytes(int dtype) { return dtype == LSH_BF16 ? 2 : 4; }
+
+struct BuildLayout {
+  size_t wt = 0, codes = 0, total = 0;
+};
+
+BuildLayout build_layout(int B, int Hkv, int N, int K, int L, int dtype, const Geometry& g, bool need_codes) {
+  BuildLayout w;
+  size_t off = 0;
+  w.wt = off;
+  off = align_up(off + static_cast<size_t>(g.LKpad) * 128 * elem_bytes(dtype));
+  w.codes = off;
+  if (need_codes) off = align_up(off + static_cast<size_t>(B) * Hkv * L * N * sizeof(uint16_t));
+  w.total = off;
+  (void)K;
+  return w;
+}
+
+struct DecodeLayout {
+  size_t qcodes = 0, bitmask = 0, chunk_nsel = 0, lnu = 0, partials = 0, total = 0;
+  int split_len = 0, nsplit = 0;
+};
+
+DecodeLayout decode_layout(int B, int Hq, int Hkv, int N, int L, const Geometry& g) {
+  DecodeLayout w;
+  // context split: ~1024 workgroups over the (sequence, kv head) units, each a
+  // multiple of 256 keys
+  const long long units = static_cast<long long>(B) * Hkv;
+  long long per = (units * N + 1023) / 1024;
+  per = (per + 255) / 256 * 256;
+  if (per < 256) per = 256;
+  if (per > N) per = (static_cast<long long>(N) + 255) / 256 * 256;
+  w.split_len = static_cast<int>(per);
+  w.nsplit = static_cast<int>((N + per - 1) / per);
+  const size_t BH = static_cast<size_t>(B) * Hq;
+  size_t off = 0;
+  w.qcodes = off;     off = align_up(off + BH * L * sizeof(uint16_t));
+  w.bitmask = off;    off = align_up(off + BH * ((N + 31) / 32) * sizeof(uint32_t));
+  w.chunk_nsel = off; off = align_up(off + BH * g.nJ * sizeof(int32_t));
+  w.lnu = off;        off = align_up(off + (lsh::kLnuTable + 1) * sizeof(float));
+  w.partials = off;   off = align_up(off + BH * w.nsplit * lsh::kPartialStride * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+lsh_status hip_status(hipError_t e) { return e == hipSuccess ? LSH_OK : LSH_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* lsh_status_string(int status) {
+  switch (status) {
+    case LSH_OK: return "LSH_OK";
+    case LSH_ERR_INVALID_ARG: return "LSH_ERR_INVALID_ARG: invalid argument";
+    case LSH_ERR_UNSUPPORTED: return "LSH_ERR_UNSUPPORTED: valid but unsupported shape or parameter";
+    case LSH_ERR_WORKSPACE: return "LSH_ERR_WORKSPACE: workspace smaller than the size query";
+    case LSH_ERR_HIP: return "LSH_ERR_HIP: HIP runtime or launch error";
+    default: return "unknown lsh_status";
+  }
+}
+
+int lsh_num_chunks(int N, int stride) {
+  if (N < 1 || stride < 1) return 0;
+  return static_cast<int>((static_cast<long long>(N) + stride - 1) / stride);
+}
+
+int lsh_default_stride(int N, int K) {
+  if (N < 1 || K < 0 || K > 15) return 0;
+  long long stride = 1ll << kMinStrideLog2;
+  while (stride < (1ll << kMaxStrideLog2) && stride * 8 < N) stride *= 2;
+  auto chunks = [&](long long s) { return (N + s - 1) / s; };
+  while (stride < (1ll << kMaxStrideLog2) && chunks(stride) > 1 &&
+         ((chunks(stride) + 1) * (1ll << K) * 10 > N || (chunks(stride) << K) > kMaxDirEntries))
+    stride *= 2;
+  return static_cast<int>(stride);
+}
+
+size_t lsh_build_workspace_size(int B, int Hkv, int N, int d, int K, int L, int stride, int dtype) {
+  Geometry g;
+  if (check_common(B, Hkv, N, d, K, L, stride, dtype, &g) != LSH_OK) return 0;
+  return build_layout(B, Hkv, N, K, L, dtype, g, true).total;
+}
+
+lsh_status lsh_build_tables(const void* keys, const void* W, int B, int Hkv, int N, int d, int K, int L,
+                            int stride, int dtype, int32_t* offsets, int32_t* indices, int32_t* bounds,
+                            uint16_t* key_codes, void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry g;
+  lsh_status st = check_common(B, Hkv, N, d, K, L, stride, dtype, &g);
+  if (st != LSH_OK) return st;
+  if (!keys || !offsets || !indices || !bounds || !workspace || (K > 0 && !W)) return LSH_ERR_INVALID_ARG;
+  const BuildLayout w = build_layout(B, Hkv, N, K, L, dtype, g, key_codes == nullptr);
+  if (workspace_bytes < w.total) return LSH_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  lsh::BuildArgs a;
+  a.keys = keys;
+  a.W = W;
+  a.wt = ws + w.wt;
+  a.codes = key_codes ? key_codes : reinterpret_cast<uint16_t*>(ws + w.codes);
+  a.offsets = offsets;
+  a.indices = indices;
+  a.bounds = bounds;
+  a.U = B * Hkv;
+  a.N = N;
+  a.K = K;
+  a.L = L;
+  a.stride_log2 = g.stride_log2;
+  a.nJ = g.nJ;
+  a.spc_log2 = g.spc_log2;
+  a.dtype = dtype;
+  return hip_status(lsh::launch_build(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t lsh_decode_workspace_size(int B, int Hq, int Hkv, int N, int d, int K, int L, int stride) {
+  Geometry g;
+  if (check_common(B, Hkv, N, d, K, L, stride, LSH_BF16, &g) != LSH_OK) return 0;
+  if (Hq < 1 || Hq % Hkv != 0 || Hq / Hkv > 16) return 0;
+  return decode_layout(B, Hq, Hkv, N, L, g).total;
+}
+
+lsh_status lsh_decode_attention(const void* q, const void* keys, const void* values, const void* W,
+                                const int32_t* indices, const int32_t* bounds, int B, int Hq, int Hkv, int N,
+                                int d, int K, int L, int T, int stride, float sm_scale, int dtype, float* out,
+                                float* lse, int32_t* nsel, uint16_t* q_codes, uint8_t* counts, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  Geometry g;
+  lsh_status st = check_common(B, Hkv, N, d, K, L, stride, dtype, &g);
+  if (st != LSH_OK) return st;
+  if (Hq < 1 || Hq % Hkv != 0 || T < 1 || T > L || !std::isfinite(sm_scale)) return LSH_ERR_INVALID_ARG;
+  if (Hq / Hkv > 16) return LSH_ERR_UNSUPPORTED;
+  if (!q || !keys || !values || !indices || !bounds || !out || !workspace || (K > 0 && !W))
+    return LSH_ERR_INVALID_ARG;
+  const DecodeLayout w = decode_layout(B, Hq, Hkv, N, L, g);
+  if (workspace_bytes < w.total) return LSH_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  lsh::DecodeArgs a;
+  a.q = q;
+  a.keys = keys;
+  a.values = values;
+  a.W = W;
+  a.indices = indices;
+  a.bounds = bounds;
+  a.qcodes = q_codes ? q_codes : reinterpret_cast<uint16_t*>(ws + w.qcodes);
+  a.bitmask = reinterpret_cast<uint32_t*>(ws + w.bitmask);
+  a.chunk_nsel = reinterpret_cast<int32_t*>(ws + w.chunk_nsel);
+  a.lnu_table = reinterpret_cast<float*>(ws + w.lnu);
+  a.partials = reinterpret_cast<float*>(ws + w.partials);
+  a.out = out;
+  a.lse = lse;
+  a.nsel = nsel;
+  a.counts = counts;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.K = K;
+  a.L = L;
+  a.T = T;
+  a.stride_log2 = g.stride_log2;
+  a.nJ = g.nJ;
+  a.split_len = w.split_len;
+  a.nsplit = w.nsplit;
+  a.scale = sm_scale;
+  a.dtype = dtype;
+  return hip_status(lsh::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal launch interface between the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lsh {
+
+struct BuildArgs {
+  const void* keys;      // [U][N][128]
+  const void* W;         // [128][L*K]
+  void* wt;              // workspace: [LKpad][128]
+  uint16_t* codes;       // [U][L][N] (caller's key_codes or workspace)
+  int32_t* offsets;      // [U][L][2^K + 1]
+  int32_t* indices;      // [U][L][N]
+  int32_t* bounds;       // [U][L][2^K][nJ + 1]
+  int U, N, K, L;
+  int stride_log2, nJ, spc_log2;
+  int dtype;             // 0 = f32, 1 = bf16
+};
+
+struct DecodeArgs {
+  const void* q;         // [B][Hq][128]
+  const void* keys;      // [U][N][128]
+  const void* values;    // [U][N][128]
+  const void* W;         // [128][L*K]
+  const int32_t* indices;
+  const int32_t* bounds;
+  uint16_t* qcodes;      // [B*Hq][L]
+  uint32_t* bitmask;     // [B*Hq][Nw]
+  int32_t* chunk_nsel;   // [B*Hq][nJ]
+  float* lnu_table;      // [kLnuTable + 1]
+  float* partials;       // [B*Hq][nsplit][130]
+  float* out;            // [B*Hq][128]
+  float* lse;            // optional [B*Hq]
+  int32_t* nsel;         // optional [B*Hq]
+  uint8_t* counts;       // optional [B*Hq][N]
+  int B, Hq, Hkv, N, K, L, T;
+  int stride_log2, nJ;
+  int split_len, nsplit;
+  float scale;
+  int dtype;
+};
+
+constexpr int kLnuTable = 2048;   // ln-u correction table intervals over theta in [0, pi]
+constexpr int kPartialStride = 130;
+
+size_t bucket_lds_bytes(int nJ, int spc_log2, int K);
+hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace lsh

@@ -1,0 +1,115 @@
+"""Comparison of the HIP path with the fp64 oracle (test helper).
+
+The oracle only ever receives the seeded inputs from ``workloads``; nothing it
+computes is fed by the GPU.  A SimHash bit whose projection lies inside the
+band |proj| < 1e-4 * ||x|| * ||w_c|| may legitimately differ between fp32 and
+fp64 arithmetic, so:
+  * codes must match the oracle bit for bit outside that band, and flips
+    inside it must stay below 1e-5 of all bits;
+  * every table whose codes agree must give bit-identical offsets, indices and
+    chunk bounds; a table with a flipped bit must still be a valid stable
+    bucketing of the GPU's own codes;
+  * collision counts and selections must agree exactly for every key whose
+    codes (and the probing query's codes) agree; others may differ by at most
+    the number of disagreeing tables;
+  * outputs must be within 2e-3 relative L2 of the oracle.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from oracle import lsh_oracle as O
+
+BAND = 1e-4
+FLIP_FRACTION_MAX = 1e-5
+OUT_RTOL = 2e-3
+LSE_ATOL = 2e-3
+
+
+def u16(t):
+    return (np.asarray(t).astype(np.int64)) & 0xFFFF
+
+
+def band_mask(x, W):
+    """[n, L*K] bool: projection of row i on column c is inside the flip band."""
+    x = np.asarray(x, np.float64)
+    W = np.asarray(W, np.float64)
+    proj = x @ W
+    scale = np.linalg.norm(x, axis=1)[:, None] * np.linalg.norm(W, axis=0)[None, :]
+    return np.abs(proj) < BAND * scale
+
+
+def compare_codes(gpu, ref, band, K, L):
+    """gpu/ref int [L, n]; band [n, L*K].  Returns the number of flipped bits."""
+    gpu = u16(gpu)
+    ref = np.asarray(ref, np.int64)
+    diff = gpu ^ ref
+    flips = 0
+    for l, n in zip(*np.nonzero(diff)):
+        for b in range(K):
+            if (diff[l, n] >> b) & 1:
+                assert band[n, l * K + b], f"code bit outside the flip band differs: table {l} key {n} bit {b}"
+                flips += 1
+    return flips
+
+
+def check_tables(gpu_off, gpu_idx, gpu_bnd, gpu_codes, ref, K, stride):
+    """Compare one unit's tables.  ``ref`` from ``O.build_tables`` on the same keys."""
+    gpu_codes = u16(gpu_codes)
+    L, N = gpu_codes.shape
+    nb = 1 << K
+    same = np.all(gpu_codes == ref["codes"], axis=1)
+    for l in range(L):
+        if same[l]:
+            np.testing.assert_array_equal(gpu_off[l], ref["offsets"][l])
+            np.testing.assert_array_equal(gpu_idx[l], ref["indices"][l])
+            np.testing.assert_array_equal(gpu_bnd[l], ref["bounds"][l])
+        else:
+            # valid stable bucketing of the GPU's own codes
+            cnt = np.bincount(gpu_codes[l], minlength=nb)
+            assert gpu_off[l][0] == 0 and gpu_off[l][nb] == N
+            np.testing.assert_array_equal(np.diff(gpu_off[l]), cnt)
+            for c in range(nb):
+                seg = gpu_idx[l][gpu_off[l][c]:gpu_off[l][c + 1]]
+                assert np.all(gpu_codes[l][seg] == c) and np.all(np.diff(seg) > 0)
+                lim = np.minimum(np.arange(gpu_bnd.shape[2]) * stride, N)
+                np.testing.assert_array_equal(gpu_bnd[l][c], gpu_off[l][c] + np.searchsorted(seg, lim))
+    return int((~same).sum())
+
+
+def check_head(gpu, ref, q_band, key_codes_gpu, key_codes_ref, K, L, T):
+    """Compare one query head.  gpu: dict of numpy (q_codes [L], counts [N] or
+    None, out [d], lse, nsel).  ref: dict from ``O.decode_head``."""
+    qflips = compare_codes(gpu["q_codes"][:, None], ref["qcodes"][:, None], q_band, K, L)
+    bad_q = u16(gpu["q_codes"]) != ref["qcodes"]                        # tables whose probe differs
+    key_bad = (u16(key_codes_gpu) != key_codes_ref)                     # [L, N]
+    affected = key_bad.copy()
+    affected[bad_q, :] = True
+    n_aff = affected.sum(axis=0)                                        # per key
+    exact_keys = n_aff == 0
+    if gpu.get("counts") is not None:
+        c = np.asarray(gpu["counts"]).astype(np.int64)
+        np.testing.assert_array_equal(c[exact_keys], ref["counts"][exact_keys])
+        assert np.all(np.abs(c - ref["counts"]) <= n_aff)
+        np.testing.assert_array_equal((c >= T)[exact_keys], ref["mask"][exact_keys])
+    if exact_keys.all():
+        assert int(gpu["nsel"]) == ref["nsel"]
+    else:
+        assert abs(int(gpu["nsel"]) - ref["nsel"]) <= int((~exact_keys).sum())
+    out = np.asarray(gpu["out"], np.float64)
+    if ref["nsel"] == 0:
+        assert int(gpu["nsel"]) == 0 or not exact_keys.all()
+        if int(gpu["nsel"]) == 0:
+            assert np.all(out == 0) and gpu["lse"] == -np.inf
+        return {"qflips": qflips, "rel": 0.0}
+    rel = np.linalg.norm(out - ref["out"]) / max(np.linalg.norm(ref["out"]), 1e-30)
+    assert rel <= OUT_RTOL, f"relative L2 error {rel:.3e} > {OUT_RTOL}"
+    assert abs(float(gpu["lse"]) - ref["lse"]) <= LSE_ATOL * max(1.0, abs(ref["lse"]))
+    return {"qflips": qflips, "rel": rel}
+
+
+def estimate_error(out, exact):
+    return float(np.linalg.norm(np.asarray(out, np.float64) - exact[0]) / max(np.linalg.norm(exact[0]), 1e-30))

@@ -1,0 +1,134 @@
+"""The C ABI loads and validates arguments on the host (no GPU work).
+
+Every call here returns before anything is enqueued: invalid arguments,
+unsupported shapes and short workspaces are rejected by the host checks.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import lsh_sampled_sparse_amd as lsh
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lsh_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(lsh.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lsh_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "lsh_build_tables" in names and "lsh_decode_attention" in names
+    L = ctypes.CDLL(lsh.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(lsh.EXPORTS) == names
+
+
+def test_status_strings():
+    for s in range(5):
+        assert lsh.lsh_status_string(s).startswith("LSH_")
+    assert lsh.lsh_status_string(99) == "unknown lsh_status"
+
+
+def test_num_chunks_and_default_stride():
+    assert lsh.lsh_num_chunks(131072, 16384) == 8
+    assert lsh.lsh_num_chunks(5000, 256) == 20
+    assert lsh.lsh_num_chunks(0, 256) == 0
+    for N, K in [(131072, 10), (16384, 10), (32768, 9), (32768, 10), (4096, 8), (1, 0), (10**6, 15)]:
+        s = lsh.lsh_default_stride(N, K)
+        assert s >= 256 and s <= 65536 and (s & (s - 1)) == 0
+        assert lsh.lsh_num_chunks(N, s) << K <= 32768 or s == 65536
+    assert lsh.lsh_default_stride(0, 3) == 0 and lsh.lsh_default_stride(10, 16) == 0
+
+
+def test_workspace_queries():
+    good = lsh.lsh_build_workspace_size(1, 4, 131072, 128, 10, 150, 16384, lsh.LSH_BF16)
+    # at least the uint16 codes of every (unit, table, key)
+    assert good >= 4 * 150 * 131072 * 2
+    assert lsh.lsh_build_workspace_size(1, 4, 131072, 64, 10, 150, 16384, 1) == 0     # d != 128
+    assert lsh.lsh_build_workspace_size(1, 4, 131072, 128, 16, 150, 16384, 1) == 0    # K > 15
+    assert lsh.lsh_build_workspace_size(1, 4, 131072, 128, 10, 150, 1000, 1) == 0     # stride not 2^k
+    dec = lsh.lsh_decode_workspace_size(1, 32, 4, 131072, 128, 10, 150, 16384)
+    assert dec >= 32 * 131072 // 8            # the selection bitmask
+    assert lsh.lsh_decode_workspace_size(1, 30, 4, 131072, 128, 10, 150, 16384) == 0  # Hq % Hkv
+    assert lsh.lsh_decode_workspace_size(1, 68, 4, 131072, 128, 10, 150, 16384) == 0  # G > 16
+
+
+def _build(**kw):
+    a = dict(keys=1, W=1, B=1, Hkv=1, N=4096, d=128, K=8, L=32, stride=4096, dtype=1,
+             offsets=1, indices=1, bounds=1, codes=None, ws=1, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    return lsh.lib().lsh_build_tables(p(a["keys"]), p(a["W"]), a["B"], a["Hkv"], a["N"], a["d"], a["K"],
+                                      a["L"], a["stride"], a["dtype"], p(a["offsets"]), p(a["indices"]),
+                                      p(a["bounds"]), p(a["codes"]), p(a["ws"]), a["ws_bytes"], a["stream"])
+
+
+def _decode(**kw):
+    a = dict(q=1, keys=1, values=1, W=1, indices=1, bounds=1, B=1, Hq=4, Hkv=1, N=4096, d=128, K=8,
+             L=32, T=2, stride=4096, scale=0.088, dtype=1, out=1, ws=1, ws_bytes=1 << 40)
+    a.update(kw)
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    return lsh.lib().lsh_decode_attention(
+        p(a["q"]), p(a["keys"]), p(a["values"]), p(a["W"]), p(a["indices"]), p(a["bounds"]),
+        a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["K"], a["L"], a["T"], a["stride"],
+        ctypes.c_float(a["scale"]), a["dtype"], p(a["out"]), None, None, None, None, p(a["ws"]),
+        a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(keys=None), lsh.LSH_ERR_INVALID_ARG),
+    (dict(W=None), lsh.LSH_ERR_INVALID_ARG),
+    (dict(offsets=None), lsh.LSH_ERR_INVALID_ARG),
+    (dict(indices=None), lsh.LSH_ERR_INVALID_ARG),
+    (dict(bounds=None), lsh.LSH_ERR_INVALID_ARG),
+    (dict(ws=None), lsh.LSH_ERR_INVALID_ARG),
+    (dict(B=0), lsh.LSH_ERR_INVALID_ARG),
+    (dict(N=0), lsh.LSH_ERR_INVALID_ARG),
+    (dict(K=-1), lsh.LSH_ERR_INVALID_ARG),
+    (dict(K=16), lsh.LSH_ERR_INVALID_ARG),
+    (dict(L=0), lsh.LSH_ERR_INVALID_ARG),
+    (dict(L=256), lsh.LSH_ERR_INVALID_ARG),
+    (dict(dtype=7), lsh.LSH_ERR_INVALID_ARG),
+    (dict(stride=3000), lsh.LSH_ERR_INVALID_ARG),
+    (dict(d=64), lsh.LSH_ERR_UNSUPPORTED),
+    (dict(stride=128), lsh.LSH_ERR_UNSUPPORTED),
+    (dict(N=1 << 20, K=15, stride=256), lsh.LSH_ERR_UNSUPPORTED),
+    (dict(ws_bytes=16), lsh.LSH_ERR_WORKSPACE),
+])
+def test_build_rejects(kw, status):
+    assert _build(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), lsh.LSH_ERR_INVALID_ARG),
+    (dict(values=None), lsh.LSH_ERR_INVALID_ARG),
+    (dict(out=None), lsh.LSH_ERR_INVALID_ARG),
+    (dict(bounds=None), lsh.LSH_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), lsh.LSH_ERR_INVALID_ARG),
+    (dict(T=0), lsh.LSH_ERR_INVALID_ARG),
+    (dict(T=33), lsh.LSH_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), lsh.LSH_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), lsh.LSH_ERR_INVALID_ARG),
+    (dict(Hq=17, Hkv=1), lsh.LSH_ERR_UNSUPPORTED),
+    (dict(d=96), lsh.LSH_ERR_UNSUPPORTED),
+    (dict(ws_bytes=100), lsh.LSH_ERR_WORKSPACE),
+])
+def test_decode_rejects(kw, status):
+    assert _decode(**kw) == status
+
+
+def test_binding_raises_without_gpu_work():
+    with pytest.raises(lsh.LshError) as e:
+        lsh.lib()  # loads fine
+        raise lsh.LshError(lsh.LSH_ERR_WORKSPACE)
+    assert "WORKSPACE" in str(e.value)

@@ -1,0 +1,183 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on the GPU.
+
+Small cases span several projection tiles, several key chunks and a ragged
+tail and are checked in full; the workload configurations are run at full
+size in the launch configuration the benchmark uses and checked on sampled
+(sequence, kv head) units, which the oracle recomputes from the same inputs.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import lsh_oracle as O
+import parity as PAR
+
+pytestmark = pytest.mark.gpu
+
+
+def _lsh():
+    import lsh_sampled_sparse_amd as lsh
+    lsh.lib()
+    return lsh
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(cfg, data, stride=None, step=0):
+    """Build + one decode step on the GPU; returns numpy copies."""
+    lsh = _lsh()
+    dev = torch.device("cuda:0")
+    keys = data["keys"].to(dev)
+    vals = data["values"].to(dev)
+    W = data["W"].to(dev)
+    q = data["q"][step].to(dev).contiguous()
+    if cfg.K == 0:
+        W = torch.empty(cfg.d, 0, dtype=keys.dtype, device=dev)
+    tb = lsh.build_tables(keys, W, cfg.K, cfg.L, stride=stride, return_codes=True)
+    r = lsh.decode_attention(q, keys, vals, W, tb, cfg.K, cfg.L, cfg.T, sm_scale=cfg.scale,
+                             return_codes=True, return_counts=True)
+    torch.cuda.synchronize()
+    return tb, r
+
+
+def to_np(t):
+    return t.detach().cpu().numpy()
+
+
+def check_case(cfg, data, units=None, heads_per_unit=None, stride=None, step=0):
+    """Full comparison on the listed units (default: all)."""
+    tb, r = run_gpu(cfg, data, stride=stride, step=step)
+    stride = tb["stride"]
+    W = data["W"].float().cpu().numpy() if cfg.K > 0 else np.zeros((cfg.d, 0))
+    q = data["q"][step].float().cpu().numpy()
+    if units is None:
+        units = [(b, g) for b in range(cfg.B) for g in range(cfg.Hkv)]
+    total_bits = flips = bad_tables = 0
+    rels, est = [], []
+    G = cfg.G
+    for (b, g) in units:
+        ku = data["keys"][b, g].float().cpu().numpy()
+        vu = data["values"][b, g].float().cpu().numpy()
+        ref = O.build_tables(ku, W, cfg.K, cfg.L, stride)
+        band = PAR.band_mask(ku, W) if cfg.K > 0 else np.zeros((cfg.N, 0), bool)
+        gcodes = to_np(tb["codes"][b, g])
+        flips += PAR.compare_codes(gcodes, ref["codes"], band, cfg.K, cfg.L)
+        total_bits += cfg.N * cfg.L * cfg.K
+        bad_tables += PAR.check_tables(to_np(tb["offsets"][b, g]), to_np(tb["indices"][b, g]),
+                                       to_np(tb["bounds"][b, g]), gcodes, ref, cfg.K, stride)
+        hs = list(range(g * G, (g + 1) * G))
+        if heads_per_unit is not None:
+            hs = hs[:heads_per_unit]
+        for h in hs:
+            rr = O.decode_head(q[b, h], ku, vu, W, ref["offsets"], ref["indices"],
+                               cfg.K, cfg.L, cfg.T, cfg.scale)
+            qb = PAR.band_mask(q[b, h][None], W) if cfg.K > 0 else np.zeros((1, 0), bool)
+            gh = {"q_codes": to_np(r["q_codes"][b, h]), "counts": to_np(r["counts"][b, h]),
+                  "out": to_np(r["out"][b, h]), "lse": float(r["lse"][b, h]), "nsel": int(r["nsel"][b, h])}
+            res = PAR.check_head(gh, rr, qb, gcodes, ref["codes"], cfg.K, cfg.L, cfg.T)
+            flips += res["qflips"]
+            total_bits += cfg.L * cfg.K
+            rels.append(res["rel"])
+            if rr["nsel"] > 0:
+                est.append(PAR.estimate_error(gh["out"], O.exact_attention(q[b, h], ku, vu, cfg.scale)))
+    if total_bits:
+        assert flips <= max(1.0, PAR.FLIP_FRACTION_MAX * total_bits), (flips, total_bits)
+    say(f"[{cfg.name}] units={len(units)} flips={flips}/{total_bits} bad_tables={bad_tables} "
+        f"max_rel={max(rels) if rels else 0:.2e} est_err_vs_exact={np.mean(est) if est else float('nan'):.3e}")
+    return tb, r
+
+
+SMALL = [
+    workloads.CONFIGS[1],
+    workloads.Config("ragged-gqa3", B=2, Hq=6, Hkv=2, N=5000, d=128, K=6, L=20, T=2, dtype="bf16",
+                     planted=4, a=0.8, offset="per_head", seed=11),
+    workloads.Config("gqa8-t3", B=1, Hq=16, Hkv=2, N=3000, d=128, K=8, L=40, T=3, dtype="bf16",
+                     planted=8, a=0.7, offset="shared_lowrank", seed=12),
+    workloads.Config("gqa16-t1", B=1, Hq=16, Hkv=1, N=2100, d=128, K=5, L=10, T=1, dtype="bf16",
+                     planted=2, a=0.8, offset="none", seed=13),
+    workloads.Config("fp32-multi", B=2, Hq=4, Hkv=2, N=1500, d=128, K=7, L=24, T=2, dtype="f32",
+                     planted=3, a=0.8, offset="per_unit", seed=14),
+    workloads.Config("n63", B=1, Hq=2, Hkv=1, N=63, d=128, K=4, L=8, T=1, dtype="bf16",
+                     planted=1, a=0.9, offset="none", seed=15),
+    workloads.Config("n1", B=1, Hq=2, Hkv=2, N=1, d=128, K=3, L=5, T=1, dtype="bf16",
+                     planted=1, a=0.9, offset="none", seed=16),
+    workloads.Config("T-eq-L", B=1, Hq=4, Hkv=1, N=700, d=128, K=8, L=8, T=8, dtype="bf16",
+                     planted=1, a=0.3, offset="none", seed=17),
+    workloads.Config("L1", B=1, Hq=3, Hkv=1, N=900, d=128, K=3, L=1, T=1, dtype="bf16",
+                     planted=1, a=0.8, offset="none", seed=18),
+    workloads.Config("K15", B=1, Hq=2, Hkv=1, N=2048, d=128, K=15, L=4, T=1, dtype="bf16",
+                     planted=1, a=0.95, offset="none", seed=19),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=[c.name for c in SMALL])
+def test_small_full_parity(cfg):
+    say(f"case {cfg.name}")
+    data = workloads.generate(cfg)
+    check_case(cfg, data)
+
+
+@pytest.mark.parametrize("stride", [256, 1024, 8192])
+def test_strides_give_identical_tables(stride):
+    cfg = SMALL[1]
+    say(f"case strides {stride}")
+    data = workloads.generate(cfg)
+    check_case(cfg, data, stride=stride)
+
+
+def test_k0_is_exact_attention():
+    cfg = workloads.Config("k0", B=1, Hq=8, Hkv=2, N=3000, d=128, K=0, L=3, T=2, dtype="bf16",
+                           planted=4, a=0.8, offset="per_head", seed=21)
+    say("case k0")
+    data = workloads.generate(cfg)
+    tb, r = check_case(cfg, data)
+    keys = data["keys"].float().numpy()
+    vals = data["values"].float().numpy()
+    q = data["q"][0].float().numpy()
+    for h in range(cfg.Hq):
+        ex, lse = O.exact_attention(q[0, h], keys[0, h // cfg.G], vals[0, h // cfg.G], cfg.scale)
+        out = to_np(r["out"][0, h])
+        assert np.linalg.norm(out - ex) / np.linalg.norm(ex) <= PAR.OUT_RTOL
+        assert int(r["nsel"][0, h]) == cfg.N
+
+
+def test_deterministic():
+    cfg = SMALL[2]
+    say("case determinism")
+    data = workloads.generate(cfg)
+    tb1, r1 = run_gpu(cfg, data)
+    tb2, r2 = run_gpu(cfg, data)
+    for k in ("offsets", "indices", "bounds", "codes"):
+        assert torch.equal(tb1[k], tb2[k]), k
+    for k in ("out", "lse", "nsel", "q_codes", "counts"):
+        assert torch.equal(r1[k], r2[k]), k
+
+
+# ----------------------------------------------------------------- full sizes
+
+FULL = {
+    2: dict(units=None, heads=None, steps=[0]),
+    3: dict(units=[(0, 0), (11, 5)], heads=4, steps=[0]),
+    4: dict(units=[(0, 1)], heads=3, steps=[0]),
+    5: dict(units=[(37, 6)], heads=2, steps=[0, 7]),
+}
+
+
+@pytest.mark.parametrize("cfg_id", sorted(FULL))
+def test_full_size_sampled(cfg_id):
+    cfg = workloads.CONFIGS[cfg_id]
+    spec = FULL[cfg_id]
+    say(f"case full cfg{cfg_id} {cfg.name}")
+    data = workloads.generate(cfg, device="cuda")
+    for step in spec["steps"]:
+        check_case(cfg, data, units=spec["units"], heads_per_unit=spec["heads"], step=step)
+    del data
+    torch.cuda.empty_cache()
