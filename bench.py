@@ -1,0 +1,311 @@
+"""Throughput of LSH-sampled decode attention on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input:
+the table build of the batch's keys (SimHash projection, bucket build) and
+one decode step (query hash, probe and count, selection, weighted attention,
+log-sum-exp merge).  Steps rotate over ``--copies`` independent input copies;
+step i builds the tables of copy i mod R and decodes copy (i - 1) mod R, whose
+tables were built one step earlier, so the decode does not read tables that
+the build just left in the 256 MB last-level cache.
+
+Prints ONE JSON line.  ``value`` is query-heads per second of whole steps
+(build + decode); the decode alone is reported under ``breakdown``.  The
+``roofline`` object is for the kernel with the largest total time, from the
+library's per-dispatch timing events; ``cpu_baseline`` times the fp64 CPU
+oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA, TFLOP/s
+
+BUILD_KERNELS = ("transpose_w", "project_codes", "bucket_tables")
+DECODE_KERNELS = ("qhash", "count_select", "attend", "merge")
+KERNEL_SOURCES = {
+    "transpose_w": "build_kernels.hip", "project_codes": "build_kernels.hip",
+    "bucket_tables": "build_kernels.hip", "qhash": "decode_kernels.hip",
+    "count_select": "decode_kernels.hip", "attend": "decode_kernels.hip",
+    "merge": "decode_kernels.hip",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=4, help="workload id in workloads.CONFIGS (default: 128K GQA-8)")
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="time the steps without per-dispatch events (roofline from a second pass)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def source_digest(kernel):
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "lsh_device.h", "lsh_kernels.h"):
+        with open(os.path.join(ROOT, "lsh_sampled_sparse_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None
+    when there are none or the kernel source changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec or rec.get("source_digest") != source_digest(kernel):
+        return None
+    return rec["bytes_per_launch"]
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
+              "(sequence, kv head) without exchange, but no multi-GPU run is built here.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import lsh_sampled_sparse_amd as lsh
+    import workloads
+
+    lsh.lib()   # fails loudly when the HIP library is missing
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = workloads.CONFIGS[args.config]
+    B, Hq, Hkv, N, d, K, L, T = cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.d, cfg.K, cfg.L, cfg.T
+    G = cfg.G
+    R = max(1, args.copies)
+    stride = lsh.lsh_default_stride(N, K)
+    nch = lsh.lsh_num_chunks(N, stride)
+    dt = lsh.LSH_BF16 if cfg.dtype == "bf16" else lsh.LSH_F32
+    esz = 2 if cfg.dtype == "bf16" else 4
+
+    # ---------------------------------------------------------------- inputs
+    copies = []
+    for r in range(R):
+        data = workloads.generate(cfg.with_(seed=cfg.seed + 1000 * r), device=dev)
+        c = {"keys": data["keys"], "values": data["values"], "W": data["W"],
+             "q": data["q"][0].contiguous()}
+        c["offsets"] = torch.empty(B, Hkv, L, (1 << K) + 1, dtype=torch.int32, device=dev)
+        c["indices"] = torch.empty(B, Hkv, L, N, dtype=torch.int32, device=dev)
+        c["bounds"] = torch.empty(B, Hkv, L, 1 << K, nch + 1, dtype=torch.int32, device=dev)
+        c["bws"] = torch.empty(max(1, lsh.lsh_build_workspace_size(B, Hkv, N, d, K, L, stride, dt)),
+                               dtype=torch.uint8, device=dev)
+        c["dws"] = torch.empty(max(1, lsh.lsh_decode_workspace_size(B, Hq, Hkv, N, d, K, L, stride)),
+                               dtype=torch.uint8, device=dev)
+        c["out"] = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+        c["lse"] = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+        c["nsel"] = torch.empty(B, Hq, dtype=torch.int32, device=dev)
+        copies.append(c)
+        del data
+    torch.cuda.synchronize()
+
+    def build(c):
+        lsh.lsh_build_tables(c["keys"], c["W"], K, L, stride, c["offsets"], c["indices"], c["bounds"],
+                             None, c["bws"])
+
+    def decode(c, counts=None):
+        lsh.lsh_decode_attention(c["q"], c["keys"], c["values"], c["W"], c["indices"], c["bounds"], K, L, T,
+                                 stride, cfg.scale, c["out"], c["lse"], c["nsel"], None, counts, c["dws"])
+
+    def step(i):
+        build(copies[i % R])
+        decode(copies[(i - 1) % R])
+
+    for c in copies:
+        build(c)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed
+    timing = not args.no_kernel_timing
+    if timing:
+        lsh.lsh_timing_begin()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, args.warmup + args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if timing:
+        ktimes = lsh.lsh_timing_end()
+    else:
+        lsh.lsh_timing_begin()
+        for i in range(args.warmup, args.warmup + args.steps):
+            step(i)
+        ktimes = lsh.lsh_timing_end()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    qh = B * Hq
+    value = qh / (ms_per_step * 1e-3)
+
+    # ------------------------------------------- measured selection statistics
+    # (untimed) one decode per copy with the collision counts returned
+    counts = torch.empty(B, Hq, N, dtype=torch.uint8, device=dev)
+    sel_rows = []    # sum over (b, g) of |union of the group's selections|
+    idx_entries = []  # sum over heads of probed-bucket entries = sum of counts
+    nsel_tot = []
+    for c in copies:
+        decode(c, counts)
+        torch.cuda.synchronize()
+        m = (counts >= T).view(B, Hkv, G, N)
+        sel_rows.append(int(m.any(dim=2).sum().item()))
+        idx_entries.append(int(counts.sum(dtype=torch.int64).item()))
+        nsel_tot.append(int(c["nsel"].sum().item()))
+    U_rows = float(np.mean(sel_rows))
+    E_idx = float(np.mean(idx_entries))
+
+    # algorithmic bytes / flops per launch
+    kv_bytes = U_rows * 2 * d * esz
+    alg = {
+        "project_codes": ("mfma", 2.0 * d * K * L * B * Hkv * N),
+        "bucket_tables": ("hbm", B * Hkv * L * (N * (2 + 4) + ((1 << K) + 1) * 4 + (1 << K) * (nch + 1) * 4)),
+        "transpose_w": ("hbm", 2.0 * d * L * K * esz),
+        "qhash": ("hbm", qh * d * esz + d * L * K * esz + qh * L * 2),
+        "count_select": ("hbm", E_idx * 4 + qh * L * 8 + qh * N / 8),
+        "attend": ("hbm", kv_bytes + qh * d * esz + qh * N / 8),
+        "merge": ("hbm", 0.0),
+    }
+    kernels = {}
+    for name, (tot_ms, n) in ktimes.items():
+        if n == 0:
+            continue
+        avg_ms = tot_ms / n
+        bound, amount = alg[name]
+        rec = {"avg_us": round(avg_ms * 1e3, 3), "launches": n, "total_ms": round(tot_ms, 4), "bound": bound}
+        if bound == "mfma":
+            rec["achieved_tflops"] = amount / (avg_ms * 1e-3) / 1e12
+        elif amount > 0:
+            rec["achieved_gbs"] = amount / (avg_ms * 1e-3) / 1e9
+        kernels[name] = rec
+    dom = max(kernels, key=lambda k: kernels[k]["total_ms"])
+    dk = kernels[dom]
+    if dk["bound"] == "mfma":
+        peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(dk["achieved_tflops"], 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(dk["achieved_tflops"] / peak, 4)}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(dk["achieved_gbs"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(dk["achieved_gbs"] / HBM_PEAK_GBS, 4)}
+    roof["avg_us"] = dk["avg_us"]
+    roof["traffic"] = measured_traffic(cfg.name, dom)
+    for k in kernels.values():
+        for f in ("achieved_tflops", "achieved_gbs"):
+            if f in k:
+                k[f] = round(k[f], 2)
+
+    build_ms = sum(ktimes[k][0] for k in BUILD_KERNELS) / args.steps
+    decode_ms = sum(ktimes[k][0] for k in DECODE_KERNELS) / args.steps
+    dec_bytes = E_idx * 4 + qh * L * 8 + kv_bytes + qh * d * (esz + 4) + d * L * K * esz
+
+    line = {
+        "metric": "LSH-attn decode queries·heads/s at 32K–128K ctx; % of HBM roofline",
+        "value": round(value, 1),
+        "unit": "queries·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "K": K, "L": L, "T": T,
+                   "kv_dtype": cfg.dtype, "stride": stride, "step": "table build + 1 decode step",
+                   "input_copies": R},
+        "roofline": roof,
+        "breakdown": {
+            "build_ms": round(build_ms, 5),
+            "decode_ms": round(decode_ms, 5),
+            "decode_qh_per_s": round(qh / (decode_ms * 1e-3), 1),
+            "decode_alg_bytes": int(dec_bytes),
+            "decode_hbm_frac": round(dec_bytes / (decode_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "build_keys_per_s": round(B * Hkv * N / (build_ms * 1e-3), 1),
+            "selected_union_rows": U_rows,
+            "selected_frac_of_keys": round(U_rows / (B * Hkv * N), 4),
+            "nsel_mean_per_head": float(np.mean(nsel_tot)) / qh,
+            "probed_index_entries": E_idx,
+            "kernels": kernels,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, copies[0], stride)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, c, stride):
+    """The fp64 oracle on one (sequence, kv head) unit: its table build and
+    the decode of its G query heads, extrapolated to the whole step."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import lsh_oracle as O
+
+    b, g = 0, 0
+    keys = c["keys"][b, g].float().cpu().numpy()
+    vals = c["values"][b, g].float().cpu().numpy()
+    W = c["W"].float().cpu().numpy()
+    q = c["q"][b].float().cpu().numpy()
+    t0 = time.perf_counter()
+    tb = O.build_tables(keys, W, cfg.K, cfg.L, stride)
+    for h in range(g * cfg.G, (g + 1) * cfg.G):
+        O.decode_head(q[h], keys, vals, W, tb["offsets"], tb["indices"], cfg.K, cfg.L, cfg.T, cfg.scale)
+    dt = time.perf_counter() - t0
+    units = cfg.B * cfg.Hkv
+    step_s = dt * units
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(cfg.B * cfg.Hq / step_s, 3), "unit": "queries·heads/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"1 of {units} (sequence, kv head) units: fp64 table build of {cfg.N} keys + decode of "
+                      f"its {cfg.G} query heads in {dt:.2f} s, scaled x{units} to one step; BLAS threads "
+                      f"{threads} (matmuls), the rest single-threaded numpy"}
+
+
+if __name__ == "__main__":
+    main()

@@ -34,9 +34,10 @@
  * Conventions for every entry point:
  *   - Every pointer argument is DEVICE memory owned by the caller, except
  *     `stream`, which is a hipStream_t handle (NULL = the null stream).  The
- *     library allocates nothing and keeps no state between calls; calls on
- *     different streams may run concurrently if they use separate outputs and
- *     workspaces.
+ *     library allocates no device memory and keeps no state between calls
+ *     (the kernel-timing window at the end of this header is the one
+ *     exception); calls on different streams may run concurrently if they use
+ *     separate outputs and workspaces.
  *   - All arrays are dense, row-major (last index fastest), 16-byte aligned.
  *   - Work is enqueued on `stream` and the call returns without waiting.
  *     The returned status covers argument checks (made before anything is
@@ -152,6 +153,32 @@ lsh_status lsh_decode_attention(const void* q, const void* keys,
                                 uint16_t* q_codes, uint8_t* counts,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* ------------------------------------------------------------------------
+ * Kernel timing (a profiling aid; process-wide, one window at a time)
+ *
+ * Between lsh_timing_begin() and lsh_timing_end() every kernel the library
+ * launches carries a start and a stop event on its own dispatch, so the
+ * measured time is the kernel's execution on the GPU, with no extra work on
+ * the stream.  Events come from a host-side pool that grows on demand and is
+ * kept for reuse (no device memory).
+ * ---------------------------------------------------------------------- */
+
+/* Number of kernel kinds; ids run 0 .. lsh_kernel_count() - 1. */
+int lsh_kernel_count(void);
+
+/* Name of kernel kind `id` (static string), or NULL for an invalid id. */
+const char* lsh_kernel_name(int id);
+
+/* Opens a timing window.  LSH_ERR_INVALID_ARG if one is already open. */
+lsh_status lsh_timing_begin(void);
+
+/* Closes the window: waits for every timed launch and writes, per kernel
+ * kind, the summed execution time in milliseconds and the number of
+ * launches into HOST arrays of lsh_kernel_count() entries (either may be
+ * NULL).  LSH_ERR_INVALID_ARG if no window is open, LSH_ERR_HIP if an event
+ * could not be read (those launches are left out of the sums). */
+lsh_status lsh_timing_end(double* total_ms, int32_t* launches);
 
 #ifdef __cplusplus
 }

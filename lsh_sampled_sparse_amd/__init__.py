@@ -29,6 +29,10 @@ EXPORTS = (
     "lsh_build_tables",
     "lsh_decode_workspace_size",
     "lsh_decode_attention",
+    "lsh_kernel_count",
+    "lsh_kernel_name",
+    "lsh_timing_begin",
+    "lsh_timing_end",
 )
 
 _lib = None
@@ -60,6 +64,14 @@ def lib():
         L.lsh_decode_attention.restype = _i
         L.lsh_decode_attention.argtypes = ([_p] * 6 + [_i] * 9 + [ctypes.c_float, _i]
                                            + [_p] * 6 + [_sz, _p])
+        L.lsh_kernel_count.restype = _i
+        L.lsh_kernel_count.argtypes = []
+        L.lsh_kernel_name.restype = ctypes.c_char_p
+        L.lsh_kernel_name.argtypes = [_i]
+        L.lsh_timing_begin.restype = _i
+        L.lsh_timing_begin.argtypes = []
+        L.lsh_timing_end.restype = _i
+        L.lsh_timing_end.argtypes = [_p, _p]
         _lib = L
     return _lib
 
@@ -144,6 +156,28 @@ def lsh_decode_attention(q, keys, values, W, indices, bounds, K, L, T, stride, s
         B, Hq, Hkv, N, d, K, L, T, stride, ctypes.c_float(sm_scale), dt,
         _ptr(out), _ptr(lse), _ptr(nsel), _ptr(q_codes), _ptr(counts),
         _ptr(workspace), workspace.numel(), _stream(keys.device)))
+
+
+def lsh_kernel_count() -> int:
+    return lib().lsh_kernel_count()
+
+
+def lsh_kernel_name(kid: int):
+    n = lib().lsh_kernel_name(int(kid))
+    return None if n is None else n.decode()
+
+
+def lsh_timing_begin() -> None:
+    _check(lib().lsh_timing_begin())
+
+
+def lsh_timing_end():
+    """Close the timing window; returns {kernel name: (total ms, launches)}."""
+    n = lsh_kernel_count()
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int32 * n)()
+    _check(lib().lsh_timing_end(ms, cnt))
+    return {lsh_kernel_name(k): (ms[k], cnt[k]) for k in range(n)}
 
 
 # ------------------------------------------------------------------ convenience

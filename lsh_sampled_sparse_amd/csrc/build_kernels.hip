@@ -294,13 +294,13 @@ static hipError_t launch_project(const void* keys, const void* W, void* WT, uint
   const int LKpad = nslab * kSlabCols;
   if (LK > 0) {
     const int total = LKpad * kHeadDim;
-    hipLaunchKernelGGL(transpose_w_kernel<T>, dim3((total + 255) / 256), dim3(256), 0, stream,
-                       static_cast<const S*>(W), static_cast<S*>(WT), LK, LKpad);
+    hipError_t e = launch(kKTransposeW, transpose_w_kernel<T>, dim3((total + 255) / 256), dim3(256), 0,
+                          stream, static_cast<const S*>(W), static_cast<S*>(WT), LK, LKpad);
+    if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(project_codes_kernel<T>, dim3((N + kProjKeys - 1) / kProjKeys, U),
-                     dim3(kProjThreads), 0, stream, static_cast<const S*>(keys),
-                     static_cast<const S*>(WT), codes, N, K, L, nslab);
-  return hipGetLastError();
+  return launch(kKProject, project_codes_kernel<T>, dim3((N + kProjKeys - 1) / kProjKeys, U),
+                dim3(kProjThreads), 0, stream, static_cast<const S*>(keys), static_cast<const S*>(WT),
+                codes, N, K, L, nslab);
 }
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream) {
@@ -312,10 +312,9 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t stream) {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(bucket_tables_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bucket_tables_kernel, dim3(a.L, a.U), dim3(kBucketThreads), lds, stream,
-                     a.codes, a.N, a.K, a.L, a.nJ, a.spc_log2, a.stride_log2 - a.spc_log2,
-                     a.offsets, a.indices, a.bounds);
-  return hipGetLastError();
+  return launch(kKBucket, bucket_tables_kernel, dim3(a.L, a.U), dim3(kBucketThreads),
+                static_cast<unsigned>(lds), stream, static_cast<const uint16_t*>(a.codes), a.N, a.K, a.L,
+                a.nJ, a.spc_log2, a.stride_log2 - a.spc_log2, a.offsets, a.indices, a.bounds);
 }
 
 size_t bucket_lds_bytes(int nJ, int spc_log2, int K) {

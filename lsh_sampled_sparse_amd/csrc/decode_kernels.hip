@@ -524,12 +524,12 @@ __global__ __launch_bounds__(kHeadDim) void merge_kernel(const float* __restrict
 // Host-side launcher
 // ---------------------------------------------------------------------------
 template <typename T, int GM>
-static void launch_attend(const DecodeArgs& a, hipStream_t stream) {
+static hipError_t launch_attend(const DecodeArgs& a, hipStream_t stream) {
   using S = typename T::storage;
-  hipLaunchKernelGGL((attend_kernel<T, GM>), dim3(a.nsplit, a.B * a.Hkv), dim3(kAttThreads), 0, stream,
-                     static_cast<const S*>(a.q), static_cast<const S*>(a.keys),
-                     static_cast<const S*>(a.values), a.bitmask, a.lnu_table, a.Hq, a.Hkv, a.N, a.K,
-                     a.T, a.scale, a.split_len, a.nsplit, a.partials);
+  return launch(kKAttend, attend_kernel<T, GM>, dim3(a.nsplit, a.B * a.Hkv), dim3(kAttThreads), 0, stream,
+                static_cast<const S*>(a.q), static_cast<const S*>(a.keys), static_cast<const S*>(a.values),
+                static_cast<const uint32_t*>(a.bitmask), static_cast<const float*>(a.lnu_table), a.Hq, a.Hkv,
+                a.N, a.K, a.T, a.scale, a.split_len, a.nsplit, a.partials);
 }
 
 template <typename T>
@@ -540,26 +540,30 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const int tpw = a.K > 0 ? 256 / a.K : 256;
   const int xblocks = (a.L + tpw - 1) / tpw;
   const int tab_blocks = (kLnuTable + 1 + xblocks * 256 - 1) / (xblocks * 256);
-  hipLaunchKernelGGL(qhash_kernel<T>, dim3(xblocks, head_blocks + tab_blocks), dim3(256), 0, stream,
-                     static_cast<const S*>(a.q), static_cast<const S*>(a.W), a.qcodes, a.lnu_table, BH,
-                     a.K, a.L, a.T, head_blocks);
-  const size_t lds = ((static_cast<size_t>(1) << a.stride_log2) + 3) & ~static_cast<size_t>(3);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(count_select_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  hipError_t e = launch(kKQhash, qhash_kernel<T>, dim3(xblocks, head_blocks + tab_blocks), dim3(256), 0,
+                        stream, static_cast<const S*>(a.q), static_cast<const S*>(a.W), a.qcodes,
+                        a.lnu_table, BH, a.K, a.L, a.T, head_blocks);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(count_select_kernel, dim3(a.nJ, BH), dim3(kCountThreads), lds, stream, a.qcodes,
-                     a.indices, a.bounds, a.Hq, a.Hkv, a.N, a.K, a.L, a.T, a.stride_log2, a.nJ, a.bitmask,
-                     a.chunk_nsel, a.counts);
+  const size_t lds = ((static_cast<size_t>(1) << a.stride_log2) + 3) & ~static_cast<size_t>(3);
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(count_select_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  e = launch(kKCountSelect, count_select_kernel, dim3(a.nJ, BH), dim3(kCountThreads),
+             static_cast<unsigned>(lds), stream, static_cast<const uint16_t*>(a.qcodes),
+             a.indices, a.bounds, a.Hq, a.Hkv, a.N, a.K, a.L, a.T, a.stride_log2, a.nJ, a.bitmask,
+             a.chunk_nsel, a.counts);
+  if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;
   if (G <= 4)
-    launch_attend<T, 4>(a, stream);
+    e = launch_attend<T, 4>(a, stream);
   else if (G <= 8)
-    launch_attend<T, 8>(a, stream);
+    e = launch_attend<T, 8>(a, stream);
   else
-    launch_attend<T, 16>(a, stream);
-  hipLaunchKernelGGL(merge_kernel, dim3(BH), dim3(kHeadDim), 0, stream, a.partials, a.chunk_nsel,
-                     a.nsplit, a.nJ, a.out, a.lse, a.nsel);
-  return hipGetLastError();
+    e = launch_attend<T, 16>(a, stream);
+  if (e != hipSuccess) return e;
+  return launch(kKMerge, merge_kernel, dim3(BH), dim3(kHeadDim), 0, stream,
+                static_cast<const float*>(a.partials), static_cast<const int32_t*>(a.chunk_nsel), a.nsplit,
+                a.nJ, a.out, a.lse, a.nsel);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

@@ -4,6 +4,8 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <mutex>
+#include <vector>
 
 #include "../../include/lsh_attn.h"
 #include "lsh_kernels.h"
@@ -102,7 +104,48 @@ DecodeLayout decode_layout(int B, int Hq, int Hkv, int N, int L, const Geometry&
 
 lsh_status hip_status(hipError_t e) { return e == hipSuccess ? LSH_OK : LSH_ERR_HIP; }
 
+// Kernel timing.  While a timing window is open every launch takes a pair of
+// events from this pool (grown on demand, reused across windows); closing the
+// window waits for them and sums the elapsed times per kernel kind.
+struct TimingRecord {
+  int id;
+  hipEvent_t start, stop;
+};
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<TimingRecord> g_timing_pool;
+size_t g_timing_used = 0;
+
 }  // namespace
+
+namespace lsh {
+
+const char* kernel_name(int id) {
+  static const char* const names[kKNumKernels] = {
+      "transpose_w", "project_codes", "bucket_tables", "qhash", "count_select", "attend", "merge"};
+  return (id >= 0 && id < kKNumKernels) ? names[id] : nullptr;
+}
+
+void timing_events(int id, hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (!g_timing_on) return;
+  if (g_timing_used == g_timing_pool.size()) {
+    TimingRecord r{id, nullptr, nullptr};
+    if (hipEventCreate(&r.start) != hipSuccess) return;
+    if (hipEventCreate(&r.stop) != hipSuccess) {
+      (void)hipEventDestroy(r.start);
+      return;
+    }
+    g_timing_pool.push_back(r);
+  }
+  TimingRecord& r = g_timing_pool[g_timing_used++];
+  r.id = id;
+  *start = r.start;
+  *stop = r.stop;
+}
+
+}  // namespace lsh
 
 extern "C" {
 
@@ -115,6 +158,41 @@ const char* lsh_status_string(int status) {
     case LSH_ERR_HIP: return "LSH_ERR_HIP: HIP runtime or launch error";
     default: return "unknown lsh_status";
   }
+}
+
+int lsh_kernel_count(void) { return lsh::kKNumKernels; }
+
+const char* lsh_kernel_name(int id) { return lsh::kernel_name(id); }
+
+lsh_status lsh_timing_begin(void) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (g_timing_on) return LSH_ERR_INVALID_ARG;
+  g_timing_on = true;
+  g_timing_used = 0;
+  return LSH_OK;
+}
+
+lsh_status lsh_timing_end(double* total_ms, int32_t* launches) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (!g_timing_on) return LSH_ERR_INVALID_ARG;
+  g_timing_on = false;
+  if (total_ms)
+    for (int k = 0; k < lsh::kKNumKernels; ++k) total_ms[k] = 0.0;
+  if (launches)
+    for (int k = 0; k < lsh::kKNumKernels; ++k) launches[k] = 0;
+  lsh_status st = LSH_OK;
+  for (size_t i = 0; i < g_timing_used; ++i) {
+    const TimingRecord& r = g_timing_pool[i];
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) {
+      st = LSH_ERR_HIP;
+      continue;
+    }
+    if (total_ms) total_ms[r.id] += ms;
+    if (launches) launches[r.id] += 1;
+  }
+  g_timing_used = 0;
+  return st;
 }
 
 int lsh_num_chunks(int N, int stride) {

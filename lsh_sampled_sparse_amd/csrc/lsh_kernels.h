@@ -1,6 +1,7 @@
 // Internal launch interface between the C-ABI layer and the HIP kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -45,6 +46,34 @@ struct DecodeArgs {
 
 constexpr int kLnuTable = 2048;   // ln-u correction table intervals over theta in [0, pi]
 constexpr int kPartialStride = 130;
+
+// Kernel kinds, in launch order; names for the timing interface.
+enum KernelId {
+  kKTransposeW = 0,
+  kKProject,
+  kKBucket,
+  kKQhash,
+  kKCountSelect,
+  kKAttend,
+  kKMerge,
+  kKNumKernels
+};
+const char* kernel_name(int id);
+
+// Start/stop events for one launch of kernel `id` while timing is on; both
+// null otherwise.
+void timing_events(int id, hipEvent_t* start, hipEvent_t* stop);
+
+// Every kernel goes through here: with timing on, the dispatch packet itself
+// carries the start and stop timestamps (no extra packets on the stream).
+template <typename F, typename... Args>
+inline hipError_t launch(int id, F kernel, dim3 grid, dim3 block, unsigned lds, hipStream_t stream,
+                         Args... args) {
+  hipEvent_t a = nullptr, b = nullptr;
+  timing_events(id, &a, &b);
+  hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, a, b, 0u, args...);
+  return hipGetLastError();
+}
 
 size_t bucket_lds_bytes(int nJ, int spc_log2, int K);
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
