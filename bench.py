@@ -35,10 +35,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA, TFLOP/s
 
-BUILD_KERNELS = ("transpose_w", "project_codes", "bucket_tables")
+BUILD_KERNELS = ("transpose_w", "project_codes", "bucket_count", "bucket_scatter", "bucket_tables")
 DECODE_KERNELS = ("qhash", "count_select", "attend", "merge")
 KERNEL_SOURCES = {
     "transpose_w": "build_kernels.hip", "project_codes": "build_kernels.hip",
+    "bucket_count": "build_kernels.hip", "bucket_scatter": "build_kernels.hip",
     "bucket_tables": "build_kernels.hip", "qhash": "decode_kernels.hip",
     "count_select": "decode_kernels.hip", "attend": "decode_kernels.hip",
     "merge": "decode_kernels.hip",
@@ -131,7 +132,7 @@ def main():
         c = {"keys": data["keys"], "values": data["values"], "W": data["W"],
              "q": data["q"][0].contiguous()}
         c["offsets"] = torch.empty(B, Hkv, L, (1 << K) + 1, dtype=torch.int32, device=dev)
-        c["indices"] = torch.empty(B, Hkv, L, N, dtype=torch.int32, device=dev)
+        c["indices"] = torch.empty(B, Hkv, L, N, dtype=torch.int16, device=dev)
         c["bounds"] = torch.empty(B, Hkv, L, 1 << K, nch + 1, dtype=torch.int32, device=dev)
         c["bws"] = torch.empty(max(1, lsh.lsh_build_workspace_size(B, Hkv, N, d, K, L, stride, dt)),
                                dtype=torch.uint8, device=dev)
@@ -201,12 +202,17 @@ def main():
 
     # algorithmic bytes / flops per launch
     kv_bytes = U_rows * 2 * d * esz
+    tables = B * Hkv * L
+    csr_out = tables * (N * 2 + ((1 << K) + 1) * 4 + (1 << K) * (nch + 1) * 4)   # indices + offsets + bounds
     alg = {
         "project_codes": ("mfma", 2.0 * d * K * L * B * Hkv * N),
-        "bucket_tables": ("hbm", B * Hkv * L * (N * (2 + 4) + ((1 << K) + 1) * 4 + (1 << K) * (nch + 1) * 4)),
+        # codes read once, CSR written once
+        "bucket_count": ("hbm", tables * N * 2),
+        "bucket_scatter": ("hbm", tables * N * 2 + csr_out),
+        "bucket_tables": ("hbm", tables * N * 2 + csr_out),
         "transpose_w": ("hbm", 2.0 * d * L * K * esz),
         "qhash": ("hbm", qh * d * esz + d * L * K * esz + qh * L * 2),
-        "count_select": ("hbm", E_idx * 4 + qh * L * 8 + qh * N / 8),
+        "count_select": ("hbm", E_idx * 2 + qh * L * 8 + qh * N / 8),
         "attend": ("hbm", kv_bytes + qh * d * esz + qh * N / 8),
         "merge": ("hbm", 0.0),
     }
@@ -240,7 +246,7 @@ def main():
 
     build_ms = sum(ktimes[k][0] for k in BUILD_KERNELS) / args.steps
     decode_ms = sum(ktimes[k][0] for k in DECODE_KERNELS) / args.steps
-    dec_bytes = E_idx * 4 + qh * L * 8 + kv_bytes + qh * d * (esz + 4) + d * L * K * esz
+    dec_bytes = E_idx * 2 + qh * L * 8 + kv_bytes + qh * d * (esz + 4) + d * L * K * esz
 
     line = {
         "metric": "LSH-attn decode queries·heads/s at 32K–128K ctx; % of HBM roofline",

@@ -100,23 +100,27 @@ size_t lsh_build_workspace_size(int B, int Hkv, int N, int d, int K, int L,
  * keys     [B, Hkv, N, d]  dtype        key cache of every (sequence, kv head)
  * W        [d, L*K]        dtype        SimHash projection, shared by all heads
  * offsets  [B, Hkv, L, 2^K + 1] int32   out: bucket c of table l of unit (b,g) is
- *                                       indices[b,g,l, offsets[c] : offsets[c+1]]
- * indices  [B, Hkv, L, N]  int32        out: key indices grouped by bucket,
- *                                       ascending inside each bucket
+ *                                       positions offsets[c] .. offsets[c+1] of
+ *                                       indices[b,g,l,:]
  * bounds   [B, Hkv, L, 2^K, nchunks + 1] int32
  *                                       out: bounds[..,c,j] = position of the first
  *                                       entry of bucket c with key index
- *                                       >= j*stride (bucket end if none), so the
- *                                       keys of chunk j in bucket c are
- *                                       indices[.., bounds[c,j] : bounds[c,j+1]];
+ *                                       >= j*stride (bucket end if none), so
+ *                                       bounds[..,c,0] = offsets[c] and the keys
+ *                                       of chunk j in bucket c sit at positions
+ *                                       bounds[c,j] .. bounds[c,j+1];
  *                                       nchunks = lsh_num_chunks(N, stride)
+ * indices  [B, Hkv, L, N]  uint16       out: the keys grouped by bucket, ascending
+ *                                       inside each bucket; an entry of chunk j
+ *                                       holds (key index - j*stride), which fits
+ *                                       16 bits since stride <= 65536
  * key_codes [B, Hkv, L, N] uint16       optional out: code_l(k_n)
  * workspace                             device scratch of the queried size
  */
 lsh_status lsh_build_tables(const void* keys, const void* W,
                             int B, int Hkv, int N, int d, int K, int L,
                             int stride, int dtype,
-                            int32_t* offsets, int32_t* indices, int32_t* bounds,
+                            int32_t* offsets, uint16_t* indices, int32_t* bounds,
                             uint16_t* key_codes,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
@@ -136,7 +140,8 @@ size_t lsh_decode_workspace_size(int B, int Hq, int Hkv, int N, int d, int K,
  * q        [B, Hq, d]      dtype        one decode query per head
  * keys, values [B, Hkv, N, d] dtype     the cache the tables were built from
  * W        [d, L*K]        dtype        the build's projection
- * indices, bounds                       the build's outputs (same stride)
+ * indices, bounds                       the build's outputs (same stride; offsets
+ *                                       are not needed: bounds[c,0] = offsets[c])
  * out      [B, Hq, d]      float        out: the estimate
  * lse      [B, Hq]         float        optional out: natural-log log-sum-exp
  * nsel     [B, Hq]         int32        optional out: |S|
@@ -145,7 +150,7 @@ size_t lsh_decode_workspace_size(int B, int Hq, int Hkv, int N, int d, int K,
  */
 lsh_status lsh_decode_attention(const void* q, const void* keys,
                                 const void* values, const void* W,
-                                const int32_t* indices, const int32_t* bounds,
+                                const uint16_t* indices, const int32_t* bounds,
                                 int B, int Hq, int Hkv, int N, int d, int K,
                                 int L, int T, int stride, float sm_scale,
                                 int dtype,

@@ -194,9 +194,10 @@ def _require(t, name, dtype=None):
 def build_tables(keys, W, K, L, stride=None, return_codes=False):
     """Build the bucket tables of every (sequence, kv head).
 
-    Returns dict: offsets [B,Hkv,L,2^K+1], indices [B,Hkv,L,N],
-    bounds [B,Hkv,L,2^K,nchunks+1] (int32), stride, and codes [B,Hkv,L,N]
-    (int16 view of uint16) when ``return_codes``.
+    Returns dict: offsets [B,Hkv,L,2^K+1] and bounds [B,Hkv,L,2^K,nchunks+1]
+    (int32), indices [B,Hkv,L,N] (int16 holding the uint16 chunk-relative key
+    index), stride, and codes [B,Hkv,L,N] (int16 holding uint16) when
+    ``return_codes``.
     """
     _require(keys, "keys")
     _require(W, "W", keys.dtype)
@@ -208,7 +209,7 @@ def build_tables(keys, W, K, L, stride=None, return_codes=False):
     nch = lsh_num_chunks(N, stride)
     dev = keys.device
     offsets = torch.empty(B, Hkv, L, (1 << K) + 1, dtype=torch.int32, device=dev)
-    indices = torch.empty(B, Hkv, L, N, dtype=torch.int32, device=dev)
+    indices = torch.empty(B, Hkv, L, N, dtype=torch.int16, device=dev)
     bounds = torch.empty(B, Hkv, L, 1 << K, nch + 1, dtype=torch.int32, device=dev)
     codes = torch.empty(B, Hkv, L, N, dtype=torch.int16, device=dev) if return_codes else None
     lsh_build_tables(keys, W, K, L, stride, offsets, indices, bounds, codes)

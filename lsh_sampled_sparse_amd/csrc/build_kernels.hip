@@ -151,90 +151,302 @@ __global__ __launch_bounds__(kProjThreads) void project_codes_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Per-table stable bucketing.
+// Per-table stable bucketing: a counting sort of key indices by code.
 //
-// Key indices of a table are split into sub-chunks of 2^sub_log2 keys; each
-// sub-chunk is owned by one wave, which walks it in order in batches of 64.
-// Inside a batch, lanes with equal codes are grouped: every lane writes its
-// lane id to a per-wave LDS slot addressed by its code; lanes that read back
-// another id belong to a group of size >= 2, and those groups are peeled one
-// code at a time with a ballot.  A lane's rank is the number of lower lanes
-// of its group, so the order inside a bucket is the key order.
+// Output format: bucket c of table l occupies positions offsets[c] ..
+// offsets[c + 1] of the table's index array, split by key chunk (chunk j =
+// keys [j stride, (j + 1) stride)) at bounds[c][j]; inside a bucket the keys
+// ascend, and each entry stores the key's index relative to its chunk start,
+// which fits 16 bits because stride <= 65536.
+//
+// Fast path (K <= 10), two kernels over tiles of at most 8192 keys that nest
+// in the chunks:
+//   bucket_count    one workgroup per table: per-tile histograms in LDS, one
+//                   scan over (bucket, tile) that writes the offsets, the chunk
+//                   bounds and every tile's start position in every bucket
+//   bucket_scatter  one workgroup per tile: a stable counting sort of the
+//                   tile in LDS (per-wave histograms for the order across
+//                   waves, an LDS match table for the order inside a wave),
+//                   then every bucket's run of the tile is written with
+//                   consecutive lanes on consecutive addresses.
+// General path (any K up to 15): bucket_tables, one workgroup per table that
+// scatters straight to global memory.
 // ---------------------------------------------------------------------------
-constexpr int kBucketThreads = 1024;
-constexpr int kBucketWaves = kBucketThreads / 64;
-constexpr int kSlotsPerWave = 1024;
+constexpr int kPrefetch = 8;            // 64-key batches whose codes are loaded ahead
 
-__device__ __forceinline__ void group_lanes(int code, bool valid, uint8_t* slots, int lane,
-                                            int& rank, int& size) {
-  // volatile: the read must observe the other lanes' writes, not this lane's
-  volatile uint8_t* vs = slots;
-  const int slot = code & (kSlotsPerWave - 1);
-  if (valid) vs[slot] = static_cast<uint8_t>(lane);
-  __builtin_amdgcn_wave_barrier();
-  const int winner = valid ? vs[slot] : lane;
-  uint64_t losers = ballot(valid && winner != lane);
-  rank = 0;
-  size = 1;
-  while (losers) {
-    const int f = __builtin_ctzll(losers);
-    const int c = __builtin_amdgcn_readlane(code, f);
-    const bool mine = valid && code == c;
-    const uint64_t m = ballot(mine);
-    if (mine) {
-      rank = mbcnt(m);
-      size = __builtin_popcountll(m);
-    }
-    losers &= ~m;
-  }
-  __builtin_amdgcn_wave_barrier();
-}
+// -------- fast path: histogram + scan
+constexpr int kCountTThreads = 512;
 
-__global__ __launch_bounds__(kBucketThreads) void bucket_tables_kernel(
+__global__ __launch_bounds__(kCountTThreads) void bucket_count_kernel(
     const uint16_t* __restrict__ codes,   // [U][L][N]
-    int N, int K, int L, int nJ, int spc_log2, int sub_log2,
+    int N, int K, int L, int tile_log2, int ntiles, int nJ, int tpc_log2,
     int32_t* __restrict__ offsets,        // [U][L][2^K + 1]
-    int32_t* __restrict__ indices,        // [U][L][N]
-    int32_t* __restrict__ bounds) {       // [U][L][2^K][nJ + 1]
-  extern __shared__ __attribute__((aligned(16))) int32_t smem[];
-  __shared__ int32_t wave_tot[kBucketWaves];
+    int32_t* __restrict__ bounds,         // [U][L][2^K][nJ + 1]
+    int32_t* __restrict__ tstart) {       // [U][L][ntiles][2^K]
+  extern __shared__ __attribute__((aligned(16))) int32_t hist[];   // [ntiles][nb]
+  __shared__ int32_t wave_tot[kCountTThreads / 64];
   const int nb = 1 << K;
-  const int nSub = nJ << spc_log2;
-  int32_t* pos = smem;                                                   // [nSub][nb]
-  uint8_t* slots = reinterpret_cast<uint8_t*>(smem + static_cast<size_t>(nSub) * nb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l = blockIdx.x, u = blockIdx.y;
   const size_t tbl = static_cast<size_t>(u) * L + l;
   const uint16_t* cd = codes + tbl * N;
-  uint8_t* my_slots = slots + wave * kSlotsPerWave;
 
-  for (int i = tid; i < nSub * nb; i += kBucketThreads) pos[i] = 0;
+  for (int i = tid; i < ntiles * nb; i += kCountTThreads) hist[i] = 0;
   __syncthreads();
-
-  // pass 1: per-sub-chunk histograms
-  for (int s = wave; s < nSub; s += kBucketWaves) {
-    const int beg = s << sub_log2, end = min(N, beg + (1 << sub_log2));
-    int32_t* ps = pos + static_cast<size_t>(s) * nb;
-    for (int b = beg; b < end; b += 64) {
-      const int n = b + lane;
-      const bool valid = n < end;
-      const int code = valid ? cd[n] : 0;
-      int rank, size;
-      group_lanes(code, valid, my_slots, lane, rank, size);
-      if (valid && rank == 0) ps[code] += size;
-      __builtin_amdgcn_wave_barrier();
+  for (int n0 = tid; n0 < N; n0 += kCountTThreads * kPrefetch) {
+    int pf[kPrefetch];
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+      const int n = n0 + k * kCountTThreads;
+      pf[k] = n < N ? static_cast<int>(cd[n]) : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+      const int n = n0 + k * kCountTThreads;
+      if (pf[k] >= 0) atomicAdd(&hist[(n >> tile_log2) * nb + pf[k]], 1);
     }
   }
   __syncthreads();
 
-  // pass 2: offsets (scan over buckets) and per-sub-chunk start positions
+  const int bpt = (nb + kCountTThreads - 1) / kCountTThreads;   // buckets per thread
+  const int c0 = tid * bpt, c1 = min(nb, c0 + bpt);
+  int local = 0;
+  for (int c = c0; c < c1; ++c)
+    for (int t = 0; t < ntiles; ++t) local += hist[t * nb + c];
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int w = 0; w < wave; ++w) run += wave_tot[w];
+  int32_t* off = offsets + tbl * (nb + 1);
+  int32_t* ts = tstart + tbl * ntiles * nb;
+  for (int c = c0; c < c1; ++c) {
+    off[c] = run;
+    int32_t* bnd = bounds + (tbl * nb + c) * (nJ + 1);
+    for (int t = 0; t < ntiles; ++t) {
+      if ((t & ((1 << tpc_log2) - 1)) == 0) bnd[t >> tpc_log2] = run;
+      ts[t * nb + c] = run;
+      run += hist[t * nb + c];
+    }
+    bnd[nJ] = run;
+  }
+  if (tid == 0) off[nb] = N;
+}
+
+// -------- fast path: per-tile stable scatter
+constexpr int kScatThreads = 512;
+constexpr int kScatWaves = kScatThreads / 64;
+constexpr int kScatBatches = 16;        // 64-key batches per wave: tiles of <= 8192 keys
+constexpr int kMaxTileLog2 = 13;
+
+// Mask of the valid lanes of this wave whose code equals this lane's, from two
+// 32-entry tables of 64-bit lane masks indexed by the low and the high five
+// code bits (K <= 10): every lane ORs its bit into both entries, and the AND
+// of the two entries it reads back holds exactly the lanes with its code.  The
+// entries are cleared again before returning.  LDS operations of one wave are
+// performed in issue order, so the reads see every lane's OR.
+__device__ __forceinline__ uint64_t match_lds(int code, bool valid, uint64_t* tab, int lane) {
+  volatile uint64_t* vt = tab;
+  const int lo = code & 31, hi = 32 + (code >> 5);
+  if (valid) {
+    atomicOr(reinterpret_cast<unsigned long long*>(&tab[lo]), 1ull << lane);
+    atomicOr(reinterpret_cast<unsigned long long*>(&tab[hi]), 1ull << lane);
+  }
+  __builtin_amdgcn_wave_barrier();
+  const uint64_t m = valid ? (vt[lo] & vt[hi]) : 0ull;
+  __builtin_amdgcn_wave_barrier();
+  if (valid) {
+    vt[lo] = 0ull;
+    vt[hi] = 0ull;
+  }
+  __builtin_amdgcn_wave_barrier();
+  return m;
+}
+
+__global__ __launch_bounds__(kScatThreads) void bucket_scatter_kernel(
+    const uint16_t* __restrict__ codes,   // [U][L][N]
+    const int32_t* __restrict__ tstart,   // [U][L][ntiles][2^K]
+    int N, int K, int L, int tile_log2, int ntiles, int stride_log2, int tables,
+    uint16_t* __restrict__ indices) {     // [U][L][N]
+  extern __shared__ __attribute__((aligned(16))) int32_t sm[];
+  const int nb = 1 << K;
+  const int T = 1 << tile_log2;
+  int32_t* wh = sm;                                   // [kScatWaves][nb] cursors
+  int32_t* lofs = wh + kScatWaves * nb;               // [nb] bucket start in the tile
+  int32_t* gst = lofs + nb;                           // [nb] bucket start in the table
+  uint64_t* mtab = reinterpret_cast<uint64_t*>(gst + nb);          // [kScatWaves][64]
+  uint16_t* obuf = reinterpret_cast<uint16_t*>(mtab + kScatWaves * 64);   // [T] chunk-relative key
+  uint16_t* ocode = obuf + T;                                        // [T] code
+  __shared__ int32_t wave_tot[kScatWaves];
+
+  // tiles of 8 consecutive tables go to one XCD (workgroups are dealt to the
+  // eight XCDs in turn), so the runs that neighbouring tiles write to the same
+  // cache lines meet in that XCD's L2
+  const int bid = blockIdx.x;
+  const int grp = bid / (8 * ntiles), rem = bid % (8 * ntiles);
+  const int t = rem / 8;
+  const int tb = grp * 8 + (rem % 8);     // table index u * L + l
+  if (tb >= tables) return;
+  const size_t table = static_cast<size_t>(tb);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tbeg = t << tile_log2;
+  const int tlen = min(T, N - tbeg);
+  const int cbase = (tbeg >> stride_log2) << stride_log2;
+  const uint16_t* cd = codes + table * N;
+
+  for (int i = tid; i < kScatWaves * nb; i += kScatThreads) wh[i] = 0;
+  for (int i = tid; i < kScatWaves * 64; i += kScatThreads) mtab[i] = 0ull;
+  const int32_t* ts = tstart + (table * ntiles + t) * nb;
+  for (int c = tid; c < nb; c += kScatThreads) gst[c] = ts[c];
+  // this wave's keys: [wbeg, wend) of the tile, batch k = keys wbeg + 64 k + lane
+  const int per = T / kScatWaves;
+  const int wbeg = tbeg + wave * per;
+  const int wend = min(tbeg + tlen, wbeg + per);
+  int cr[kScatBatches];
+#pragma unroll
+  for (int k = 0; k < kScatBatches; ++k) {
+    const int n = wbeg + 64 * k + lane;
+    cr[k] = (64 * k < per && n < wend) ? static_cast<int>(cd[n]) : -1;
+  }
+  __syncthreads();
+  int32_t* my = wh + wave * nb;
+#pragma unroll
+  for (int k = 0; k < kScatBatches; ++k)
+    if (cr[k] >= 0) atomicAdd(&my[cr[k]], 1);
+  __syncthreads();
+
+  // bucket c: exclusive prefix over waves in place, tile-local start in lofs
+  const int bpt = (nb + kScatThreads - 1) / kScatThreads;
+  const int c0 = tid * bpt, c1 = min(nb, c0 + bpt);
+  int local = 0;
+  for (int c = c0; c < c1; ++c)
+    for (int w = 0; w < kScatWaves; ++w) local += wh[w * nb + c];
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int w = 0; w < wave; ++w) run += wave_tot[w];
+  for (int c = c0; c < c1; ++c) {
+    lofs[c] = run;
+    for (int w = 0; w < kScatWaves; ++w) {
+      const int x = wh[w * nb + c];
+      wh[w * nb + c] = run;
+      run += x;
+    }
+  }
+  __syncthreads();
+
+  // stable placement of this wave's keys into the tile's local CSR
+  uint64_t* mt = mtab + wave * 64;
+#pragma unroll
+  for (int k = 0; k < kScatBatches; ++k) {
+    if (64 * k >= per) break;
+    const bool valid = cr[k] >= 0;
+    const int code = valid ? cr[k] : 0;
+    const uint64_t m = match_lds(code, valid, mt, lane);
+    const int rank = mbcnt(m);
+    const int p = valid ? my[code] : 0;
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      obuf[p + rank] = static_cast<uint16_t>(wbeg + 64 * k + lane - cbase);
+      ocode[p + rank] = static_cast<uint16_t>(code);
+      if (rank == 0) my[code] = p + __builtin_popcountll(m);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+
+  // every bucket's run of this tile: entry e of the local CSR goes to table
+  // position gst[c] + (e - lofs[c])
+  uint16_t* out = indices + table * N;
+  for (int e = tid; e < tlen; e += kScatThreads) {
+    const int c = ocode[e];
+    out[gst[c] + (e - lofs[c])] = obuf[e];
+  }
+}
+
+size_t scatter_lds_bytes(int K, int tile_log2) {
+  const size_t nb = size_t(1) << K;
+  return (kScatWaves * nb + 2 * nb) * 4 + kScatWaves * 64 * 8 + (size_t(2) << tile_log2) * 2;
+}
+
+// -------- general path (any K): one workgroup per table
+//
+// Key indices are split into sub-chunks of 2^sub_log2 keys, each owned by
+// one wave that walks it in order in batches of 64:
+//   pass 1  per-sub-chunk histograms with LDS atomic adds
+//   pass 2  one scan over (bucket, sub-chunk) gives the offsets, the chunk
+//           bounds and every sub-chunk's start position in every bucket
+//   pass 3  scatter: the lanes of a batch holding the same code are found
+//           with one ballot per code bit; a lane's rank among them is the
+//           number of such lanes below it.
+constexpr int kBucketThreads = 1024;
+constexpr int kBucketWaves = kBucketThreads / 64;
+
+// Mask of the valid lanes whose code equals this lane's: the AND over the K
+// code bits of the ballot of the bit where this lane's bit is 1, or of its
+// complement where it is 0.
+__device__ __forceinline__ uint64_t match_code(int code, bool valid, int K) {
+  uint64_t m = ballot(valid);
+  for (int b = 0; b < K; ++b) {
+    const bool bit = (code >> b) & 1;
+    const uint64_t B = ballot(bit);
+    m &= bit ? B : ~B;
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(kBucketThreads) void bucket_tables_kernel(
+    const uint16_t* __restrict__ codes,   // [U][L][N]
+    int N, int K, int L, int nJ, int spc_log2, int sub_log2, int stride_log2,
+    int32_t* __restrict__ offsets,        // [U][L][2^K + 1]
+    uint16_t* __restrict__ indices,       // [U][L][N]
+    int32_t* __restrict__ bounds) {       // [U][L][2^K][nJ + 1]
+  extern __shared__ __attribute__((aligned(16))) int32_t pos[];   // [nSub][nb]
+  __shared__ int32_t wave_tot[kBucketWaves];
+  const int nb = 1 << K;
+  const int nSub = nJ << spc_log2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l = blockIdx.x, u = blockIdx.y;
+  const size_t tbl = static_cast<size_t>(u) * L + l;
+  const uint16_t* cd = codes + tbl * N;
+
+  for (int i = tid; i < nSub * nb; i += kBucketThreads) pos[i] = 0;
+  __syncthreads();
+
+  for (int s = wave; s < nSub; s += kBucketWaves) {
+    const int beg = s << sub_log2, end = min(N, beg + (1 << sub_log2));
+    int32_t* ps = pos + static_cast<size_t>(s) * nb;
+    for (int b0 = beg; b0 < end; b0 += 64 * kPrefetch) {
+      int pf[kPrefetch];
+#pragma unroll
+      for (int k = 0; k < kPrefetch; ++k) {
+        const int n = b0 + 64 * k + lane;
+        pf[k] = n < end ? static_cast<int>(cd[n]) : -1;
+      }
+#pragma unroll
+      for (int k = 0; k < kPrefetch; ++k)
+        if (pf[k] >= 0) atomicAdd(&ps[pf[k]], 1);
+    }
+  }
+  __syncthreads();
+
   {
-    const int bpt = (nb + kBucketThreads - 1) / kBucketThreads;   // buckets per thread
+    const int bpt = (nb + kBucketThreads - 1) / kBucketThreads;
     const int c0 = tid * bpt, c1 = min(nb, c0 + bpt);
     int local = 0;
     for (int c = c0; c < c1; ++c)
       for (int s = 0; s < nSub; ++s) local += pos[static_cast<size_t>(s) * nb + c];
-    // block exclusive scan of `local`
     int incl = local;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -262,24 +474,38 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_tables_kernel(
   }
   __syncthreads();
 
-  // pass 3: stable scatter
-  int32_t* out = indices + tbl * N;
+  uint16_t* out = indices + tbl * N;
   for (int s = wave; s < nSub; s += kBucketWaves) {
     const int beg = s << sub_log2, end = min(N, beg + (1 << sub_log2));
+    const int cbase = (beg >> stride_log2) << stride_log2;
     int32_t* ps = pos + static_cast<size_t>(s) * nb;
-    for (int b = beg; b < end; b += 64) {
-      const int n = b + lane;
-      const bool valid = n < end;
-      const int code = valid ? cd[n] : 0;
-      int rank, size;
-      group_lanes(code, valid, my_slots, lane, rank, size);
-      const int p = valid ? ps[code] : 0;
-      __builtin_amdgcn_wave_barrier();
-      if (valid) out[p + rank] = n;
-      if (valid && rank == 0) ps[code] = p + size;
-      __builtin_amdgcn_wave_barrier();
+    for (int b0 = beg; b0 < end; b0 += 64 * kPrefetch) {
+      int pf[kPrefetch];
+#pragma unroll
+      for (int k = 0; k < kPrefetch; ++k) {
+        const int n = b0 + 64 * k + lane;
+        pf[k] = n < end ? static_cast<int>(cd[n]) : -1;
+      }
+#pragma unroll
+      for (int k = 0; k < kPrefetch; ++k) {
+        if (b0 + 64 * k >= end) break;
+        const int n = b0 + 64 * k + lane;
+        const bool valid = pf[k] >= 0;
+        const int code = valid ? pf[k] : 0;
+        const uint64_t m = match_code(code, valid, K);
+        const int rank = mbcnt(m);
+        const int p = valid ? ps[code] : 0;
+        __builtin_amdgcn_wave_barrier();
+        if (valid) out[p + rank] = static_cast<uint16_t>(n - cbase);
+        if (valid && rank == 0) ps[code] = p + __builtin_popcountll(m);
+        __builtin_amdgcn_wave_barrier();
+      }
     }
   }
+}
+
+size_t bucket_lds_bytes(int nJ, int spc_log2, int K) {
+  return static_cast<size_t>(nJ << spc_log2) * (size_t(1) << K) * 4;
 }
 
 // ---------------------------------------------------------------------------
@@ -303,23 +529,47 @@ static hipError_t launch_project(const void* keys, const void* W, void* WT, uint
                 codes, N, K, L, nslab);
 }
 
+bool bucket_fast_path(int N, int K, int stride_log2, int* tile_log2, int* ntiles) {
+  const int tl = stride_log2 < kMaxTileLog2 ? stride_log2 : kMaxTileLog2;
+  const long long nt = (static_cast<long long>(N) + (1ll << tl) - 1) >> tl;
+  if (tile_log2) *tile_log2 = tl;
+  if (ntiles) *ntiles = static_cast<int>(nt);
+  return K <= 10 && (nt << K) <= 32768;
+}
+
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream) {
   hipError_t e = (a.dtype == 1)
       ? launch_project<BF16>(a.keys, a.W, a.wt, a.codes, a.U, a.N, a.K, a.L, stream)
       : launch_project<F32>(a.keys, a.W, a.wt, a.codes, a.U, a.N, a.K, a.L, stream);
   if (e != hipSuccess) return e;
+  int tile_log2 = 0, ntiles = 0;
+  if (a.tstart && bucket_fast_path(a.N, a.K, a.stride_log2, &tile_log2, &ntiles)) {
+    const size_t lds1 = static_cast<size_t>(ntiles) << a.K << 2;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bucket_count_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds1));
+    if (e != hipSuccess) return e;
+    e = launch(kKBucketCount, bucket_count_kernel, dim3(a.L, a.U), dim3(kCountTThreads),
+               static_cast<unsigned>(lds1), stream, static_cast<const uint16_t*>(a.codes), a.N, a.K, a.L,
+               tile_log2, ntiles, a.nJ, a.stride_log2 - tile_log2, a.offsets, a.bounds, a.tstart);
+    if (e != hipSuccess) return e;
+    const size_t lds2 = scatter_lds_bytes(a.K, tile_log2);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bucket_scatter_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds2));
+    if (e != hipSuccess) return e;
+    const int tables = a.U * a.L;
+    const int ngroups = (tables + 7) / 8;
+    return launch(kKBucketScatter, bucket_scatter_kernel, dim3(ngroups * 8 * ntiles), dim3(kScatThreads),
+                  static_cast<unsigned>(lds2), stream, static_cast<const uint16_t*>(a.codes),
+                  static_cast<const int32_t*>(a.tstart), a.N, a.K, a.L, tile_log2, ntiles, a.stride_log2,
+                  tables, a.indices);
+  }
   const size_t lds = bucket_lds_bytes(a.nJ, a.spc_log2, a.K);
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(bucket_tables_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
   return launch(kKBucket, bucket_tables_kernel, dim3(a.L, a.U), dim3(kBucketThreads),
                 static_cast<unsigned>(lds), stream, static_cast<const uint16_t*>(a.codes), a.N, a.K, a.L,
-                a.nJ, a.spc_log2, a.stride_log2 - a.spc_log2, a.offsets, a.indices, a.bounds);
-}
-
-size_t bucket_lds_bytes(int nJ, int spc_log2, int K) {
-  return static_cast<size_t>(nJ << spc_log2) * (size_t(1) << K) * 4 +
-         static_cast<size_t>(kBucketWaves) * kSlotsPerWave;
+                a.nJ, a.spc_log2, a.stride_log2 - a.spc_log2, a.stride_log2, a.offsets, a.indices, a.bounds);
 }
 
 }  // namespace lsh

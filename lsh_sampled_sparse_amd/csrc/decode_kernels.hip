@@ -35,26 +35,45 @@ constexpr float kLnUFloor = -69.07755278982137f;   // ln(1e-30)
 // fp64 at theta_j = j pi / kLnuTable and interpolated linearly; T ln P is
 // evaluated exactly from ln p = log1p(-theta/pi).
 // ---------------------------------------------------------------------------
-__device__ double lnu_correction(double theta, int K, int L, int T) {
+__device__ __forceinline__ double wave_max_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// g(theta) for one table entry, computed by one wave: lane handles the terms
+// i = T + lane + 64 k of the sum, whose log binomial coefficients are in
+// lc[i] = ln C(L, i); the terms are combined by a log-sum-exp over the wave.
+__device__ double lnu_correction_wave(double theta, int K, int L, int T, const double* lc, int lane) {
   const double p = 1.0 - theta / 3.14159265358979323846;
   const double P = (K == 0) ? 1.0 : pow(p, static_cast<double>(K));
   const double lP = log(P), lQ = log1p(-P);
-  const double lgL = lgamma(static_cast<double>(L) + 1.0);
-  // streaming log-sum-exp over the terms i = T..L
-  double m = -INFINITY, s = 0.0;
-  for (int i = T; i <= L; ++i) {
-    double t = lgL - lgamma(static_cast<double>(i) + 1.0) - lgamma(static_cast<double>(L - i) + 1.0);
-    if (i > T) t += (i - T) * lP;
-    if (L > i) t += (L - i) * lQ;
-    if (t == -INFINITY) continue;
-    if (t > m) {
-      s = s * exp(m - t) + 1.0;
-      m = t;
-    } else {
-      s += exp(t - m);
+  double t[4];
+  double m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = T + lane + 64 * k;
+    double x = -INFINITY;
+    if (i <= L) {
+      x = lc[i];
+      if (i > T) x += (i - T) * lP;   // 0 * ln 0 is 1 here: skip the zero power
+      if (L > i) x += (L - i) * lQ;
     }
+    t[k] = x;
+    m = fmax(m, x);
   }
-  return m + log(s);
+  m = wave_max_f64(m);
+  double sum = 0.0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (t[k] != -INFINITY) sum += exp(t[k] - m);
+  sum = wave_sum_f64(sum);
+  return m + log(sum);
 }
 
 __device__ __forceinline__ float log_inclusion(float cosv, const float* tab, float TK) {
@@ -69,34 +88,46 @@ __device__ __forceinline__ float log_inclusion(float cosv, const float* tab, flo
 }
 
 // ---------------------------------------------------------------------------
-// qhash: codes of up to 4 query heads x a block of whole tables per workgroup.
-// Workgroups with blockIdx.y >= head_blocks fill the ln-u table instead.
+// qhash: SimHash codes of 16 query heads x a block of whole tables (at most
+// 64 projection columns) per workgroup.  Lane c of every wave owns column c of
+// the block and wave w sums dims [32 w, 32 w + 32), so each lane issues its 32
+// W loads at once; the four partial sums meet in LDS.  Workgroups with
+// blockIdx.y >= head_blocks fill the ln-u table instead, one entry per wave.
 // ---------------------------------------------------------------------------
+constexpr int kQHeads = 16;
+
 template <typename T>
 __global__ __launch_bounds__(256) void qhash_kernel(const typename T::storage* __restrict__ q,
                                                     const typename T::storage* __restrict__ W,
                                                     uint16_t* __restrict__ qcodes, float* __restrict__ lnu_tab,
                                                     int BH, int K, int L, int Tth, int head_blocks) {
-  __shared__ float qs[4][kHeadDim];
-  __shared__ uint8_t sgn[4][256];
-  const int tid = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) float qs[kQHeads][kHeadDim];
+  __shared__ float part[4][kQHeads][64];
+  __shared__ uint8_t sgn[kQHeads][64];
+  __shared__ double lc[256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (static_cast<int>(blockIdx.y) >= head_blocks) {
-    const int j = ((blockIdx.y - head_blocks) * gridDim.x + blockIdx.x) * 256 + tid;
-    if (j <= kLnuTable && K > 0)
-      lnu_tab[j] = static_cast<float>(lnu_correction(j * (3.14159265358979323846 / kLnuTable), K, L, Tth));
+    if (K == 0) return;
+    if (tid <= L)
+      lc[tid] = lgamma(static_cast<double>(L) + 1.0) - lgamma(static_cast<double>(tid) + 1.0) -
+                lgamma(static_cast<double>(L - tid) + 1.0);
+    __syncthreads();
+    const int j = ((blockIdx.y - head_blocks) * gridDim.x + blockIdx.x) * 4 + wave;
+    const double g = lnu_correction_wave(j * (3.14159265358979323846 / kLnuTable), K, L, Tth, lc, lane);
+    if (j <= kLnuTable && lane == 0) lnu_tab[j] = static_cast<float>(g);
     return;
   }
-  const int h0 = blockIdx.y * 4;
+  const int h0 = blockIdx.y * kQHeads;
   if (K == 0) {
-    for (int e = blockIdx.x * 256 + tid; e < 4 * L; e += gridDim.x * 256) {
+    for (int e = blockIdx.x * 256 + tid; e < kQHeads * L; e += gridDim.x * 256) {
       const int h = h0 + e / L;
       if (h < BH) qcodes[static_cast<size_t>(h) * L + e % L] = 0;
     }
     return;
   }
-  const int tpw = 256 / K;              // whole tables per workgroup
+  const int tpw = 64 / K;               // whole tables per workgroup
   const int l0 = blockIdx.x * tpw;
-  for (int e = tid; e < 4 * kHeadDim; e += 256) {
+  for (int e = tid; e < kQHeads * kHeadDim; e += 256) {
     const int h = h0 + e / kHeadDim;
     float v = 0.f;
     if (h < BH) {
@@ -109,28 +140,44 @@ __global__ __launch_bounds__(256) void qhash_kernel(const typename T::storage* _
   }
   __syncthreads();
   const int LK = L * K;
-  const int col = l0 * K + tid;
-  if (tid < tpw * K && col < LK) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < kHeadDim; ++i) {
-      float w;
-      if constexpr (sizeof(typename T::storage) == 2)
-        w = bf16_to_f32(W[static_cast<size_t>(i) * LK + col]);
-      else
-        w = W[static_cast<size_t>(i) * LK + col];
+  const int col = l0 * K + lane;
+  const bool colv = lane < tpw * K && col < LK;
+  float w[32];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = fmaf(qs[j][i], w, acc[j]);
+  for (int i = 0; i < 32; ++i) {
+    const size_t at = static_cast<size_t>(32 * wave + i) * LK + (colv ? col : 0);
+    if constexpr (sizeof(typename T::storage) == 2)
+      w[i] = bf16_to_f32(W[at]);
+    else
+      w[i] = W[at];
+  }
+#pragma unroll
+  for (int hh = 0; hh < kQHeads; ++hh) {
+    const floatx4_t* qv = reinterpret_cast<const floatx4_t*>(&qs[hh][32 * wave]);
+    float acc = 0.f;
+#pragma unroll
+    for (int i4 = 0; i4 < 8; ++i4) {
+      const floatx4_t x = qv[i4];
+      acc = fmaf(x[0], w[4 * i4 + 0], acc);
+      acc = fmaf(x[1], w[4 * i4 + 1], acc);
+      acc = fmaf(x[2], w[4 * i4 + 2], acc);
+      acc = fmaf(x[3], w[4 * i4 + 3], acc);
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sgn[j][tid] = acc[j] > 0.f ? 1 : 0;
+    part[wave][hh][lane] = acc;
   }
   __syncthreads();
-  if (tid < 4 * tpw) {
-    const int j = tid / tpw, t = tid % tpw;
-    const int l = l0 + t, h = h0 + j;
+  for (int e = tid; e < kQHeads * 64; e += 256) {
+    const int hh = e >> 6, c = e & 63;
+    const float x = part[0][hh][c] + part[1][hh][c] + part[2][hh][c] + part[3][hh][c];
+    sgn[hh][c] = x > 0.f ? 1 : 0;
+  }
+  __syncthreads();
+  for (int e = tid; e < kQHeads * tpw; e += 256) {
+    const int hh = e / tpw, t = e % tpw;
+    const int l = l0 + t, h = h0 + hh;
     if (h < BH && l < L) {
       uint32_t code = 0;
-      for (int b = 0; b < K; ++b) code |= static_cast<uint32_t>(sgn[j][t * K + b]) << b;
+      for (int b = 0; b < K; ++b) code |= static_cast<uint32_t>(sgn[hh][t * K + b]) << b;
       qcodes[static_cast<size_t>(h) * L + l] = static_cast<uint16_t>(code);
     }
   }
@@ -139,11 +186,12 @@ __global__ __launch_bounds__(256) void qhash_kernel(const typename T::storage* _
 // ---------------------------------------------------------------------------
 // count_select: one workgroup per (query head, key chunk).
 // ---------------------------------------------------------------------------
-constexpr int kCountThreads = 256;
+constexpr int kCountThreads = 1024;
+constexpr int kCountUnroll = 8;   // index loads each thread keeps in flight
 
 __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
     const uint16_t* __restrict__ qcodes,   // [BH][L]
-    const int32_t* __restrict__ indices,   // [U][L][N]
+    const uint16_t* __restrict__ indices,  // [U][L][N] chunk-relative key indices
     const int32_t* __restrict__ bounds,    // [U][L][2^K][nJ + 1]
     int Hq, int Hkv, int N, int K, int L, int T, int stride_log2, int nJ,
     uint32_t* __restrict__ bitmask,        // [BH][Nw]
@@ -165,13 +213,14 @@ __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
   for (int i = tid; i < cwords; i += kCountThreads) cnt[i] = 0;
 
   // segment of bucket qcode_l restricted to this chunk, for every table l
+  // (L <= 255, so the first four waves hold one table per thread)
   int len = 0;
   if (tid < L) {
     const int qc = qcodes[static_cast<size_t>(bh) * L + tid];
     const int32_t* bp = bounds + ((static_cast<size_t>(u) * L + tid) * nb + qc) * (nJ + 1) + J;
-    const int s = bp[0];
-    len = bp[1] - s;
-    seg_start[tid] = s;
+    const int s0 = bp[0];
+    len = bp[1] - s0;
+    seg_start[tid] = s0;
   }
   int incl = len;
 #pragma unroll
@@ -179,22 +228,35 @@ __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
     const int v = __shfl_up(incl, o);
     if (lane >= o) incl += v;
   }
-  if (lane == 63) wave_tot[wave] = incl;
+  if (lane == 63 && wave < 4) wave_tot[wave] = incl;
   __syncthreads();
-  int wbase = 0;
-  for (int w = 0; w < wave; ++w) wbase += wave_tot[w];
-  seg_v[tid + 1] = wbase + incl;
-  if (tid == 0) seg_v[0] = 0;
+  if (tid < 256) {
+    int wbase = 0;
+    for (int w = 0; w < wave; ++w) wbase += wave_tot[w];
+    seg_v[tid + 1] = wbase + incl;
+    if (tid == 0) seg_v[0] = 0;
+  }
   __syncthreads();
 
+  // walk the concatenated segments: entry v of segment l is
+  // indices[u][l][seg_start[l] + v - seg_v[l]], the key's offset in this chunk
   const int total = seg_v[L];
-  const int32_t* ib = indices + static_cast<size_t>(u) * L * N;
+  const uint16_t* ib = indices + static_cast<size_t>(u) * L * N;
   int l = 0;
-  for (int v = tid; v < total; v += kCountThreads) {
-    while (v >= seg_v[l + 1]) ++l;
-    const int n = ib[static_cast<size_t>(l) * N + seg_start[l] + (v - seg_v[l])];
-    const int loc = n - cbeg;
-    atomicAdd(&cnt[loc >> 2], 1u << ((loc & 3) * 8));
+  for (int v0 = tid; v0 < total; v0 += kCountThreads * kCountUnroll) {
+    int loc[kCountUnroll];
+#pragma unroll
+    for (int k = 0; k < kCountUnroll; ++k) {
+      const int v = v0 + k * kCountThreads;
+      loc[k] = -1;
+      if (v < total) {
+        while (v >= seg_v[l + 1]) ++l;
+        loc[k] = ib[static_cast<size_t>(l) * N + seg_start[l] + (v - seg_v[l])];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kCountUnroll; ++k)
+      if (loc[k] >= 0) atomicAdd(&cnt[loc[k] >> 2], 1u << ((loc[k] & 3) * 8));
   }
   __syncthreads();
 
@@ -226,9 +288,9 @@ __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
   if (lane == 0) wave_tot[wave] = mysel;
   __syncthreads();
   if (tid == 0) {
-    int s = 0;
-    for (int w = 0; w < kCountThreads / 64; ++w) s += wave_tot[w];
-    chunk_nsel[static_cast<size_t>(bh) * nJ + J] = s;
+    int t = 0;
+    for (int w = 0; w < kCountThreads / 64; ++w) t += wave_tot[w];
+    chunk_nsel[static_cast<size_t>(bh) * nJ + J] = t;
   }
 }
 
@@ -489,33 +551,72 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// merge: one workgroup per query head.
+// merge: one workgroup (4 waves) per query head.  Wave w folds the splits
+// s = w, w + 4, ... into a running (max, sum, acc) with each lane owning two
+// dims; the four wave states are combined through LDS.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kHeadDim) void merge_kernel(const float* __restrict__ partials,
-                                                         const int32_t* __restrict__ chunk_nsel,
-                                                         int nsplit, int nJ, float* __restrict__ out,
-                                                         float* __restrict__ lse, int32_t* __restrict__ nsel) {
-  const int bh = blockIdx.x, d = threadIdx.x;
+constexpr int kMergeThreads = 256;
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ partials,
+                                                              const int32_t* __restrict__ chunk_nsel,
+                                                              int nsplit, int nJ, float* __restrict__ out,
+                                                              float* __restrict__ lse, int32_t* __restrict__ nsel) {
+  __shared__ float wm[4], wl[4];
+  __shared__ float wacc[4][kHeadDim];
+  __shared__ int wn[4];
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* P = partials + static_cast<size_t>(bh) * nsplit * kPartialStride;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, P[s * kPartialStride + kHeadDim]);
-  float A = 0.f, Lm = 0.f;
+  // the overall max first, so that every split's weight exp(m_s - M) is known
+  // without a running rescale and the loads of all splits can be in flight
+  float mx = -INFINITY;
+  for (int s = tid; s < nsplit; s += kMergeThreads) mx = fmaxf(mx, P[static_cast<size_t>(s) * kPartialStride + kHeadDim]);
+  mx = wave_max(mx);
+  if (lane == 0) wm[wave] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+  __syncthreads();
+  float l = 0.f, a0 = 0.f, a1 = 0.f;
+  const float m = M;
   if (M != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = P[s * kPartialStride + kHeadDim];
-      if (ms == -INFINITY) continue;
-      const float f = __expf(ms - M);
-      A = fmaf(P[s * kPartialStride + d], f, A);
-      Lm = fmaf(P[s * kPartialStride + kHeadDim + 1], f, Lm);
+#pragma unroll 4
+    for (int s = wave; s < nsplit; s += 4) {
+      const float* ps = P + static_cast<size_t>(s) * kPartialStride;
+      const float ms = ps[kHeadDim];
+      const float f = (ms == -INFINITY) ? 0.f : __expf(ms - M);
+      l = fmaf(ps[kHeadDim + 1], f, l);
+      a0 = fmaf(ps[2 * lane], f, a0);
+      a1 = fmaf(ps[2 * lane + 1], f, a1);
     }
   }
-  out[static_cast<size_t>(bh) * kHeadDim + d] = (M == -INFINITY) ? 0.f : A / Lm;
-  if (d == 0) {
-    if (lse) lse[bh] = (M == -INFINITY) ? -INFINITY : M + logf(Lm);
-    if (nsel) {
-      int t = 0;
-      for (int j = 0; j < nJ; ++j) t += chunk_nsel[static_cast<size_t>(bh) * nJ + j];
-      nsel[bh] = t;
+  int cnt = 0;
+  for (int j = tid; j < nJ; j += kMergeThreads) cnt += chunk_nsel[static_cast<size_t>(bh) * nJ + j];
+  cnt = wave_sum_int(cnt);
+  if (lane == 0) {
+    wm[wave] = m;
+    wl[wave] = l;
+    wn[wave] = cnt;
+  }
+  wacc[wave][2 * lane] = a0;
+  wacc[wave][2 * lane + 1] = a1;
+  __syncthreads();
+  if (tid < kHeadDim) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w]);
+    float A = 0.f, Lm = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (wm[w] == -INFINITY) continue;
+        const float f = __expf(wm[w] - M);
+        A = fmaf(wacc[w][tid], f, A);
+        Lm = fmaf(wl[w], f, Lm);
+      }
+    }
+    out[static_cast<size_t>(bh) * kHeadDim + tid] = (M == -INFINITY) ? 0.f : A / Lm;
+    if (tid == 0) {
+      if (lse) lse[bh] = (M == -INFINITY) ? -INFINITY : M + logf(Lm);
+      if (nsel) nsel[bh] = wn[0] + wn[1] + wn[2] + wn[3];
     }
   }
 }
@@ -536,10 +637,10 @@ template <typename T>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   using S = typename T::storage;
   const int BH = a.B * a.Hq;
-  const int head_blocks = (BH + 3) / 4;
-  const int tpw = a.K > 0 ? 256 / a.K : 256;
+  const int head_blocks = (BH + kQHeads - 1) / kQHeads;
+  const int tpw = a.K > 0 ? 64 / a.K : 256;
   const int xblocks = (a.L + tpw - 1) / tpw;
-  const int tab_blocks = (kLnuTable + 1 + xblocks * 256 - 1) / (xblocks * 256);
+  const int tab_blocks = (kLnuTable + 1 + xblocks * 4 - 1) / (xblocks * 4);   // 4 entries per workgroup
   hipError_t e = launch(kKQhash, qhash_kernel<T>, dim3(xblocks, head_blocks + tab_blocks), dim3(256), 0,
                         stream, static_cast<const S*>(a.q), static_cast<const S*>(a.W), a.qcodes,
                         a.lnu_table, BH, a.K, a.L, a.T, head_blocks);
@@ -561,7 +662,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   else
     e = launch_attend<T, 16>(a, stream);
   if (e != hipSuccess) return e;
-  return launch(kKMerge, merge_kernel, dim3(BH), dim3(kHeadDim), 0, stream,
+  return launch(kKMerge, merge_kernel, dim3(BH), dim3(kMergeThreads), 0, stream,
                 static_cast<const float*>(a.partials), static_cast<const int32_t*>(a.chunk_nsel), a.nsplit,
                 a.nJ, a.out, a.lse, a.nsel);
 }

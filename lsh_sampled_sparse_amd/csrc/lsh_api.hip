@@ -60,7 +60,8 @@ lsh_status check_common(int B, int Hkv, int N, int d, int K, int L, int stride, 
 int elem_bytes(int dtype) { return dtype == LSH_BF16 ? 2 : 4; }
 
 struct BuildLayout {
-  size_t wt = 0, codes = 0, total = 0;
+  size_t wt = 0, codes = 0, tstart = 0, total = 0;
+  bool fast = false;
 };
 
 BuildLayout build_layout(int B, int Hkv, int N, int K, int L, int dtype, const Geometry& g, bool need_codes) {
@@ -70,8 +71,11 @@ BuildLayout build_layout(int B, int Hkv, int N, int K, int L, int dtype, const G
   off = align_up(off + static_cast<size_t>(g.LKpad) * 128 * elem_bytes(dtype));
   w.codes = off;
   if (need_codes) off = align_up(off + static_cast<size_t>(B) * Hkv * L * N * sizeof(uint16_t));
+  int tile_log2 = 0, ntiles = 0;
+  w.fast = lsh::bucket_fast_path(N, K, g.stride_log2, &tile_log2, &ntiles);
+  w.tstart = off;
+  if (w.fast) off = align_up(off + static_cast<size_t>(B) * Hkv * L * ntiles * (size_t(1) << K) * sizeof(int32_t));
   w.total = off;
-  (void)K;
   return w;
 }
 
@@ -122,7 +126,8 @@ namespace lsh {
 
 const char* kernel_name(int id) {
   static const char* const names[kKNumKernels] = {
-      "transpose_w", "project_codes", "bucket_tables", "qhash", "count_select", "attend", "merge"};
+      "transpose_w", "project_codes", "bucket_count", "bucket_scatter", "bucket_tables", "qhash",
+      "count_select", "attend", "merge"};
   return (id >= 0 && id < kKNumKernels) ? names[id] : nullptr;
 }
 
@@ -218,7 +223,7 @@ size_t lsh_build_workspace_size(int B, int Hkv, int N, int d, int K, int L, int 
 }
 
 lsh_status lsh_build_tables(const void* keys, const void* W, int B, int Hkv, int N, int d, int K, int L,
-                            int stride, int dtype, int32_t* offsets, int32_t* indices, int32_t* bounds,
+                            int stride, int dtype, int32_t* offsets, uint16_t* indices, int32_t* bounds,
                             uint16_t* key_codes, void* workspace, size_t workspace_bytes, void* stream) {
   Geometry g;
   lsh_status st = check_common(B, Hkv, N, d, K, L, stride, dtype, &g);
@@ -235,6 +240,7 @@ lsh_status lsh_build_tables(const void* keys, const void* W, int B, int Hkv, int
   a.offsets = offsets;
   a.indices = indices;
   a.bounds = bounds;
+  a.tstart = w.fast ? reinterpret_cast<int32_t*>(ws + w.tstart) : nullptr;
   a.U = B * Hkv;
   a.N = N;
   a.K = K;
@@ -254,7 +260,7 @@ size_t lsh_decode_workspace_size(int B, int Hq, int Hkv, int N, int d, int K, in
 }
 
 lsh_status lsh_decode_attention(const void* q, const void* keys, const void* values, const void* W,
-                                const int32_t* indices, const int32_t* bounds, int B, int Hq, int Hkv, int N,
+                                const uint16_t* indices, const int32_t* bounds, int B, int Hq, int Hkv, int N,
                                 int d, int K, int L, int T, int stride, float sm_scale, int dtype, float* out,
                                 float* lse, int32_t* nsel, uint16_t* q_codes, uint8_t* counts, void* workspace,
                                 size_t workspace_bytes, void* stream) {

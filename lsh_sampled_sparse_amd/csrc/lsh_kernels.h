@@ -14,8 +14,9 @@ struct BuildArgs {
   void* wt;              // workspace: [LKpad][128]
   uint16_t* codes;       // [U][L][N] (caller's key_codes or workspace)
   int32_t* offsets;      // [U][L][2^K + 1]
-  int32_t* indices;      // [U][L][N]
+  uint16_t* indices;     // [U][L][N] chunk-relative key indices
   int32_t* bounds;       // [U][L][2^K][nJ + 1]
+  int32_t* tstart;       // workspace [U][L][ntiles][2^K] (fast path), or null
   int U, N, K, L;
   int stride_log2, nJ, spc_log2;
   int dtype;             // 0 = f32, 1 = bf16
@@ -26,7 +27,7 @@ struct DecodeArgs {
   const void* keys;      // [U][N][128]
   const void* values;    // [U][N][128]
   const void* W;         // [128][L*K]
-  const int32_t* indices;
+  const uint16_t* indices;
   const int32_t* bounds;
   uint16_t* qcodes;      // [B*Hq][L]
   uint32_t* bitmask;     // [B*Hq][Nw]
@@ -51,6 +52,8 @@ constexpr int kPartialStride = 130;
 enum KernelId {
   kKTransposeW = 0,
   kKProject,
+  kKBucketCount,
+  kKBucketScatter,
   kKBucket,
   kKQhash,
   kKCountSelect,
@@ -76,6 +79,8 @@ inline hipError_t launch(int id, F kernel, dim3 grid, dim3 block, unsigned lds, 
 }
 
 size_t bucket_lds_bytes(int nJ, int spc_log2, int K);
+// Tiling of the fast bucket build (K <= 10 and ntiles * 2^K <= 32768).
+bool bucket_fast_path(int N, int K, int stride_log2, int* tile_log2, int* ntiles);
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -56,8 +56,28 @@ def compare_codes(gpu, ref, band, K, L):
     return flips
 
 
+def indices_to_global(idx, bnd, stride):
+    """Chunk-relative uint16 entries [L, N] -> key indices (int64), using the
+    chunk bounds [L, 2^K, nchunks + 1]: positions bnd[c, j] .. bnd[c, j + 1]
+    hold keys of chunk j, stored as (key - j * stride)."""
+    idx = u16(idx)
+    bnd = np.asarray(bnd, np.int64)
+    L, N = idx.shape
+    nb, nJ = bnd.shape[1], bnd.shape[2] - 1
+    out = np.empty_like(idx)
+    for l in range(L):
+        lens = np.diff(bnd[l], axis=1).ravel()            # (bucket, chunk) runs in position order
+        assert bnd[l, 0, 0] == 0 and lens.sum() == N and np.all(lens >= 0)
+        assert np.all(bnd[l, 1:, 0] == bnd[l, :-1, nJ])
+        chunk = np.repeat(np.tile(np.arange(nJ, dtype=np.int64), nb), lens)
+        out[l] = idx[l] + chunk * stride
+    return out
+
+
 def check_tables(gpu_off, gpu_idx, gpu_bnd, gpu_codes, ref, K, stride):
-    """Compare one unit's tables.  ``ref`` from ``O.build_tables`` on the same keys."""
+    """Compare one unit's tables.  ``ref`` from ``O.build_tables`` on the same
+    keys; ``gpu_idx`` holds the library's chunk-relative entries."""
+    gpu_idx = indices_to_global(gpu_idx, gpu_bnd, stride)
     gpu_codes = u16(gpu_codes)
     L, N = gpu_codes.shape
     nb = 1 << K
