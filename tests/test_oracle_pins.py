@@ -391,3 +391,32 @@ def test_pins_catch_planted_mistakes(monkeypatch, gold):
     with pytest.raises(AssertionError):
         test_tiny_brute_force(0)
     monkeypatch.undo()
+
+    # 5. sign rule with ties counted as 1 (proj >= 0)
+    def ge_codes(x, W, K, L):
+        x = np.asarray(x, dtype=np.float64)
+        codes = np.zeros((L, x.shape[0]), dtype=np.int64)
+        if K == 0:
+            return codes
+        bits = (x @ np.asarray(W, np.float64) >= 0.0).astype(np.int64)
+        for l in range(L):
+            for b in range(K):
+                codes[l] += bits[:, l * K + b] << b
+        return codes
+    monkeypatch.setattr(O, "simhash_codes", ge_codes)
+    with pytest.raises(AssertionError):
+        test_golden_codes_tables_bounds(gold)
+    monkeypatch.undo()
+
+    # 6. the K-th power dropped from the collision probability
+    real_cp = O.collision_prob
+    monkeypatch.setattr(O, "collision_prob", lambda cos, K: real_cp(cos, 1))
+    with pytest.raises(AssertionError):
+        test_golden_inclusion_and_collision(gold)
+    monkeypatch.undo()
+
+    # 7. strict threshold (count > T) in the selection
+    monkeypatch.setattr(O, "select", lambda counts, T: np.asarray(counts) > T)
+    with pytest.raises(AssertionError):
+        test_golden_probe_counts_select(gold)
+    monkeypatch.undo()
