@@ -41,7 +41,7 @@ KERNEL_SOURCES = {
     "transpose_w": "build_kernels.hip", "project_codes": "build_kernels.hip",
     "bucket_count": "build_kernels.hip", "bucket_scatter": "build_kernels.hip",
     "bucket_tables": "build_kernels.hip", "qhash": "decode_kernels.hip",
-    "count_select": "decode_kernels.hip", "attend": "decode_kernels.hip",
+    "count_select": "decode_kernels.hip", "attend": "attend_bf16.hip",
     "merge": "decode_kernels.hip",
 }
 
@@ -83,16 +83,18 @@ def measured_traffic(workload, kernel):
 
 
 def copy_calibration():
+    """A plain elementwise kernel (torch.neg over 2^28 fp32 = 1 GiB) that reads
+    exactly 1 GiB and writes exactly 1 GiB: the reference against which the
+    HBM byte counters (FETCH_SIZE, WRITE_SIZE) are scaled."""
     import torch
-    n = 1 << 30
-    src = torch.empty(n, dtype=torch.uint8, device="cuda")
-    src.fill_(1)
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(5):
-        dst.copy_(src)
+        torch.neg(src, out=dst)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+    print(json.dumps({"copy_calibration_bytes": 4 * n, "launches": 5, "kernel": "torch.neg fp32"}), flush=True)
 
 
 def main():
@@ -216,37 +218,62 @@ def main():
         "attend": ("hbm", kv_bytes + qh * d * esz + qh * N / 8),
         "merge": ("hbm", 0.0),
     }
-    kernels = {}
-    for name, (tot_ms, n) in ktimes.items():
-        if n == 0:
-            continue
-        avg_ms = tot_ms / n
-        bound, amount = alg[name]
-        rec = {"avg_us": round(avg_ms * 1e3, 3), "launches": n, "total_ms": round(tot_ms, 4), "bound": bound}
-        if bound == "mfma":
-            rec["achieved_tflops"] = amount / (avg_ms * 1e-3) / 1e12
-        elif amount > 0:
-            rec["achieved_gbs"] = amount / (avg_ms * 1e-3) / 1e9
-        kernels[name] = rec
+    def kernel_table(times):
+        out = {}
+        for name, (tot_ms, n) in times.items():
+            if n == 0:
+                continue
+            avg_ms = tot_ms / n
+            bound, amount = alg[name]
+            rec = {"avg_us": round(avg_ms * 1e3, 3), "launches": n, "total_ms": round(tot_ms, 4), "bound": bound}
+            if bound == "mfma":
+                rec["achieved_tflops"] = round(amount / (avg_ms * 1e-3) / 1e12, 2)
+            elif amount > 0:
+                rec["achieved_gbs"] = round(amount / (avg_ms * 1e-3) / 1e9, 2)
+            out[name] = rec
+        return out
+
+    def roofline_of(name, rec, traffic):
+        if rec["bound"] == "mfma":
+            peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+            r = {"kernel": name, "bound": "mfma", "achieved": rec["achieved_tflops"], "peak": peak,
+                 "unit": "TFLOP/s", "frac": round(rec["achieved_tflops"] / peak, 4)}
+        else:
+            r = {"kernel": name, "bound": "hbm", "achieved": rec["achieved_gbs"], "peak": HBM_PEAK_GBS,
+                 "unit": "GB/s", "frac": round(rec["achieved_gbs"] / HBM_PEAK_GBS, 4)}
+        r["avg_us"] = rec["avg_us"]
+        r["traffic"] = traffic
+        return r
+
+    kernels = kernel_table(ktimes)
     dom = max(kernels, key=lambda k: kernels[k]["total_ms"])
-    dk = kernels[dom]
-    if dk["bound"] == "mfma":
-        peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(dk["achieved_tflops"], 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(dk["achieved_tflops"] / peak, 4)}
-    else:
-        roof = {"kernel": dom, "bound": "hbm", "achieved": round(dk["achieved_gbs"], 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(dk["achieved_gbs"] / HBM_PEAK_GBS, 4)}
-    roof["avg_us"] = dk["avg_us"]
-    roof["traffic"] = measured_traffic(cfg.name, dom)
-    for k in kernels.values():
-        for f in ("achieved_tflops", "achieved_gbs"):
-            if f in k:
-                k[f] = round(k[f], 2)
+    roof = roofline_of(dom, kernels[dom], measured_traffic(cfg.name, dom))
+
+    # decode alone in steady state: consecutive decode steps over the rotating
+    # copies with no table build in between (the build's ~0.5 GB of writes
+    # otherwise reach HBM while the next decode reads)
+    lsh.lsh_timing_begin()
+    torch.cuda.synchronize()
+    td0 = time.perf_counter()
+    for i in range(args.steps):
+        decode(copies[i % R])
+    torch.cuda.synchronize()
+    td1 = time.perf_counter()
+    dtimes = lsh.lsh_timing_end()
+    dkernels = kernel_table(dtimes)
+    dec_ms_steady = sum(dtimes[k][0] for k in DECODE_KERNELS) / args.steps
 
     build_ms = sum(ktimes[k][0] for k in BUILD_KERNELS) / args.steps
     decode_ms = sum(ktimes[k][0] for k in DECODE_KERNELS) / args.steps
     dec_bytes = E_idx * 2 + qh * L * 8 + kv_bytes + qh * d * (esz + 4) + d * L * K * esz
+    decode_steady = {
+        "ms": round(dec_ms_steady, 5),
+        "wall_ms_per_step": round((td1 - td0) * 1e3 / args.steps, 5),
+        "qh_per_s": round(qh / (dec_ms_steady * 1e-3), 1),
+        "hbm_frac": round(dec_bytes / (dec_ms_steady * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "attend_roofline": roofline_of("attend", dkernels["attend"], measured_traffic(cfg.name, "attend")),
+        "kernels": dkernels,
+    }
 
     line = {
         "metric": "LSH-attn decode queries·heads/s at 32K–128K ctx; % of HBM roofline",
@@ -277,6 +304,7 @@ def main():
             "nsel_mean_per_head": float(np.mean(nsel_tot)) / qh,
             "probed_index_entries": E_idx,
             "kernels": kernels,
+            "decode_steady": decode_steady,
         },
     }
 

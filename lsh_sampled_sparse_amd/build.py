@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblsh_attn.so")
-SOURCES = ["lsh_api.hip", "build_kernels.hip", "decode_kernels.hip"]
+SOURCES = ["lsh_api.hip", "build_kernels.hip", "decode_kernels.hip", "attend_bf16.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

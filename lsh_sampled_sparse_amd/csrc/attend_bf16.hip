@@ -1,0 +1,416 @@
+// Weighted partial attention over the selected keys, bf16 K/V, gfx950.
+//
+// One workgroup (4 waves) per (sequence, kv head, context split); each wave
+// owns a quarter of the split.  The selected keys of the group (the union of
+// its query heads' selections) are compacted with ballots into a per-wave LDS
+// ring and processed in tiles of 32:
+//   * the tile's K rows are loaded straight into MFMA fragments and its V
+//     rows into registers; the next tile's loads are issued before the current
+//     tile's softmax and P.V, so each wave keeps a tile of K/V in flight;
+//   * S = q.k on MFMA 16x16x32 (fp32 accumulate), logits s q.k - ln u with the
+//     1/u importance weight, online softmax per head;
+//   * P.V on MFMA: V goes through LDS row-major and comes back as the B operand
+//     with transposing LDS reads (ds_read_b64_tr_b16: within each 16-lane group
+//     lane j receives element j & 3 of source lanes (j >> 2) + 4 i, i = 0..3);
+//     P is split into bf16 high and low parts (two MFMAs) so the weights keep
+//     about 16 mantissa bits.
+// The 1/u weight needs arccos of the q-k cosine: a polynomial (Abramowitz &
+// Stegun 4.4.46) and the hardware log2 keep it to ~35 instructions per pair.
+// The four waves' (max, sum, acc) states are merged through LDS into one
+// partial per query head and split, for the log-sum-exp merge that follows.
+#include <math.h>
+
+#include "lsh_device.h"
+#include "lsh_kernels.h"
+
+namespace lsh {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kTile = 32;         // keys per tile (the K extent of one MFMA 16x16x32)
+constexpr int kRingN = 128;       // per-wave ring of compacted keys
+constexpr int kVRow = 136;        // LDS row of one V row: 128 dims + 8 pad (272 B)
+constexpr int kBlock = 512;       // keys whose mask words are fetched together
+constexpr float kPiF = 3.14159265358979323846f;
+constexpr float kLnUFloorF = -69.07755278982137f;   // ln(1e-30)
+
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// 8 bytes from LDS, transposed across each 16-lane group (see above).
+__device__ __forceinline__ s16x4_t ds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+}
+
+__device__ __forceinline__ bf16x8_t join8(s16x4_t a, s16x4_t b) {
+  struct P2 {
+    s16x4_t a, b;
+  } x{a, b};
+  return __builtin_bit_cast(bf16x8_t, x);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+struct Bf16Pairs {
+  bf16x2_t p[4];
+};
+
+// arccos on [-1, 1] from the approximation of Abramowitz & Stegun 4.4.46
+// (Hastings): acos(x) = sqrt(1 - x) * sum_{i<8} a_i x^i for 0 <= x <= 1 with
+// |error| <= 2e-8, and acos(-x) = pi - acos(x).  In fp32 the error is about
+// 3e-7 rad, i.e. a few 1e-6 in ln u.
+__device__ __forceinline__ float acos_as(float c) {
+  const float x = fabsf(c);
+  float p = -0.0012624911f;
+  p = fmaf(p, x, 0.0066700901f);
+  p = fmaf(p, x, -0.0170881256f);
+  p = fmaf(p, x, 0.0308918810f);
+  p = fmaf(p, x, -0.0501743046f);
+  p = fmaf(p, x, 0.0889789874f);
+  p = fmaf(p, x, -0.2145988016f);
+  p = fmaf(p, x, 1.5707963050f);
+  const float r = __builtin_amdgcn_sqrtf(1.f - x) * p;
+  return c < 0.f ? kPiF - r : r;
+}
+
+// ln u of a key at cosine c with the query: T K ln(1 - theta / pi) + g(theta),
+// g interpolated from the (value, slope) table; clamped at ln(1e-30).
+__device__ __forceinline__ float lnu_of_cos(float c, const float2* tab2, float TKln2) {
+  const float th = acos_as(fminf(1.f, fmaxf(-1.f, c)));
+  const float x = th * (static_cast<float>(kLnuTable) / kPiF);
+  const int j = min(static_cast<int>(x), kLnuTable - 1);
+  const float2 e = tab2[j];
+  const float g = fmaf(x - static_cast<float>(j), e.y, e.x);
+  // log2 of p = 1 - theta / pi with the hardware log (absolute error ~1e-7)
+  const float l2p = __builtin_amdgcn_logf(fmaxf(0.f, 1.f - th * (1.0f / kPiF)));
+  return fmaxf(fmaf(TKln2, l2p, g), kLnUFloorF);
+}
+
+// sum of squares of a lane's 32 bf16 values with packed bf16 dot products
+__device__ __forceinline__ float sumsq(const Frag<BF16>& f) {
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const Bf16Pairs pr = __builtin_bit_cast(Bf16Pairs, f.v[k]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_fdot2_f32_bf16(pr.p[j], pr.p[j], s, false);
+  }
+  return s;
+}
+
+// DPP lane permutations inside rows of 16 lanes
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// max / sum over the 16 lanes of a row: pairs, quads, half-row mirror, row
+// mirror; every lane ends with the same value (each step adds disjoint sets)
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp<0x141>(v));   // row_half_mirror
+  return fmaxf(v, dpp<0x140>(v));  // row_mirror
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  return v + dpp<0x140>(v);
+}
+
+}  // namespace
+
+// GW = number of 64-lane mask words per head and 512-key block that a lane
+// holds: the G heads' 16 words per block are spread over GW loads.
+template <int GW>
+__global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
+    const uint16_t* __restrict__ q,        // [B][Hq][128]
+    const uint16_t* __restrict__ keys,     // [U][N][128]
+    const uint16_t* __restrict__ values,   // [U][N][128]
+    const uint32_t* __restrict__ bitmask,  // [B*Hq][Nw]
+    const float* __restrict__ lnu_tab,     // [kLnuTable + 1]
+    int Hq, int Hkv, int N, int K, int Tth, float scale, int split_len, int nsplit,
+    float* __restrict__ partials) {        // [B*Hq][nsplit][130]
+  __shared__ float2 tab2[kLnuTable];      // (g_j, g_{j+1} - g_j)
+  __shared__ int ring_idx[kWaves][kRingN];
+  __shared__ uint16_t ring_hm[kWaves][kRingN];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kWaves][kTile * kVRow];
+  __shared__ __attribute__((aligned(16))) uint16_t pt[kWaves][2][kTile * 16];
+  __shared__ float ep_m[kWaves][16], ep_l[kWaves][16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, sl = lane & 15;
+  const int s = blockIdx.x, u = blockIdx.y;
+  const int G = Hq / Hkv;
+  const int b = u / Hkv, g = u % Hkv;
+  const int bh0 = b * Hq + g * G;
+  const int Nw = (N + 31) >> 5;
+  const uint16_t* kb = keys + static_cast<size_t>(u) * N * kHeadDim;
+  const uint16_t* vb = values + static_cast<size_t>(u) * N * kHeadDim;
+  const bool k0 = (K == 0);
+  const float TKln2 = static_cast<float>(Tth * K) * 0.69314718055994531f;
+
+  for (int i = tid; i < kLnuTable; i += 256)
+    tab2[i] = k0 ? make_float2(0.f, 0.f) : make_float2(lnu_tab[i], lnu_tab[i + 1] - lnu_tab[i]);
+
+  // q fragments (MFMA A operand): lane holds head sl, dims [32 g4, 32 g4 + 32)
+  Frag<BF16> Qf;
+  Qf.load(q + static_cast<size_t>(bh0 + (sl < G ? sl : 0)) * kHeadDim + g4 * 32, sl < G);
+  float qss = sumsq(Qf);
+  qss += __shfl_xor(qss, 16);
+  qss += __shfl_xor(qss, 32);
+  // reciprocal norms of this lane's output heads 4 g4 + i (lane h < 16 holds
+  // head h); a zero norm gives 0, so the cosine is 0
+  float rq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x = __shfl(qss, 4 * g4 + i);
+    rq[i] = x > 0.f ? __builtin_amdgcn_rsqf(x) : 0.f;
+  }
+
+  const int sb = s * split_len;
+  const int se = min(N, sb + split_len);
+  const int wq = split_len / kWaves;
+  const int wb = min(se, sb + wave * wq), we = min(se, sb + (wave + 1) * wq);
+
+  int* ridx = ring_idx[wave];
+  uint16_t* rhm = ring_hm[wave];
+  uint16_t* V = vt[wave];
+  uint16_t* Phi = pt[wave][0];
+  uint16_t* Plo = pt[wave][1];
+
+  // ---- selection masks: the 16 words (512 keys) of every head of the group
+  // for one block; word w of head h sits in lane (h % 4) * 16 + w of load h / 4
+  uint32_t mw[GW], mw_next[GW];
+  auto load_block = [&](int blk0, uint32_t (&dst)[GW]) {
+#pragma unroll
+    for (int k = 0; k < GW; ++k) {
+      const int hh = 4 * k + g4;
+      const int wi = (blk0 >> 5) + sl;
+      dst[k] = (hh < G && blk0 < we && wi < Nw) ? bitmask[static_cast<size_t>(bh0 + hh) * Nw + wi] : 0u;
+    }
+  };
+  int blk = wb;                        // next window to compact
+  int blk_loaded = wb;                 // block start of mw
+  load_block(wb, mw);
+  load_block(wb + kBlock, mw_next);
+
+  int rhead = 0, rcnt = 0;
+  // compact windows of 64 keys until a full tile is queued or the range ends
+  auto fill = [&]() {
+    while (rcnt < kTile && blk < we) {
+      if (blk >= blk_loaded + kBlock) {
+        blk_loaded += kBlock;
+#pragma unroll
+        for (int k = 0; k < GW; ++k) mw[k] = mw_next[k];
+        load_block(blk_loaded + kBlock, mw_next);
+      }
+      const int wsel = ((blk - blk_loaded) >> 5) + (lane >> 5);   // word of this lane's key in the block
+      int hm = 0;
+#pragma unroll
+      for (int k = 0; k < GW; ++k)
+#pragma unroll
+        for (int hq = 0; hq < 4; ++hq) {
+          const uint32_t w = __shfl(mw[k], hq * 16 + wsel);
+          hm |= static_cast<int>((w >> (lane & 31)) & 1u) << (4 * k + hq);
+        }
+      const int n = blk + lane;
+      const bool any = n < we && hm != 0;
+      const uint64_t bal = ballot(any);
+      if (any) {
+        const int e = (rhead + rcnt + mbcnt(bal)) & (kRingN - 1);
+        ridx[e] = n;
+        rhm[e] = static_cast<uint16_t>(hm);
+      }
+      rcnt += __builtin_popcountll(bal);
+      blk += 64;
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  // ---- tile loads: K rows as two 16-key MFMA B fragments (lane = key sl of
+  // the group, dims [32 g4, +32)); V rows as 16-byte pieces (lane = piece sl of
+  // rows g4 + 4 j)
+  Frag<BF16> Kf[2];
+  u32x4_t vr[8];
+  int hmk[2];
+  auto issue = [&](int nt) {
+#pragma unroll
+    for (int gp = 0; gp < 2; ++gp) {
+      const int slot = 16 * gp + sl;
+      const int e = (rhead + (slot < nt ? slot : 0)) & (kRingN - 1);
+      hmk[gp] = slot < nt ? static_cast<int>(rhm[e]) : 0;
+      Kf[gp].load(kb + static_cast<size_t>(ridx[e]) * kHeadDim + g4 * 32, true);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = g4 + 4 * j;
+      const int e = (rhead + (row < nt ? row : 0)) & (kRingN - 1);
+      vr[j] = *reinterpret_cast<const u32x4_t*>(vb + static_cast<size_t>(ridx[e]) * kHeadDim + sl * 8);
+    }
+  };
+
+  float m_run[4], l_run[4];
+  floatx4_t O[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m_run[i] = -INFINITY;
+    l_run[i] = 0.f;
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) O[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  __syncthreads();   // ln u table in LDS
+
+  fill();
+  int nt = min(kTile, rcnt);
+  if (nt > 0) issue(nt);
+  while (nt > 0) {
+    // V of this tile into LDS (row-major, padded rows)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4_t*>(&V[(g4 + 4 * j) * kVRow + sl * 8]) = vr[j];
+    // S = q.k for keys sl (group 0) and 16 + sl (group 1); rows = heads 4 g4 + i
+    floatx4_t S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+    S0 = Qf.mma(Kf[0], S0);
+    S1 = Qf.mma(Kf[1], S1);
+    float ks0 = sumsq(Kf[0]), ks1 = sumsq(Kf[1]);
+    ks0 += __shfl_xor(ks0, 16);
+    ks0 += __shfl_xor(ks0, 32);
+    ks1 += __shfl_xor(ks1, 16);
+    ks1 += __shfl_xor(ks1, 32);
+    const float rk0 = ks0 > 0.f ? __builtin_amdgcn_rsqf(ks0) : 0.f;
+    const float rk1 = ks1 > 0.f ? __builtin_amdgcn_rsqf(ks1) : 0.f;
+    const int hm0 = hmk[0], hm1 = hmk[1];
+
+    // retire the tile from the ring, queue the next one and start its loads
+    rhead = (rhead + nt) & (kRingN - 1);
+    rcnt -= nt;
+    fill();
+    const int nnext = min(kTile, rcnt);
+    if (nnext > 0) issue(nnext);
+
+    // logits s q.k - ln u for this lane's 8 (head, key) pairs, computed
+    // without branches so the eight independent chains interleave; pairs whose
+    // key the head did not select are masked to -inf afterwards
+    float lg[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x0 = S0[i], x1 = S1[i];
+      const float u0 = k0 ? 0.f : lnu_of_cos(x0 * rq[i] * rk0, tab2, TKln2);
+      const float u1 = k0 ? 0.f : lnu_of_cos(x1 * rq[i] * rk1, tab2, TKln2);
+      const int hh = 4 * g4 + i;
+      const bool ok = hh < G;
+      lg[0][i] = (ok && ((hm0 >> hh) & 1)) ? fmaf(scale, x0, -u0) : -INFINITY;
+      lg[1][i] = (ok && ((hm1 >> hh) & 1)) ? fmaf(scale, x1, -u1) : -INFINITY;
+    }
+    // online softmax per head, P = exp(logit - m) as bf16 hi + lo
+    bf16x2_t phi[2][2], plo[2][2];
+    bool rescale = false;
+    float alpha[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lg0 = lg[0][i], lg1 = lg[1][i];
+      const float mt = row_max16(fmaxf(lg0, lg1));
+      const float mnew = fmaxf(m_run[i], mt);
+      alpha[i] = (mnew == -INFINITY) ? 1.f : __expf(m_run[i] - mnew);
+      rescale |= alpha[i] != 1.f;
+      const float p0 = (lg0 == -INFINITY) ? 0.f : __expf(lg0 - mnew);
+      const float p1 = (lg1 == -INFINITY) ? 0.f : __expf(lg1 - mnew);
+      l_run[i] = fmaf(l_run[i], alpha[i], row_sum16(p0 + p1));
+      m_run[i] = mnew;
+      const __bf16 h0 = static_cast<__bf16>(p0), h1 = static_cast<__bf16>(p1);
+      phi[0][i >> 1][i & 1] = h0;
+      phi[1][i >> 1][i & 1] = h1;
+      plo[0][i >> 1][i & 1] = static_cast<__bf16>(p0 - static_cast<float>(h0));
+      plo[1][i >> 1][i & 1] = static_cast<__bf16>(p1 - static_cast<float>(h1));
+    }
+    if (ballot(rescale)) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[t][i] *= alpha[i];
+    }
+    // P tiles in LDS as [key][16 heads]: this lane's 4 heads of keys sl, 16 + sl
+#pragma unroll
+    for (int gp = 0; gp < 2; ++gp) {
+      const int key = 16 * gp + sl;
+      *reinterpret_cast<uint2*>(&Phi[key * 16 + 4 * g4]) =
+          make_uint2(__builtin_bit_cast(uint32_t, phi[gp][0]), __builtin_bit_cast(uint32_t, phi[gp][1]));
+      *reinterpret_cast<uint2*>(&Plo[key * 16 + 4 * g4]) =
+          make_uint2(__builtin_bit_cast(uint32_t, plo[gp][0]), __builtin_bit_cast(uint32_t, plo[gp][1]));
+    }
+    __builtin_amdgcn_wave_barrier();
+    // O[head][dim] += P[head][key] V[key][dim]: A = P (keys 8 g4 .. 8 g4 + 7 of
+    // head sl), B = V (same keys, dim 16 t + sl)
+    const int r0 = 8 * g4 + (sl >> 2), c0 = 4 * (sl & 3);
+    const bf16x8_t Ahi = join8(ds_read_tr16(&Phi[r0 * 16 + c0]), ds_read_tr16(&Phi[(r0 + 4) * 16 + c0]));
+    const bf16x8_t Alo = join8(ds_read_tr16(&Plo[r0 * 16 + c0]), ds_read_tr16(&Plo[(r0 + 4) * 16 + c0]));
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const bf16x8_t Bv = join8(ds_read_tr16(&V[r0 * kVRow + 16 * t + c0]),
+                                ds_read_tr16(&V[(r0 + 4) * kVRow + 16 * t + c0]));
+      O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi, Bv, O[t], 0, 0, 0);
+      O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo, Bv, O[t], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+    nt = nnext;
+  }
+
+  // ---- merge the four waves' states per head; O[t][i] is head 4 g4 + i, dim 16 t + sl
+  __syncthreads();
+  float* wacc = reinterpret_cast<float*>(&vt[0][0]);   // [kWaves][16][128]
+  if (sl == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ep_m[wave][4 * g4 + i] = m_run[i];
+      ep_l[wave][4 * g4 + i] = l_run[i];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wacc[(wave * 16 + 4 * g4 + i) * kHeadDim + 16 * t + sl] = O[t][i];
+  __syncthreads();
+  for (int e = tid; e < G * kHeadDim; e += 256) {
+    const int hh = e / kHeadDim, d = e % kHeadDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ep_m[w][hh]);
+    float A = 0.f, Lm = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        if (ep_m[w][hh] == -INFINITY) continue;
+        const float f = __expf(ep_m[w][hh] - M);
+        A = fmaf(wacc[(w * 16 + hh) * kHeadDim + d], f, A);
+        Lm = fmaf(ep_l[w][hh], f, Lm);
+      }
+    }
+    float* dst = partials + (static_cast<size_t>(bh0 + hh) * nsplit + s) * kPartialStride;
+    dst[d] = A;
+    if (d == 0) {
+      dst[kHeadDim] = M;
+      dst[kHeadDim + 1] = Lm;
+    }
+  }
+}
+
+hipError_t launch_attend_bf16(const DecodeArgs& a, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  const dim3 grid(a.nsplit, a.B * a.Hkv);
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+  const uint16_t* kp = static_cast<const uint16_t*>(a.keys);
+  const uint16_t* vp = static_cast<const uint16_t*>(a.values);
+  const uint32_t* bm = a.bitmask;
+  const float* lt = a.lnu_table;
+  if (G <= 4)
+    return launch(kKAttend, attend_bf16_kernel<1>, grid, dim3(256), 0, stream, qp, kp, vp, bm, lt, a.Hq,
+                  a.Hkv, a.N, a.K, a.T, a.scale, a.split_len, a.nsplit, a.partials);
+  if (G <= 8)
+    return launch(kKAttend, attend_bf16_kernel<2>, grid, dim3(256), 0, stream, qp, kp, vp, bm, lt, a.Hq,
+                  a.Hkv, a.N, a.K, a.T, a.scale, a.split_len, a.nsplit, a.partials);
+  return launch(kKAttend, attend_bf16_kernel<4>, grid, dim3(256), 0, stream, qp, kp, vp, bm, lt, a.Hq, a.Hkv,
+                a.N, a.K, a.T, a.scale, a.split_len, a.nsplit, a.partials);
+}
+
+}  // namespace lsh

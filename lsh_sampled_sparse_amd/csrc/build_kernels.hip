@@ -193,17 +193,43 @@ __global__ __launch_bounds__(kCountTThreads) void bucket_count_kernel(
 
   for (int i = tid; i < ntiles * nb; i += kCountTThreads) hist[i] = 0;
   __syncthreads();
-  for (int n0 = tid; n0 < N; n0 += kCountTThreads * kPrefetch) {
-    int pf[kPrefetch];
+  if ((N & 7) == 0) {
+    // 16-byte loads: 8 codes of one tile per lane (tiles hold >= 256 keys)
+    const u32x4_t* cv = reinterpret_cast<const u32x4_t*>(cd);
+    const int nv = N >> 3;
+    for (int v0 = tid; v0 < nv; v0 += kCountTThreads * 4) {
+      u32x4_t pf[4];
 #pragma unroll
-    for (int k = 0; k < kPrefetch; ++k) {
-      const int n = n0 + k * kCountTThreads;
-      pf[k] = n < N ? static_cast<int>(cd[n]) : -1;
+      for (int k = 0; k < 4; ++k) {
+        const int v = v0 + k * kCountTThreads;
+        pf[k] = v < nv ? cv[v] : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int v = v0 + k * kCountTThreads;
+        if (v < nv) {
+          int32_t* h = hist + ((v << 3) >> tile_log2) * nb;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            atomicAdd(&h[pf[k][j] & 0xffffu], 1);
+            atomicAdd(&h[pf[k][j] >> 16], 1);
+          }
+        }
+      }
     }
+  } else {
+    for (int n0 = tid; n0 < N; n0 += kCountTThreads * kPrefetch) {
+      int pf[kPrefetch];
 #pragma unroll
-    for (int k = 0; k < kPrefetch; ++k) {
-      const int n = n0 + k * kCountTThreads;
-      if (pf[k] >= 0) atomicAdd(&hist[(n >> tile_log2) * nb + pf[k]], 1);
+      for (int k = 0; k < kPrefetch; ++k) {
+        const int n = n0 + k * kCountTThreads;
+        pf[k] = n < N ? static_cast<int>(cd[n]) : -1;
+      }
+#pragma unroll
+      for (int k = 0; k < kPrefetch; ++k) {
+        const int n = n0 + k * kCountTThreads;
+        if (pf[k] >= 0) atomicAdd(&hist[(n >> tile_log2) * nb + pf[k]], 1);
+      }
     }
   }
   __syncthreads();
@@ -243,28 +269,35 @@ constexpr int kScatThreads = 512;
 constexpr int kScatWaves = kScatThreads / 64;
 constexpr int kScatBatches = 16;        // 64-key batches per wave: tiles of <= 8192 keys
 constexpr int kMaxTileLog2 = 13;
+constexpr int kMatchLo = 8;             // code bits matched through the LDS lane-mask table
 
-// Mask of the valid lanes of this wave whose code equals this lane's, from two
-// 32-entry tables of 64-bit lane masks indexed by the low and the high five
-// code bits (K <= 10): every lane ORs its bit into both entries, and the AND
-// of the two entries it reads back holds exactly the lanes with its code.  The
-// entries are cleared again before returning.  LDS operations of one wave are
-// performed in issue order, so the reads see every lane's OR.
-__device__ __forceinline__ uint64_t match_lds(int code, bool valid, uint64_t* tab, int lane) {
-  volatile uint64_t* vt = tab;
-  const int lo = code & 31, hi = 32 + (code >> 5);
-  if (valid) {
-    atomicOr(reinterpret_cast<unsigned long long*>(&tab[lo]), 1ull << lane);
-    atomicOr(reinterpret_cast<unsigned long long*>(&tab[hi]), 1ull << lane);
+// One workgroup per tile.  Each wave owns a contiguous eighth of the tile and
+// walks it in batches of 64 keys.  The lanes of a batch holding the same code
+// are found in two steps: a per-wave LDS table of 64-bit lane masks indexed by
+// the low 8 code bits (every lane ORs its bit into its entry and reads the
+// entry back; LDS operations of one wave are performed in issue order; the
+// entry is cleared afterwards), then one ballot per remaining code bit.  A
+// lane's rank is the number of matching lanes below it, so the order inside a
+// bucket is the key order.
+//   phase 1  per-wave histograms (the first lane of each code adds the count)
+//   phase 2  scan: tile-local start of each bucket, per-wave cursors, and the
+//            shift from tile-local to table position of each bucket
+//   phase 3  placement into the tile's local CSR in LDS (key and code packed)
+//   phase 4  the runs are written with consecutive lanes on consecutive
+//            addresses of the table's index array
+__device__ __forceinline__ uint64_t match_lanes(int code, bool valid, int K, uint64_t* mt, int lane) {
+  volatile uint64_t* vt = mt;
+  const int lo = code & ((1 << kMatchLo) - 1);
+  if (valid) atomicOr(reinterpret_cast<unsigned long long*>(&mt[lo]), 1ull << lane);
+  __builtin_amdgcn_wave_barrier();
+  uint64_t m = valid ? vt[lo] : 0ull;
+  __builtin_amdgcn_wave_barrier();
+  if (valid) vt[lo] = 0ull;
+  for (int b = kMatchLo; b < K; ++b) {
+    const bool bit = (code >> b) & 1;
+    const uint64_t B = ballot(bit);
+    m &= bit ? B : ~B;
   }
-  __builtin_amdgcn_wave_barrier();
-  const uint64_t m = valid ? (vt[lo] & vt[hi]) : 0ull;
-  __builtin_amdgcn_wave_barrier();
-  if (valid) {
-    vt[lo] = 0ull;
-    vt[hi] = 0ull;
-  }
-  __builtin_amdgcn_wave_barrier();
   return m;
 }
 
@@ -273,15 +306,14 @@ __global__ __launch_bounds__(kScatThreads) void bucket_scatter_kernel(
     const int32_t* __restrict__ tstart,   // [U][L][ntiles][2^K]
     int N, int K, int L, int tile_log2, int ntiles, int stride_log2, int tables,
     uint16_t* __restrict__ indices) {     // [U][L][N]
-  extern __shared__ __attribute__((aligned(16))) int32_t sm[];
+  extern __shared__ __attribute__((aligned(16))) uint64_t smem64[];
   const int nb = 1 << K;
   const int T = 1 << tile_log2;
-  int32_t* wh = sm;                                   // [kScatWaves][nb] cursors
-  int32_t* lofs = wh + kScatWaves * nb;               // [nb] bucket start in the tile
-  int32_t* gst = lofs + nb;                           // [nb] bucket start in the table
-  uint64_t* mtab = reinterpret_cast<uint64_t*>(gst + nb);          // [kScatWaves][64]
-  uint16_t* obuf = reinterpret_cast<uint16_t*>(mtab + kScatWaves * 64);   // [T] chunk-relative key
-  uint16_t* ocode = obuf + T;                                        // [T] code
+  constexpr int kMt = 1 << kMatchLo;
+  uint64_t* mt = smem64;                                               // [kScatWaves][256] lane masks
+  int32_t* delta = reinterpret_cast<int32_t*>(mt + kScatWaves * kMt);   // [nb]
+  uint32_t* buf = reinterpret_cast<uint32_t*>(delta + nb);             // [T] key | code << 16
+  uint16_t* wh = reinterpret_cast<uint16_t*>(buf + T);                // [kScatWaves][nb] counts, cursors
   __shared__ int32_t wave_tot[kScatWaves];
 
   // tiles of 8 consecutive tables go to one XCD (workgroups are dealt to the
@@ -299,11 +331,9 @@ __global__ __launch_bounds__(kScatThreads) void bucket_scatter_kernel(
   const int cbase = (tbeg >> stride_log2) << stride_log2;
   const uint16_t* cd = codes + table * N;
 
+  for (int i = tid; i < kScatWaves * kMt; i += kScatThreads) mt[i] = 0ull;
   for (int i = tid; i < kScatWaves * nb; i += kScatThreads) wh[i] = 0;
-  for (int i = tid; i < kScatWaves * 64; i += kScatThreads) mtab[i] = 0ull;
-  const int32_t* ts = tstart + (table * ntiles + t) * nb;
-  for (int c = tid; c < nb; c += kScatThreads) gst[c] = ts[c];
-  // this wave's keys: [wbeg, wend) of the tile, batch k = keys wbeg + 64 k + lane
+  // this wave's keys: batch k = keys wbeg + 64 k + lane, up to wend
   const int per = T / kScatWaves;
   const int wbeg = tbeg + wave * per;
   const int wend = min(tbeg + tlen, wbeg + per);
@@ -314,13 +344,27 @@ __global__ __launch_bounds__(kScatThreads) void bucket_scatter_kernel(
     cr[k] = (64 * k < per && n < wend) ? static_cast<int>(cd[n]) : -1;
   }
   __syncthreads();
-  int32_t* my = wh + wave * nb;
+
+  uint64_t* my_mt = mt + wave * kMt;
+  uint16_t* my_wh = wh + wave * nb;
+  volatile uint16_t* vwh = my_wh;
+  int rs[kScatBatches];                 // rank | count << 8 of this lane's key in its batch
 #pragma unroll
-  for (int k = 0; k < kScatBatches; ++k)
-    if (cr[k] >= 0) atomicAdd(&my[cr[k]], 1);
+  for (int k = 0; k < kScatBatches; ++k) {
+    rs[k] = 0;
+    if (64 * k >= per) continue;        // wave-uniform: tiles shorter than 8192 keys
+    const bool valid = cr[k] >= 0;
+    const int code = valid ? cr[k] : 0;
+    const uint64_t m = match_lanes(code, valid, K, my_mt, lane);
+    const int rank = mbcnt(m), cnt = __builtin_popcountll(m);
+    rs[k] = rank | (cnt << 8);
+    if (valid && rank == 0) vwh[code] = static_cast<uint16_t>(vwh[code] + cnt);
+    __builtin_amdgcn_wave_barrier();
+  }
   __syncthreads();
 
-  // bucket c: exclusive prefix over waves in place, tile-local start in lofs
+  // phase 2: bucket c's tile-local start, per-wave cursors, table shift
+  const int32_t* ts = tstart + (table * ntiles + t) * nb;
   const int bpt = (nb + kScatThreads - 1) / kScatThreads;
   const int c0 = tid * bpt, c1 = min(nb, c0 + bpt);
   int local = 0;
@@ -337,47 +381,44 @@ __global__ __launch_bounds__(kScatThreads) void bucket_scatter_kernel(
   int run = incl - local;
   for (int w = 0; w < wave; ++w) run += wave_tot[w];
   for (int c = c0; c < c1; ++c) {
-    lofs[c] = run;
+    delta[c] = ts[c] - run;
     for (int w = 0; w < kScatWaves; ++w) {
       const int x = wh[w * nb + c];
-      wh[w * nb + c] = run;
+      wh[w * nb + c] = static_cast<uint16_t>(run);
       run += x;
     }
   }
   __syncthreads();
 
-  // stable placement of this wave's keys into the tile's local CSR
-  uint64_t* mt = mtab + wave * 64;
+  // phase 3: placement into the local CSR
 #pragma unroll
   for (int k = 0; k < kScatBatches; ++k) {
-    if (64 * k >= per) break;
+    if (64 * k >= per) continue;
     const bool valid = cr[k] >= 0;
     const int code = valid ? cr[k] : 0;
-    const uint64_t m = match_lds(code, valid, mt, lane);
-    const int rank = mbcnt(m);
-    const int p = valid ? my[code] : 0;
+    const int rank = rs[k] & 0xff, cnt = rs[k] >> 8;
+    const int p = valid ? static_cast<int>(vwh[code]) : 0;
     __builtin_amdgcn_wave_barrier();
     if (valid) {
-      obuf[p + rank] = static_cast<uint16_t>(wbeg + 64 * k + lane - cbase);
-      ocode[p + rank] = static_cast<uint16_t>(code);
-      if (rank == 0) my[code] = p + __builtin_popcountll(m);
+      buf[p + rank] = static_cast<uint32_t>(wbeg + 64 * k + lane - cbase) | (static_cast<uint32_t>(code) << 16);
+      if (rank == 0) vwh[code] = static_cast<uint16_t>(p + cnt);
     }
     __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
 
-  // every bucket's run of this tile: entry e of the local CSR goes to table
-  // position gst[c] + (e - lofs[c])
+  // phase 4: entry e of the local CSR goes to table position delta[code] + e
   uint16_t* out = indices + table * N;
+#pragma unroll 4
   for (int e = tid; e < tlen; e += kScatThreads) {
-    const int c = ocode[e];
-    out[gst[c] + (e - lofs[c])] = obuf[e];
+    const uint32_t v = buf[e];
+    out[delta[v >> 16] + e] = static_cast<uint16_t>(v & 0xffffu);
   }
 }
 
 size_t scatter_lds_bytes(int K, int tile_log2) {
   const size_t nb = size_t(1) << K;
-  return (kScatWaves * nb + 2 * nb) * 4 + kScatWaves * 64 * 8 + (size_t(2) << tile_log2) * 2;
+  return kScatWaves * (size_t(1) << kMatchLo) * 8 + nb * 4 + (size_t(4) << tile_log2) + kScatWaves * nb * 2;
 }
 
 // -------- general path (any K): one workgroup per table

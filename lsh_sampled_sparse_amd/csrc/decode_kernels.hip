@@ -295,7 +295,9 @@ __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// attend: one workgroup (4 waves) per (sequence, kv head, context split).
+// attend (fp32 K/V): one workgroup (4 waves) per (sequence, kv head, context
+// split); tiles of 16 selected keys, q.k on fp32 MFMA, P.V with FMAs.  The bf16
+// path has its own kernel (attend_bf16.hip).
 // ---------------------------------------------------------------------------
 constexpr int kAttThreads = 256;
 constexpr int kRing = 128;              // per-wave ring of selected keys
@@ -655,7 +657,9 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
              a.chunk_nsel, a.counts);
   if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;
-  if (G <= 4)
+  if constexpr (sizeof(S) == 2)
+    e = launch_attend_bf16(a, stream);
+  else if (G <= 4)
     e = launch_attend<T, 4>(a, stream);
   else if (G <= 8)
     e = launch_attend<T, 8>(a, stream);

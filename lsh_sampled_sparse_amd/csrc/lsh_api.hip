@@ -86,10 +86,10 @@ struct DecodeLayout {
 
 DecodeLayout decode_layout(int B, int Hq, int Hkv, int N, int L, const Geometry& g) {
   DecodeLayout w;
-  // context split: ~1024 workgroups over the (sequence, kv head) units, each a
-  // multiple of 256 keys
+  // context split: about two resident workgroups per CU (512 over the 256
+  // CUs) over the (sequence, kv head) units, each split a multiple of 256 keys
   const long long units = static_cast<long long>(B) * Hkv;
-  long long per = (units * N + 1023) / 1024;
+  long long per = (units * N + 511) / 512;
   per = (per + 255) / 256 * 256;
   if (per < 256) per = 256;
   if (per > N) per = (static_cast<long long>(N) + 255) / 256 * 256;

@@ -45,7 +45,7 @@ struct DecodeArgs {
   int dtype;
 };
 
-constexpr int kLnuTable = 2048;   // ln-u correction table intervals over theta in [0, pi]
+constexpr int kLnuTable = 1024;   // ln-u correction table intervals over theta in [0, pi]
 constexpr int kPartialStride = 130;
 
 // Kernel kinds, in launch order; names for the timing interface.
@@ -83,5 +83,7 @@ size_t bucket_lds_bytes(int nJ, int spc_log2, int K);
 bool bucket_fast_path(int N, int K, int stride_log2, int* tile_log2, int* ntiles);
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// The bf16 weighted-attention kernel (MFMA for q.k and P.V).
+hipError_t launch_attend_bf16(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace lsh
