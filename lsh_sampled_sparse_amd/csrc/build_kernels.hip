@@ -17,137 +17,170 @@
 namespace lsh {
 
 // ---------------------------------------------------------------------------
-// W transpose
+// Projection layout.
+//
+// The projection is D = W^T K on MFMA 16x16 tiles whose rows are projection
+// columns and whose columns are keys.  In such a tile lane (g, n) (g = lane /
+// 16) holds rows 4 g .. 4 g + 3 for key n.  A slab is NCT tiles of rows, so
+// every lane group g owns P = 4 NCT rows of the slab, and the rows are
+// assigned so that those P rows are the K columns of TPG whole tables: each
+// lane then packs the codes of its key from its own accumulators, with no
+// data exchanged between lanes.  NCT (at most 8) is chosen per K to waste as
+// few rows as possible; the transposed, permuted W (WT, zero rows for the
+// unused positions) lives in the build workspace.
 // ---------------------------------------------------------------------------
+struct ProjShape {
+  int nct, tpg;
+};
+__host__ __device__ constexpr ProjShape proj_shape(int K) {
+  switch (K) {
+    case 1: return {1, 4};
+    case 2: return {1, 2};
+    case 3: return {3, 4};
+    case 4: return {1, 1};
+    case 5: return {5, 4};
+    case 6: return {3, 2};
+    case 7: return {7, 4};
+    case 8: return {2, 1};
+    case 9: return {7, 3};
+    case 10: return {5, 2};
+    case 11: return {3, 1};
+    case 12: return {3, 1};
+    case 13: return {7, 2};
+    case 14: return {7, 2};
+    case 15: return {4, 1};
+    default: return {1, 1};
+  }
+}
+
+int proj_wt_rows(int K, int L) {
+  if (K <= 0) return 0;
+  const ProjShape ps = proj_shape(K);
+  const int tps = 4 * ps.tpg;
+  return (L + tps - 1) / tps * ps.nct * 16;
+}
+
+// WT[R][d] for row R = (slab, tile ct, row r = 4 g + i).  The kernel below
+// shifts the signs of a lane group's positions j = 4 ct + i into a word in
+// increasing j, so position j lands on bit P - 1 - j; that bit is bit b of
+// table tt of the group when P - 1 - j = tt K + b, i.e. table
+// slab * 4 TPG + g * TPG + tt.
 template <typename T>
 __global__ void transpose_w_kernel(const typename T::storage* __restrict__ W,
-                                   typename T::storage* __restrict__ WT, int LK, int LKpad) {
+                                   typename T::storage* __restrict__ WT, int K, int L, int nct, int tpg,
+                                   int rows) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= LKpad * kHeadDim) return;
-  const int c = idx / kHeadDim, i = idx % kHeadDim;
-  WT[idx] = (c < LK) ? W[static_cast<size_t>(i) * LK + c] : typename T::storage(0);
+  if (idx >= rows * kHeadDim) return;
+  const int R = idx / kHeadDim, d = idx % kHeadDim;
+  const int slab = R / (nct * 16), p = R % (nct * 16);
+  const int ct = p / 16, r = p % 16;
+  const int g = r / 4, j = ct * 4 + r % 4;
+  const int jr = 4 * nct - 1 - j;
+  const int tt = jr / K, b = jr % K;
+  const int t = slab * 4 * tpg + g * tpg + tt;
+  const bool valid = tt < tpg && t < L;
+  WT[idx] = valid ? W[static_cast<size_t>(d) * L * K + t * K + b] : typename T::storage(0);
 }
 
 constexpr int kProjThreads = 256;              // 4 waves
 constexpr int kProjKeys = 256;                 // 64 keys per wave = 4 tiles of 16
-constexpr int kSlabCols = 64;                  // projection columns per LDS slab
-template <typename T>
-struct ProjLds {
-  // slab row stride padded by 16 bytes so 16 rows read at one offset hit
-  // different LDS banks
-  static constexpr int kRow = kHeadDim + 16 / T::bytes;
-  static constexpr int kSlabElems = kSlabCols * kRow;
-  static constexpr int kChunksPerThread = kSlabCols * kHeadDim * T::bytes / 16 / kProjThreads;
-};
 
-// codes[u][l][n] for n in this workgroup's 256 keys.
-template <typename T>
+// codes[u][l][n] for this workgroup's 256 keys.
+template <typename T, int KB>
 __global__ __launch_bounds__(kProjThreads) void project_codes_kernel(
     const typename T::storage* __restrict__ keys,   // [U][N][128]
-    const typename T::storage* __restrict__ WT,     // [LKpad][128]
+    const typename T::storage* __restrict__ WT,     // [nslab * NCT * 16][128], permuted
     uint16_t* __restrict__ codes,                   // [U][L][N]
-    int N, int K, int L, int nslab) {
+    int N, int L, int nslab) {
   using S = typename T::storage;
-  using PL = ProjLds<T>;
-  __shared__ __attribute__((aligned(16))) S wt[2][PL::kSlabElems];
-  // sign masks of one slab: [slab & 1][col tile][key tile][i]; bit (16 q + c) of
-  // mask i is the sign of proj[key 4 q + i][col c] within the 16 x 16 tile
-  __shared__ uint64_t ring[2][4][16][4];
+  constexpr ProjShape PS = proj_shape(KB);
+  constexpr int NCT = PS.nct, TPG = PS.tpg, TPS = 4 * TPG;
+  constexpr int kRows = NCT * 16;                                  // WT rows per slab
+  constexpr int kRow = kHeadDim + 16 / T::bytes;                   // padded LDS row
+  constexpr int kChunksPerRow = kHeadDim * T::bytes / 16;
+  constexpr int kCPT = kRows * kChunksPerRow / kProjThreads;       // 16-byte pieces per thread
+  constexpr uint32_t kMask = (1u << KB) - 1u;
+  __shared__ __attribute__((aligned(16))) S wt[2][kRows * kRow];
 
   const int u = blockIdx.y;
   const int n0 = blockIdx.x * kProjKeys;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4;
   const S* kb = keys + static_cast<size_t>(u) * N * kHeadDim;
   uint16_t* cb = codes + static_cast<size_t>(u) * L * N;
-  const int n = n0 + tid;
 
-  if (K == 0) {
-    if (n < N)
-      for (int l = 0; l < L; ++l) cb[static_cast<size_t>(l) * N + n] = 0;
-    return;
-  }
-
+  // key fragments (MFMA B operand): lane holds key lane & 15 of tile a, dims
+  // [32 g, 32 g + 32)
   Frag<T> A[4];
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     const int key = n0 + wave * 64 + a * 16 + (lane & 15);
     const bool valid = key < N;
-    A[a].load(kb + static_cast<size_t>(valid ? key : 0) * kHeadDim + (lane >> 4) * 32, valid);
+    A[a].load(kb + static_cast<size_t>(valid ? key : 0) * kHeadDim + g * 32, valid);
   }
 
-  // slab s of WT is the contiguous block WT[64 s : 64 s + 64][:]; each thread
-  // moves kChunksPerThread 16-byte pieces of it into the padded LDS rows
-  constexpr int kCPT = PL::kChunksPerThread;
-  constexpr int kChunksPerRow = kHeadDim * T::bytes / 16;
   u32x4_t pre[kCPT];
-  {
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(WT);
+  auto fetch = [&](int slab) {
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(WT + static_cast<size_t>(slab) * kRows * kHeadDim);
 #pragma unroll
     for (int k = 0; k < kCPT; ++k) pre[k] = src[tid + k * kProjThreads];
+  };
+  auto stash = [&](int buf) {
 #pragma unroll
     for (int k = 0; k < kCPT; ++k) {
       const int chunk = tid + k * kProjThreads;
-      *reinterpret_cast<u32x4_t*>(&wt[0][(chunk / kChunksPerRow) * PL::kRow +
-                                       (chunk % kChunksPerRow) * (16 / T::bytes)]) = pre[k];
+      *reinterpret_cast<u32x4_t*>(&wt[buf][(chunk / kChunksPerRow) * kRow +
+                                          (chunk % kChunksPerRow) * (16 / T::bytes)]) = pre[k];
     }
-  }
+  };
+  fetch(0);
+  stash(0);
   __syncthreads();
-
-  const int key_tile = tid >> 4, key_row = tid & 15;
 
   for (int s = 0; s < nslab; ++s) {
     const int buf = s & 1;
-    if (s + 1 < nslab) {
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(WT + static_cast<size_t>(s + 1) * kSlabCols * kHeadDim);
-#pragma unroll
-      for (int k = 0; k < kCPT; ++k) pre[k] = src[tid + k * kProjThreads];
-    }
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      Frag<T> Bf;
-      Bf.load(&wt[buf][(ct * 16 + (lane & 15)) * PL::kRow + (lane >> 4) * 32], true);
+    if (s + 1 < nslab) fetch(s + 1);
+    // sign bits of the P rows of lane group g, for this lane's key in each
+    // tile, shifted in row order (s = 2 s + [x > 0]).  The column-tile loop is
+    // kept rolled: four accumulators are live at a time, which leaves room for
+    // several waves per SIMD to overlap one wave's MFMAs with another's signs.
+    uint32_t sg[4] = {0u, 0u, 0u, 0u};
+#pragma unroll 1
+    for (int ct = 0; ct < NCT; ++ct) {
+      Frag<T> Wf;
+      Wf.load(&wt[buf][(ct * 16 + (lane & 15)) * kRow + g * 32], true);
+      floatx4_t acc[4];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-        acc = A[a].mma(Bf, acc);
-        const uint64_t m0 = ballot(acc[0] > 0.f);
-        const uint64_t m1 = ballot(acc[1] > 0.f);
-        const uint64_t m2 = ballot(acc[2] > 0.f);
-        const uint64_t m3 = ballot(acc[3] > 0.f);
-        if (lane == 0) {
-          uint64_t* dst = ring[buf][ct][wave * 4 + a];
-          dst[0] = m0; dst[1] = m1; dst[2] = m2; dst[3] = m3;
-        }
+        acc[a] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        acc[a] = Wf.mma(A[a], acc[a]);   // acc[a][i]: row 4 g + i, key lane & 15 of tile a
       }
-    }
-    if (s + 1 < nslab) {
 #pragma unroll
-      for (int k = 0; k < kCPT; ++k) {
-        const int chunk = tid + k * kProjThreads;
-        *reinterpret_cast<u32x4_t*>(&wt[buf ^ 1][(chunk / kChunksPerRow) * PL::kRow +
-                                               (chunk % kChunksPerRow) * (16 / T::bytes)]) = pre[k];
-      }
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sg[a] = sg[a] * 2u + (acc[a][i] > 0.f ? 1u : 0u);
     }
-    __syncthreads();
-    // tables whose last bit lies in this slab
-    const int lb = min(L, (kSlabCols * s) / K);
-    const int le = min(L, (kSlabCols * (s + 1)) / K);
-    if (n < N) {
-      for (int l = lb; l < le; ++l) {
-        const int col0 = l * K, ct0 = col0 >> 4, sh = col0 & 15;
-        // 16 sign bits of this thread's key in column tiles ct0 and ct0 + 1
-        const uint64_t m0 = ring[(ct0 >> 2) & 1][ct0 & 3][key_tile][key_row & 3];
-        uint32_t w = static_cast<uint32_t>(m0 >> (16 * (key_row >> 2))) & 0xffffu;
-        if (sh + K > 16) {
-          const int ct1 = ct0 + 1;
-          const uint64_t m1 = ring[(ct1 >> 2) & 1][ct1 & 3][key_tile][key_row & 3];
-          w |= (static_cast<uint32_t>(m1 >> (16 * (key_row >> 2))) & 0xffffu) << 16;
+    if (s + 1 < nslab) stash(buf ^ 1);
+    // codes of tables s * TPS + g * TPG + tt
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int key = n0 + wave * 64 + a * 16 + (lane & 15);
+      if (key < N) {
+#pragma unroll
+        for (int tt = 0; tt < TPG; ++tt) {
+          const int t = s * TPS + g * TPG + tt;
+          if (t < L) cb[static_cast<size_t>(t) * N + key] = static_cast<uint16_t>((sg[a] >> (tt * KB)) & kMask);
         }
-        cb[static_cast<size_t>(l) * N + n] = static_cast<uint16_t>((w >> sh) & ((1u << K) - 1u));
       }
     }
     __syncthreads();
   }
+}
+
+// K = 0: every code is 0.
+__global__ void zero_codes_kernel(uint16_t* __restrict__ codes, size_t n) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) codes[i] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -552,22 +585,48 @@ size_t bucket_lds_bytes(int nJ, int spc_log2, int K) {
 // ---------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------
+template <typename T, int KB>
+static hipError_t launch_project_k(const void* keys, const void* WT, uint16_t* codes, int U, int N, int L,
+                                   int nslab, hipStream_t stream) {
+  using S = typename T::storage;
+  return launch(kKProject, project_codes_kernel<T, KB>, dim3((N + kProjKeys - 1) / kProjKeys, U),
+                dim3(kProjThreads), 0, stream, static_cast<const S*>(keys), static_cast<const S*>(WT), codes, N,
+                L, nslab);
+}
+
 template <typename T>
 static hipError_t launch_project(const void* keys, const void* W, void* WT, uint16_t* codes,
                                  int U, int N, int K, int L, hipStream_t stream) {
   using S = typename T::storage;
-  const int LK = L * K;
-  const int nslab = (LK + kSlabCols - 1) / kSlabCols;
-  const int LKpad = nslab * kSlabCols;
-  if (LK > 0) {
-    const int total = LKpad * kHeadDim;
-    hipError_t e = launch(kKTransposeW, transpose_w_kernel<T>, dim3((total + 255) / 256), dim3(256), 0,
-                          stream, static_cast<const S*>(W), static_cast<S*>(WT), LK, LKpad);
-    if (e != hipSuccess) return e;
+  if (K == 0) {
+    const size_t n = static_cast<size_t>(U) * L * N;
+    return launch(kKProject, zero_codes_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
+                  codes, n);
   }
-  return launch(kKProject, project_codes_kernel<T>, dim3((N + kProjKeys - 1) / kProjKeys, U),
-                dim3(kProjThreads), 0, stream, static_cast<const S*>(keys), static_cast<const S*>(WT),
-                codes, N, K, L, nslab);
+  const ProjShape ps = proj_shape(K);
+  const int rows = proj_wt_rows(K, L);
+  const int nslab = rows / (ps.nct * 16);
+  hipError_t e = launch(kKTransposeW, transpose_w_kernel<T>, dim3((rows * kHeadDim + 255) / 256), dim3(256), 0,
+                        stream, static_cast<const S*>(W), static_cast<S*>(WT), K, L, ps.nct, ps.tpg, rows);
+  if (e != hipSuccess) return e;
+  switch (K) {
+    case 1: return launch_project_k<T, 1>(keys, WT, codes, U, N, L, nslab, stream);
+    case 2: return launch_project_k<T, 2>(keys, WT, codes, U, N, L, nslab, stream);
+    case 3: return launch_project_k<T, 3>(keys, WT, codes, U, N, L, nslab, stream);
+    case 4: return launch_project_k<T, 4>(keys, WT, codes, U, N, L, nslab, stream);
+    case 5: return launch_project_k<T, 5>(keys, WT, codes, U, N, L, nslab, stream);
+    case 6: return launch_project_k<T, 6>(keys, WT, codes, U, N, L, nslab, stream);
+    case 7: return launch_project_k<T, 7>(keys, WT, codes, U, N, L, nslab, stream);
+    case 8: return launch_project_k<T, 8>(keys, WT, codes, U, N, L, nslab, stream);
+    case 9: return launch_project_k<T, 9>(keys, WT, codes, U, N, L, nslab, stream);
+    case 10: return launch_project_k<T, 10>(keys, WT, codes, U, N, L, nslab, stream);
+    case 11: return launch_project_k<T, 11>(keys, WT, codes, U, N, L, nslab, stream);
+    case 12: return launch_project_k<T, 12>(keys, WT, codes, U, N, L, nslab, stream);
+    case 13: return launch_project_k<T, 13>(keys, WT, codes, U, N, L, nslab, stream);
+    case 14: return launch_project_k<T, 14>(keys, WT, codes, U, N, L, nslab, stream);
+    case 15: return launch_project_k<T, 15>(keys, WT, codes, U, N, L, nslab, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 bool bucket_fast_path(int N, int K, int stride_log2, int* tile_log2, int* ntiles) {

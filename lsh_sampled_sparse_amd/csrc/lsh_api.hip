@@ -52,8 +52,7 @@ lsh_status check_common(int B, int Hkv, int N, int d, int K, int L, int stride, 
          (static_cast<long long>(nJ) << (spc + 1 + K)) <= kMaxDirEntries)
     ++spc;
   g->spc_log2 = spc;
-  const int LK = L * K;
-  g->LKpad = (LK + 63) / 64 * 64;
+  g->LKpad = lsh::proj_wt_rows(K, L);
   return LSH_OK;
 }
 

@@ -11,7 +11,7 @@ namespace lsh {
 struct BuildArgs {
   const void* keys;      // [U][N][128]
   const void* W;         // [128][L*K]
-  void* wt;              // workspace: [LKpad][128]
+  void* wt;              // workspace: [proj_wt_rows(K, L)][128]
   uint16_t* codes;       // [U][L][N] (caller's key_codes or workspace)
   int32_t* offsets;      // [U][L][2^K + 1]
   uint16_t* indices;     // [U][L][N] chunk-relative key indices
@@ -79,6 +79,9 @@ inline hipError_t launch(int id, F kernel, dim3 grid, dim3 block, unsigned lds, 
 }
 
 size_t bucket_lds_bytes(int nJ, int spc_log2, int K);
+// Rows of the transposed, permuted projection matrix the build keeps in its
+// workspace ([rows][128] of the input dtype).
+int proj_wt_rows(int K, int L);
 // Tiling of the fast bucket build (K <= 10 and ntiles * 2^K <= 32768).
 bool bucket_fast_path(int N, int K, int stride_log2, int* tile_log2, int* ntiles);
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
