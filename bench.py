@@ -35,12 +35,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA, TFLOP/s
 
-BUILD_KERNELS = ("transpose_w", "project_codes", "bucket_count", "bucket_scatter", "bucket_tables")
+BUILD_KERNELS = ("transpose_w", "project_codes", "chunk_sort")
 DECODE_KERNELS = ("qhash", "count_select", "attend", "merge")
 KERNEL_SOURCES = {
     "transpose_w": "build_kernels.hip", "project_codes": "build_kernels.hip",
-    "bucket_count": "build_kernels.hip", "bucket_scatter": "build_kernels.hip",
-    "bucket_tables": "build_kernels.hip", "qhash": "decode_kernels.hip",
+    "chunk_sort": "build_kernels.hip", "qhash": "decode_kernels.hip",
     "count_select": "decode_kernels.hip", "attend": "attend_bf16.hip",
     "merge": "decode_kernels.hip",
 }
@@ -133,9 +132,8 @@ def main():
         data = workloads.generate(cfg.with_(seed=cfg.seed + 1000 * r), device=dev)
         c = {"keys": data["keys"], "values": data["values"], "W": data["W"],
              "q": data["q"][0].contiguous()}
-        c["offsets"] = torch.empty(B, Hkv, L, (1 << K) + 1, dtype=torch.int32, device=dev)
+        c["offsets"] = torch.empty(B, Hkv, L, nch, 1 << K, dtype=torch.int16, device=dev)
         c["indices"] = torch.empty(B, Hkv, L, N, dtype=torch.int16, device=dev)
-        c["bounds"] = torch.empty(B, Hkv, L, 1 << K, nch + 1, dtype=torch.int32, device=dev)
         c["bws"] = torch.empty(max(1, lsh.lsh_build_workspace_size(B, Hkv, N, d, K, L, stride, dt)),
                                dtype=torch.uint8, device=dev)
         c["dws"] = torch.empty(max(1, lsh.lsh_decode_workspace_size(B, Hq, Hkv, N, d, K, L, stride)),
@@ -148,11 +146,10 @@ def main():
     torch.cuda.synchronize()
 
     def build(c):
-        lsh.lsh_build_tables(c["keys"], c["W"], K, L, stride, c["offsets"], c["indices"], c["bounds"],
-                             None, c["bws"])
+        lsh.lsh_build_tables(c["keys"], c["W"], K, L, stride, c["offsets"], c["indices"], None, c["bws"])
 
     def decode(c, counts=None):
-        lsh.lsh_decode_attention(c["q"], c["keys"], c["values"], c["W"], c["indices"], c["bounds"], K, L, T,
+        lsh.lsh_decode_attention(c["q"], c["keys"], c["values"], c["W"], c["indices"], c["offsets"], K, L, T,
                                  stride, cfg.scale, c["out"], c["lse"], c["nsel"], None, counts, c["dws"])
 
     def step(i):
@@ -205,16 +202,15 @@ def main():
     # algorithmic bytes / flops per launch
     kv_bytes = U_rows * 2 * d * esz
     tables = B * Hkv * L
-    csr_out = tables * (N * 2 + ((1 << K) + 1) * 4 + (1 << K) * (nch + 1) * 4)   # indices + offsets + bounds
+    csr_out = tables * (N * 2 + nch * (1 << K) * 2)   # uint16 indices + per-chunk bucket offsets
     alg = {
         "project_codes": ("mfma", 2.0 * d * K * L * B * Hkv * N),
         # codes read once, CSR written once
-        "bucket_count": ("hbm", tables * N * 2),
-        "bucket_scatter": ("hbm", tables * N * 2 + csr_out),
-        "bucket_tables": ("hbm", tables * N * 2 + csr_out),
+        "chunk_sort": ("hbm", tables * N * 2 + csr_out),
         "transpose_w": ("hbm", 2.0 * d * L * K * esz),
         "qhash": ("hbm", qh * d * esz + d * L * K * esz + qh * L * 2),
-        "count_select": ("hbm", E_idx * 2 + qh * L * 8 + qh * N / 8),
+        # probed entries, query codes, two bucket offsets per (head, table, chunk), bitmask
+        "count_select": ("hbm", E_idx * 2 + qh * L * 2 + qh * L * nch * 4 + qh * N / 8),
         "attend": ("hbm", kv_bytes + qh * d * esz + qh * N / 8),
         "merge": ("hbm", 0.0),
     }

@@ -75,21 +75,28 @@ const char* lsh_status_string(int status);
 /* Number of key chunks of a table: ceil(N / stride). */
 int lsh_num_chunks(int N, int stride);
 
-/* A chunk stride for N keys and K bits: the smallest power of two >= 256
- * giving at most 8 chunks, doubled while the chunk bounds would exceed about
- * a tenth of the index array ((nchunks + 1) * 2^K * 10 > N, with nchunks > 1)
- * or the build's limit (nchunks * 2^K > 32768), capped at 65536.  Any valid
- * stride gives the same offsets and indices; the stride only sets the bounds
- * array and the decode's work split.  Returns 0 for N < 1 or K outside 0..15. */
+/* A chunk stride for N keys and K bits: the smallest power of two >= 256 and
+ * >= N, capped at 8192.  Any valid stride describes the same buckets; the
+ * stride sets how the keys are split into chunks, each sorted on its own.
+ * Returns 0 for N < 1 or K outside 0..15. */
 int lsh_default_stride(int N, int K);
 
 /* ------------------------------------------------------------------------
  * Table build
  *
  * Size limits: B, Hkv, N >= 1; d == 128 (else LSH_ERR_UNSUPPORTED);
- * 0 <= K <= 15; 1 <= L <= 255; stride a power of two in [256, 65536] with
- * ceil(N / stride) * 2^K <= 32768 (else LSH_ERR_UNSUPPORTED);
- * B*Hkv*L*N < 2^40 and N < 2^31.
+ * 0 <= K <= 15; 1 <= L <= 255; stride a power of two in [256, 8192]
+ * (else LSH_ERR_UNSUPPORTED); B*Hkv*L*N < 2^40 and B*Hkv*L < 2^31.
+ *
+ * Layout of the tables (two-level CSR, chunk-major).  The keys of a table are
+ * cut into nchunks = lsh_num_chunks(N, stride) chunks of `stride` keys (the
+ * last one ragged); chunk j holds keys j*stride .. min(N, (j+1)*stride) - 1 and
+ * owns positions j*stride .. of indices[b,g,l,:].  Inside its region a chunk
+ * lists its keys grouped by bucket in ascending code order, ascending key index
+ * inside each bucket, each entry holding (key index - j*stride).  Bucket c of
+ * chunk j therefore occupies region positions offsets[b,g,l,j,c] ..
+ * offsets[b,g,l,j,c+1] (for c = 2^K - 1: .. the chunk's length).  Bucket c of
+ * the whole table is the concatenation over j of these segments.
  * ---------------------------------------------------------------------- */
 
 /* Bytes of device workspace lsh_build_tables needs (0 on invalid sizes). */
@@ -99,28 +106,18 @@ size_t lsh_build_workspace_size(int B, int Hkv, int N, int d, int K, int L,
 /*
  * keys     [B, Hkv, N, d]  dtype        key cache of every (sequence, kv head)
  * W        [d, L*K]        dtype        SimHash projection, shared by all heads
- * offsets  [B, Hkv, L, 2^K + 1] int32   out: bucket c of table l of unit (b,g) is
- *                                       positions offsets[c] .. offsets[c+1] of
- *                                       indices[b,g,l,:]
- * bounds   [B, Hkv, L, 2^K, nchunks + 1] int32
- *                                       out: bounds[..,c,j] = position of the first
- *                                       entry of bucket c with key index
- *                                       >= j*stride (bucket end if none), so
- *                                       bounds[..,c,0] = offsets[c] and the keys
- *                                       of chunk j in bucket c sit at positions
- *                                       bounds[c,j] .. bounds[c,j+1];
- *                                       nchunks = lsh_num_chunks(N, stride)
- * indices  [B, Hkv, L, N]  uint16       out: the keys grouped by bucket, ascending
- *                                       inside each bucket; an entry of chunk j
- *                                       holds (key index - j*stride), which fits
- *                                       16 bits since stride <= 65536
+ * offsets  [B, Hkv, L, nchunks, 2^K] uint16
+ *                                       out: start of bucket c inside chunk j's
+ *                                       region (see the layout above)
+ * indices  [B, Hkv, L, N]  uint16       out: chunk-relative key indices, grouped
+ *                                       by chunk, then bucket, then key
  * key_codes [B, Hkv, L, N] uint16       optional out: code_l(k_n)
  * workspace                             device scratch of the queried size
  */
 lsh_status lsh_build_tables(const void* keys, const void* W,
                             int B, int Hkv, int N, int d, int K, int L,
                             int stride, int dtype,
-                            int32_t* offsets, uint16_t* indices, int32_t* bounds,
+                            uint16_t* offsets, uint16_t* indices,
                             uint16_t* key_codes,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
@@ -140,8 +137,8 @@ size_t lsh_decode_workspace_size(int B, int Hq, int Hkv, int N, int d, int K,
  * q        [B, Hq, d]      dtype        one decode query per head
  * keys, values [B, Hkv, N, d] dtype     the cache the tables were built from
  * W        [d, L*K]        dtype        the build's projection
- * indices, bounds                       the build's outputs (same stride; offsets
- *                                       are not needed: bounds[c,0] = offsets[c])
+ * indices, offsets                      the build's outputs (built with the same
+ *                                       stride)
  * out      [B, Hq, d]      float        out: the estimate
  * lse      [B, Hq]         float        optional out: natural-log log-sum-exp
  * nsel     [B, Hq]         int32        optional out: |S|
@@ -150,7 +147,7 @@ size_t lsh_decode_workspace_size(int B, int Hq, int Hkv, int N, int d, int K,
  */
 lsh_status lsh_decode_attention(const void* q, const void* keys,
                                 const void* values, const void* W,
-                                const uint16_t* indices, const int32_t* bounds,
+                                const uint16_t* indices, const uint16_t* offsets,
                                 int B, int Hq, int Hkv, int N, int d, int K,
                                 int L, int T, int stride, float sm_scale,
                                 int dtype,

@@ -58,7 +58,7 @@ def lib():
         L.lsh_build_workspace_size.restype = _sz
         L.lsh_build_workspace_size.argtypes = [_i] * 8
         L.lsh_build_tables.restype = _i
-        L.lsh_build_tables.argtypes = [_p, _p] + [_i] * 8 + [_p, _p, _p, _p, _p, _sz, _p]
+        L.lsh_build_tables.argtypes = [_p, _p] + [_i] * 8 + [_p, _p, _p, _p, _sz, _p]
         L.lsh_decode_workspace_size.restype = _sz
         L.lsh_decode_workspace_size.argtypes = [_i] * 8
         L.lsh_decode_attention.restype = _i
@@ -125,8 +125,7 @@ def lsh_decode_workspace_size(B, Hq, Hkv, N, d, K, L, stride) -> int:
     return lib().lsh_decode_workspace_size(B, Hq, Hkv, N, d, K, L, stride)
 
 
-def lsh_build_tables(keys, W, K, L, stride, offsets, indices, bounds, key_codes=None,
-                     workspace=None):
+def lsh_build_tables(keys, W, K, L, stride, offsets, indices, key_codes=None, workspace=None):
     """Marshal tensors to ``lsh_build_tables``; outputs are filled in place.
 
     keys [B, Hkv, N, d], W [d, L*K] (bf16 or fp32, contiguous, on the GPU).
@@ -138,11 +137,11 @@ def lsh_build_tables(keys, W, K, L, stride, offsets, indices, bounds, key_codes=
                                 dtype=torch.uint8, device=keys.device)
     _check(lib().lsh_build_tables(
         _ptr(keys), _ptr(W), B, Hkv, N, d, K, L, stride, dt,
-        _ptr(offsets), _ptr(indices), _ptr(bounds), _ptr(key_codes),
+        _ptr(offsets), _ptr(indices), _ptr(key_codes),
         _ptr(workspace), workspace.numel(), _stream(keys.device)))
 
 
-def lsh_decode_attention(q, keys, values, W, indices, bounds, K, L, T, stride, sm_scale, out,
+def lsh_decode_attention(q, keys, values, W, indices, offsets, K, L, T, stride, sm_scale, out,
                          lse=None, nsel=None, q_codes=None, counts=None, workspace=None):
     """Marshal tensors to ``lsh_decode_attention``; outputs are filled in place."""
     B, Hq, d = q.shape
@@ -152,7 +151,7 @@ def lsh_decode_attention(q, keys, values, W, indices, bounds, K, L, T, stride, s
         workspace = torch.empty(max(1, lsh_decode_workspace_size(B, Hq, Hkv, N, d, K, L, stride)),
                                 dtype=torch.uint8, device=keys.device)
     _check(lib().lsh_decode_attention(
-        _ptr(q), _ptr(keys), _ptr(values), _ptr(W), _ptr(indices), _ptr(bounds),
+        _ptr(q), _ptr(keys), _ptr(values), _ptr(W), _ptr(indices), _ptr(offsets),
         B, Hq, Hkv, N, d, K, L, T, stride, ctypes.c_float(sm_scale), dt,
         _ptr(out), _ptr(lse), _ptr(nsel), _ptr(q_codes), _ptr(counts),
         _ptr(workspace), workspace.numel(), _stream(keys.device)))
@@ -194,10 +193,10 @@ def _require(t, name, dtype=None):
 def build_tables(keys, W, K, L, stride=None, return_codes=False):
     """Build the bucket tables of every (sequence, kv head).
 
-    Returns dict: offsets [B,Hkv,L,2^K+1] and bounds [B,Hkv,L,2^K,nchunks+1]
-    (int32), indices [B,Hkv,L,N] (int16 holding the uint16 chunk-relative key
-    index), stride, and codes [B,Hkv,L,N] (int16 holding uint16) when
-    ``return_codes``.
+    Returns dict: offsets [B,Hkv,L,nchunks,2^K] (int16 holding the uint16
+    start of each bucket inside each chunk's region), indices [B,Hkv,L,N]
+    (int16 holding the uint16 chunk-relative key index, chunk-major), stride,
+    and codes [B,Hkv,L,N] (int16 holding uint16) when ``return_codes``.
     """
     _require(keys, "keys")
     _require(W, "W", keys.dtype)
@@ -208,12 +207,11 @@ def build_tables(keys, W, K, L, stride=None, return_codes=False):
         stride = lsh_default_stride(N, K)
     nch = lsh_num_chunks(N, stride)
     dev = keys.device
-    offsets = torch.empty(B, Hkv, L, (1 << K) + 1, dtype=torch.int32, device=dev)
+    offsets = torch.empty(B, Hkv, L, nch, 1 << K, dtype=torch.int16, device=dev)
     indices = torch.empty(B, Hkv, L, N, dtype=torch.int16, device=dev)
-    bounds = torch.empty(B, Hkv, L, 1 << K, nch + 1, dtype=torch.int32, device=dev)
     codes = torch.empty(B, Hkv, L, N, dtype=torch.int16, device=dev) if return_codes else None
-    lsh_build_tables(keys, W, K, L, stride, offsets, indices, bounds, codes)
-    res = {"offsets": offsets, "indices": indices, "bounds": bounds, "stride": stride}
+    lsh_build_tables(keys, W, K, L, stride, offsets, indices, codes)
+    res = {"offsets": offsets, "indices": indices, "stride": stride}
     if return_codes:
         res["codes"] = codes
     return res
@@ -237,7 +235,7 @@ def decode_attention(q, keys, values, W, tables, K, L, T, sm_scale=None, return_
     nsel = torch.empty(B, Hq, dtype=torch.int32, device=dev)
     qc = torch.empty(B, Hq, L, dtype=torch.int16, device=dev) if return_codes else None
     cnt = torch.empty(B, Hq, N, dtype=torch.uint8, device=dev) if return_counts else None
-    lsh_decode_attention(q, keys, values, W, tables["indices"], tables["bounds"], K, L, T,
+    lsh_decode_attention(q, keys, values, W, tables["indices"], tables["offsets"], K, L, T,
                          tables["stride"], sm_scale, out, lse, nsel, qc, cnt, workspace)
     res = {"out": out, "lse": lse, "nsel": nsel}
     if return_codes:

@@ -6,7 +6,7 @@
 //   qhash          SimHash codes of every query head (same W and sign rule as
 //                  the keys); extra workgroups fill the ln-u correction table
 //   count_select   per (query head, key chunk): probe the head's L buckets,
-//                  restricted to the chunk through the build's chunk bounds,
+//                  restricted to the chunk through the chunk's bucket offsets,
 //                  count collisions in LDS byte counters, and emit the
 //                  selection bitmask (count >= T)
 //   attend         per (sequence, kv head, context split): union of the
@@ -191,8 +191,8 @@ constexpr int kCountUnroll = 8;   // index loads each thread keeps in flight
 
 __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
     const uint16_t* __restrict__ qcodes,   // [BH][L]
-    const uint16_t* __restrict__ indices,  // [U][L][N] chunk-relative key indices
-    const int32_t* __restrict__ bounds,    // [U][L][2^K][nJ + 1]
+    const uint16_t* __restrict__ indices,  // [U][L][N] chunk-major, chunk-relative key indices
+    const uint16_t* __restrict__ offsets,  // [U][L][nJ][2^K] bucket starts inside each chunk
     int Hq, int Hkv, int N, int K, int L, int T, int stride_log2, int nJ,
     uint32_t* __restrict__ bitmask,        // [BH][Nw]
     int32_t* __restrict__ chunk_nsel,      // [BH][nJ]
@@ -217,10 +217,13 @@ __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
   int len = 0;
   if (tid < L) {
     const int qc = qcodes[static_cast<size_t>(bh) * L + tid];
-    const int32_t* bp = bounds + ((static_cast<size_t>(u) * L + tid) * nb + qc) * (nJ + 1) + J;
-    const int s0 = bp[0];
-    len = bp[1] - s0;
-    seg_start[tid] = s0;
+    const uint16_t* op = offsets + ((static_cast<size_t>(u) * L + tid) * nJ + J) * nb + qc;
+    // clamped into the chunk: tables that do not match the stride cannot
+    // send the walk outside the chunk's region
+    const int s0 = min(static_cast<int>(op[0]), clen);
+    const int e0 = qc + 1 < nb ? min(static_cast<int>(op[1]), clen) : clen;
+    len = max(e0 - s0, 0);
+    seg_start[tid] = cbeg + s0;
   }
   int incl = len;
 #pragma unroll
@@ -653,7 +656,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   e = launch(kKCountSelect, count_select_kernel, dim3(a.nJ, BH), dim3(kCountThreads),
              static_cast<unsigned>(lds), stream, static_cast<const uint16_t*>(a.qcodes),
-             a.indices, a.bounds, a.Hq, a.Hkv, a.N, a.K, a.L, a.T, a.stride_log2, a.nJ, a.bitmask,
+             a.indices, a.offsets, a.Hq, a.Hkv, a.N, a.K, a.L, a.T, a.stride_log2, a.nJ, a.bitmask,
              a.chunk_nsel, a.counts);
   if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;

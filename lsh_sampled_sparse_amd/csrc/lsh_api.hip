@@ -13,9 +13,8 @@
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxStrideLog2 = 16;
+constexpr int kMaxStrideLog2 = 13;     // a chunk is sorted in one workgroup's LDS
 constexpr int kMinStrideLog2 = 8;
-constexpr int kMaxDirEntries = 32768;   // nchunks * 2^K held in LDS by the bucket build
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
@@ -27,7 +26,7 @@ int ilog2_exact(int x) {
 }
 
 struct Geometry {
-  int stride_log2 = 0, nJ = 0, spc_log2 = 0, LKpad = 0;
+  int stride_log2 = 0, nJ = 0, LKpad = 0;
 };
 
 // Checks shared by build and decode.  Returns LSH_OK and fills `g`.
@@ -40,18 +39,9 @@ lsh_status check_common(int B, int Hkv, int N, int d, int K, int L, int stride, 
   if (d != 128) return LSH_ERR_UNSUPPORTED;
   if (sl < kMinStrideLog2 || sl > kMaxStrideLog2) return LSH_ERR_UNSUPPORTED;
   const long long units = static_cast<long long>(B) * Hkv;
-  if (units * L * static_cast<long long>(N) >= (1ll << 40)) return LSH_ERR_UNSUPPORTED;
-  const int nJ = lsh_num_chunks(N, stride);
-  if (static_cast<long long>(nJ) << K > kMaxDirEntries) return LSH_ERR_UNSUPPORTED;
+  if (units * L * static_cast<long long>(N) >= (1ll << 40) || units * L >= (1ll << 31)) return LSH_ERR_UNSUPPORTED;
   g->stride_log2 = sl;
-  g->nJ = nJ;
-  // sub-chunks per chunk for the bucket build: aim for >= 16 sub-chunks (one
-  // per wave), each >= 64 keys, within the LDS budget
-  int spc = 0;
-  while ((nJ << (spc + 1)) <= 16 && (sl - spc - 1) >= 6 &&
-         (static_cast<long long>(nJ) << (spc + 1 + K)) <= kMaxDirEntries)
-    ++spc;
-  g->spc_log2 = spc;
+  g->nJ = lsh_num_chunks(N, stride);
   g->LKpad = lsh::proj_wt_rows(K, L);
   return LSH_OK;
 }
@@ -59,21 +49,16 @@ lsh_status check_common(int B, int Hkv, int N, int d, int K, int L, int stride, 
 int elem_bytes(int dtype) { return dtype == LSH_BF16 ? 2 : 4; }
 
 struct BuildLayout {
-  size_t wt = 0, codes = 0, tstart = 0, total = 0;
-  bool fast = false;
+  size_t wt = 0, codes = 0, total = 0;
 };
 
-BuildLayout build_layout(int B, int Hkv, int N, int K, int L, int dtype, const Geometry& g, bool need_codes) {
+BuildLayout build_layout(int B, int Hkv, int N, int L, int dtype, const Geometry& g, bool need_codes) {
   BuildLayout w;
   size_t off = 0;
   w.wt = off;
   off = align_up(off + static_cast<size_t>(g.LKpad) * 128 * elem_bytes(dtype));
   w.codes = off;
   if (need_codes) off = align_up(off + static_cast<size_t>(B) * Hkv * L * N * sizeof(uint16_t));
-  int tile_log2 = 0, ntiles = 0;
-  w.fast = lsh::bucket_fast_path(N, K, g.stride_log2, &tile_log2, &ntiles);
-  w.tstart = off;
-  if (w.fast) off = align_up(off + static_cast<size_t>(B) * Hkv * L * ntiles * (size_t(1) << K) * sizeof(int32_t));
   w.total = off;
   return w;
 }
@@ -125,8 +110,7 @@ namespace lsh {
 
 const char* kernel_name(int id) {
   static const char* const names[kKNumKernels] = {
-      "transpose_w", "project_codes", "bucket_count", "bucket_scatter", "bucket_tables", "qhash",
-      "count_select", "attend", "merge"};
+      "transpose_w", "project_codes", "chunk_sort", "qhash", "count_select", "attend", "merge"};
   return (id >= 0 && id < kKNumKernels) ? names[id] : nullptr;
 }
 
@@ -206,29 +190,25 @@ int lsh_num_chunks(int N, int stride) {
 
 int lsh_default_stride(int N, int K) {
   if (N < 1 || K < 0 || K > 15) return 0;
-  long long stride = 1ll << kMinStrideLog2;
-  while (stride < (1ll << kMaxStrideLog2) && stride * 8 < N) stride *= 2;
-  auto chunks = [&](long long s) { return (N + s - 1) / s; };
-  while (stride < (1ll << kMaxStrideLog2) && chunks(stride) > 1 &&
-         ((chunks(stride) + 1) * (1ll << K) * 10 > N || (chunks(stride) << K) > kMaxDirEntries))
-    stride *= 2;
-  return static_cast<int>(stride);
+  int stride = 1 << kMinStrideLog2;
+  while (stride < (1 << kMaxStrideLog2) && stride < N) stride *= 2;
+  return stride;
 }
 
 size_t lsh_build_workspace_size(int B, int Hkv, int N, int d, int K, int L, int stride, int dtype) {
   Geometry g;
   if (check_common(B, Hkv, N, d, K, L, stride, dtype, &g) != LSH_OK) return 0;
-  return build_layout(B, Hkv, N, K, L, dtype, g, true).total;
+  return build_layout(B, Hkv, N, L, dtype, g, true).total;
 }
 
 lsh_status lsh_build_tables(const void* keys, const void* W, int B, int Hkv, int N, int d, int K, int L,
-                            int stride, int dtype, int32_t* offsets, uint16_t* indices, int32_t* bounds,
-                            uint16_t* key_codes, void* workspace, size_t workspace_bytes, void* stream) {
+                            int stride, int dtype, uint16_t* offsets, uint16_t* indices, uint16_t* key_codes,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   Geometry g;
   lsh_status st = check_common(B, Hkv, N, d, K, L, stride, dtype, &g);
   if (st != LSH_OK) return st;
-  if (!keys || !offsets || !indices || !bounds || !workspace || (K > 0 && !W)) return LSH_ERR_INVALID_ARG;
-  const BuildLayout w = build_layout(B, Hkv, N, K, L, dtype, g, key_codes == nullptr);
+  if (!keys || !offsets || !indices || !workspace || (K > 0 && !W)) return LSH_ERR_INVALID_ARG;
+  const BuildLayout w = build_layout(B, Hkv, N, L, dtype, g, key_codes == nullptr);
   if (workspace_bytes < w.total) return LSH_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   lsh::BuildArgs a;
@@ -238,15 +218,12 @@ lsh_status lsh_build_tables(const void* keys, const void* W, int B, int Hkv, int
   a.codes = key_codes ? key_codes : reinterpret_cast<uint16_t*>(ws + w.codes);
   a.offsets = offsets;
   a.indices = indices;
-  a.bounds = bounds;
-  a.tstart = w.fast ? reinterpret_cast<int32_t*>(ws + w.tstart) : nullptr;
   a.U = B * Hkv;
   a.N = N;
   a.K = K;
   a.L = L;
   a.stride_log2 = g.stride_log2;
   a.nJ = g.nJ;
-  a.spc_log2 = g.spc_log2;
   a.dtype = dtype;
   return hip_status(lsh::launch_build(a, static_cast<hipStream_t>(stream)));
 }
@@ -259,7 +236,7 @@ size_t lsh_decode_workspace_size(int B, int Hq, int Hkv, int N, int d, int K, in
 }
 
 lsh_status lsh_decode_attention(const void* q, const void* keys, const void* values, const void* W,
-                                const uint16_t* indices, const int32_t* bounds, int B, int Hq, int Hkv, int N,
+                                const uint16_t* indices, const uint16_t* offsets, int B, int Hq, int Hkv, int N,
                                 int d, int K, int L, int T, int stride, float sm_scale, int dtype, float* out,
                                 float* lse, int32_t* nsel, uint16_t* q_codes, uint8_t* counts, void* workspace,
                                 size_t workspace_bytes, void* stream) {
@@ -268,7 +245,7 @@ lsh_status lsh_decode_attention(const void* q, const void* keys, const void* val
   if (st != LSH_OK) return st;
   if (Hq < 1 || Hq % Hkv != 0 || T < 1 || T > L || !std::isfinite(sm_scale)) return LSH_ERR_INVALID_ARG;
   if (Hq / Hkv > 16) return LSH_ERR_UNSUPPORTED;
-  if (!q || !keys || !values || !indices || !bounds || !out || !workspace || (K > 0 && !W))
+  if (!q || !keys || !values || !indices || !offsets || !out || !workspace || (K > 0 && !W))
     return LSH_ERR_INVALID_ARG;
   const DecodeLayout w = decode_layout(B, Hq, Hkv, N, L, g);
   if (workspace_bytes < w.total) return LSH_ERR_WORKSPACE;
@@ -279,7 +256,7 @@ lsh_status lsh_decode_attention(const void* q, const void* keys, const void* val
   a.values = values;
   a.W = W;
   a.indices = indices;
-  a.bounds = bounds;
+  a.offsets = offsets;
   a.qcodes = q_codes ? q_codes : reinterpret_cast<uint16_t*>(ws + w.qcodes);
   a.bitmask = reinterpret_cast<uint32_t*>(ws + w.bitmask);
   a.chunk_nsel = reinterpret_cast<int32_t*>(ws + w.chunk_nsel);

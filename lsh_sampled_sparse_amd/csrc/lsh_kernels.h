@@ -13,12 +13,10 @@ struct BuildArgs {
   const void* W;         // [128][L*K]
   void* wt;              // workspace: [proj_wt_rows(K, L)][128]
   uint16_t* codes;       // [U][L][N] (caller's key_codes or workspace)
-  int32_t* offsets;      // [U][L][2^K + 1]
-  uint16_t* indices;     // [U][L][N] chunk-relative key indices
-  int32_t* bounds;       // [U][L][2^K][nJ + 1]
-  int32_t* tstart;       // workspace [U][L][ntiles][2^K] (fast path), or null
+  uint16_t* offsets;     // [U][L][nJ][2^K] bucket starts inside each chunk
+  uint16_t* indices;     // [U][L][N] chunk-major, key - chunk start
   int U, N, K, L;
-  int stride_log2, nJ, spc_log2;
+  int stride_log2, nJ;
   int dtype;             // 0 = f32, 1 = bf16
 };
 
@@ -27,8 +25,8 @@ struct DecodeArgs {
   const void* keys;      // [U][N][128]
   const void* values;    // [U][N][128]
   const void* W;         // [128][L*K]
-  const uint16_t* indices;
-  const int32_t* bounds;
+  const uint16_t* indices;   // [U][L][N] chunk-major
+  const uint16_t* offsets;   // [U][L][nJ][2^K]
   uint16_t* qcodes;      // [B*Hq][L]
   uint32_t* bitmask;     // [B*Hq][Nw]
   int32_t* chunk_nsel;   // [B*Hq][nJ]
@@ -52,9 +50,7 @@ constexpr int kPartialStride = 130;
 enum KernelId {
   kKTransposeW = 0,
   kKProject,
-  kKBucketCount,
-  kKBucketScatter,
-  kKBucket,
+  kKChunkSort,
   kKQhash,
   kKCountSelect,
   kKAttend,
@@ -78,12 +74,10 @@ inline hipError_t launch(int id, F kernel, dim3 grid, dim3 block, unsigned lds, 
   return hipGetLastError();
 }
 
-size_t bucket_lds_bytes(int nJ, int spc_log2, int K);
 // Rows of the transposed, permuted projection matrix the build keeps in its
 // workspace ([rows][128] of the input dtype).
 int proj_wt_rows(int K, int L);
-// Tiling of the fast bucket build (K <= 10 and ntiles * 2^K <= 32768).
-bool bucket_fast_path(int N, int K, int stride_log2, int* tile_log2, int* ntiles);
+
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // The bf16 weighted-attention kernel (MFMA for q.k and P.V).

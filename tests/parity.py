@@ -6,9 +6,10 @@ band |proj| < 1e-4 * ||x|| * ||w_c|| may legitimately differ between fp32 and
 fp64 arithmetic, so:
   * codes must match the oracle bit for bit outside that band, and flips
     inside it must stay below 1e-5 of all bits;
-  * every table whose codes agree must give bit-identical offsets, indices and
-    chunk bounds; a table with a flipped bit must still be a valid stable
-    bucketing of the GPU's own codes;
+  * every table whose codes agree must give bit-identical chunk offsets and
+    indices (the oracle's buckets, split by key chunk through its chunk
+    bounds and laid out chunk-major); a table with a flipped bit must still be
+    a valid stable bucketing of the GPU's own codes;
   * collision counts and selections must agree exactly for every key whose
     codes (and the probing query's codes) agree; others may differ by at most
     the number of disagreeing tables;
@@ -56,47 +57,59 @@ def compare_codes(gpu, ref, band, K, L):
     return flips
 
 
-def indices_to_global(idx, bnd, stride):
-    """Chunk-relative uint16 entries [L, N] -> key indices (int64), using the
-    chunk bounds [L, 2^K, nchunks + 1]: positions bnd[c, j] .. bnd[c, j + 1]
-    hold keys of chunk j, stored as (key - j * stride)."""
+def indices_to_global(idx, stride):
+    """Chunk-major uint16 entries [L, N] -> key indices (int64): position p
+    lies in chunk p // stride and holds (key - chunk * stride)."""
     idx = u16(idx)
-    bnd = np.asarray(bnd, np.int64)
-    L, N = idx.shape
-    nb, nJ = bnd.shape[1], bnd.shape[2] - 1
-    out = np.empty_like(idx)
+    N = idx.shape[-1]
+    return idx + (np.arange(N, dtype=np.int64) // stride) * stride
+
+
+def expected_chunk_layout(ref, stride):
+    """The chunk-major layout of the oracle's tables.
+
+    Bucket c of chunk j is ref indices[l, bounds[l, c, j]:bounds[l, c, j + 1]];
+    chunk j lists its buckets in code order.  Returns (offsets [L, nJ, nb],
+    global key order [L, N])."""
+    bnd = np.asarray(ref["bounds"], np.int64)
+    idx = np.asarray(ref["indices"], np.int64)
+    L, nb, nJ1 = bnd.shape
+    lens = np.diff(bnd, axis=2).transpose(0, 2, 1)              # [L, nJ, nb]
+    off = np.cumsum(lens, axis=2) - lens
+    order = np.empty_like(idx)
     for l in range(L):
-        lens = np.diff(bnd[l], axis=1).ravel()            # (bucket, chunk) runs in position order
-        assert bnd[l, 0, 0] == 0 and lens.sum() == N and np.all(lens >= 0)
-        assert np.all(bnd[l, 1:, 0] == bnd[l, :-1, nJ])
-        chunk = np.repeat(np.tile(np.arange(nJ, dtype=np.int64), nb), lens)
-        out[l] = idx[l] + chunk * stride
-    return out
+        # runs (bucket c, chunk j) in chunk-major order: j outer, c inner
+        starts = bnd[l, :, :-1].T.ravel()
+        ln = lens[l].ravel()
+        pos = np.repeat(starts - np.concatenate(([0], np.cumsum(ln)[:-1])), ln) + np.arange(ln.sum())
+        order[l] = idx[l][pos]
+    return off, order
 
 
-def check_tables(gpu_off, gpu_idx, gpu_bnd, gpu_codes, ref, K, stride):
+def check_tables(gpu_off, gpu_idx, gpu_codes, ref, K, stride):
     """Compare one unit's tables.  ``ref`` from ``O.build_tables`` on the same
-    keys; ``gpu_idx`` holds the library's chunk-relative entries."""
-    gpu_idx = indices_to_global(gpu_idx, gpu_bnd, stride)
+    keys; ``gpu_off`` [L, nJ, 2^K] and ``gpu_idx`` [L, N] are the library's
+    chunk-major outputs.  Returns the number of tables with a flipped bit."""
+    gpu_idx = indices_to_global(gpu_idx, stride)
+    gpu_off = u16(gpu_off)
     gpu_codes = u16(gpu_codes)
     L, N = gpu_codes.shape
     nb = 1 << K
+    nJ = gpu_off.shape[1]
+    assert nJ == O.num_chunks(N, stride)
+    exp_off, exp_idx = expected_chunk_layout(ref, stride)
     same = np.all(gpu_codes == ref["codes"], axis=1)
+    chunk = np.arange(N, dtype=np.int64) // stride
     for l in range(L):
         if same[l]:
-            np.testing.assert_array_equal(gpu_off[l], ref["offsets"][l])
-            np.testing.assert_array_equal(gpu_idx[l], ref["indices"][l])
-            np.testing.assert_array_equal(gpu_bnd[l], ref["bounds"][l])
+            np.testing.assert_array_equal(gpu_off[l], exp_off[l])
+            np.testing.assert_array_equal(gpu_idx[l], exp_idx[l])
         else:
-            # valid stable bucketing of the GPU's own codes
-            cnt = np.bincount(gpu_codes[l], minlength=nb)
-            assert gpu_off[l][0] == 0 and gpu_off[l][nb] == N
-            np.testing.assert_array_equal(np.diff(gpu_off[l]), cnt)
-            for c in range(nb):
-                seg = gpu_idx[l][gpu_off[l][c]:gpu_off[l][c + 1]]
-                assert np.all(gpu_codes[l][seg] == c) and np.all(np.diff(seg) > 0)
-                lim = np.minimum(np.arange(gpu_bnd.shape[2]) * stride, N)
-                np.testing.assert_array_equal(gpu_bnd[l][c], gpu_off[l][c] + np.searchsorted(seg, lim))
+            # valid stable bucketing of the GPU's own codes, chunk by chunk
+            hist = np.bincount(chunk * nb + gpu_codes[l], minlength=nJ * nb).reshape(nJ, nb)
+            np.testing.assert_array_equal(gpu_off[l], np.cumsum(hist, axis=1) - hist)
+            keys = np.arange(N, dtype=np.int64)
+            np.testing.assert_array_equal(gpu_idx[l], keys[np.lexsort((keys, gpu_codes[l], chunk))])
     return int((~same).sum())
 
 

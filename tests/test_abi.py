@@ -45,41 +45,43 @@ def test_num_chunks_and_default_stride():
     assert lsh.lsh_num_chunks(0, 256) == 0
     for N, K in [(131072, 10), (16384, 10), (32768, 9), (32768, 10), (4096, 8), (1, 0), (10**6, 15)]:
         s = lsh.lsh_default_stride(N, K)
-        assert s >= 256 and s <= 65536 and (s & (s - 1)) == 0
-        assert lsh.lsh_num_chunks(N, s) << K <= 32768 or s == 65536
+        assert 256 <= s <= 8192 and (s & (s - 1)) == 0
+        assert s >= min(N, 8192)
+    assert lsh.lsh_default_stride(300, 8) == 512
     assert lsh.lsh_default_stride(0, 3) == 0 and lsh.lsh_default_stride(10, 16) == 0
 
 
 def test_workspace_queries():
-    good = lsh.lsh_build_workspace_size(1, 4, 131072, 128, 10, 150, 16384, lsh.LSH_BF16)
+    good = lsh.lsh_build_workspace_size(1, 4, 131072, 128, 10, 150, 8192, lsh.LSH_BF16)
     # at least the uint16 codes of every (unit, table, key)
     assert good >= 4 * 150 * 131072 * 2
-    assert lsh.lsh_build_workspace_size(1, 4, 131072, 64, 10, 150, 16384, 1) == 0     # d != 128
-    assert lsh.lsh_build_workspace_size(1, 4, 131072, 128, 16, 150, 16384, 1) == 0    # K > 15
+    assert lsh.lsh_build_workspace_size(1, 4, 131072, 64, 10, 150, 8192, 1) == 0      # d != 128
+    assert lsh.lsh_build_workspace_size(1, 4, 131072, 128, 16, 150, 8192, 1) == 0     # K > 15
     assert lsh.lsh_build_workspace_size(1, 4, 131072, 128, 10, 150, 1000, 1) == 0     # stride not 2^k
-    dec = lsh.lsh_decode_workspace_size(1, 32, 4, 131072, 128, 10, 150, 16384)
+    assert lsh.lsh_build_workspace_size(1, 4, 131072, 128, 10, 150, 16384, 1) == 0    # stride > 8192
+    dec = lsh.lsh_decode_workspace_size(1, 32, 4, 131072, 128, 10, 150, 8192)
     assert dec >= 32 * 131072 // 8            # the selection bitmask
-    assert lsh.lsh_decode_workspace_size(1, 30, 4, 131072, 128, 10, 150, 16384) == 0  # Hq % Hkv
-    assert lsh.lsh_decode_workspace_size(1, 68, 4, 131072, 128, 10, 150, 16384) == 0  # G > 16
+    assert lsh.lsh_decode_workspace_size(1, 30, 4, 131072, 128, 10, 150, 8192) == 0   # Hq % Hkv
+    assert lsh.lsh_decode_workspace_size(1, 68, 4, 131072, 128, 10, 150, 8192) == 0   # G > 16
 
 
 def _build(**kw):
     a = dict(keys=1, W=1, B=1, Hkv=1, N=4096, d=128, K=8, L=32, stride=4096, dtype=1,
-             offsets=1, indices=1, bounds=1, codes=None, ws=1, ws_bytes=1 << 40, stream=None)
+             offsets=1, indices=1, codes=None, ws=1, ws_bytes=1 << 40, stream=None)
     a.update(kw)
     p = lambda v: None if v is None else ctypes.c_void_p(v)
     return lsh.lib().lsh_build_tables(p(a["keys"]), p(a["W"]), a["B"], a["Hkv"], a["N"], a["d"], a["K"],
                                       a["L"], a["stride"], a["dtype"], p(a["offsets"]), p(a["indices"]),
-                                      p(a["bounds"]), p(a["codes"]), p(a["ws"]), a["ws_bytes"], a["stream"])
+                                      p(a["codes"]), p(a["ws"]), a["ws_bytes"], a["stream"])
 
 
 def _decode(**kw):
-    a = dict(q=1, keys=1, values=1, W=1, indices=1, bounds=1, B=1, Hq=4, Hkv=1, N=4096, d=128, K=8,
+    a = dict(q=1, keys=1, values=1, W=1, indices=1, offsets=1, B=1, Hq=4, Hkv=1, N=4096, d=128, K=8,
              L=32, T=2, stride=4096, scale=0.088, dtype=1, out=1, ws=1, ws_bytes=1 << 40)
     a.update(kw)
     p = lambda v: None if v is None else ctypes.c_void_p(v)
     return lsh.lib().lsh_decode_attention(
-        p(a["q"]), p(a["keys"]), p(a["values"]), p(a["W"]), p(a["indices"]), p(a["bounds"]),
+        p(a["q"]), p(a["keys"]), p(a["values"]), p(a["W"]), p(a["indices"]), p(a["offsets"]),
         a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["K"], a["L"], a["T"], a["stride"],
         ctypes.c_float(a["scale"]), a["dtype"], p(a["out"]), None, None, None, None, p(a["ws"]),
         a["ws_bytes"], None)
@@ -90,7 +92,6 @@ def _decode(**kw):
     (dict(W=None), lsh.LSH_ERR_INVALID_ARG),
     (dict(offsets=None), lsh.LSH_ERR_INVALID_ARG),
     (dict(indices=None), lsh.LSH_ERR_INVALID_ARG),
-    (dict(bounds=None), lsh.LSH_ERR_INVALID_ARG),
     (dict(ws=None), lsh.LSH_ERR_INVALID_ARG),
     (dict(B=0), lsh.LSH_ERR_INVALID_ARG),
     (dict(N=0), lsh.LSH_ERR_INVALID_ARG),
@@ -102,7 +103,7 @@ def _decode(**kw):
     (dict(stride=3000), lsh.LSH_ERR_INVALID_ARG),
     (dict(d=64), lsh.LSH_ERR_UNSUPPORTED),
     (dict(stride=128), lsh.LSH_ERR_UNSUPPORTED),
-    (dict(N=1 << 20, K=15, stride=256), lsh.LSH_ERR_UNSUPPORTED),
+    (dict(stride=16384), lsh.LSH_ERR_UNSUPPORTED),
     (dict(ws_bytes=16), lsh.LSH_ERR_WORKSPACE),
 ])
 def test_build_rejects(kw, status):
@@ -113,7 +114,7 @@ def test_build_rejects(kw, status):
     (dict(q=None), lsh.LSH_ERR_INVALID_ARG),
     (dict(values=None), lsh.LSH_ERR_INVALID_ARG),
     (dict(out=None), lsh.LSH_ERR_INVALID_ARG),
-    (dict(bounds=None), lsh.LSH_ERR_INVALID_ARG),
+    (dict(offsets=None), lsh.LSH_ERR_INVALID_ARG),
     (dict(Hq=6, Hkv=4), lsh.LSH_ERR_INVALID_ARG),
     (dict(T=0), lsh.LSH_ERR_INVALID_ARG),
     (dict(T=33), lsh.LSH_ERR_INVALID_ARG),

@@ -72,7 +72,7 @@ def check_case(cfg, data, units=None, heads_per_unit=None, stride=None, step=0):
         flips += PAR.compare_codes(gcodes, ref["codes"], band, cfg.K, cfg.L)
         total_bits += cfg.N * cfg.L * cfg.K
         bad_tables += PAR.check_tables(to_np(tb["offsets"][b, g]), to_np(tb["indices"][b, g]),
-                                       to_np(tb["bounds"][b, g]), gcodes, ref, cfg.K, stride)
+                                       gcodes, ref, cfg.K, stride)
         hs = list(range(g * G, (g + 1) * G))
         if heads_per_unit is not None:
             hs = hs[:heads_per_unit]
@@ -115,6 +115,8 @@ SMALL = [
                      planted=1, a=0.8, offset="none", seed=18),
     workloads.Config("K15", B=1, Hq=2, Hkv=1, N=2048, d=128, K=15, L=4, T=1, dtype="bf16",
                      planted=1, a=0.95, offset="none", seed=19),
+    workloads.Config("K12-odd", B=1, Hq=4, Hkv=1, N=9001, d=128, K=12, L=6, T=1, dtype="bf16",
+                     planted=2, a=0.9, offset="none", seed=20),
 ]
 
 
@@ -126,7 +128,7 @@ def test_small_full_parity(cfg):
 
 
 @pytest.mark.parametrize("stride", [256, 1024, 8192])
-def test_strides_give_identical_tables(stride):
+def test_strides(stride):
     cfg = SMALL[1]
     say(f"case strides {stride}")
     data = workloads.generate(cfg)
@@ -155,7 +157,7 @@ def test_deterministic():
     data = workloads.generate(cfg)
     tb1, r1 = run_gpu(cfg, data)
     tb2, r2 = run_gpu(cfg, data)
-    for k in ("offsets", "indices", "bounds", "codes"):
+    for k in ("offsets", "indices", "codes"):
         assert torch.equal(tb1[k], tb2[k]), k
     for k in ("out", "lse", "nsel", "q_codes", "counts"):
         assert torch.equal(r1[k], r2[k]), k
