@@ -8,7 +8,7 @@
 //   project_codes   SimHash codes of every key: a dense bf16 (or fp32) MFMA
 //                   contraction keys x W with fp32 accumulation, sign bits
 //                   packed with wave ballots, codes written table-major
-//   chunk_sort      per (table, key chunk): a stable counting sort of the
+//   chunk_sort      per (table, key chunk): a stable LSD radix sort of the
 //                   chunk's keys by code into the chunk's own region of the
 //                   index array, with the chunk's bucket offsets
 #include "lsh_device.h"
@@ -184,7 +184,7 @@ __global__ void zero_codes_kernel(uint16_t* __restrict__ codes, size_t n) {
 }
 
 // ---------------------------------------------------------------------------
-// Bucketing: a stable counting sort of every (table, key chunk) by code.
+// Bucketing: a stable sort of every (table, key chunk) by code.
 //
 // Output format (chunk-major two-level CSR): chunk j of table l covers keys
 // [j stride, (j + 1) stride) and owns positions [j stride, (j + 1) stride)
@@ -194,226 +194,246 @@ __global__ void zero_codes_kernel(uint16_t* __restrict__ codes, size_t n) {
 // positions offsets[j][c] .. offsets[j][c + 1] (the chunk's length for the
 // last bucket).  No scan crosses chunks, so every (table, chunk) is sorted by
 // one workgroup, and its region is written contiguously.
+//
+// The sort is a least-significant-digit radix sort held in LDS, on digits of
+// up to 5 code bits (K <= 15: at most three passes).  Elements are packed as
+// code << 16 | key.  In every pass thread t owns the E consecutive positions
+// E t .. E t + E - 1 of the current order, so a key's stable rank is
+//   (elements of smaller digit) + (elements of its digit owned by threads
+//   below t) + (elements of its digit earlier in thread t).
+// Each thread counts its digits in 32 private 16-bit counters, two to a
+// 32-bit word; word w of thread t sits in row w of cnt[16][nthr], at column
+// swz(t), so the lanes of a wave touch distinct banks whatever their digits.
+// Digit d lives in word d & 15, half d >> 4.  One exclusive scan over the
+// word array in (w, t) order then gives every low half its start; a high
+// half also needs the count of all low-half digits, which the block total
+// carries in its low 16 bits.  A rank is bfe(start + count before it, half):
+// low halves never exceed the chunk length, so no carry reaches the high half.
+//
+// The buffer has E * nthr slots; slots at or past the chunk's length hold
+// code 0xffff, whose every digit is the largest, so they stay behind all keys
+// in every pass and the loops need no validity tests.
 // ---------------------------------------------------------------------------
-constexpr int kSortThreads = 512;
-constexpr int kSortWaves = kSortThreads / 64;
-constexpr int kSortBatches = 16;        // 64-key batches per wave: chunks of <= 8192 keys
-constexpr int kMatchLo = 8;             // code bits matched through the LDS lane-mask table
+constexpr int kSortMaxThreads = 512;
+constexpr int kSortE = 16;              // elements per thread
+constexpr int kDigitBits = 5;
+constexpr int kCntWords = 16;           // 32 digit counters of 16 bits per thread
 
-// Mask of the valid lanes of this wave whose code equals this lane's, in two
-// steps: a per-wave LDS table of 64-bit lane masks indexed by the low 8 code
-// bits (every lane ORs its bit into its entry and reads the entry back; LDS
-// operations of one wave are performed in issue order; the entry is cleared
-// afterwards), then one ballot per remaining code bit.
-__device__ __forceinline__ uint64_t match_lanes(int code, bool valid, int K, uint64_t* mt, int lane) {
-  volatile uint64_t* vt = mt;
-  const int lo = code & ((1 << kMatchLo) - 1);
-  if (valid) atomicOr(reinterpret_cast<unsigned long long*>(&mt[lo]), 1ull << lane);
-  __builtin_amdgcn_wave_barrier();
-  uint64_t m = valid ? vt[lo] : 0ull;
-  __builtin_amdgcn_wave_barrier();
-  if (valid) vt[lo] = 0ull;
-  for (int b = kMatchLo; b < K; ++b) {
-    const bool bit = (code >> b) & 1;
-    const uint64_t B = ballot(bit);
-    m &= bit ? B : ~B;
+// LDS bank swizzle of a counter word index: bits 5-6 are folded into bits
+// 2-3.  A 4-word quad stays contiguous, so a lane reading 16 consecutive
+// words as four 16-byte loads spreads every 8 lanes over all 32 banks, while
+// 32 consecutive indices (one per lane) still hit 32 distinct banks.
+__device__ __forceinline__ int swz(int x) { return x ^ ((x >> 3) & 12); }
+
+// Element buffer slot of position p: four padding words after every 32, for
+// the same reason (a lane's run of 16 is four quads; 8 lanes cover 32 banks).
+__device__ __forceinline__ int slot(int p) { return p + ((p >> 5) << 2); }
+
+__device__ __forceinline__ void load_run(const uint32_t* buf, int p, uint32_t (&e)[kSortE]) {
+#pragma unroll
+  for (int q = 0; q < kSortE / 4; ++q) {
+    const uint4 v = *reinterpret_cast<const uint4*>(buf + slot(p + 4 * q));
+    e[4 * q] = v.x;
+    e[4 * q + 1] = v.y;
+    e[4 * q + 2] = v.z;
+    e[4 * q + 3] = v.w;
   }
-  return m;
 }
 
-// One workgroup (8 waves) per (table, chunk); K <= 12 so the per-wave
-// histograms fit.  Each wave owns a contiguous eighth of the chunk and walks
-// it in batches of 64 keys held in registers.  A lane's rank is the number of
-// lanes below it with its code, so buckets keep the key order.
-//   phase 1  per-wave histograms (the first lane of each code adds the count)
-//   phase 2  scan: bucket starts in the chunk (the offsets output) and each
-//            wave's cursor in each bucket
-//   phase 3  placement into the chunk's sorted list in LDS
-//   phase 4  the list is written to the chunk's region, lane i to position i
-__global__ __launch_bounds__(kSortThreads) void chunk_sort_kernel(
-    const uint16_t* __restrict__ codes,   // [U][L][N]
-    int N, int K, int stride_log2, int nJ,
-    uint16_t* __restrict__ offsets,       // [U][L][nJ][2^K]
-    uint16_t* __restrict__ indices) {     // [U][L][N]
-  extern __shared__ __attribute__((aligned(16))) uint64_t smem64[];
-  const int nb = 1 << K;
-  constexpr int kMt = 1 << kMatchLo;
-  uint64_t* mt = smem64;                                               // [kSortWaves][256] lane masks
-  uint16_t* buf = reinterpret_cast<uint16_t*>(mt + kSortWaves * kMt);  // [chunk] key - chunk start
-  uint16_t* wh = buf + (1 << stride_log2);                             // [kSortWaves][nb] counts, cursors
-  __shared__ int32_t wave_tot[kSortWaves];
-
-  const int j = blockIdx.x;
-  const size_t table = blockIdx.y;      // u * L + l
+// Exclusive scan of the packed counter words, in place.  Thread s scans the
+// 16 consecutive words 16 s .. 16 s + 15 of the (w, t) order; word (w, t) is
+// stored at w * nthr + swz(t).
+__device__ __forceinline__ void scan_counters(uint32_t* cnt, int nthr, uint32_t* wave_tot) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cbeg = j << stride_log2;
-  const int clen = min(1 << stride_log2, N - cbeg);
-  const uint16_t* cd = codes + table * N + cbeg;
-
-  for (int i = tid; i < kSortWaves * kMt; i += kSortThreads) mt[i] = 0ull;
-  for (int i = tid; i < kSortWaves * nb; i += kSortThreads) wh[i] = 0;
-  // this wave's keys: batch k = chunk keys wbeg + 64 k + lane, below wend
-  const int per = (1 << stride_log2) / kSortWaves;
-  const int wbeg = wave * per;
-  const int wend = min(clen, wbeg + per);
-  int cr[kSortBatches];
+  int addr[kCntWords / 4];
+  uint32_t x[kCntWords];
 #pragma unroll
-  for (int k = 0; k < kSortBatches; ++k) {
-    const int n = wbeg + 64 * k + lane;
-    cr[k] = (64 * k < per && n < wend) ? static_cast<int>(cd[n]) : -1;
+  for (int q = 0; q < kCntWords / 4; ++q) {
+    const int f = kCntWords * tid + 4 * q;
+    const int w = f / nthr, t = f - w * nthr;
+    addr[q] = w * nthr + swz(t);
+    const uint4 v = *reinterpret_cast<const uint4*>(cnt + addr[q]);
+    x[4 * q] = v.x;
+    x[4 * q + 1] = v.y;
+    x[4 * q + 2] = v.z;
+    x[4 * q + 3] = v.w;
   }
-  __syncthreads();
-
-  uint64_t* my_mt = mt + wave * kMt;
-  volatile uint16_t* vwh = wh + wave * nb;
-  int rs[kSortBatches];                 // rank | count << 8 of this lane's key in its batch
+  uint32_t run = 0;
 #pragma unroll
-  for (int k = 0; k < kSortBatches; ++k) {
-    rs[k] = 0;
-    if (64 * k >= per) continue;        // wave-uniform: chunks shorter than 8192 keys
-    const bool valid = cr[k] >= 0;
-    const int code = valid ? cr[k] : 0;
-    const uint64_t m = match_lanes(code, valid, K, my_mt, lane);
-    const int rank = mbcnt(m), cnt = __builtin_popcountll(m);
-    rs[k] = rank | (cnt << 8);
-    if (valid && rank == 0) vwh[code] = static_cast<uint16_t>(vwh[code] + cnt);
-    __builtin_amdgcn_wave_barrier();
+  for (int q = 0; q < kCntWords; ++q) {
+    const uint32_t v = x[q];
+    x[q] = run;
+    run += v;
   }
-  __syncthreads();
-
-  // phase 2
-  uint16_t* off = offsets + (table * nJ + j) * nb;
-  const int bpt = (nb + kSortThreads - 1) / kSortThreads;
-  const int c0 = tid * bpt, c1 = min(nb, c0 + bpt);
-  int local = 0;
-  for (int c = c0; c < c1; ++c)
-    for (int w = 0; w < kSortWaves; ++w) local += wh[w * nb + c];
-  int incl = local;
+  uint32_t incl = run;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o);
+    const uint32_t v = __shfl_up(incl, o);
     if (lane >= o) incl += v;
   }
   if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
-  int run = incl - local;
-  for (int w = 0; w < wave; ++w) run += wave_tot[w];
-  for (int c = c0; c < c1; ++c) {
-    off[c] = static_cast<uint16_t>(run);
-    for (int w = 0; w < kSortWaves; ++w) {
-      const int x = wh[w * nb + c];
-      wh[w * nb + c] = static_cast<uint16_t>(run);
-      run += x;
-    }
+  uint32_t base = incl - run, total = 0;
+  const int nw = nthr >> 6;
+  for (int w = 0; w < nw; ++w) {
+    const uint32_t t = wave_tot[w];
+    base += w < wave ? t : 0u;
+    total += t;
   }
-  __syncthreads();
-
-  // phase 3
+  base += (total & 0xffffu) << 16;      // high halves start after every low-half digit
 #pragma unroll
-  for (int k = 0; k < kSortBatches; ++k) {
-    if (64 * k >= per) continue;
-    const bool valid = cr[k] >= 0;
-    const int code = valid ? cr[k] : 0;
-    const int rank = rs[k] & 0xff, cnt = rs[k] >> 8;
-    const int p = valid ? static_cast<int>(vwh[code]) : 0;
-    __builtin_amdgcn_wave_barrier();
-    if (valid) {
-      buf[p + rank] = static_cast<uint16_t>(wbeg + 64 * k + lane);
-      if (rank == 0) vwh[code] = static_cast<uint16_t>(p + cnt);
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-  __syncthreads();
-
-  // phase 4: two entries per lane, 4-byte stores when the region allows it
-  uint16_t* out = indices + table * N + cbeg;
-  if ((N & 1) == 0) {
-    const uint32_t* b2 = reinterpret_cast<const uint32_t*>(buf);
-    uint32_t* o2 = reinterpret_cast<uint32_t*>(out);
-    for (int e = tid; e < (clen >> 1); e += kSortThreads) o2[e] = b2[e];
-    if ((clen & 1) && tid == 0) out[clen - 1] = buf[clen - 1];
-  } else {
-    for (int e = tid; e < clen; e += kSortThreads) out[e] = buf[e];
-  }
+  for (int q = 0; q < kCntWords / 4; ++q)
+    *reinterpret_cast<uint4*>(cnt + addr[q]) =
+        make_uint4(base + x[4 * q], base + x[4 * q + 1], base + x[4 * q + 2], base + x[4 * q + 3]);
 }
 
-size_t chunk_sort_lds_bytes(int K, int stride_log2) {
-  const size_t nb = size_t(1) << K;
-  return kSortWaves * (size_t(1) << kMatchLo) * 8 + (size_t(2) << stride_log2) + kSortWaves * nb * 2;
-}
-
-// Any K (up to 15): one wave per (table, chunk) walks the chunk twice from
-// global memory: histogram, scan, then placement with the same rank rule.
-constexpr int kSortOneThreads = 64;
-
-__global__ __launch_bounds__(kSortOneThreads) void chunk_sort_one_kernel(
-    const uint16_t* __restrict__ codes, int N, int K, int stride_log2, int nJ,
-    uint16_t* __restrict__ offsets, uint16_t* __restrict__ indices) {
-  extern __shared__ __attribute__((aligned(16))) uint64_t smem64[];
-  const int nb = 1 << K;
-  constexpr int kMt = 1 << kMatchLo;
-  uint64_t* mt = smem64;                                      // [256]
-  uint16_t* buf = reinterpret_cast<uint16_t*>(mt + kMt);      // [chunk]
-  uint16_t* cur = buf + (1 << stride_log2);                   // [nb]
+// One workgroup of nthr = chunk / E threads (at least one wave) per (table,
+// chunk); LDS: counters [16][nthr] and the padded element buffer, 32-bit,
+// reused at the end for the bucket starts [2^K] (16-bit).
+__global__ __launch_bounds__(kSortMaxThreads, 4) void chunk_sort_kernel(
+    const uint16_t* __restrict__ codes,   // [U][L][N]
+    int N, int K, int stride_log2, int nJ,
+    uint16_t* __restrict__ offsets,       // [U][L][nJ][2^K]
+    uint16_t* __restrict__ indices) {     // [U][L][N]
+  constexpr int E = kSortE;
+  extern __shared__ __attribute__((aligned(16))) uint32_t smem32[];
+  __shared__ uint32_t wave_tot[kSortMaxThreads / 64];
+  const int nthr = blockDim.x;
+  uint32_t* cnt = smem32;                       // [16][nthr]
+  uint32_t* buf = smem32 + kCntWords * nthr;    // slot(position): code << 16 | key
   const int j = blockIdx.x;
-  const size_t table = blockIdx.y;
-  const int lane = threadIdx.x;
+  const size_t table = blockIdx.y;              // u * L + l
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nb = 1 << K;
   const int cbeg = j << stride_log2;
   const int clen = min(1 << stride_log2, N - cbeg);
-  const uint16_t* cd = codes + table * N + cbeg;
-  volatile uint16_t* vcur = cur;
+  const int p0 = tid * E;
+  const bool full = p0 + E <= clen;
+  const bool vec = ((table * N) & 7) == 0;      // the chunk's codes are 16-byte aligned
 
-  for (int i = lane; i < kMt; i += 64) mt[i] = 0ull;
-  for (int i = lane; i < nb; i += 64) cur[i] = 0;
+  // this thread's E positions, straight from the codes
+  uint32_t e[E];
+  {
+    const uint16_t* cd = codes + table * N + cbeg + p0;
+    if (full && vec) {
+      const uint4* c4 = reinterpret_cast<const uint4*>(cd);
+#pragma unroll
+      for (int q = 0; q < E / 8; ++q) {
+        const uint4 v = c4[q];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t p = static_cast<uint32_t>(p0 + 8 * q + 2 * k);
+          e[8 * q + 2 * k] = (w[k] << 16) | p;
+          e[8 * q + 2 * k + 1] = (w[k] & 0xffff0000u) | (p + 1);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const uint32_t c = (p0 + i < clen) ? static_cast<uint32_t>(cd[i]) : 0xffffu;
+        e[i] = (c << 16) | static_cast<uint32_t>(p0 + i);
+      }
+    }
+  }
+
+  const int col = swz(tid);                     // this thread's counter column
+  const int passes = (K + kDigitBits - 1) / kDigitBits;
+  for (int r = 0; r < passes; ++r) {
+    const int sh = 16 + r * kDigitBits;
+#pragma unroll
+    for (int w = 0; w < kCntWords; ++w) cnt[w * nthr + col] = 0u;
+    // own column only: no barrier needed before counting
+    uint32_t* ca[E];
+    uint32_t old[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const uint32_t w = (e[i] >> sh) & 15u;
+      const uint32_t hi = (e[i] >> (sh + 4)) & 1u;
+      ca[i] = cnt + w * nthr + col;
+      old[i] = atomicAdd(ca[i], hi * 0xffffu + 1u);   // +1 in the digit's half
+    }
+    __syncthreads();
+    scan_counters(cnt, nthr, wave_tot);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < E; ++i) old[i] += *ca[i];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const uint32_t half = ((e[i] >> (sh + 4)) & 1u) << 4;
+      buf[slot(static_cast<int>((old[i] >> half) & 0xffffu))] = e[i];
+    }
+    __syncthreads();
+    load_run(buf, p0, e);                       // two barriers pass before buf is written again
+  }
+
+  // the sorted region: thread t writes its E positions
+  uint16_t* out = indices + table * N + cbeg;
+  if (full && vec) {
+    uint4* o4 = reinterpret_cast<uint4*>(out + p0);
+#pragma unroll
+    for (int q = 0; q < E / 8; ++q) {
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = (e[8 * q + 2 * k] & 0xffffu) | (e[8 * q + 2 * k + 1] << 16);
+      o4[q] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      if (p0 + i < clen) out[p0 + i] = static_cast<uint16_t>(e[i]);
+  }
+
+  // bucket starts: st[c] = first position of code c (clen when c is empty),
+  // then offsets[c] = min over c' >= c of st[c'] (a suffix minimum).  The
+  // code before this thread's run is the last one of the previous thread.
+  int prev = __shfl_up(static_cast<int>(e[E - 1] >> 16), 1);
+  if (lane == 63) wave_tot[wave] = e[E - 1] >> 16;
   __syncthreads();
-  for (int b = 0; b < clen; b += 64) {
-    const int n = b + lane;
-    const bool valid = n < clen;
-    const int code = valid ? static_cast<int>(cd[n]) : 0;
-    const uint64_t m = match_lanes(code, valid, K, mt, lane);
-    if (valid && mbcnt(m) == 0) vcur[code] = static_cast<uint16_t>(vcur[code] + __builtin_popcountll(m));
-    __builtin_amdgcn_wave_barrier();
+  if (lane == 0) prev = wave > 0 ? static_cast<int>(wave_tot[wave - 1]) : -1;
+  uint16_t* st = reinterpret_cast<uint16_t*>(smem32);
+  for (int c = tid; c < nb; c += nthr) st[c] = static_cast<uint16_t>(clen);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int c = min(static_cast<int>(e[i] >> 16), nb - 1);   // codes are < 2^K
+    if (p0 + i < clen && c != prev) st[c] = static_cast<uint16_t>(p0 + i);
+    prev = c;
   }
   __syncthreads();
   uint16_t* off = offsets + (table * nJ + j) * nb;
-  int base = 0;
-  for (int c0 = 0; c0 < nb; c0 += 64) {
-    const int c = c0 + lane;
-    const int x = c < nb ? static_cast<int>(cur[c]) : 0;
-    int incl = x;
+  // thread t owns buckets [t bpt, (t + 1) bpt); suffix minimum across threads
+  // through the wave (reversed lane order) and the wave totals
+  const int bpt = (nb + nthr - 1) / nthr;
+  const int c0 = tid * bpt, c1 = min(nb, c0 + bpt);
+  int mine = clen;
+  for (int c = c1 - 1; c >= c0; --c) mine = min(mine, static_cast<int>(st[c]));
+  int suf = mine;                                   // min over lanes >= lane of this wave
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o);
-      if (lane >= o) incl += v;
-    }
-    if (c < nb) {
-      off[c] = static_cast<uint16_t>(base + incl - x);
-      cur[c] = static_cast<uint16_t>(base + incl - x);
-    }
-    base += __shfl(incl, 63);
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_down(suf, o);
+    if (lane + o < 64) suf = min(suf, v);
   }
+  __syncthreads();                                  // wave_tot is reused
+  if (lane == 0) wave_tot[wave] = static_cast<uint32_t>(suf);
   __syncthreads();
-  for (int b = 0; b < clen; b += 64) {
-    const int n = b + lane;
-    const bool valid = n < clen;
-    const int code = valid ? static_cast<int>(cd[n]) : 0;
-    const uint64_t m = match_lanes(code, valid, K, mt, lane);
-    const int rank = mbcnt(m);
-    const int p = valid ? static_cast<int>(vcur[code]) : 0;
-    __builtin_amdgcn_wave_barrier();
-    if (valid) {
-      buf[p + rank] = static_cast<uint16_t>(n);
-      if (rank == 0) vcur[code] = static_cast<uint16_t>(p + __builtin_popcountll(m));
-    }
-    __builtin_amdgcn_wave_barrier();
+  int after = __shfl_down(suf, 1);                  // min over lanes > lane
+  if (lane == 63) after = clen;
+  const int nw = nthr >> 6;
+  for (int w = wave + 1; w < nw; ++w) after = min(after, static_cast<int>(wave_tot[w]));
+  for (int c = c1 - 1; c >= c0; --c) {
+    after = min(after, static_cast<int>(st[c]));
+    off[c] = static_cast<uint16_t>(after);
   }
-  __syncthreads();
-  uint16_t* out = indices + table * N + cbeg;
-  for (int e = lane; e < clen; e += 64) out[e] = buf[e];
 }
 
-size_t chunk_sort_one_lds_bytes(int K, int stride_log2) {
-  return (size_t(1) << kMatchLo) * 8 + (size_t(2) << stride_log2) + (size_t(2) << K);
+// Block size for a chunk of 2^stride_log2 keys, and the LDS it needs.
+static int sort_threads(int stride_log2) { return max(64, (1 << stride_log2) / kSortE); }
+
+size_t chunk_sort_lds_bytes(int stride_log2, int K) {
+  const size_t nthr = static_cast<size_t>(sort_threads(stride_log2));
+  const size_t elems = nthr * kSortE;
+  return max((kCntWords * nthr + elems + (elems >> 3)) * 4, size_t(2) << K);
 }
 
 // ---------------------------------------------------------------------------
@@ -469,20 +489,12 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t stream) {
       : launch_project<F32>(a.keys, a.W, a.wt, a.codes, a.U, a.N, a.K, a.L, stream);
   if (e != hipSuccess) return e;
   const dim3 grid(a.nJ, a.U * a.L);
-  if (a.K <= 12) {
-    const size_t lds = chunk_sort_lds_bytes(a.K, a.stride_log2);
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_sort_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    return launch(kKChunkSort, chunk_sort_kernel, grid, dim3(kSortThreads), static_cast<unsigned>(lds), stream,
-                  static_cast<const uint16_t*>(a.codes), a.N, a.K, a.stride_log2, a.nJ, a.offsets, a.indices);
-  }
-  const size_t lds = chunk_sort_one_lds_bytes(a.K, a.stride_log2);
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_sort_one_kernel),
+  const size_t lds = chunk_sort_lds_bytes(a.stride_log2, a.K);
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_sort_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  return launch(kKChunkSort, chunk_sort_one_kernel, grid, dim3(kSortOneThreads), static_cast<unsigned>(lds), stream,
-                static_cast<const uint16_t*>(a.codes), a.N, a.K, a.stride_log2, a.nJ, a.offsets, a.indices);
+  return launch(kKChunkSort, chunk_sort_kernel, grid, dim3(sort_threads(a.stride_log2)), static_cast<unsigned>(lds),
+                stream, static_cast<const uint16_t*>(a.codes), a.N, a.K, a.stride_log2, a.nJ, a.offsets, a.indices);
 }
 
 }  // namespace lsh

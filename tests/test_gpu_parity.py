@@ -135,6 +135,15 @@ def test_strides(stride):
     check_case(cfg, data, stride=stride)
 
 
+def test_k15_small_stride():
+    # 2^15 bucket starts per chunk exceed the sort's own LDS at this stride
+    cfg = SMALL[9]
+    assert cfg.K == 15
+    say("case K15 stride 256")
+    data = workloads.generate(cfg)
+    check_case(cfg, data, stride=256)
+
+
 def test_k0_is_exact_attention():
     cfg = workloads.Config("k0", B=1, Hq=8, Hkv=2, N=3000, d=128, K=0, L=3, T=2, dtype="bf16",
                            planted=4, a=0.8, offset="per_head", seed=21)
