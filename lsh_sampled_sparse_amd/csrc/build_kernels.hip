@@ -82,12 +82,21 @@ __global__ void transpose_w_kernel(const typename T::storage* __restrict__ W,
   WT[idx] = valid ? W[static_cast<size_t>(d) * L * K + t * K + b] : typename T::storage(0);
 }
 
+// (s << 1) | [x > 0]: the bits of a float, read as an integer, are positive
+// exactly when the float is positive and nonzero, so the saturating 0 - bits
+// is negative exactly then (saturation keeps -0.0, read as INT_MIN,
+// positive); a funnel shift appends its sign bit to s.
+__device__ __forceinline__ uint32_t push_positive_bit(uint32_t s, float x) {
+  const int t = __builtin_elementwise_sub_sat(0, __float_as_int(x));
+  return __builtin_amdgcn_alignbit(s, static_cast<uint32_t>(t), 31u);
+}
+
 constexpr int kProjThreads = 256;              // 4 waves
 constexpr int kProjKeys = 256;                 // 64 keys per wave = 4 tiles of 16
 
 // codes[u][l][n] for this workgroup's 256 keys.
 template <typename T, int KB>
-__global__ __launch_bounds__(kProjThreads) void project_codes_kernel(
+__global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_codes_kernel(
     const typename T::storage* __restrict__ keys,   // [U][N][128]
     const typename T::storage* __restrict__ WT,     // [nslab * NCT * 16][128], permuted
     uint16_t* __restrict__ codes,                   // [U][L][N]
@@ -100,7 +109,11 @@ __global__ __launch_bounds__(kProjThreads) void project_codes_kernel(
   constexpr int kChunksPerRow = kHeadDim * T::bytes / 16;
   constexpr int kCPT = kRows * kChunksPerRow / kProjThreads;       // 16-byte pieces per thread
   constexpr uint32_t kMask = (1u << KB) - 1u;
+  constexpr int kStgRow = kProjKeys + 8;                           // padded staging row (uint16)
   __shared__ __attribute__((aligned(16))) S wt[2][kRows * kRow];
+  // codes of one slab, [table in slab][key in block], double-buffered so that
+  // the write-out after a slab's barrier never races the next slab's writes
+  __shared__ __attribute__((aligned(16))) uint16_t stg[2][TPS * kStgRow];
 
   const int u = blockIdx.y;
   const int n0 = blockIdx.x * kProjKeys;
@@ -133,47 +146,87 @@ __global__ __launch_bounds__(kProjThreads) void project_codes_kernel(
                                           (chunk % kChunksPerRow) * (16 / T::bytes)]) = pre[k];
     }
   };
-  fetch(0);
+  // workgroups walk the slabs from different starting points, so that the
+  // CUs sharing an L2 do not all read the same slab of WT at once
+  const int s0 = static_cast<int>((blockIdx.x + 5u * blockIdx.y) % static_cast<unsigned>(nslab));
+  auto slab_of = [&](int s) { return s0 + s < nslab ? s0 + s : s0 + s - nslab; };
+  fetch(slab_of(0));
   stash(0);
   __syncthreads();
 
   for (int s = 0; s < nslab; ++s) {
     const int buf = s & 1;
-    if (s + 1 < nslab) fetch(s + 1);
+    if (s + 1 < nslab) fetch(slab_of(s + 1));
     // sign bits of the P rows of lane group g, for this lane's key in each
-    // tile, shifted in row order (s = 2 s + [x > 0]).  The column-tile loop is
-    // kept rolled: four accumulators are live at a time, which leaves room for
-    // several waves per SIMD to overlap one wave's MFMAs with another's signs.
+    // tile, shifted in row order (s = 2 s + [x > 0]).  Software pipelined
+    // over column tiles: each of the 16 MFMAs of tile ct is paired with one
+    // sign update of tile ct - 1 (two accumulator sets, two W fragments), and
+    // the pairs are fenced so that the VALU work issues while the matrix
+    // pipe runs; the W fragment of tile ct + 1 is read during tile ct.
     uint32_t sg[4] = {0u, 0u, 0u, 0u};
-#pragma unroll 1
-    for (int ct = 0; ct < NCT; ++ct) {
-      Frag<T> Wf;
-      Wf.load(&wt[buf][(ct * 16 + (lane & 15)) * kRow + g * 32], true);
-      floatx4_t acc[4];
+    floatx4_t accA[4], accB[4];
+    Frag<T> Wa, Wb;
+    const S* wrow = &wt[buf][(lane & 15) * kRow + g * 32];
+    auto wtile = [&](int ct) { return wrow + min(ct, NCT - 1) * 16 * kRow; };
+    // MFMAs of one tile (W -> acc), paired with the signs of the previous one
+    auto half = [&](const Frag<T>& W, floatx4_t (&acc)[4], const floatx4_t (&prev)[4], bool signs) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        acc[a] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        acc[a] = Wf.mma(A[a], acc[a]);   // acc[a][i]: row 4 g + i, key lane & 15 of tile a
+      for (int a = 0; a < 4; ++a) acc[a] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        W.mma_step(q >> 2, A[q & 3], acc[q & 3]);       // k-step q / 4 of key tile q % 4
+        if (signs) sg[q >> 2] = push_positive_bit(sg[q >> 2], prev[q >> 2][q & 3]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    };
+    auto signs_of = [&](const floatx4_t (&acc)[4]) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sg[a] = sg[a] * 2u + (acc[a][i] > 0.f ? 1u : 0u);
+        for (int i = 0; i < 4; ++i) sg[a] = push_positive_bit(sg[a], acc[a][i]);
+    };
+    Wa.load(wtile(0), true);
+    Wb.load(wtile(1), true);
+    half(Wa, accA, accB, false);                        // tile 0
+    int ct = 1;
+#pragma unroll 1
+    for (; ct + 1 < NCT; ct += 2) {
+      Wa.load(wtile(ct + 1), true);
+      half(Wb, accB, accA, true);                       // tile ct, signs of ct - 1
+      Wb.load(wtile(ct + 2), true);
+      half(Wa, accA, accB, true);                       // tile ct + 1, signs of ct
     }
+    if (NCT % 2 == 0) {
+      half(Wb, accB, accA, true);                       // tile NCT - 1
+      signs_of(accB);
+    } else {
+      signs_of(accA);
+    }
+    // codes of tables slab_of(s) * TPS + g * TPG + tt, staged per table row
+    uint16_t* sb = stg[s & 1];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int tt = 0; tt < TPG; ++tt)
+        sb[(g * TPG + tt) * kStgRow + wave * 64 + a * 16 + (lane & 15)] =
+            static_cast<uint16_t>((sg[a] >> (tt * KB)) & kMask);
     if (s + 1 < nslab) stash(buf ^ 1);
-    // codes of tables s * TPS + g * TPG + tt
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int key = n0 + wave * 64 + a * 16 + (lane & 15);
-      if (key < N) {
-#pragma unroll
-        for (int tt = 0; tt < TPG; ++tt) {
-          const int t = s * TPS + g * TPG + tt;
-          if (t < L) cb[static_cast<size_t>(t) * N + key] = static_cast<uint16_t>((sg[a] >> (tt * KB)) & kMask);
+    __syncthreads();
+    // write-out: 8 consecutive keys of one table per 16-byte piece
+    for (int c = tid; c < TPS * (kProjKeys / 8); c += kProjThreads) {
+      const int r = c / (kProjKeys / 8), k8 = (c % (kProjKeys / 8)) * 8;
+      const int t = slab_of(s) * TPS + r, key = n0 + k8;
+      if (t < L) {
+        const uint16_t* src = sb + r * kStgRow + k8;
+        uint16_t* dst = cb + static_cast<size_t>(t) * N + key;
+        if (key + 8 <= N && (N & 7) == 0) {
+          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        } else {
+          for (int e = 0; e < 8; ++e)
+            if (key + e < N) dst[e] = src[e];
         }
       }
     }
-    __syncthreads();
   }
 }
 
@@ -242,16 +295,17 @@ __device__ __forceinline__ void load_run(const uint32_t* buf, int p, uint32_t (&
 
 // Exclusive scan of the packed counter words, in place.  Thread s scans the
 // 16 consecutive words 16 s .. 16 s + 15 of the (w, t) order; word (w, t) is
-// stored at w * nthr + swz(t).
-__device__ __forceinline__ void scan_counters(uint32_t* cnt, int nthr, uint32_t* wave_tot) {
+// stored at w * NTHR + swz(t).
+template <int NTHR>
+__device__ __forceinline__ void scan_counters(uint32_t* cnt, uint32_t* wave_tot) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int addr[kCntWords / 4];
   uint32_t x[kCntWords];
 #pragma unroll
   for (int q = 0; q < kCntWords / 4; ++q) {
     const int f = kCntWords * tid + 4 * q;
-    const int w = f / nthr, t = f - w * nthr;
-    addr[q] = w * nthr + swz(t);
+    const int w = f / NTHR, t = f % NTHR;
+    addr[q] = w * NTHR + swz(t);
     const uint4 v = *reinterpret_cast<const uint4*>(cnt + addr[q]);
     x[4 * q] = v.x;
     x[4 * q + 1] = v.y;
@@ -274,8 +328,8 @@ __device__ __forceinline__ void scan_counters(uint32_t* cnt, int nthr, uint32_t*
   if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
   uint32_t base = incl - run, total = 0;
-  const int nw = nthr >> 6;
-  for (int w = 0; w < nw; ++w) {
+#pragma unroll
+  for (int w = 0; w < NTHR / 64; ++w) {
     const uint32_t t = wave_tot[w];
     base += w < wave ? t : 0u;
     total += t;
@@ -287,20 +341,21 @@ __device__ __forceinline__ void scan_counters(uint32_t* cnt, int nthr, uint32_t*
         make_uint4(base + x[4 * q], base + x[4 * q + 1], base + x[4 * q + 2], base + x[4 * q + 3]);
 }
 
-// One workgroup of nthr = chunk / E threads (at least one wave) per (table,
-// chunk); LDS: counters [16][nthr] and the padded element buffer, 32-bit,
-// reused at the end for the bucket starts [2^K] (16-bit).
-__global__ __launch_bounds__(kSortMaxThreads, 4) void chunk_sort_kernel(
+// One workgroup of NTHR = max(64, chunk / E) threads per (table, chunk);
+// LDS: counters [16][NTHR] and the padded element buffer, 32-bit, reused at
+// the end for the bucket starts [2^K] (16-bit).
+template <int NTHR>
+__global__ __launch_bounds__(NTHR, NTHR >= 256 ? 4 : 1) void chunk_sort_kernel(
     const uint16_t* __restrict__ codes,   // [U][L][N]
     int N, int K, int stride_log2, int nJ,
     uint16_t* __restrict__ offsets,       // [U][L][nJ][2^K]
     uint16_t* __restrict__ indices) {     // [U][L][N]
   constexpr int E = kSortE;
   extern __shared__ __attribute__((aligned(16))) uint32_t smem32[];
-  __shared__ uint32_t wave_tot[kSortMaxThreads / 64];
-  const int nthr = blockDim.x;
-  uint32_t* cnt = smem32;                       // [16][nthr]
-  uint32_t* buf = smem32 + kCntWords * nthr;    // slot(position): code << 16 | key
+  __shared__ uint32_t wave_tot[NTHR / 64];
+  constexpr int nthr = NTHR;
+  uint32_t* cnt = smem32;                       // [16][NTHR]
+  uint32_t* buf = smem32 + kCntWords * NTHR;    // slot(position): code << 16 | key
   const int j = blockIdx.x;
   const size_t table = blockIdx.y;              // u * L + l
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -337,32 +392,30 @@ __global__ __launch_bounds__(kSortMaxThreads, 4) void chunk_sort_kernel(
     }
   }
 
-  const int col = swz(tid);                     // this thread's counter column
+  uint32_t* ccol = cnt + swz(tid);              // this thread's counter column
   const int passes = (K + kDigitBits - 1) / kDigitBits;
   for (int r = 0; r < passes; ++r) {
     const int sh = 16 + r * kDigitBits;
 #pragma unroll
-    for (int w = 0; w < kCntWords; ++w) cnt[w * nthr + col] = 0u;
-    // own column only: no barrier needed before counting
+    for (int w = 0; w < kCntWords; ++w) ccol[w * NTHR] = 0u;
+    // own column only: no barrier needed before counting.  hs: 0 or 16, the
+    // digit's half of its counter word
     uint32_t* ca[E];
-    uint32_t old[E];
+    uint32_t old[E], hs[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      const uint32_t w = (e[i] >> sh) & 15u;
-      const uint32_t hi = (e[i] >> (sh + 4)) & 1u;
-      ca[i] = cnt + w * nthr + col;
-      old[i] = atomicAdd(ca[i], hi * 0xffffu + 1u);   // +1 in the digit's half
+      const uint32_t x = e[i] >> sh;
+      hs[i] = x & 16u;
+      ca[i] = ccol + (x & 15u) * NTHR;
+      old[i] = atomicAdd(ca[i], 1u << hs[i]);
     }
     __syncthreads();
-    scan_counters(cnt, nthr, wave_tot);
+    scan_counters<NTHR>(cnt, wave_tot);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < E; ++i) old[i] += *ca[i];
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const uint32_t half = ((e[i] >> (sh + 4)) & 1u) << 4;
-      buf[slot(static_cast<int>((old[i] >> half) & 0xffffu))] = e[i];
-    }
+    for (int i = 0; i < E; ++i) buf[slot(static_cast<int>(__builtin_amdgcn_ubfe(old[i], hs[i], 16)))] = e[i];
     __syncthreads();
     load_run(buf, p0, e);                       // two barriers pass before buf is written again
   }
@@ -436,6 +489,17 @@ size_t chunk_sort_lds_bytes(int stride_log2, int K) {
   return max((kCntWords * nthr + elems + (elems >> 3)) * 4, size_t(2) << K);
 }
 
+template <int NTHR>
+static hipError_t launch_chunk_sort(const BuildArgs& a, hipStream_t stream) {
+  const size_t lds = chunk_sort_lds_bytes(a.stride_log2, a.K);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_sort_kernel<NTHR>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  return launch(kKChunkSort, chunk_sort_kernel<NTHR>, dim3(a.nJ, a.U * a.L), dim3(NTHR),
+                static_cast<unsigned>(lds), stream, static_cast<const uint16_t*>(a.codes), a.N, a.K, a.stride_log2,
+                a.nJ, a.offsets, a.indices);
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------
@@ -488,13 +552,13 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t stream) {
       ? launch_project<BF16>(a.keys, a.W, a.wt, a.codes, a.U, a.N, a.K, a.L, stream)
       : launch_project<F32>(a.keys, a.W, a.wt, a.codes, a.U, a.N, a.K, a.L, stream);
   if (e != hipSuccess) return e;
-  const dim3 grid(a.nJ, a.U * a.L);
-  const size_t lds = chunk_sort_lds_bytes(a.stride_log2, a.K);
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_sort_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  if (e != hipSuccess) return e;
-  return launch(kKChunkSort, chunk_sort_kernel, grid, dim3(sort_threads(a.stride_log2)), static_cast<unsigned>(lds),
-                stream, static_cast<const uint16_t*>(a.codes), a.N, a.K, a.stride_log2, a.nJ, a.offsets, a.indices);
+  switch (sort_threads(a.stride_log2)) {
+    case 64: return launch_chunk_sort<64>(a, stream);
+    case 128: return launch_chunk_sort<128>(a, stream);
+    case 256: return launch_chunk_sort<256>(a, stream);
+    case 512: return launch_chunk_sort<512>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace lsh

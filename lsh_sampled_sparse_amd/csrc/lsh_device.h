@@ -91,6 +91,10 @@ struct Frag<BF16> {
     for (int k = 0; k < 4; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[k], b.v[k], acc, 0, 0, 0);
     return acc;
   }
+  // one of the four k-steps of mma()
+  __device__ __forceinline__ void mma_step(int k, const Frag& b, floatx4_t& acc) const {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[k], b.v[k], acc, 0, 0, 0);
+  }
 };
 
 template <>
@@ -109,6 +113,11 @@ struct Frag<F32> {
 #pragma unroll
     for (int k = 0; k < 32; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v[k], b.v[k], acc, 0, 0, 0);
     return acc;
+  }
+  // one quarter (8 of the 32 k-steps) of mma()
+  __device__ __forceinline__ void mma_step(int k, const Frag& b, floatx4_t& acc) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v[8 * k + j], b.v[8 * k + j], acc, 0, 0, 0);
   }
 };
 

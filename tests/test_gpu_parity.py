@@ -135,6 +135,17 @@ def test_strides(stride):
     check_case(cfg, data, stride=stride)
 
 
+def test_zero_keys():
+    # all-zero key rows: every projection is exactly zero (no flip band), so
+    # their codes must be 0, and their cosine is taken as 0
+    cfg = SMALL[2]
+    say("case zero keys")
+    data = workloads.generate(cfg)
+    data["keys"][0, 0, 100:140] = 0
+    data["keys"][0, 1, 2990:] = 0
+    check_case(cfg, data)
+
+
 def test_k15_small_stride():
     # 2^15 bucket starts per chunk exceed the sort's own LDS at this stride
     cfg = SMALL[9]
