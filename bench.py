@@ -9,12 +9,14 @@ tables were built one step earlier, so the decode does not read tables that
 the build just left in the 256 MB last-level cache.
 
 Prints ONE JSON line.  ``value`` is query-heads per second of whole steps
-(build + decode); the decode alone is reported under ``breakdown``.  The
-``roofline`` object is for the kernel with the largest total time, from the
-library's per-dispatch timing events; ``cpu_baseline`` times the fp64 CPU
-oracle on a bounded sample of the same workload.
+(build + decode), timed over steps replayed from HIP graphs (``--launch
+eager`` launches them one by one instead); the decode alone is reported under
+``breakdown``.  The ``roofline`` object is for the kernel with the largest
+total time, from the library's per-dispatch timing events in a separate eager
+pass over the same steps; ``cpu_baseline`` times the fp64 CPU oracle on a
+bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4] [--launch graph|eager]
 """
 
 from __future__ import annotations
@@ -53,8 +55,8 @@ def parse():
     ap.add_argument("--config", type=int, default=4, help="workload id in workloads.CONFIGS (default: 128K GQA-8)")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-kernel-timing", action="store_true",
-                    help="time the steps without per-dispatch events (roofline from a second pass)")
+    ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
+                    help="replay each step from a HIP graph (default) or launch it eagerly")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -163,22 +165,42 @@ def main():
     torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- timed
-    timing = not args.no_kernel_timing
-    if timing:
-        lsh.lsh_timing_begin()
+    # Steps are replayed from HIP graphs (one per input copy) unless --launch
+    # eager; the kernels and their arguments are those of the eager step.
+    launch_mode = args.launch
+    graphs = []
+    if launch_mode == "graph":
+        try:
+            for r in range(R):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    step(r)
+                graphs.append(g)
+            for i in range(R):
+                graphs[i].replay()
+            torch.cuda.synchronize()
+        except Exception as exc:  # capture unsupported here: time eager launches instead
+            print(f"graph capture failed ({exc}); timing eager launches", file=sys.stderr)
+            launch_mode, graphs = "eager", []
+
+    def run(i):
+        if graphs:
+            graphs[i % R].replay()
+        else:
+            step(i)
+
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.warmup, args.warmup + args.steps):
-        step(i)
+        run(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    if timing:
-        ktimes = lsh.lsh_timing_end()
-    else:
-        lsh.lsh_timing_begin()
-        for i in range(args.warmup, args.warmup + args.steps):
-            step(i)
-        ktimes = lsh.lsh_timing_end()
+    # per-dispatch kernel times from a second, eager pass (events ride on the
+    # dispatch packets, so they are not part of the timed steps above)
+    lsh.lsh_timing_begin()
+    for i in range(args.warmup, args.warmup + args.steps):
+        step(i)
+    ktimes = lsh.lsh_timing_end()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     qh = B * Hq
     value = qh / (ms_per_step * 1e-3)
@@ -285,7 +307,7 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "K": K, "L": L, "T": T,
-                   "kv_dtype": cfg.dtype, "stride": stride, "step": "table build + 1 decode step",
+                   "kv_dtype": cfg.dtype, "stride": stride, "step": "table build + 1 decode step", "launch": launch_mode,
                    "input_copies": R},
         "roofline": roof,
         "breakdown": {

@@ -492,8 +492,7 @@ size_t chunk_sort_lds_bytes(int stride_log2, int K) {
 template <int NTHR>
 static hipError_t launch_chunk_sort(const BuildArgs& a, hipStream_t stream) {
   const size_t lds = chunk_sort_lds_bytes(a.stride_log2, a.K);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_sort_kernel<NTHR>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(chunk_sort_kernel<NTHR>), lds);
   if (e != hipSuccess) return e;
   return launch(kKChunkSort, chunk_sort_kernel<NTHR>, dim3(a.nJ, a.U * a.L), dim3(NTHR),
                 static_cast<unsigned>(lds), stream, static_cast<const uint16_t*>(a.codes), a.N, a.K, a.stride_log2,

@@ -651,8 +651,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
                         a.lnu_table, BH, a.K, a.L, a.T, head_blocks);
   if (e != hipSuccess) return e;
   const size_t lds = ((static_cast<size_t>(1) << a.stride_log2) + 3) & ~static_cast<size_t>(3);
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(count_select_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  e = ensure_lds_limit(reinterpret_cast<const void*>(count_select_kernel), lds);
   if (e != hipSuccess) return e;
   e = launch(kKCountSelect, count_select_kernel, dim3(a.nJ, BH), dim3(kCountThreads),
              static_cast<unsigned>(lds), stream, static_cast<const uint16_t*>(a.qcodes),

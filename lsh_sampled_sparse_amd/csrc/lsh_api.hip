@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <map>
 #include <mutex>
 #include <vector>
 
@@ -112,6 +113,20 @@ const char* kernel_name(int id) {
   static const char* const names[kKNumKernels] = {
       "transpose_w", "project_codes", "chunk_sort", "qhash", "count_select", "attend", "merge"};
   return (id >= 0 && id < kKNumKernels) ? names[id] : nullptr;
+}
+
+hipError_t ensure_lds_limit(const void* kernel, size_t bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, size_t> done;
+  std::lock_guard<std::mutex> lk(mu);
+  size_t& cur = done[{kernel, dev}];
+  if (cur >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+  if (e == hipSuccess) cur = bytes;
+  return e;
 }
 
 void timing_events(int id, hipEvent_t* start, hipEvent_t* stop) {

@@ -74,6 +74,12 @@ inline hipError_t launch(int id, F kernel, dim3 grid, dim3 block, unsigned lds, 
   return hipGetLastError();
 }
 
+// Raises a kernel's dynamic-LDS limit to at least `bytes` on the current
+// device.  The attribute is set at most once per (kernel, device, size), so
+// launches after the first make no runtime call besides the launch itself
+// (which keeps them capturable into a graph).
+hipError_t ensure_lds_limit(const void* kernel, size_t bytes);
+
 // Rows of the transposed, permuted projection matrix the build keeps in its
 // workspace ([rows][128] of the input dtype).
 int proj_wt_rows(int K, int L);
