@@ -60,11 +60,12 @@ int proj_wt_rows(int K, int L) {
   return (L + tps - 1) / tps * ps.nct * 16;
 }
 
-// WT[R][d] for row R = (slab, tile ct, row r = 4 g + i).  The kernel below
-// shifts the signs of a lane group's positions j = 4 ct + i into a word in
-// increasing j, so position j lands on bit P - 1 - j; that bit is bit b of
-// table tt of the group when P - 1 - j = tt K + b, i.e. table
-// slab * 4 TPG + g * TPG + tt.
+// WT[R][d] = -W[d][column] for row R = (slab, tile ct, row r = 4 g + i).  The
+// kernel below shifts the signs of a lane group's positions j = 4 ct + i into
+// a word in increasing j, so position j lands on bit P - 1 - j; that bit is
+// bit b of table tt of the group when P - 1 - j = tt K + b, i.e. table
+// slab * 4 TPG + g * TPG + tt.  W is negated so that the code bit [k.w > 0]
+// is the sign bit of the MFMA result k.(-w) (see push_code_bit).
 template <typename T>
 __global__ void transpose_w_kernel(const typename T::storage* __restrict__ W,
                                    typename T::storage* __restrict__ WT, int K, int L, int nct, int tpg,
@@ -79,16 +80,70 @@ __global__ void transpose_w_kernel(const typename T::storage* __restrict__ W,
   const int tt = jr / K, b = jr % K;
   const int t = slab * 4 * tpg + g * tpg + tt;
   const bool valid = tt < tpg && t < L;
-  WT[idx] = valid ? W[static_cast<size_t>(d) * L * K + t * K + b] : typename T::storage(0);
+  WT[idx] = valid ? negate(W[static_cast<size_t>(d) * L * K + t * K + b]) : typename T::storage(0);
 }
 
-// (s << 1) | [x > 0]: the bits of a float, read as an integer, are positive
-// exactly when the float is positive and nonzero, so the saturating 0 - bits
-// is negative exactly then (saturation keeps -0.0, read as INT_MIN,
-// positive); a funnel shift appends its sign bit to s.
-__device__ __forceinline__ uint32_t push_positive_bit(uint32_t s, float x) {
-  const int t = __builtin_elementwise_sub_sat(0, __float_as_int(x));
-  return __builtin_amdgcn_alignbit(s, static_cast<uint32_t>(t), 31u);
+// (s << 1) | [k.w > 0] from y = k.(-w), the MFMA result against the negated
+// W: one funnel shift appends the sign bit of y.  y < 0 exactly when k.w > 0.
+// A sum that is exactly zero comes out as +0: the accumulator starts at +0.0
+// and an IEEE sum holding a +0 term is +0 unless it rounds from a nonzero
+// value, so exact zeros give bit 0, as [k.w > 0] requires; a tiny sum that
+// underflows keeps its sign.
+__device__ __forceinline__ uint32_t push_code_bit(uint32_t s, float y) {
+  return __builtin_amdgcn_alignbit(s, __float_as_uint(y), 31u);
+}
+
+// Sign bits of one slab (NCT column tiles of 16 projection columns) for this
+// lane's key in each of the four key tiles: sg[a] collects the P = 4 NCT rows
+// of lane group g in row order (s = 2 s + [x > 0]).  `wrow` points at this
+// lane's W row (tile 0, row lane % 16, dims [32 g, 32 g + 32)) in LDS; rows
+// are `row` elements apart.  Software pipelined over column tiles: each of the
+// 16 MFMAs of tile ct is paired with one sign update of tile ct - 1 (two
+// accumulator sets, two W fragments), and the pairs are fenced so that the
+// VALU work issues while the matrix pipe runs; the W fragment of tile ct + 1
+// is read during tile ct.
+template <typename T, int NCT>
+__device__ __forceinline__ void slab_signs(const typename T::storage* wrow, int row, const Frag<T> (&A)[4],
+                                           uint32_t (&sg)[4]) {
+#pragma unroll
+  for (int a = 0; a < 4; ++a) sg[a] = 0u;
+  floatx4_t accA[4], accB[4];
+  Frag<T> Wa, Wb;
+  auto wtile = [&](int ct) { return wrow + min(ct, NCT - 1) * 16 * row; };
+  // MFMAs of one tile (W -> acc), paired with the signs of the previous one
+  auto half = [&](const Frag<T>& W, floatx4_t (&acc)[4], const floatx4_t (&prev)[4], bool signs) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) acc[a] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      W.mma_step(q >> 2, A[q & 3], acc[q & 3]);       // k-step q / 4 of key tile q % 4
+      if (signs) sg[q >> 2] = push_code_bit(sg[q >> 2], prev[q >> 2][q & 3]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto signs_of = [&](const floatx4_t (&acc)[4]) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sg[a] = push_code_bit(sg[a], acc[a][i]);
+  };
+  Wa.load(wtile(0), true);
+  Wb.load(wtile(1), true);
+  half(Wa, accA, accB, false);                        // tile 0
+  int ct = 1;
+#pragma unroll 1
+  for (; ct + 1 < NCT; ct += 2) {
+    Wa.load(wtile(ct + 1), true);
+    half(Wb, accB, accA, true);                       // tile ct, signs of ct - 1
+    Wb.load(wtile(ct + 2), true);
+    half(Wa, accA, accB, true);                       // tile ct + 1, signs of ct
+  }
+  if (NCT % 2 == 0) {
+    half(Wb, accB, accA, true);                       // tile NCT - 1
+    signs_of(accB);
+  } else {
+    signs_of(accA);
+  }
 }
 
 constexpr int kProjThreads = 256;              // 4 waves
@@ -157,51 +212,8 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
   for (int s = 0; s < nslab; ++s) {
     const int buf = s & 1;
     if (s + 1 < nslab) fetch(slab_of(s + 1));
-    // sign bits of the P rows of lane group g, for this lane's key in each
-    // tile, shifted in row order (s = 2 s + [x > 0]).  Software pipelined
-    // over column tiles: each of the 16 MFMAs of tile ct is paired with one
-    // sign update of tile ct - 1 (two accumulator sets, two W fragments), and
-    // the pairs are fenced so that the VALU work issues while the matrix
-    // pipe runs; the W fragment of tile ct + 1 is read during tile ct.
-    uint32_t sg[4] = {0u, 0u, 0u, 0u};
-    floatx4_t accA[4], accB[4];
-    Frag<T> Wa, Wb;
-    const S* wrow = &wt[buf][(lane & 15) * kRow + g * 32];
-    auto wtile = [&](int ct) { return wrow + min(ct, NCT - 1) * 16 * kRow; };
-    // MFMAs of one tile (W -> acc), paired with the signs of the previous one
-    auto half = [&](const Frag<T>& W, floatx4_t (&acc)[4], const floatx4_t (&prev)[4], bool signs) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) acc[a] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        W.mma_step(q >> 2, A[q & 3], acc[q & 3]);       // k-step q / 4 of key tile q % 4
-        if (signs) sg[q >> 2] = push_positive_bit(sg[q >> 2], prev[q >> 2][q & 3]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    auto signs_of = [&](const floatx4_t (&acc)[4]) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sg[a] = push_positive_bit(sg[a], acc[a][i]);
-    };
-    Wa.load(wtile(0), true);
-    Wb.load(wtile(1), true);
-    half(Wa, accA, accB, false);                        // tile 0
-    int ct = 1;
-#pragma unroll 1
-    for (; ct + 1 < NCT; ct += 2) {
-      Wa.load(wtile(ct + 1), true);
-      half(Wb, accB, accA, true);                       // tile ct, signs of ct - 1
-      Wb.load(wtile(ct + 2), true);
-      half(Wa, accA, accB, true);                       // tile ct + 1, signs of ct
-    }
-    if (NCT % 2 == 0) {
-      half(Wb, accB, accA, true);                       // tile NCT - 1
-      signs_of(accB);
-    } else {
-      signs_of(accA);
-    }
+    uint32_t sg[4];
+    slab_signs<T, NCT>(&wt[buf][(lane & 15) * kRow + (lane >> 4) * 32], kRow, A, sg);
     // codes of tables slab_of(s) * TPS + g * TPG + tt, staged per table row
     uint16_t* sb = stg[s & 1];
 #pragma unroll

@@ -24,6 +24,10 @@ struct F32 {
   static constexpr int bytes = 4;
 };
 
+// -x of a stored element (bf16: flip the sign bit).
+__device__ __forceinline__ uint16_t negate(uint16_t h) { return static_cast<uint16_t>(h ^ 0x8000u); }
+__device__ __forceinline__ float negate(float x) { return -x; }
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
