@@ -280,7 +280,7 @@ __global__ void zero_codes_kernel(uint16_t* __restrict__ codes, size_t n) {
 // in every pass and the loops need no validity tests.
 // ---------------------------------------------------------------------------
 constexpr int kSortMaxThreads = 512;
-constexpr int kSortE = 16;              // elements per thread
+constexpr int kSortE = 32;              // elements per thread
 constexpr int kDigitBits = 5;
 constexpr int kCntWords = 16;           // 32 digit counters of 16 bits per thread
 
@@ -357,7 +357,7 @@ __device__ __forceinline__ void scan_counters(uint32_t* cnt, uint32_t* wave_tot)
 // LDS: counters [16][NTHR] and the padded element buffer, 32-bit, reused at
 // the end for the bucket starts [2^K] (16-bit).
 template <int NTHR>
-__global__ __launch_bounds__(NTHR, NTHR >= 256 ? 4 : 1) void chunk_sort_kernel(
+__global__ __launch_bounds__(NTHR, NTHR >= 256 ? 3 : 1) void chunk_sort_kernel(
     const uint16_t* __restrict__ codes,   // [U][L][N]
     int N, int K, int stride_log2, int nJ,
     uint16_t* __restrict__ offsets,       // [U][L][nJ][2^K]
@@ -567,7 +567,6 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t stream) {
     case 64: return launch_chunk_sort<64>(a, stream);
     case 128: return launch_chunk_sort<128>(a, stream);
     case 256: return launch_chunk_sort<256>(a, stream);
-    case 512: return launch_chunk_sort<512>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
