@@ -272,8 +272,9 @@ __global__ void zero_codes_kernel(uint16_t* __restrict__ codes, size_t n) {
 // Digit d lives in word d & 15, half d >> 4.  One exclusive scan over the
 // word array in (w, t) order then gives every low half its start; a high
 // half also needs the count of all low-half digits, which the block total
-// carries in its low 16 bits.  A rank is bfe(start + count before it, half):
-// low halves never exceed the chunk length, so no carry reaches the high half.
+// carries in its low 16 bits.  Counters step by 4, so a rank comes out as the
+// byte offset bfe(start + count before it, half) of the element's position:
+// low halves never exceed 4 x 8192, so no carry reaches the high half.
 //
 // The buffer has E * nthr slots; slots at or past the chunk's length hold
 // code 0xffff, whose every digit is the largest, so they stay behind all keys
@@ -410,24 +411,29 @@ __global__ __launch_bounds__(NTHR, NTHR >= 256 ? 3 : 1) void chunk_sort_kernel(
     const int sh = 16 + r * kDigitBits;
 #pragma unroll
     for (int w = 0; w < kCntWords; ++w) ccol[w * NTHR] = 0u;
-    // own column only: no barrier needed before counting.  hs: 0 or 16, the
-    // digit's half of its counter word
+    // own column only: no barrier needed before counting
     uint32_t* ca[E];
-    uint32_t old[E], hs[E];
+    uint32_t old[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      const uint32_t x = e[i] >> sh;
-      hs[i] = x & 16u;
-      ca[i] = ccol + (x & 15u) * NTHR;
-      old[i] = atomicAdd(ca[i], 1u << hs[i]);
+      const uint32_t hb = __builtin_amdgcn_ubfe(e[i], sh + 4, 1);
+      ca[i] = ccol + __builtin_amdgcn_ubfe(e[i], sh, 4) * NTHR;
+      old[i] = atomicAdd(ca[i], hb * 0x3fffcu + 4u);    // 4 in the digit's half
     }
     __syncthreads();
     scan_counters<NTHR>(cnt, wave_tot);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < E; ++i) old[i] += *ca[i];
+    // old: byte offset of the element's position in the unpadded order; the
+    // padded slot adds 16 bytes per 128
+    char* bbuf = reinterpret_cast<char*>(buf);
 #pragma unroll
-    for (int i = 0; i < E; ++i) buf[slot(static_cast<int>(__builtin_amdgcn_ubfe(old[i], hs[i], 16)))] = e[i];
+    for (int i = 0; i < E; ++i) {
+      const uint32_t hs = e[i] >> (sh + 4 - 4) & 16u;     // the digit's half: 0 or 16
+      const uint32_t pos4 = __builtin_amdgcn_ubfe(old[i], hs, 16);
+      *reinterpret_cast<uint32_t*>(bbuf + pos4 + ((pos4 >> 7) << 4)) = e[i];
+    }
     __syncthreads();
     load_run(buf, p0, e);                       // two barriers pass before buf is written again
   }
