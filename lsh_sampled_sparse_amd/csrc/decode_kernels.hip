@@ -242,17 +242,30 @@ __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
   __syncthreads();
 
   // walk the concatenated segments: entry v of segment l is
-  // indices[u][l][seg_start[l] + v - seg_v[l]], the key's offset in this chunk
+  // indices[u][l][seg_start[l] + v - seg_v[l]], the key's offset in this chunk.
+  // Every wave takes a contiguous range of entries, so its 64 lanes read 64
+  // consecutive entries and cross at most one segment boundary per step.
   const int total = seg_v[L];
+  constexpr int kWaves = kCountThreads / 64;
+  const int per = ((total + kWaves - 1) / kWaves + 63) & ~63;
+  const int wstart = wave * per, wend = min(total, wstart + per);
   const uint16_t* ib = indices + static_cast<size_t>(u) * L * N;
-  int l = 0;
-  for (int v0 = tid; v0 < total; v0 += kCountThreads * kCountUnroll) {
+  int l = 0;                                      // last segment starting at or before wstart
+  {
+    int lo = 0, hi = L - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seg_v[mid] <= wstart) lo = mid; else hi = mid - 1;
+    }
+    l = lo;
+  }
+  for (int v0 = wstart + lane; v0 < wend; v0 += 64 * kCountUnroll) {
     int loc[kCountUnroll];
 #pragma unroll
     for (int k = 0; k < kCountUnroll; ++k) {
-      const int v = v0 + k * kCountThreads;
+      const int v = v0 + 64 * k;
       loc[k] = -1;
-      if (v < total) {
+      if (v < wend) {
         while (v >= seg_v[l + 1]) ++l;
         loc[k] = ib[static_cast<size_t>(l) * N + seg_start[l] + (v - seg_v[l])];
       }
