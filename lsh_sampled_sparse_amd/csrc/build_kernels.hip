@@ -438,16 +438,24 @@ __global__ __launch_bounds__(NTHR, NTHR >= 256 ? 3 : 1) void chunk_sort_kernel(
     load_run(buf, p0, e);                       // two barriers pass before buf is written again
   }
 
-  // the sorted region: thread t writes its E positions
+  // the sorted region.  After a radix pass the chunk sits in LDS in position
+  // order, so 8 consecutive entries go to each lane and a wave writes 1 KB
+  // of contiguous index array per store, as streaming stores: the tables are
+  // read by a later decode, not by anything that runs while they would still
+  // be in the cache.  (K = 0 sorts nothing: thread t writes its own run.)
   uint16_t* out = indices + table * N + cbeg;
-  if (full && vec) {
-    uint4* o4 = reinterpret_cast<uint4*>(out + p0);
-#pragma unroll
-    for (int q = 0; q < E / 8; ++q) {
-      uint32_t w[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) w[k] = (e[8 * q + 2 * k] & 0xffffu) | (e[8 * q + 2 * k + 1] << 16);
-      o4[q] = make_uint4(w[0], w[1], w[2], w[3]);
+  if (passes > 0) {
+    for (int c = tid; c * 8 < clen; c += NTHR) {
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(buf + slot(8 * c));
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(buf + slot(8 * c) + 4);
+      if (vec && 8 * c + 8 <= clen) {
+        const u32x4_t v = {__builtin_amdgcn_perm(lo[1], lo[0], 0x05040100u), __builtin_amdgcn_perm(lo[3], lo[2], 0x05040100u),
+                           __builtin_amdgcn_perm(hi[1], hi[0], 0x05040100u), __builtin_amdgcn_perm(hi[3], hi[2], 0x05040100u)};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(out + 8 * c));
+      } else {
+        const uint32_t w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        for (int k = 0; k < 8 && 8 * c + k < clen; ++k) out[8 * c + k] = static_cast<uint16_t>(w[k]);
+      }
     }
   } else {
 #pragma unroll
