@@ -355,10 +355,10 @@ __device__ __forceinline__ void scan_counters(uint32_t* cnt, uint32_t* wave_tot)
 }
 
 // One workgroup of NTHR = max(64, chunk / E) threads per (table, chunk);
-// LDS: counters [16][NTHR] and the padded element buffer, 32-bit, reused at
-// the end for the bucket starts [2^K] (16-bit).
+// LDS: counters [16][NTHR] and the padded element buffer, 32-bit, in the same
+// region, reused at the end for the bucket starts [2^K] (16-bit).
 template <int NTHR>
-__global__ __launch_bounds__(NTHR, NTHR >= 256 ? 3 : 1) void chunk_sort_kernel(
+__global__ __launch_bounds__(NTHR, NTHR >= 256 ? 4 : 1) void chunk_sort_kernel(
     const uint16_t* __restrict__ codes,   // [U][L][N]
     int N, int K, int stride_log2, int nJ,
     uint16_t* __restrict__ offsets,       // [U][L][nJ][2^K]
@@ -367,8 +367,11 @@ __global__ __launch_bounds__(NTHR, NTHR >= 256 ? 3 : 1) void chunk_sort_kernel(
   extern __shared__ __attribute__((aligned(16))) uint32_t smem32[];
   __shared__ uint32_t wave_tot[NTHR / 64];
   constexpr int nthr = NTHR;
+  // the counters and the element buffer share LDS: the elements are in
+  // registers from the run load to the scatter, and the counters are dead
+  // once every thread has read its ranks (barriers on both sides)
   uint32_t* cnt = smem32;                       // [16][NTHR]
-  uint32_t* buf = smem32 + kCntWords * NTHR;    // slot(position): code << 16 | key
+  uint32_t* buf = smem32;                       // slot(position): code << 16 | key
   const int j = blockIdx.x;
   const size_t table = blockIdx.y;              // u * L + l
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -409,22 +412,28 @@ __global__ __launch_bounds__(NTHR, NTHR >= 256 ? 3 : 1) void chunk_sort_kernel(
   const int passes = (K + kDigitBits - 1) / kDigitBits;
   for (int r = 0; r < passes; ++r) {
     const int sh = 16 + r * kDigitBits;
+    if (r > 0) __syncthreads();                 // every run load of buf is done
 #pragma unroll
     for (int w = 0; w < kCntWords; ++w) ccol[w * NTHR] = 0u;
     // own column only: no barrier needed before counting
-    uint32_t* ca[E];
+    // the counter word of an element's digit (recomputed where needed, to
+    // keep registers for occupancy)
+    auto cword = [&](uint32_t x) { return ccol + __builtin_amdgcn_ubfe(x, sh, 4) * NTHR; };
     uint32_t old[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       const uint32_t hb = __builtin_amdgcn_ubfe(e[i], sh + 4, 1);
-      ca[i] = ccol + __builtin_amdgcn_ubfe(e[i], sh, 4) * NTHR;
-      old[i] = atomicAdd(ca[i], hb * 0x3fffcu + 4u);    // 4 in the digit's half
+      old[i] = atomicAdd(cword(e[i]), hb * 0x3fffcu + 4u);    // 4 in the digit's half
     }
     __syncthreads();
     scan_counters<NTHR>(cnt, wave_tot);
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < E; ++i) old[i] += *ca[i];
+    for (int i = 0; i < E; ++i) {
+      asm volatile("" : "+v"(e[i]));   // recompute the address rather than keep it live
+      old[i] += *cword(e[i]);
+    }
+    __syncthreads();                            // every rank is read: buf may overwrite the counters
     // old: byte offset of the element's position in the unpadded order; the
     // padded slot adds 16 bytes per 128
     char* bbuf = reinterpret_cast<char*>(buf);
@@ -512,7 +521,7 @@ static int sort_threads(int stride_log2) { return max(64, (1 << stride_log2) / k
 size_t chunk_sort_lds_bytes(int stride_log2, int K) {
   const size_t nthr = static_cast<size_t>(sort_threads(stride_log2));
   const size_t elems = nthr * kSortE;
-  return max((kCntWords * nthr + elems + (elems >> 3)) * 4, size_t(2) << K);
+  return max(max(kCntWords * nthr, elems + (elems >> 3)) * 4, size_t(2) << K);
 }
 
 template <int NTHR>
