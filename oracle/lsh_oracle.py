@@ -301,6 +301,43 @@ def decode_head(q, keys, values, W, offsets, indices, K, L, T, scale, qcodes=Non
             "nsel": int(mask.sum()), "u": u, "out": out, "lse": lse}
 
 
+def exact_set(N, n_sink, n_window):
+    """The keys a hybrid decode attends exactly: the first n_sink keys
+    (attention sinks) and the last n_window keys (the recent window).
+
+    MagicPIG pairs dense attention with sampled sparse attention ("How
+    infini-ai-lab/magicpig works", overview: CPU sparse attention complementing
+    GPU attention; sourcepulse summary, "How It Works"); the pages do not say
+    which keys the dense part takes.  The reading here is a static set of
+    sinks plus a recent window, the set MAC-Attention recomputes exactly and
+    merges by log-sum-exp ("MAC-Attention" README, "How It Works", front
+    sinks).  Returns bool [N]."""
+    E = np.zeros(N, dtype=bool)
+    E[:max(0, min(N, n_sink))] = True
+    if n_window > 0:
+        E[max(0, N - n_window):] = True
+    return E
+
+
+def hybrid_decode_head(q, keys, values, W, offsets, indices, K, L, T, scale, n_sink, n_window, qcodes=None):
+    """Hybrid decode of one query head: exact softmax attention over the
+    static set E = exact_set(N, n_sink, n_window), the 1/u-weighted estimate
+    over the selected keys outside E, and the log-sum-exp merge of the two.
+
+    Returns dict: as decode_head, with mask = selected keys outside E,
+    nsel = |mask|, exact = E, and out / lse of the merge.
+    """
+    r = decode_head(q, keys, values, W, offsets, indices, K, L, T, scale, qcodes=qcodes)
+    N = np.asarray(keys).shape[0]
+    E = exact_set(N, n_sink, n_window)
+    sampled = r["mask"] & ~E
+    part_s = weighted_softmax_attention(q, keys, values, sampled, r["u"], scale)
+    part_e = weighted_softmax_attention(q, keys, values, E, np.ones(N), scale)
+    out, lse = lse_merge([part_s, part_e])
+    r.update({"mask": sampled, "nsel": int(sampled.sum()), "exact": E, "out": out, "lse": lse})
+    return r
+
+
 def decode(q, keys, values, W, tables, K, L, T, scale, heads=None):
     """Decode over a batch: q [B, Hq, d], keys/values [B, Hkv, N, d].
 
