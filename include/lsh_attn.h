@@ -156,6 +156,40 @@ lsh_status lsh_decode_attention(const void* q, const void* keys,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/*
+ * Hybrid decode: exact attention over a static set of keys, the LSH estimate
+ * over the rest.  MagicPIG pairs dense attention with sampled sparse
+ * attention ("How infini-ai-lab/magicpig works", overview; sourcepulse
+ * summary, "How It Works"); the static set taken here is the first n_sink
+ * keys (attention sinks) and the last n_window keys (the recent window), the
+ * keys MAC-Attention recomputes exactly and merges by log-sum-exp
+ * ("MAC-Attention" README, "How It Works").
+ *
+ *   E    = { n : n < n_sink } U { n : n >= N - n_window }
+ *   S'   = S \ E                (selected keys outside the exact set)
+ *   out  = sum_{n in E} e^{s q.k_n} v_n + sum_{n in S'} e^{l(n)} v_n,
+ *          divided by the same sum without v_n;  lse = ln of that sum
+ *          (l(n) as in lsh_decode_attention; E and S' empty: out = 0,
+ *          lse = -inf)
+ *   nsel = |S'|;  counts (optional) are the collision counts of every key.
+ *
+ * Arguments are those of lsh_decode_attention plus n_sink, n_window >= 0
+ * (LSH_ERR_INVALID_ARG if negative; values past N are clamped).  The exact
+ * part runs in one workgroup per query head, for sets of up to a few
+ * thousand keys.  n_sink = n_window = 0 is lsh_decode_attention.  Same
+ * workspace size.
+ */
+lsh_status lsh_decode_attention_hybrid(const void* q, const void* keys,
+                                       const void* values, const void* W,
+                                       const uint16_t* indices, const uint16_t* offsets,
+                                       int B, int Hq, int Hkv, int N, int d, int K,
+                                       int L, int T, int stride, float sm_scale,
+                                       int dtype, int n_sink, int n_window,
+                                       float* out, float* lse, int32_t* nsel,
+                                       uint16_t* q_codes, uint8_t* counts,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
 /* ------------------------------------------------------------------------
  * Kernel timing (a profiling aid; process-wide, one window at a time)
  *

@@ -29,6 +29,7 @@ EXPORTS = (
     "lsh_build_tables",
     "lsh_decode_workspace_size",
     "lsh_decode_attention",
+    "lsh_decode_attention_hybrid",
     "lsh_kernel_count",
     "lsh_kernel_name",
     "lsh_timing_begin",
@@ -64,6 +65,9 @@ def lib():
         L.lsh_decode_attention.restype = _i
         L.lsh_decode_attention.argtypes = ([_p] * 6 + [_i] * 9 + [ctypes.c_float, _i]
                                            + [_p] * 6 + [_sz, _p])
+        L.lsh_decode_attention_hybrid.restype = _i
+        L.lsh_decode_attention_hybrid.argtypes = ([_p] * 6 + [_i] * 9 + [ctypes.c_float, _i, _i, _i]
+                                                  + [_p] * 6 + [_sz, _p])
         L.lsh_kernel_count.restype = _i
         L.lsh_kernel_count.argtypes = []
         L.lsh_kernel_name.restype = ctypes.c_char_p
@@ -157,6 +161,22 @@ def lsh_decode_attention(q, keys, values, W, indices, offsets, K, L, T, stride, 
         _ptr(workspace), workspace.numel(), _stream(keys.device)))
 
 
+def lsh_decode_attention_hybrid(q, keys, values, W, indices, offsets, K, L, T, stride, sm_scale, n_sink,
+                                n_window, out, lse=None, nsel=None, q_codes=None, counts=None, workspace=None):
+    """Marshal tensors to ``lsh_decode_attention_hybrid``; outputs are filled in place."""
+    B, Hq, d = q.shape
+    _, Hkv, N, _ = keys.shape
+    dt = _dtype_code(keys.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(1, lsh_decode_workspace_size(B, Hq, Hkv, N, d, K, L, stride)),
+                                dtype=torch.uint8, device=keys.device)
+    _check(lib().lsh_decode_attention_hybrid(
+        _ptr(q), _ptr(keys), _ptr(values), _ptr(W), _ptr(indices), _ptr(offsets),
+        B, Hq, Hkv, N, d, K, L, T, stride, ctypes.c_float(sm_scale), dt, int(n_sink), int(n_window),
+        _ptr(out), _ptr(lse), _ptr(nsel), _ptr(q_codes), _ptr(counts),
+        _ptr(workspace), workspace.numel(), _stream(keys.device)))
+
+
 def lsh_kernel_count() -> int:
     return lib().lsh_kernel_count()
 
@@ -218,9 +238,11 @@ def build_tables(keys, W, K, L, stride=None, return_codes=False):
 
 
 def decode_attention(q, keys, values, W, tables, K, L, T, sm_scale=None, return_codes=False,
-                     return_counts=False, workspace=None):
+                     return_counts=False, workspace=None, n_sink=0, n_window=0):
     """One decode step.  Returns dict: out [B,Hq,d] fp32, lse [B,Hq], nsel [B,Hq],
-    and q_codes [B,Hq,L] / counts [B,Hq,N] (uint8) when requested."""
+    and q_codes [B,Hq,L] / counts [B,Hq,N] (uint8) when requested.  With
+    n_sink / n_window > 0 it is the hybrid decode: the first n_sink and the
+    last n_window keys are attended exactly and merged with the estimate."""
     for name, t in (("q", q), ("keys", keys), ("values", values)):
         _require(t, name, keys.dtype)
     B, Hq, d = q.shape
@@ -235,8 +257,13 @@ def decode_attention(q, keys, values, W, tables, K, L, T, sm_scale=None, return_
     nsel = torch.empty(B, Hq, dtype=torch.int32, device=dev)
     qc = torch.empty(B, Hq, L, dtype=torch.int16, device=dev) if return_codes else None
     cnt = torch.empty(B, Hq, N, dtype=torch.uint8, device=dev) if return_counts else None
-    lsh_decode_attention(q, keys, values, W, tables["indices"], tables["offsets"], K, L, T,
-                         tables["stride"], sm_scale, out, lse, nsel, qc, cnt, workspace)
+    if n_sink or n_window:
+        lsh_decode_attention_hybrid(q, keys, values, W, tables["indices"], tables["offsets"], K, L, T,
+                                    tables["stride"], sm_scale, n_sink, n_window, out, lse, nsel, qc, cnt,
+                                    workspace)
+    else:
+        lsh_decode_attention(q, keys, values, W, tables["indices"], tables["offsets"], K, L, T,
+                             tables["stride"], sm_scale, out, lse, nsel, qc, cnt, workspace)
     res = {"out": out, "lse": lse, "nsel": nsel}
     if return_codes:
         res["q_codes"] = qc

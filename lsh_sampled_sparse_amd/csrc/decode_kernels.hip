@@ -196,7 +196,8 @@ __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
     int Hq, int Hkv, int N, int K, int L, int T, int stride_log2, int nJ,
     uint32_t* __restrict__ bitmask,        // [BH][Nw]
     int32_t* __restrict__ chunk_nsel,      // [BH][nJ]
-    uint8_t* __restrict__ counts) {        // optional [BH][N]
+    uint8_t* __restrict__ counts,          // optional [BH][N]
+    int exact_head, int exact_tail) {      // keys attended exactly, never sampled
   extern __shared__ __attribute__((aligned(16))) uint32_t cnt[];   // one byte per key of the chunk
   __shared__ int seg_start[256];
   __shared__ int seg_v[257];
@@ -288,7 +289,9 @@ __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int key = w * 32 + j * 4 + k;
-        if (key < clen && static_cast<int>((c4 >> (8 * k)) & 0xffu) >= T) m |= 1u << (j * 4 + k);
+        const int n = cbeg + key;
+        const bool exact = n < exact_head || n >= N - exact_tail;
+        if (key < clen && !exact && static_cast<int>((c4 >> (8 * k)) & 0xffu) >= T) m |= 1u << (j * 4 + k);
       }
     }
     bitmask[static_cast<size_t>(bh) * Nw + (cbeg >> 5) + w] = m;
@@ -571,17 +574,32 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
 // ---------------------------------------------------------------------------
 // merge: one workgroup (4 waves) per query head.  Wave w folds the splits
 // s = w, w + 4, ... into a running (max, sum, acc) with each lane owning two
-// dims; the four wave states are combined through LDS.
+// dims; the four wave states are combined through LDS.  With an exact set
+// (the hybrid decode: keys [0, exact_head) and [N - exact_tail, N), which
+// count_select left out of the selection) the workgroup also computes the
+// plain softmax partial of those keys, (max, sum, acc) with u = 1, and merges
+// it last.  That part is one workgroup per head: it is meant for sinks plus a
+// recent window, a few thousand keys at most.
 // ---------------------------------------------------------------------------
 constexpr int kMergeThreads = 256;
+constexpr int kExactBatch = 4 * kMergeThreads;   // exact-set weights staged per batch
 
+template <typename T>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ partials,
                                                               const int32_t* __restrict__ chunk_nsel,
                                                               int nsplit, int nJ, float* __restrict__ out,
-                                                              float* __restrict__ lse, int32_t* __restrict__ nsel) {
+                                                              float* __restrict__ lse, int32_t* __restrict__ nsel,
+                                                              const typename T::storage* __restrict__ q,
+                                                              const typename T::storage* __restrict__ keys,
+                                                              const typename T::storage* __restrict__ values,
+                                                              int Hq, int Hkv, int N, float scale,
+                                                              int exact_head, int exact_tail) {
   __shared__ float wm[4], wl[4];
   __shared__ float wacc[4][kHeadDim];
   __shared__ int wn[4];
+  __shared__ float qs[kHeadDim];
+  __shared__ float wexp[kExactBatch];
+  __shared__ float wx[4];                          // per-wave max / sum of the exact part
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* P = partials + static_cast<size_t>(bh) * nsplit * kPartialStride;
   // the overall max first, so that every split's weight exp(m_s - M) is known
@@ -617,23 +635,82 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   wacc[wave][2 * lane] = a0;
   wacc[wave][2 * lane + 1] = a1;
   __syncthreads();
+
+  // exact part over the keys of the exact set (unit b * Hkv + h / G)
+  const int ne = exact_head + exact_tail;
+  float me = -INFINITY, le = 0.f, ae = 0.f;   // ae: dim tid of the acc (tid < 128)
+  if (ne > 0) {
+    using S = typename T::storage;
+    const int b = bh / Hq, h = bh % Hq;
+    const int u = b * Hkv + h / (Hq / Hkv);
+    const S* kb = keys + static_cast<size_t>(u) * N * kHeadDim;
+    const S* vb = values + static_cast<size_t>(u) * N * kHeadDim;
+    auto key_of = [&](int i) { return i < exact_head ? i : N - exact_tail + (i - exact_head); };
+    auto elem = [&](const S* p, int i) {
+      if constexpr (sizeof(S) == 2) return bf16_to_f32(p[i]); else return static_cast<float>(p[i]);
+    };
+    auto logit = [&](int n) {
+      const S* k = kb + static_cast<size_t>(n) * kHeadDim;
+      float x = 0.f;
+      for (int i = 0; i < kHeadDim; ++i) x = fmaf(qs[i], elem(k, i), x);
+      return scale * x;
+    };
+    if (tid < kHeadDim) qs[tid] = elem(q + static_cast<size_t>(bh) * kHeadDim, tid);
+    __syncthreads();
+    float mt = -INFINITY;
+    for (int i = tid; i < ne; i += kMergeThreads) mt = fmaxf(mt, logit(key_of(i)));
+    mt = wave_max(mt);
+    if (lane == 0) wx[wave] = mt;
+    __syncthreads();
+    me = fmaxf(fmaxf(wx[0], wx[1]), fmaxf(wx[2], wx[3]));
+    float ls = 0.f;
+    for (int b0 = 0; b0 < ne; b0 += kExactBatch) {
+      __syncthreads();
+      for (int k = tid; k < kExactBatch; k += kMergeThreads) {
+        const int i = b0 + k;
+        const float w = i < ne ? __expf(logit(key_of(i)) - me) : 0.f;
+        wexp[k] = w;
+        ls += w;
+      }
+      __syncthreads();
+      if (tid < kHeadDim) {
+        const int nb = min(kExactBatch, ne - b0);
+        for (int k = 0; k < nb; ++k)
+          ae = fmaf(wexp[k], elem(vb + static_cast<size_t>(key_of(b0 + k)) * kHeadDim, tid), ae);
+      }
+    }
+    ls = wave_sum(ls);
+    __syncthreads();                                 // every wave has read the max from wx
+    if (lane == 0) wx[wave] = ls;
+    __syncthreads();
+    le = wx[0] + wx[1] + wx[2] + wx[3];
+  }
+
   if (tid < kHeadDim) {
-    float M = -INFINITY;
+    float Ms = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w]);
+    for (int w = 0; w < 4; ++w) Ms = fmaxf(Ms, wm[w]);
     float A = 0.f, Lm = 0.f;
-    if (M != -INFINITY) {
+    if (Ms != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         if (wm[w] == -INFINITY) continue;
-        const float f = __expf(wm[w] - M);
+        const float f = __expf(wm[w] - Ms);
         A = fmaf(wacc[w][tid], f, A);
         Lm = fmaf(wl[w], f, Lm);
       }
     }
-    out[static_cast<size_t>(bh) * kHeadDim + tid] = (M == -INFINITY) ? 0.f : A / Lm;
+    // the sampled state (A, Lm at Ms) and the exact one (ae, le at me)
+    const float Mt = fmaxf(Ms, me);
+    if (Mt != -INFINITY) {
+      const float fs = Ms == -INFINITY ? 0.f : __expf(Ms - Mt);
+      const float fe = me == -INFINITY ? 0.f : __expf(me - Mt);
+      A = A * fs + ae * fe;
+      Lm = Lm * fs + le * fe;
+    }
+    out[static_cast<size_t>(bh) * kHeadDim + tid] = (Mt == -INFINITY) ? 0.f : A / Lm;
     if (tid == 0) {
-      if (lse) lse[bh] = (M == -INFINITY) ? -INFINITY : M + logf(Lm);
+      if (lse) lse[bh] = (Mt == -INFINITY) ? -INFINITY : Mt + logf(Lm);
       if (nsel) nsel[bh] = wn[0] + wn[1] + wn[2] + wn[3];
     }
   }
@@ -669,7 +746,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   e = launch(kKCountSelect, count_select_kernel, dim3(a.nJ, BH), dim3(kCountThreads),
              static_cast<unsigned>(lds), stream, static_cast<const uint16_t*>(a.qcodes),
              a.indices, a.offsets, a.Hq, a.Hkv, a.N, a.K, a.L, a.T, a.stride_log2, a.nJ, a.bitmask,
-             a.chunk_nsel, a.counts);
+             a.chunk_nsel, a.counts, a.exact_head, a.exact_tail);
   if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;
   if constexpr (sizeof(S) == 2)
@@ -681,9 +758,10 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   else
     e = launch_attend<T, 16>(a, stream);
   if (e != hipSuccess) return e;
-  return launch(kKMerge, merge_kernel, dim3(BH), dim3(kMergeThreads), 0, stream,
+  return launch(kKMerge, merge_kernel<T>, dim3(BH), dim3(kMergeThreads), 0, stream,
                 static_cast<const float*>(a.partials), static_cast<const int32_t*>(a.chunk_nsel), a.nsplit,
-                a.nJ, a.out, a.lse, a.nsel);
+                a.nJ, a.out, a.lse, a.nsel, static_cast<const S*>(a.q), static_cast<const S*>(a.keys),
+                static_cast<const S*>(a.values), a.Hq, a.Hkv, a.N, a.scale, a.exact_head, a.exact_tail);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

@@ -3,6 +3,7 @@
 // every operation are in include/lsh_attn.h.
 #include <stdint.h>
 
+#include <algorithm>
 #include <cmath>
 #include <map>
 #include <mutex>
@@ -250,15 +251,17 @@ size_t lsh_decode_workspace_size(int B, int Hq, int Hkv, int N, int d, int K, in
   return decode_layout(B, Hq, Hkv, N, L, g).total;
 }
 
-lsh_status lsh_decode_attention(const void* q, const void* keys, const void* values, const void* W,
-                                const uint16_t* indices, const uint16_t* offsets, int B, int Hq, int Hkv, int N,
-                                int d, int K, int L, int T, int stride, float sm_scale, int dtype, float* out,
-                                float* lse, int32_t* nsel, uint16_t* q_codes, uint8_t* counts, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+lsh_status lsh_decode_attention_hybrid(const void* q, const void* keys, const void* values, const void* W,
+                                       const uint16_t* indices, const uint16_t* offsets, int B, int Hq, int Hkv,
+                                       int N, int d, int K, int L, int T, int stride, float sm_scale, int dtype,
+                                       int n_sink, int n_window, float* out, float* lse, int32_t* nsel,
+                                       uint16_t* q_codes, uint8_t* counts, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
   Geometry g;
   lsh_status st = check_common(B, Hkv, N, d, K, L, stride, dtype, &g);
   if (st != LSH_OK) return st;
   if (Hq < 1 || Hq % Hkv != 0 || T < 1 || T > L || !std::isfinite(sm_scale)) return LSH_ERR_INVALID_ARG;
+  if (n_sink < 0 || n_window < 0) return LSH_ERR_INVALID_ARG;
   if (Hq / Hkv > 16) return LSH_ERR_UNSUPPORTED;
   if (!q || !keys || !values || !indices || !offsets || !out || !workspace || (K > 0 && !W))
     return LSH_ERR_INVALID_ARG;
@@ -294,7 +297,19 @@ lsh_status lsh_decode_attention(const void* q, const void* keys, const void* val
   a.nsplit = w.nsplit;
   a.scale = sm_scale;
   a.dtype = dtype;
+  a.exact_head = std::min(n_sink, N);
+  a.exact_tail = std::min(n_window, N - a.exact_head);
   return hip_status(lsh::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+lsh_status lsh_decode_attention(const void* q, const void* keys, const void* values, const void* W,
+                                const uint16_t* indices, const uint16_t* offsets, int B, int Hq, int Hkv, int N,
+                                int d, int K, int L, int T, int stride, float sm_scale, int dtype, float* out,
+                                float* lse, int32_t* nsel, uint16_t* q_codes, uint8_t* counts, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return lsh_decode_attention_hybrid(q, keys, values, W, indices, offsets, B, Hq, Hkv, N, d, K, L, T, stride,
+                                     sm_scale, dtype, 0, 0, out, lse, nsel, q_codes, counts, workspace,
+                                     workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -41,6 +41,7 @@ struct DecodeArgs {
   int split_len, nsplit;
   float scale;
   int dtype;
+  int exact_head, exact_tail;  // exact set: keys [0, exact_head) and [N - exact_tail, N), disjoint
 };
 
 constexpr int kLnuTable = 1024;   // ln-u correction table intervals over theta in [0, pi]

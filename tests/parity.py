@@ -113,9 +113,13 @@ def check_tables(gpu_off, gpu_idx, gpu_codes, ref, K, stride):
     return int((~same).sum())
 
 
-def check_head(gpu, ref, q_band, key_codes_gpu, key_codes_ref, K, L, T):
+def check_head(gpu, ref, q_band, key_codes_gpu, key_codes_ref, K, L, T, exact=None):
     """Compare one query head.  gpu: dict of numpy (q_codes [L], counts [N] or
-    None, out [d], lse, nsel).  ref: dict from ``O.decode_head``."""
+    None, out [d], lse, nsel).  ref: dict from ``O.decode_head``, or from
+    ``O.hybrid_decode_head`` with ``exact`` its exact set (bool [N]): those
+    keys keep their collision counts but are never part of the selection."""
+    N = len(ref["counts"])
+    excl = np.zeros(N, bool) if exact is None else np.asarray(exact, bool)
     qflips = compare_codes(gpu["q_codes"][:, None], ref["qcodes"][:, None], q_band, K, L)
     bad_q = u16(gpu["q_codes"]) != ref["qcodes"]                        # tables whose probe differs
     key_bad = (u16(key_codes_gpu) != key_codes_ref)                     # [L, N]
@@ -127,13 +131,13 @@ def check_head(gpu, ref, q_band, key_codes_gpu, key_codes_ref, K, L, T):
         c = np.asarray(gpu["counts"]).astype(np.int64)
         np.testing.assert_array_equal(c[exact_keys], ref["counts"][exact_keys])
         assert np.all(np.abs(c - ref["counts"]) <= n_aff)
-        np.testing.assert_array_equal((c >= T)[exact_keys], ref["mask"][exact_keys])
+        np.testing.assert_array_equal(((c >= T) & ~excl)[exact_keys], ref["mask"][exact_keys])
     if exact_keys.all():
         assert int(gpu["nsel"]) == ref["nsel"]
     else:
         assert abs(int(gpu["nsel"]) - ref["nsel"]) <= int((~exact_keys).sum())
     out = np.asarray(gpu["out"], np.float64)
-    if ref["nsel"] == 0:
+    if ref["nsel"] == 0 and not excl.any():
         assert int(gpu["nsel"]) == 0 or not exact_keys.all()
         if int(gpu["nsel"]) == 0:
             assert np.all(out == 0) and gpu["lse"] == -np.inf

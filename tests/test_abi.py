@@ -128,6 +128,29 @@ def test_decode_rejects(kw, status):
     assert _decode(**kw) == status
 
 
+def _hybrid(n_sink, n_window, **kw):
+    a = dict(q=1, keys=1, values=1, W=1, indices=1, offsets=1, B=1, Hq=4, Hkv=1, N=4096, d=128, K=8,
+             L=32, T=2, stride=4096, scale=0.088, dtype=1, out=1, ws=1, ws_bytes=1 << 40)
+    a.update(kw)
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    return lsh.lib().lsh_decode_attention_hybrid(
+        p(a["q"]), p(a["keys"]), p(a["values"]), p(a["W"]), p(a["indices"]), p(a["offsets"]),
+        a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["K"], a["L"], a["T"], a["stride"],
+        ctypes.c_float(a["scale"]), a["dtype"], n_sink, n_window, p(a["out"]), None, None, None, None,
+        p(a["ws"]), a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("n_sink,n_window,kw,status", [
+    (-1, 0, {}, lsh.LSH_ERR_INVALID_ARG),
+    (0, -5, {}, lsh.LSH_ERR_INVALID_ARG),
+    (4, 64, dict(q=None), lsh.LSH_ERR_INVALID_ARG),
+    (4, 64, dict(T=0), lsh.LSH_ERR_INVALID_ARG),
+    (4, 64, dict(ws_bytes=100), lsh.LSH_ERR_WORKSPACE),
+])
+def test_hybrid_rejects(n_sink, n_window, kw, status):
+    assert _hybrid(n_sink, n_window, **kw) == status
+
+
 def test_binding_raises_without_gpu_work():
     with pytest.raises(lsh.LshError) as e:
         lsh.lib()  # loads fine

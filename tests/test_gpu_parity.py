@@ -31,8 +31,9 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_gpu(cfg, data, stride=None, step=0):
-    """Build + one decode step on the GPU; returns numpy copies."""
+def run_gpu(cfg, data, stride=None, step=0, n_sink=0, n_window=0):
+    """Build + one decode step on the GPU (the hybrid decode when n_sink or
+    n_window is set)."""
     lsh = _lsh()
     dev = torch.device("cuda:0")
     keys = data["keys"].to(dev)
@@ -43,7 +44,7 @@ def run_gpu(cfg, data, stride=None, step=0):
         W = torch.empty(cfg.d, 0, dtype=keys.dtype, device=dev)
     tb = lsh.build_tables(keys, W, cfg.K, cfg.L, stride=stride, return_codes=True)
     r = lsh.decode_attention(q, keys, vals, W, tb, cfg.K, cfg.L, cfg.T, sm_scale=cfg.scale,
-                             return_codes=True, return_counts=True)
+                             return_codes=True, return_counts=True, n_sink=n_sink, n_window=n_window)
     torch.cuda.synchronize()
     return tb, r
 
@@ -52,9 +53,10 @@ def to_np(t):
     return t.detach().cpu().numpy()
 
 
-def check_case(cfg, data, units=None, heads_per_unit=None, stride=None, step=0):
+def check_case(cfg, data, units=None, heads_per_unit=None, stride=None, step=0, n_sink=0, n_window=0):
     """Full comparison on the listed units (default: all)."""
-    tb, r = run_gpu(cfg, data, stride=stride, step=step)
+    hybrid = bool(n_sink or n_window)
+    tb, r = run_gpu(cfg, data, stride=stride, step=step, n_sink=n_sink, n_window=n_window)
     stride = tb["stride"]
     W = data["W"].float().cpu().numpy() if cfg.K > 0 else np.zeros((cfg.d, 0))
     q = data["q"][step].float().cpu().numpy()
@@ -77,20 +79,25 @@ def check_case(cfg, data, units=None, heads_per_unit=None, stride=None, step=0):
         if heads_per_unit is not None:
             hs = hs[:heads_per_unit]
         for h in hs:
-            rr = O.decode_head(q[b, h], ku, vu, W, ref["offsets"], ref["indices"],
-                               cfg.K, cfg.L, cfg.T, cfg.scale)
+            if hybrid:
+                rr = O.hybrid_decode_head(q[b, h], ku, vu, W, ref["offsets"], ref["indices"],
+                                          cfg.K, cfg.L, cfg.T, cfg.scale, n_sink, n_window)
+            else:
+                rr = O.decode_head(q[b, h], ku, vu, W, ref["offsets"], ref["indices"],
+                                   cfg.K, cfg.L, cfg.T, cfg.scale)
             qb = PAR.band_mask(q[b, h][None], W) if cfg.K > 0 else np.zeros((1, 0), bool)
             gh = {"q_codes": to_np(r["q_codes"][b, h]), "counts": to_np(r["counts"][b, h]),
                   "out": to_np(r["out"][b, h]), "lse": float(r["lse"][b, h]), "nsel": int(r["nsel"][b, h])}
-            res = PAR.check_head(gh, rr, qb, gcodes, ref["codes"], cfg.K, cfg.L, cfg.T)
+            res = PAR.check_head(gh, rr, qb, gcodes, ref["codes"], cfg.K, cfg.L, cfg.T,
+                                 exact=rr.get("exact"))
             flips += res["qflips"]
             total_bits += cfg.L * cfg.K
             rels.append(res["rel"])
-            if rr["nsel"] > 0:
+            if rr["nsel"] > 0 or hybrid:
                 est.append(PAR.estimate_error(gh["out"], O.exact_attention(q[b, h], ku, vu, cfg.scale)))
     if total_bits:
         assert flips <= max(1.0, PAR.FLIP_FRACTION_MAX * total_bits), (flips, total_bits)
-    say(f"[{cfg.name}] units={len(units)} flips={flips}/{total_bits} bad_tables={bad_tables} "
+    say(f"[{cfg.name}{f' sink={n_sink} window={n_window}' if hybrid else ''}] units={len(units)} flips={flips}/{total_bits} bad_tables={bad_tables} "
         f"max_rel={max(rels) if rels else 0:.2e} est_err_vs_exact={np.mean(est) if est else float('nan'):.3e}")
     return tb, r
 
@@ -201,5 +208,80 @@ def test_full_size_sampled(cfg_id):
     data = workloads.generate(cfg, device="cuda")
     for step in spec["steps"]:
         check_case(cfg, data, units=spec["units"], heads_per_unit=spec["heads"], step=step)
+    del data
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------ hybrid decode
+# exact attention over the first n_sink and the last n_window keys, merged by
+# log-sum-exp with the estimate over the selected keys outside that set
+
+HYBRID = [
+    (SMALL[1], 4, 64, None),          # ragged, several chunks
+    (SMALL[1], 16, 1500, 1024),       # window spans chunk boundaries
+    (SMALL[2], 3000, 3000, None),     # sink and window overlap: everything exact
+    (SMALL[3], 0, 100, None),         # window only
+    (SMALL[4], 7, 0, None),           # fp32, sinks only
+    (SMALL[6], 1, 1, None),           # N = 1: the key is both sink and window
+    (SMALL[7], 8, 32, None),          # T = L: the selection is mostly empty
+    (SMALL[10], 5, 2000, None),       # K = 12, N = 9001
+]
+
+
+@pytest.mark.parametrize("cfg,n_sink,n_window,stride", HYBRID,
+                         ids=[f"{c.name}-s{a}-w{b}" for c, a, b, _ in HYBRID])
+def test_hybrid_parity(cfg, n_sink, n_window, stride):
+    say(f"case hybrid {cfg.name} sink={n_sink} window={n_window} stride={stride}")
+    data = workloads.generate(cfg)
+    check_case(cfg, data, stride=stride, n_sink=n_sink, n_window=n_window)
+
+
+def test_hybrid_all_exact_is_attention():
+    # an exact set covering every key leaves nothing to sample: exact attention
+    cfg = SMALL[1]
+    say("case hybrid all exact")
+    data = workloads.generate(cfg)
+    tb, r = run_gpu(cfg, data, n_sink=10, n_window=cfg.N)
+    keys = data["keys"].float().numpy()
+    vals = data["values"].float().numpy()
+    q = data["q"][0].float().numpy()
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            ex, lse = O.exact_attention(q[b, h], keys[b, h // cfg.G], vals[b, h // cfg.G], cfg.scale)
+            out = to_np(r["out"][b, h])
+            assert np.linalg.norm(out - ex) / np.linalg.norm(ex) <= PAR.OUT_RTOL
+            assert abs(float(r["lse"][b, h]) - lse) <= PAR.LSE_ATOL * max(1.0, abs(lse))
+            assert int(r["nsel"][b, h]) == 0
+
+
+def test_hybrid_zero_set_is_plain_decode():
+    # n_sink = n_window = 0 through the hybrid entry point: the plain decode, bit for bit
+    lsh = _lsh()
+    cfg = SMALL[2]
+    say("case hybrid empty set")
+    data = workloads.generate(cfg)
+    dev = torch.device("cuda:0")
+    keys, vals, W = data["keys"].to(dev), data["values"].to(dev), data["W"].to(dev)
+    q = data["q"][0].to(dev).contiguous()
+    tb = lsh.build_tables(keys, W, cfg.K, cfg.L)
+    r0 = lsh.decode_attention(q, keys, vals, W, tb, cfg.K, cfg.L, cfg.T, sm_scale=cfg.scale)
+    outs = []
+    for _ in range(2):
+        out = torch.empty_like(r0["out"])
+        lse = torch.empty_like(r0["lse"])
+        nsel = torch.empty_like(r0["nsel"])
+        lsh.lsh_decode_attention_hybrid(q, keys, vals, W, tb["indices"], tb["offsets"], cfg.K, cfg.L, cfg.T,
+                                        tb["stride"], cfg.scale, 0, 0, out, lse, nsel)
+        outs.append((out, lse, nsel))
+    torch.cuda.synchronize()
+    for out, lse, nsel in outs:
+        assert torch.equal(out, r0["out"]) and torch.equal(lse, r0["lse"]) and torch.equal(nsel, r0["nsel"])
+
+
+def test_hybrid_full_size_128k():
+    cfg = workloads.CONFIGS[4]
+    say(f"case hybrid full {cfg.name}")
+    data = workloads.generate(cfg, device="cuda")
+    check_case(cfg, data, units=[(0, 2)], heads_per_unit=2, n_sink=4, n_window=1024)
     del data
     torch.cuda.empty_cache()
