@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--config", type=int, default=4, help="workload id in workloads.CONFIGS (default: 128K GQA-8)")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hybrid-sink", type=int, default=4,
+                    help="sink keys of the hybrid decode timed beside the plain one")
+    ap.add_argument("--hybrid-window", type=int, default=1024,
+                    help="recent-window keys of the hybrid decode timed beside the plain one")
     ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
                     help="replay each step from a HIP graph (default) or launch it eagerly")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -153,6 +157,11 @@ def main():
     def decode(c, counts=None):
         lsh.lsh_decode_attention(c["q"], c["keys"], c["values"], c["W"], c["indices"], c["offsets"], K, L, T,
                                  stride, cfg.scale, c["out"], c["lse"], c["nsel"], None, counts, c["dws"])
+
+    def decode_hybrid(c):
+        lsh.lsh_decode_attention_hybrid(c["q"], c["keys"], c["values"], c["W"], c["indices"], c["offsets"], K, L,
+                                        T, stride, cfg.scale, args.hybrid_sink, args.hybrid_window, c["out"],
+                                        c["lse"], c["nsel"], None, None, c["dws"])
 
     def step(i):
         build(copies[i % R])
@@ -281,6 +290,25 @@ def main():
     dkernels = kernel_table(dtimes)
     dec_ms_steady = sum(dtimes[k][0] for k in DECODE_KERNELS) / args.steps
 
+    # the hybrid decode in steady state: the exact sink + window part runs in
+    # the merge kernel, the selection leaves those keys out
+    lsh.lsh_timing_begin()
+    for i in range(args.steps):
+        decode_hybrid(copies[i % R])
+    htimes = lsh.lsh_timing_end()
+    hk = kernel_table(htimes)
+    n_exact = min(N, args.hybrid_sink + args.hybrid_window)
+    hyb_ms = sum(htimes[k][0] for k in DECODE_KERNELS) / args.steps
+    decode_hybrid_steady = {
+        "n_sink": args.hybrid_sink, "n_window": args.hybrid_window,
+        "ms": round(hyb_ms, 5),
+        "qh_per_s": round(qh / (hyb_ms * 1e-3), 1),
+        "merge_avg_us": hk["merge"]["avg_us"],
+        # keys and values of the exact set, once per (sequence, kv head)
+        "exact_kv_bytes": int(B * Hkv * n_exact * 2 * d * esz),
+        "kernels": {k: v["avg_us"] for k, v in hk.items()},
+    }
+
     build_ms = sum(ktimes[k][0] for k in BUILD_KERNELS) / args.steps
     decode_ms = sum(ktimes[k][0] for k in DECODE_KERNELS) / args.steps
     dec_bytes = E_idx * 2 + qh * L * 8 + kv_bytes + qh * d * (esz + 4) + d * L * K * esz
@@ -323,6 +351,7 @@ def main():
             "probed_index_entries": E_idx,
             "kernels": kernels,
             "decode_steady": decode_steady,
+            "decode_hybrid_steady": decode_hybrid_steady,
         },
     }
 

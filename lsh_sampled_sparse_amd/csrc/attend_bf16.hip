@@ -18,6 +18,11 @@
 // Stegun 4.4.46) and the hardware log2 keep it to ~35 instructions per pair.
 // The four waves' (max, sum, acc) states are merged through LDS into one
 // partial per query head and split, for the log-sum-exp merge that follows.
+// Workgroups past the context splits take the hybrid decode's exact set
+// (keys [0, exact_head) and [N - exact_tail, N), counted 0 .. ne - 1 across
+// both ranges), a piece of exact_len keys each: every key is taken for every
+// head of the group and weighted 1 (u = 1), which is plain softmax attention
+// on the same tiles.
 #include <math.h>
 
 #include "lsh_device.h"
@@ -130,7 +135,8 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
     const uint32_t* __restrict__ bitmask,  // [B*Hq][Nw]
     const float* __restrict__ lnu_tab,     // [kLnuTable + 1]
     int Hq, int Hkv, int N, int K, int Tth, float scale, int split_len, int nsplit,
-    float* __restrict__ partials) {        // [B*Hq][nsplit][130]
+    int exact_head, int exact_tail, int exact_len, int nexact,
+    float* __restrict__ partials) {        // [B*Hq][nsplit + nexact][130]
   __shared__ float2 tab2[kLnuTable];      // (g_j, g_{j+1} - g_j)
   __shared__ int ring_idx[kWaves][kRingN];
   __shared__ uint16_t ring_hm[kWaves][kRingN];
@@ -148,6 +154,11 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
   const uint16_t* kb = keys + static_cast<size_t>(u) * N * kHeadDim;
   const uint16_t* vb = values + static_cast<size_t>(u) * N * kHeadDim;
   const bool k0 = (K == 0);
+  const bool exact = s >= nsplit;          // a piece of the exact set
+  const bool nolnu = k0 || exact;
+  const int ne = exact_head + exact_tail;
+  const int npart = nsplit + nexact;
+  const uint16_t gmask = static_cast<uint16_t>((1u << G) - 1u);
   const float TKln2 = static_cast<float>(Tth * K) * 0.69314718055994531f;
 
   for (int i = tid; i < kLnuTable; i += 256)
@@ -168,9 +179,11 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
     rq[i] = x > 0.f ? __builtin_amdgcn_rsqf(x) : 0.f;
   }
 
-  const int sb = s * split_len;
-  const int se = min(N, sb + split_len);
-  const int wq = split_len / kWaves;
+  // this wave's range: keys of the context split, or exact-set positions
+  const int plen = exact ? exact_len : split_len;
+  const int sb = exact ? (s - nsplit) * exact_len : s * split_len;
+  const int se = min(exact ? ne : N, sb + plen);
+  const int wq = plen / kWaves;
   const int wb = min(se, sb + wave * wq), we = min(se, sb + (wave + 1) * wq);
 
   int* ridx = ring_idx[wave];
@@ -181,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
 
   // ---- selection masks: the 16 words (512 keys) of every head of the group
   // for one block; word w of head h sits in lane (h % 4) * 16 + w of load h / 4
-  uint32_t mw[GW], mw_next[GW];
+  uint32_t mw[GW] = {}, mw_next[GW] = {};
   auto load_block = [&](int blk0, uint32_t (&dst)[GW]) {
 #pragma unroll
     for (int k = 0; k < GW; ++k) {
@@ -192,12 +205,32 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
   };
   int blk = wb;                        // next window to compact
   int blk_loaded = wb;                 // block start of mw
-  load_block(wb, mw);
-  load_block(wb + kBlock, mw_next);
+  if (!exact) {
+    load_block(wb, mw);
+    load_block(wb + kBlock, mw_next);
+  }
 
   int rhead = 0, rcnt = 0;
   // compact windows of 64 keys until a full tile is queued or the range ends
   auto fill = [&]() {
+    if (exact) {
+      // every position of the range, all heads; the lanes that take one are
+      // lanes 0 .. count - 1, so a lane's ring slot follows from its index
+      while (rcnt < kTile && blk < we) {
+        const int i = blk + lane;
+        const bool any = i < we;
+        const uint64_t bal = ballot(any);
+        if (any) {
+          const int e = (rhead + rcnt + lane) & (kRingN - 1);
+          ridx[e] = i < exact_head ? i : i + (N - ne);
+          rhm[e] = gmask;
+        }
+        rcnt += __builtin_popcountll(bal);
+        blk += 64;
+      }
+      __builtin_amdgcn_wave_barrier();
+      return;
+    }
     while (rcnt < kTile && blk < we) {
       if (blk >= blk_loaded + kBlock) {
         blk_loaded += kBlock;
@@ -296,8 +329,8 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float x0 = S0[i], x1 = S1[i];
-      const float u0 = k0 ? 0.f : lnu_of_cos(x0 * rq[i] * rk0, tab2, TKln2);
-      const float u1 = k0 ? 0.f : lnu_of_cos(x1 * rq[i] * rk1, tab2, TKln2);
+      const float u0 = nolnu ? 0.f : lnu_of_cos(x0 * rq[i] * rk0, tab2, TKln2);
+      const float u1 = nolnu ? 0.f : lnu_of_cos(x1 * rq[i] * rk1, tab2, TKln2);
       const int hh = 4 * g4 + i;
       const bool ok = hh < G;
       lg[0][i] = (ok && ((hm0 >> hh) & 1)) ? fmaf(scale, x0, -u0) : -INFINITY;
@@ -386,7 +419,7 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
         Lm = fmaf(ep_l[w][hh], f, Lm);
       }
     }
-    float* dst = partials + (static_cast<size_t>(bh0 + hh) * nsplit + s) * kPartialStride;
+    float* dst = partials + (static_cast<size_t>(bh0 + hh) * npart + s) * kPartialStride;
     dst[d] = A;
     if (d == 0) {
       dst[kHeadDim] = M;
@@ -397,7 +430,7 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
 
 hipError_t launch_attend_bf16(const DecodeArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
-  const dim3 grid(a.nsplit, a.B * a.Hkv);
+  const dim3 grid(a.nsplit + a.nexact, a.B * a.Hkv);
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
   const uint16_t* kp = static_cast<const uint16_t*>(a.keys);
   const uint16_t* vp = static_cast<const uint16_t*>(a.values);
@@ -405,12 +438,15 @@ hipError_t launch_attend_bf16(const DecodeArgs& a, hipStream_t stream) {
   const float* lt = a.lnu_table;
   if (G <= 4)
     return launch(kKAttend, attend_bf16_kernel<1>, grid, dim3(256), 0, stream, qp, kp, vp, bm, lt, a.Hq,
-                  a.Hkv, a.N, a.K, a.T, a.scale, a.split_len, a.nsplit, a.partials);
+                  a.Hkv, a.N, a.K, a.T, a.scale, a.split_len, a.nsplit, a.exact_head, a.exact_tail, a.exact_len, a.nexact,
+                  a.partials);
   if (G <= 8)
     return launch(kKAttend, attend_bf16_kernel<2>, grid, dim3(256), 0, stream, qp, kp, vp, bm, lt, a.Hq,
-                  a.Hkv, a.N, a.K, a.T, a.scale, a.split_len, a.nsplit, a.partials);
+                  a.Hkv, a.N, a.K, a.T, a.scale, a.split_len, a.nsplit, a.exact_head, a.exact_tail, a.exact_len, a.nexact,
+                  a.partials);
   return launch(kKAttend, attend_bf16_kernel<4>, grid, dim3(256), 0, stream, qp, kp, vp, bm, lt, a.Hq, a.Hkv,
-                a.N, a.K, a.T, a.scale, a.split_len, a.nsplit, a.partials);
+                a.N, a.K, a.T, a.scale, a.split_len, a.nsplit, a.exact_head, a.exact_tail, a.exact_len, a.nexact,
+                  a.partials);
 }
 
 }  // namespace lsh

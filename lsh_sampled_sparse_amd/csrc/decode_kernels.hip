@@ -377,7 +377,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
     const uint32_t* __restrict__ bitmask,            // [BH][Nw]
     const float* __restrict__ lnu_tab,               // [kLnuTable + 1]
     int Hq, int Hkv, int N, int K, int Tth, float scale, int split_len, int nsplit,
-    float* __restrict__ partials) {                  // [BH][nsplit][130]
+    int exact_head, int exact_tail, int exact_len, int nexact,
+    float* __restrict__ partials) {                  // [BH][nsplit + nexact][130]
   using S = typename T::storage;
   __shared__ float tab[kLnuTable + 1];
   __shared__ float qn[16];
@@ -397,6 +398,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
   const S* kb = keys + static_cast<size_t>(u) * N * kHeadDim;
   const S* vb = values + static_cast<size_t>(u) * N * kHeadDim;
   const bool k0 = (K == 0);
+  const bool exact = s >= nsplit;     // a piece of the exact set (all heads, u = 1)
+  const bool nolnu = k0 || exact;
+  const int ne = exact_head + exact_tail;
+  const int npart = nsplit + nexact;
   const float TK = static_cast<float>(Tth * K);
 
   for (int i = tid; i <= kLnuTable; i += kAttThreads) tab[i] = k0 ? 0.f : lnu_tab[i];
@@ -412,9 +417,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
   }
   __syncthreads();
 
-  const int sb = s * split_len;
-  const int se = min(N, sb + split_len);
-  const int wq = split_len / 4;
+  const int plen = exact ? exact_len : split_len;
+  const int sb = exact ? (s - nsplit) * exact_len : s * split_len;
+  const int se = min(exact ? ne : N, sb + plen);
+  const int wq = plen / 4;
   const int wb = min(se, sb + wave * wq), we = min(se, sb + (wave + 1) * wq);
 
   const int grp = lane >> 4, slot = lane & 15;
@@ -458,7 +464,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
         const float x = sc[i];
         const float nn = qn[hh] * kn;
         const float cs = nn > 0.f ? x / nn : 0.f;
-        logit = scale * x - (k0 ? 0.f : log_inclusion(cs, tab, TK));
+        logit = scale * x - (nolnu ? 0.f : log_inclusion(cs, tab, TK));
       }
       const float mt = row16_max(logit);
       const float mnew = fmaxf(m_run[i], mt);
@@ -494,17 +500,22 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
   };
 
   for (int blk = wb; blk < we; blk += 64) {
-    const int n = blk + lane;
-    const int w0 = blk >> 5;
-    int hm = 0;
-    for (int hh = 0; hh < G; ++hh) {
-      const uint32_t* bm = bitmask + static_cast<size_t>(bh0 + hh) * Nw;
-      const uint32_t lo = bm[w0];
-      const uint32_t hi = (w0 + 1 < Nw) ? bm[w0 + 1] : 0u;
-      const uint32_t word = lane < 32 ? lo : hi;
-      hm |= static_cast<int>((word >> (lane & 31)) & 1u) << hh;
+    const int i = blk + lane;           // key, or position in the exact set
+    int n = i, hm = 0;
+    if (exact) {
+      n = i < exact_head ? i : i + (N - ne);
+      hm = (1 << G) - 1;
+    } else {
+      const int w0 = blk >> 5;
+      for (int hh = 0; hh < G; ++hh) {
+        const uint32_t* bm = bitmask + static_cast<size_t>(bh0 + hh) * Nw;
+        const uint32_t lo = bm[w0];
+        const uint32_t hi = (w0 + 1 < Nw) ? bm[w0 + 1] : 0u;
+        const uint32_t word = lane < 32 ? lo : hi;
+        hm |= static_cast<int>((word >> (lane & 31)) & 1u) << hh;
+      }
     }
-    const bool any = (n < we) && hm != 0;
+    const bool any = (i < we) && hm != 0;
     const uint64_t bal = ballot(any);
     if (any) {
       const int e = (head + cnt + mbcnt(bal)) & (kRing - 1);
@@ -562,7 +573,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
         Lm = fmaf(wl[w][hh], f, Lm);
       }
     }
-    float* dst = partials + (static_cast<size_t>(bh0 + hh) * nsplit + s) * kPartialStride;
+    float* dst = partials + (static_cast<size_t>(bh0 + hh) * npart + s) * kPartialStride;
     dst[d] = A;
     if (d == 0) {
       dst[kHeadDim] = M;
@@ -572,50 +583,35 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// merge: one workgroup (4 waves) per query head.  Wave w folds the splits
-// s = w, w + 4, ... into a running (max, sum, acc) with each lane owning two
-// dims; the four wave states are combined through LDS.  With an exact set
-// (the hybrid decode: keys [0, exact_head) and [N - exact_tail, N), which
-// count_select left out of the selection) the workgroup also computes the
-// plain softmax partial of those keys, (max, sum, acc) with u = 1, and merges
-// it last.  That part is one workgroup per head: it is meant for sinks plus a
-// recent window, a few thousand keys at most.
+// merge: one workgroup (4 waves) per query head.  Wave w folds the partials
+// s = w, w + 4, ... (the context splits, then the pieces of the exact set of
+// the hybrid decode) into a running (max, sum, acc) with each lane owning two
+// dims; the four wave states are combined through LDS.
 // ---------------------------------------------------------------------------
 constexpr int kMergeThreads = 256;
-constexpr int kExactBatch = 4 * kMergeThreads;   // exact-set weights staged per batch
 
-template <typename T>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ partials,
                                                               const int32_t* __restrict__ chunk_nsel,
-                                                              int nsplit, int nJ, float* __restrict__ out,
-                                                              float* __restrict__ lse, int32_t* __restrict__ nsel,
-                                                              const typename T::storage* __restrict__ q,
-                                                              const typename T::storage* __restrict__ keys,
-                                                              const typename T::storage* __restrict__ values,
-                                                              int Hq, int Hkv, int N, float scale,
-                                                              int exact_head, int exact_tail) {
+                                                              int npart, int nJ, float* __restrict__ out,
+                                                              float* __restrict__ lse, int32_t* __restrict__ nsel) {
   __shared__ float wm[4], wl[4];
   __shared__ float wacc[4][kHeadDim];
   __shared__ int wn[4];
-  __shared__ float qs[kHeadDim];
-  __shared__ float wexp[kExactBatch];
-  __shared__ float wx[4];                          // per-wave max / sum of the exact part
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* P = partials + static_cast<size_t>(bh) * nsplit * kPartialStride;
-  // the overall max first, so that every split's weight exp(m_s - M) is known
-  // without a running rescale and the loads of all splits can be in flight
+  const float* P = partials + static_cast<size_t>(bh) * npart * kPartialStride;
+  // the overall max first, so that every partial's weight exp(m_s - M) is
+  // known without a running rescale and the loads of all of them can be in flight
   float mx = -INFINITY;
-  for (int s = tid; s < nsplit; s += kMergeThreads) mx = fmaxf(mx, P[static_cast<size_t>(s) * kPartialStride + kHeadDim]);
+  for (int s = tid; s < npart; s += kMergeThreads) mx = fmaxf(mx, P[static_cast<size_t>(s) * kPartialStride + kHeadDim]);
   mx = wave_max(mx);
   if (lane == 0) wm[wave] = mx;
   __syncthreads();
   const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
   __syncthreads();
   float l = 0.f, a0 = 0.f, a1 = 0.f;
-  const float m = M;
   if (M != -INFINITY) {
 #pragma unroll 4
-    for (int s = wave; s < nsplit; s += 4) {
+    for (int s = wave; s < npart; s += 4) {
       const float* ps = P + static_cast<size_t>(s) * kPartialStride;
       const float ms = ps[kHeadDim];
       const float f = (ms == -INFINITY) ? 0.f : __expf(ms - M);
@@ -628,89 +624,18 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   for (int j = tid; j < nJ; j += kMergeThreads) cnt += chunk_nsel[static_cast<size_t>(bh) * nJ + j];
   cnt = wave_sum_int(cnt);
   if (lane == 0) {
-    wm[wave] = m;
     wl[wave] = l;
     wn[wave] = cnt;
   }
   wacc[wave][2 * lane] = a0;
   wacc[wave][2 * lane + 1] = a1;
   __syncthreads();
-
-  // exact part over the keys of the exact set (unit b * Hkv + h / G)
-  const int ne = exact_head + exact_tail;
-  float me = -INFINITY, le = 0.f, ae = 0.f;   // ae: dim tid of the acc (tid < 128)
-  if (ne > 0) {
-    using S = typename T::storage;
-    const int b = bh / Hq, h = bh % Hq;
-    const int u = b * Hkv + h / (Hq / Hkv);
-    const S* kb = keys + static_cast<size_t>(u) * N * kHeadDim;
-    const S* vb = values + static_cast<size_t>(u) * N * kHeadDim;
-    auto key_of = [&](int i) { return i < exact_head ? i : N - exact_tail + (i - exact_head); };
-    auto elem = [&](const S* p, int i) {
-      if constexpr (sizeof(S) == 2) return bf16_to_f32(p[i]); else return static_cast<float>(p[i]);
-    };
-    auto logit = [&](int n) {
-      const S* k = kb + static_cast<size_t>(n) * kHeadDim;
-      float x = 0.f;
-      for (int i = 0; i < kHeadDim; ++i) x = fmaf(qs[i], elem(k, i), x);
-      return scale * x;
-    };
-    if (tid < kHeadDim) qs[tid] = elem(q + static_cast<size_t>(bh) * kHeadDim, tid);
-    __syncthreads();
-    float mt = -INFINITY;
-    for (int i = tid; i < ne; i += kMergeThreads) mt = fmaxf(mt, logit(key_of(i)));
-    mt = wave_max(mt);
-    if (lane == 0) wx[wave] = mt;
-    __syncthreads();
-    me = fmaxf(fmaxf(wx[0], wx[1]), fmaxf(wx[2], wx[3]));
-    float ls = 0.f;
-    for (int b0 = 0; b0 < ne; b0 += kExactBatch) {
-      __syncthreads();
-      for (int k = tid; k < kExactBatch; k += kMergeThreads) {
-        const int i = b0 + k;
-        const float w = i < ne ? __expf(logit(key_of(i)) - me) : 0.f;
-        wexp[k] = w;
-        ls += w;
-      }
-      __syncthreads();
-      if (tid < kHeadDim) {
-        const int nb = min(kExactBatch, ne - b0);
-        for (int k = 0; k < nb; ++k)
-          ae = fmaf(wexp[k], elem(vb + static_cast<size_t>(key_of(b0 + k)) * kHeadDim, tid), ae);
-      }
-    }
-    ls = wave_sum(ls);
-    __syncthreads();                                 // every wave has read the max from wx
-    if (lane == 0) wx[wave] = ls;
-    __syncthreads();
-    le = wx[0] + wx[1] + wx[2] + wx[3];
-  }
-
   if (tid < kHeadDim) {
-    float Ms = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) Ms = fmaxf(Ms, wm[w]);
-    float A = 0.f, Lm = 0.f;
-    if (Ms != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        if (wm[w] == -INFINITY) continue;
-        const float f = __expf(wm[w] - Ms);
-        A = fmaf(wacc[w][tid], f, A);
-        Lm = fmaf(wl[w], f, Lm);
-      }
-    }
-    // the sampled state (A, Lm at Ms) and the exact one (ae, le at me)
-    const float Mt = fmaxf(Ms, me);
-    if (Mt != -INFINITY) {
-      const float fs = Ms == -INFINITY ? 0.f : __expf(Ms - Mt);
-      const float fe = me == -INFINITY ? 0.f : __expf(me - Mt);
-      A = A * fs + ae * fe;
-      Lm = Lm * fs + le * fe;
-    }
-    out[static_cast<size_t>(bh) * kHeadDim + tid] = (Mt == -INFINITY) ? 0.f : A / Lm;
+    const float A = wacc[0][tid] + wacc[1][tid] + wacc[2][tid] + wacc[3][tid];
+    const float Lm = wl[0] + wl[1] + wl[2] + wl[3];
+    out[static_cast<size_t>(bh) * kHeadDim + tid] = (M == -INFINITY) ? 0.f : A / Lm;
     if (tid == 0) {
-      if (lse) lse[bh] = (Mt == -INFINITY) ? -INFINITY : Mt + logf(Lm);
+      if (lse) lse[bh] = (M == -INFINITY) ? -INFINITY : M + logf(Lm);
       if (nsel) nsel[bh] = wn[0] + wn[1] + wn[2] + wn[3];
     }
   }
@@ -722,10 +647,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
 template <typename T, int GM>
 static hipError_t launch_attend(const DecodeArgs& a, hipStream_t stream) {
   using S = typename T::storage;
-  return launch(kKAttend, attend_kernel<T, GM>, dim3(a.nsplit, a.B * a.Hkv), dim3(kAttThreads), 0, stream,
+  return launch(kKAttend, attend_kernel<T, GM>, dim3(a.nsplit + a.nexact, a.B * a.Hkv), dim3(kAttThreads), 0, stream,
                 static_cast<const S*>(a.q), static_cast<const S*>(a.keys), static_cast<const S*>(a.values),
                 static_cast<const uint32_t*>(a.bitmask), static_cast<const float*>(a.lnu_table), a.Hq, a.Hkv,
-                a.N, a.K, a.T, a.scale, a.split_len, a.nsplit, a.partials);
+                a.N, a.K, a.T, a.scale, a.split_len, a.nsplit, a.exact_head, a.exact_tail, a.exact_len, a.nexact,
+                a.partials);
 }
 
 template <typename T>
@@ -758,10 +684,9 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   else
     e = launch_attend<T, 16>(a, stream);
   if (e != hipSuccess) return e;
-  return launch(kKMerge, merge_kernel<T>, dim3(BH), dim3(kMergeThreads), 0, stream,
-                static_cast<const float*>(a.partials), static_cast<const int32_t*>(a.chunk_nsel), a.nsplit,
-                a.nJ, a.out, a.lse, a.nsel, static_cast<const S*>(a.q), static_cast<const S*>(a.keys),
-                static_cast<const S*>(a.values), a.Hq, a.Hkv, a.N, a.scale, a.exact_head, a.exact_tail);
+  return launch(kKMerge, merge_kernel, dim3(BH), dim3(kMergeThreads), 0, stream,
+                static_cast<const float*>(a.partials), static_cast<const int32_t*>(a.chunk_nsel),
+                a.nsplit + a.nexact, a.nJ, a.out, a.lse, a.nsel);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

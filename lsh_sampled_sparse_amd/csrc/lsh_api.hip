@@ -87,7 +87,9 @@ DecodeLayout decode_layout(int B, int Hq, int Hkv, int N, int L, const Geometry&
   w.bitmask = off;    off = align_up(off + BH * ((N + 31) / 32) * sizeof(uint32_t));
   w.chunk_nsel = off; off = align_up(off + BH * g.nJ * sizeof(int32_t));
   w.lnu = off;        off = align_up(off + (lsh::kLnuTable + 1) * sizeof(float));
-  w.partials = off;   off = align_up(off + BH * w.nsplit * lsh::kPartialStride * sizeof(float));
+  // one partial per head and context split, plus the exact set's pieces
+  w.partials = off;
+  off = align_up(off + BH * (w.nsplit + lsh::kMaxExactSplits) * lsh::kPartialStride * sizeof(float));
   w.total = off;
   return w;
 }
@@ -299,6 +301,13 @@ lsh_status lsh_decode_attention_hybrid(const void* q, const void* keys, const vo
   a.dtype = dtype;
   a.exact_head = std::min(n_sink, N);
   a.exact_tail = std::min(n_window, N - a.exact_head);
+  // the exact set goes to the attention kernel as extra workgroups over
+  // pieces of at least 128 keys (one 32-key tile per wave), at most
+  // kMaxExactSplits of them
+  const int ne = a.exact_head + a.exact_tail;
+  const int per_piece = (ne + lsh::kMaxExactSplits - 1) / lsh::kMaxExactSplits;
+  a.exact_len = std::max(128, (per_piece + 127) / 128 * 128);
+  a.nexact = (ne + a.exact_len - 1) / a.exact_len;
   return hip_status(lsh::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -31,7 +31,7 @@ struct DecodeArgs {
   uint32_t* bitmask;     // [B*Hq][Nw]
   int32_t* chunk_nsel;   // [B*Hq][nJ]
   float* lnu_table;      // [kLnuTable + 1]
-  float* partials;       // [B*Hq][nsplit][130]
+  float* partials;       // [B*Hq][nsplit + nexact][130]
   float* out;            // [B*Hq][128]
   float* lse;            // optional [B*Hq]
   int32_t* nsel;         // optional [B*Hq]
@@ -42,10 +42,12 @@ struct DecodeArgs {
   float scale;
   int dtype;
   int exact_head, exact_tail;  // exact set: keys [0, exact_head) and [N - exact_tail, N), disjoint
+  int exact_len, nexact;       // the exact set in nexact pieces of exact_len keys, one workgroup each
 };
 
 constexpr int kLnuTable = 1024;   // ln-u correction table intervals over theta in [0, pi]
 constexpr int kPartialStride = 130;
+constexpr int kMaxExactSplits = 16;   // partial slots per head reserved for the exact set
 
 // Kernel kinds, in launch order; names for the timing interface.
 enum KernelId {
