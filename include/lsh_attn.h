@@ -122,6 +122,46 @@ lsh_status lsh_build_tables(const void* keys, const void* W,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/*
+ * Table update for a growing key cache.  The pages build the tables once
+ * over the prompt (sourcepulse summary, "Highlighted Details": hash-table
+ * construction) and say nothing of the keys a decode appends; MAC-Attention
+ * updates its caches for the next token inside the decode step
+ * ("MAC-Attention" README, "How It Works").  Here the tables of a cache with
+ * room for n_cap keys per (sequence, kv head) hold its first n keys, and
+ *
+ *   after lsh_update_tables(n_old, n_new), the tables are exactly those that
+ *   lsh_build_tables would produce from keys 0 .. n_new - 1
+ *
+ * (same codes, buckets, order and offsets), laid out with the pitch n_cap:
+ *
+ * keys     [B, Hkv, n_cap, d] dtype     keys 0 .. n_new - 1 written
+ * offsets  [B, Hkv, L, lsh_num_chunks(n_cap, stride), 2^K] uint16
+ *                                       in/out: chunks j < n_old / stride are
+ *                                       kept; the rest are rewritten
+ * indices  [B, Hkv, L, n_cap] uint16    in/out: positions below
+ *                                       (n_old / stride) * stride are kept
+ * key_codes [B, Hkv, L, n_cap] uint16   optional out: codes of the keys from
+ *                                       (n_old / stride) * stride on
+ * workspace                             lsh_build_workspace_size(.., n_cap, ..)
+ *
+ * (n_old / stride rounds down.)  The inputs must hold the tables of keys
+ * 0 .. n_old - 1 built with the same W, K, L, stride and n_cap (n_old = 0:
+ * nothing); keys of positions >= n_new are never read.  The call rebuilds the
+ * chunks from the one holding key n_old to the last, reading their keys: one
+ * new key per step costs one chunk of keys per (sequence, kv head).
+ * 0 <= n_old <= n_new <= n_cap, else LSH_ERR_INVALID_ARG; n_old == n_new
+ * launches nothing.  Size limits as for lsh_build_tables with N = n_cap.
+ * lsh_build_tables(.., N, ..) is this call with n_old = 0, n_new = n_cap = N.
+ */
+lsh_status lsh_update_tables(const void* keys, const void* W,
+                             int B, int Hkv, int n_old, int n_new, int n_cap,
+                             int d, int K, int L, int stride, int dtype,
+                             uint16_t* offsets, uint16_t* indices,
+                             uint16_t* key_codes,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* ------------------------------------------------------------------------
  * Decode
  *
@@ -129,7 +169,9 @@ lsh_status lsh_build_tables(const void* keys, const void* W,
  * G = Hq / Hkv <= 16, 1 <= T <= L and a finite sm_scale.
  * ---------------------------------------------------------------------- */
 
-/* Bytes of device workspace lsh_decode_attention needs (0 on invalid sizes). */
+/* Bytes of device workspace lsh_decode_attention needs (0 on invalid sizes).
+ * The size never decreases with N, so the size at a cache's capacity serves
+ * every decode over a shorter prefix of it. */
 size_t lsh_decode_workspace_size(int B, int Hq, int Hkv, int N, int d, int K,
                                  int L, int stride);
 
@@ -175,9 +217,10 @@ lsh_status lsh_decode_attention(const void* q, const void* keys,
  *
  * Arguments are those of lsh_decode_attention plus n_sink, n_window >= 0
  * (LSH_ERR_INVALID_ARG if negative; values past N are clamped).  The exact
- * part runs in one workgroup per query head, for sets of up to a few
- * thousand keys.  n_sink = n_window = 0 is lsh_decode_attention.  Same
- * workspace size.
+ * set is attended in at most 16 pieces, one workgroup per piece and
+ * (sequence, kv head), for all query heads of the group at once: it reads
+ * each of its keys and values once per kv head.  n_sink = n_window = 0 is
+ * lsh_decode_attention.  Same workspace size.
  */
 lsh_status lsh_decode_attention_hybrid(const void* q, const void* keys,
                                        const void* values, const void* W,
@@ -185,6 +228,29 @@ lsh_status lsh_decode_attention_hybrid(const void* q, const void* keys,
                                        int B, int Hq, int Hkv, int N, int d, int K,
                                        int L, int T, int stride, float sm_scale,
                                        int dtype, int n_sink, int n_window,
+                                       float* out, float* lse, int32_t* nsel,
+                                       uint16_t* q_codes, uint8_t* counts,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/*
+ * Decode over the first N keys of a cache with room for n_cap keys: the
+ * hybrid decode above with keys, values [B, Hkv, n_cap, d] and tables of the
+ * pitch lsh_update_tables uses (indices [B, Hkv, L, n_cap], offsets
+ * [B, Hkv, L, lsh_num_chunks(n_cap, stride), 2^K]) holding keys 0 .. N - 1.
+ * Keys and values from position N on are never read.  counts, when given, is
+ * [B, Hq, N].  N <= n_cap, else LSH_ERR_INVALID_ARG.  The recent window is the
+ * last n_window of the N keys.  Workspace: lsh_decode_workspace_size at N (or
+ * at n_cap, which is never smaller).  lsh_decode_attention_hybrid is this call
+ * with n_cap = N.
+ */
+lsh_status lsh_decode_attention_cached(const void* q, const void* keys,
+                                       const void* values, const void* W,
+                                       const uint16_t* indices, const uint16_t* offsets,
+                                       int B, int Hq, int Hkv, int N, int n_cap,
+                                       int d, int K, int L, int T, int stride,
+                                       float sm_scale, int dtype,
+                                       int n_sink, int n_window,
                                        float* out, float* lse, int32_t* nsel,
                                        uint16_t* q_codes, uint8_t* counts,
                                        void* workspace, size_t workspace_bytes,

@@ -27,9 +27,11 @@ EXPORTS = (
     "lsh_default_stride",
     "lsh_build_workspace_size",
     "lsh_build_tables",
+    "lsh_update_tables",
     "lsh_decode_workspace_size",
     "lsh_decode_attention",
     "lsh_decode_attention_hybrid",
+    "lsh_decode_attention_cached",
     "lsh_kernel_count",
     "lsh_kernel_name",
     "lsh_timing_begin",
@@ -60,6 +62,8 @@ def lib():
         L.lsh_build_workspace_size.argtypes = [_i] * 8
         L.lsh_build_tables.restype = _i
         L.lsh_build_tables.argtypes = [_p, _p] + [_i] * 8 + [_p, _p, _p, _p, _sz, _p]
+        L.lsh_update_tables.restype = _i
+        L.lsh_update_tables.argtypes = [_p, _p] + [_i] * 10 + [_p, _p, _p, _p, _sz, _p]
         L.lsh_decode_workspace_size.restype = _sz
         L.lsh_decode_workspace_size.argtypes = [_i] * 8
         L.lsh_decode_attention.restype = _i
@@ -67,6 +71,9 @@ def lib():
                                            + [_p] * 6 + [_sz, _p])
         L.lsh_decode_attention_hybrid.restype = _i
         L.lsh_decode_attention_hybrid.argtypes = ([_p] * 6 + [_i] * 9 + [ctypes.c_float, _i, _i, _i]
+                                                  + [_p] * 6 + [_sz, _p])
+        L.lsh_decode_attention_cached.restype = _i
+        L.lsh_decode_attention_cached.argtypes = ([_p] * 6 + [_i] * 10 + [ctypes.c_float, _i, _i, _i]
                                                   + [_p] * 6 + [_sz, _p])
         L.lsh_kernel_count.restype = _i
         L.lsh_kernel_count.argtypes = []
@@ -142,6 +149,37 @@ def lsh_build_tables(keys, W, K, L, stride, offsets, indices, key_codes=None, wo
     _check(lib().lsh_build_tables(
         _ptr(keys), _ptr(W), B, Hkv, N, d, K, L, stride, dt,
         _ptr(offsets), _ptr(indices), _ptr(key_codes),
+        _ptr(workspace), workspace.numel(), _stream(keys.device)))
+
+
+def lsh_update_tables(keys, W, K, L, stride, n_old, n_new, offsets, indices, key_codes=None, workspace=None):
+    """Marshal tensors to ``lsh_update_tables``; keys [B, Hkv, n_cap, d] is the
+    cache, offsets / indices are updated in place."""
+    B, Hkv, n_cap, d = keys.shape
+    dt = _dtype_code(keys.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(1, lsh_build_workspace_size(B, Hkv, n_cap, d, K, L, stride, dt)),
+                                dtype=torch.uint8, device=keys.device)
+    _check(lib().lsh_update_tables(
+        _ptr(keys), _ptr(W), B, Hkv, int(n_old), int(n_new), n_cap, d, K, L, stride, dt,
+        _ptr(offsets), _ptr(indices), _ptr(key_codes),
+        _ptr(workspace), workspace.numel(), _stream(keys.device)))
+
+
+def lsh_decode_attention_cached(q, keys, values, W, indices, offsets, N, K, L, T, stride, sm_scale, n_sink,
+                                n_window, out, lse=None, nsel=None, q_codes=None, counts=None, workspace=None):
+    """Marshal tensors to ``lsh_decode_attention_cached``: keys / values
+    [B, Hkv, n_cap, d], of which the first N are attended."""
+    B, Hq, d = q.shape
+    _, Hkv, n_cap, _ = keys.shape
+    dt = _dtype_code(keys.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(1, lsh_decode_workspace_size(B, Hq, Hkv, N, d, K, L, stride)),
+                                dtype=torch.uint8, device=keys.device)
+    _check(lib().lsh_decode_attention_cached(
+        _ptr(q), _ptr(keys), _ptr(values), _ptr(W), _ptr(indices), _ptr(offsets),
+        B, Hq, Hkv, int(N), n_cap, d, K, L, T, stride, ctypes.c_float(sm_scale), dt, int(n_sink), int(n_window),
+        _ptr(out), _ptr(lse), _ptr(nsel), _ptr(q_codes), _ptr(counts),
         _ptr(workspace), workspace.numel(), _stream(keys.device)))
 
 
@@ -237,18 +275,55 @@ def build_tables(keys, W, K, L, stride=None, return_codes=False):
     return res
 
 
+def alloc_tables(keys, K, L, stride=None, return_codes=False):
+    """Empty tables for a key cache keys [B, Hkv, n_cap, d] that will grow to
+    n_cap keys; fill them with ``update_tables``.  Returns the dict of
+    ``build_tables`` with the pitch n_cap and "n" = 0 keys held."""
+    B, Hkv, n_cap, d = keys.shape
+    if stride is None:
+        stride = lsh_default_stride(n_cap, K)
+    nch = lsh_num_chunks(n_cap, stride)
+    dev = keys.device
+    res = {"offsets": torch.empty(B, Hkv, L, nch, 1 << K, dtype=torch.int16, device=dev),
+           "indices": torch.empty(B, Hkv, L, n_cap, dtype=torch.int16, device=dev),
+           "stride": stride, "n": 0, "n_cap": n_cap}
+    if return_codes:
+        res["codes"] = torch.empty(B, Hkv, L, n_cap, dtype=torch.int16, device=dev)
+    return res
+
+
+def update_tables(keys, W, tables, n_new, K, L, workspace=None):
+    """Extend ``tables`` (from ``alloc_tables``) to hold keys 0 .. n_new - 1
+    of the cache ``keys``; afterwards they equal a build over those keys."""
+    _require(keys, "keys")
+    _require(W, "W", keys.dtype)
+    if keys.shape[2] != tables["n_cap"]:
+        raise ValueError("keys and tables disagree on the capacity")
+    lsh_update_tables(keys, W, K, L, tables["stride"], tables["n"], n_new, tables["offsets"], tables["indices"],
+                      tables.get("codes"), workspace)
+    tables["n"] = int(n_new)
+    return tables
+
+
 def decode_attention(q, keys, values, W, tables, K, L, T, sm_scale=None, return_codes=False,
                      return_counts=False, workspace=None, n_sink=0, n_window=0):
     """One decode step.  Returns dict: out [B,Hq,d] fp32, lse [B,Hq], nsel [B,Hq],
     and q_codes [B,Hq,L] / counts [B,Hq,N] (uint8) when requested.  With
     n_sink / n_window > 0 it is the hybrid decode: the first n_sink and the
-    last n_window keys are attended exactly and merged with the estimate."""
+    last n_window keys are attended exactly and merged with the estimate.
+    Tables from ``alloc_tables`` / ``update_tables`` attend the first
+    tables["n"] keys of the cache."""
     for name, t in (("q", q), ("keys", keys), ("values", values)):
         _require(t, name, keys.dtype)
     B, Hq, d = q.shape
     _, Hkv, N, _ = keys.shape
     if tuple(values.shape) != tuple(keys.shape) or keys.shape[0] != B or keys.shape[3] != d:
         raise ValueError("q [B,Hq,d] and keys/values [B,Hkv,N,d] disagree")
+    cached = "n_cap" in tables
+    if cached:
+        if tables["n_cap"] != N:
+            raise ValueError("keys and tables disagree on the capacity")
+        N = tables["n"]
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     dev = keys.device
@@ -257,7 +332,11 @@ def decode_attention(q, keys, values, W, tables, K, L, T, sm_scale=None, return_
     nsel = torch.empty(B, Hq, dtype=torch.int32, device=dev)
     qc = torch.empty(B, Hq, L, dtype=torch.int16, device=dev) if return_codes else None
     cnt = torch.empty(B, Hq, N, dtype=torch.uint8, device=dev) if return_counts else None
-    if n_sink or n_window:
+    if cached:
+        lsh_decode_attention_cached(q, keys, values, W, tables["indices"], tables["offsets"], N, K, L, T,
+                                    tables["stride"], sm_scale, n_sink, n_window, out, lse, nsel, qc, cnt,
+                                    workspace)
+    elif n_sink or n_window:
         lsh_decode_attention_hybrid(q, keys, values, W, tables["indices"], tables["offsets"], K, L, T,
                                     tables["stride"], sm_scale, n_sink, n_window, out, lse, nsel, qc, cnt,
                                     workspace)

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
     const uint16_t* __restrict__ values,   // [U][N][128]
     const uint32_t* __restrict__ bitmask,  // [B*Hq][Nw]
     const float* __restrict__ lnu_tab,     // [kLnuTable + 1]
-    int Hq, int Hkv, int N, int K, int Tth, float scale, int split_len, int nsplit,
+    int Hq, int Hkv, int N, int P, int K, int Tth, float scale, int split_len, int nsplit,
     int exact_head, int exact_tail, int exact_len, int nexact,
     float* __restrict__ partials) {        // [B*Hq][nsplit + nexact][130]
   __shared__ float2 tab2[kLnuTable];      // (g_j, g_{j+1} - g_j)
@@ -151,8 +151,8 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
   const int b = u / Hkv, g = u % Hkv;
   const int bh0 = b * Hq + g * G;
   const int Nw = (N + 31) >> 5;
-  const uint16_t* kb = keys + static_cast<size_t>(u) * N * kHeadDim;
-  const uint16_t* vb = values + static_cast<size_t>(u) * N * kHeadDim;
+  const uint16_t* kb = keys + static_cast<size_t>(u) * P * kHeadDim;
+  const uint16_t* vb = values + static_cast<size_t>(u) * P * kHeadDim;
   const bool k0 = (K == 0);
   const bool exact = s >= nsplit;          // a piece of the exact set
   const bool nolnu = k0 || exact;
@@ -438,14 +438,14 @@ hipError_t launch_attend_bf16(const DecodeArgs& a, hipStream_t stream) {
   const float* lt = a.lnu_table;
   if (G <= 4)
     return launch(kKAttend, attend_bf16_kernel<1>, grid, dim3(256), 0, stream, qp, kp, vp, bm, lt, a.Hq,
-                  a.Hkv, a.N, a.K, a.T, a.scale, a.split_len, a.nsplit, a.exact_head, a.exact_tail, a.exact_len, a.nexact,
+                  a.Hkv, a.N, a.P, a.K, a.T, a.scale, a.split_len, a.nsplit, a.exact_head, a.exact_tail, a.exact_len, a.nexact,
                   a.partials);
   if (G <= 8)
     return launch(kKAttend, attend_bf16_kernel<2>, grid, dim3(256), 0, stream, qp, kp, vp, bm, lt, a.Hq,
-                  a.Hkv, a.N, a.K, a.T, a.scale, a.split_len, a.nsplit, a.exact_head, a.exact_tail, a.exact_len, a.nexact,
+                  a.Hkv, a.N, a.P, a.K, a.T, a.scale, a.split_len, a.nsplit, a.exact_head, a.exact_tail, a.exact_len, a.nexact,
                   a.partials);
   return launch(kKAttend, attend_bf16_kernel<4>, grid, dim3(256), 0, stream, qp, kp, vp, bm, lt, a.Hq, a.Hkv,
-                a.N, a.K, a.T, a.scale, a.split_len, a.nsplit, a.exact_head, a.exact_tail, a.exact_len, a.nexact,
+                a.N, a.P, a.K, a.T, a.scale, a.split_len, a.nsplit, a.exact_head, a.exact_tail, a.exact_len, a.nexact,
                   a.partials);
 }
 

@@ -152,10 +152,10 @@ constexpr int kProjKeys = 256;                 // 64 keys per wave = 4 tiles of 
 // codes[u][l][n] for this workgroup's 256 keys.
 template <typename T, int KB>
 __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_codes_kernel(
-    const typename T::storage* __restrict__ keys,   // [U][N][128]
+    const typename T::storage* __restrict__ keys,   // [U][P][128]
     const typename T::storage* __restrict__ WT,     // [nslab * NCT * 16][128], permuted
-    uint16_t* __restrict__ codes,                   // [U][L][N]
-    int N, int L, int nslab) {
+    uint16_t* __restrict__ codes,                   // [U][L][P]
+    int N, int P, int n_first, int L, int nslab) {  // keys n_first .. N - 1
   using S = typename T::storage;
   constexpr ProjShape PS = proj_shape(KB);
   constexpr int NCT = PS.nct, TPG = PS.tpg, TPS = 4 * TPG;
@@ -171,11 +171,11 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
   __shared__ __attribute__((aligned(16))) uint16_t stg[2][TPS * kStgRow];
 
   const int u = blockIdx.y;
-  const int n0 = blockIdx.x * kProjKeys;
+  const int n0 = n_first + blockIdx.x * kProjKeys;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4;
-  const S* kb = keys + static_cast<size_t>(u) * N * kHeadDim;
-  uint16_t* cb = codes + static_cast<size_t>(u) * L * N;
+  const S* kb = keys + static_cast<size_t>(u) * P * kHeadDim;
+  uint16_t* cb = codes + static_cast<size_t>(u) * L * P;
 
   // key fragments (MFMA B operand): lane holds key lane & 15 of tile a, dims
   // [32 g, 32 g + 32)
@@ -230,8 +230,8 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
       const int t = slab_of(s) * TPS + r, key = n0 + k8;
       if (t < L) {
         const uint16_t* src = sb + r * kStgRow + k8;
-        uint16_t* dst = cb + static_cast<size_t>(t) * N + key;
-        if (key + 8 <= N && (N & 7) == 0) {
+        uint16_t* dst = cb + static_cast<size_t>(t) * P + key;
+        if (key + 8 <= N && (P & 7) == 0) {
           *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
         } else {
           for (int e = 0; e < 8; ++e)
@@ -242,10 +242,11 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
   }
 }
 
-// K = 0: every code is 0.
-__global__ void zero_codes_kernel(uint16_t* __restrict__ codes, size_t n) {
+// K = 0: every code is 0 (keys n_first .. N - 1 of every [U][L] row of pitch P).
+__global__ void zero_codes_kernel(uint16_t* __restrict__ codes, size_t rows, int n_first, int N, int P) {
   const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) codes[i] = 0;
+  const size_t w = static_cast<size_t>(N - n_first);
+  if (i < rows * w) codes[(i / w) * P + n_first + i % w] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -359,10 +360,10 @@ __device__ __forceinline__ void scan_counters(uint32_t* cnt, uint32_t* wave_tot)
 // region, reused at the end for the bucket starts [2^K] (16-bit).
 template <int NTHR>
 __global__ __launch_bounds__(NTHR, NTHR >= 256 ? 4 : 1) void chunk_sort_kernel(
-    const uint16_t* __restrict__ codes,   // [U][L][N]
-    int N, int K, int stride_log2, int nJ,
-    uint16_t* __restrict__ offsets,       // [U][L][nJ][2^K]
-    uint16_t* __restrict__ indices) {     // [U][L][N]
+    const uint16_t* __restrict__ codes,   // [U][L][P]
+    int N, int P, int K, int stride_log2, int nJP, int j0,   // chunks j0 + blockIdx.x
+    uint16_t* __restrict__ offsets,       // [U][L][nJP][2^K]
+    uint16_t* __restrict__ indices) {     // [U][L][P]
   constexpr int E = kSortE;
   extern __shared__ __attribute__((aligned(16))) uint32_t smem32[];
   __shared__ uint32_t wave_tot[NTHR / 64];
@@ -372,7 +373,7 @@ __global__ __launch_bounds__(NTHR, NTHR >= 256 ? 4 : 1) void chunk_sort_kernel(
   // once every thread has read its ranks (barriers on both sides)
   uint32_t* cnt = smem32;                       // [16][NTHR]
   uint32_t* buf = smem32;                       // slot(position): code << 16 | key
-  const int j = blockIdx.x;
+  const int j = j0 + blockIdx.x;
   const size_t table = blockIdx.y;              // u * L + l
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = 1 << K;
@@ -380,12 +381,12 @@ __global__ __launch_bounds__(NTHR, NTHR >= 256 ? 4 : 1) void chunk_sort_kernel(
   const int clen = min(1 << stride_log2, N - cbeg);
   const int p0 = tid * E;
   const bool full = p0 + E <= clen;
-  const bool vec = ((table * N) & 7) == 0;      // the chunk's codes are 16-byte aligned
+  const bool vec = ((table * P) & 7) == 0;      // the chunk's codes are 16-byte aligned
 
   // this thread's E positions, straight from the codes
   uint32_t e[E];
   {
-    const uint16_t* cd = codes + table * N + cbeg + p0;
+    const uint16_t* cd = codes + table * P + cbeg + p0;
     if (full && vec) {
       const uint4* c4 = reinterpret_cast<const uint4*>(cd);
 #pragma unroll
@@ -452,7 +453,7 @@ __global__ __launch_bounds__(NTHR, NTHR >= 256 ? 4 : 1) void chunk_sort_kernel(
   // of contiguous index array per store, as streaming stores: the tables are
   // read by a later decode, not by anything that runs while they would still
   // be in the cache.  (K = 0 sorts nothing: thread t writes its own run.)
-  uint16_t* out = indices + table * N + cbeg;
+  uint16_t* out = indices + table * P + cbeg;
   if (passes > 0) {
     for (int c = tid; c * 8 < clen; c += NTHR) {
       const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(buf + slot(8 * c));
@@ -489,7 +490,7 @@ __global__ __launch_bounds__(NTHR, NTHR >= 256 ? 4 : 1) void chunk_sort_kernel(
     prev = c;
   }
   __syncthreads();
-  uint16_t* off = offsets + (table * nJ + j) * nb;
+  uint16_t* off = offsets + (table * nJP + j) * nb;
   // thread t owns buckets [t bpt, (t + 1) bpt); suffix minimum across threads
   // through the wave (reversed lane order) and the wave totals
   const int bpt = (nb + nthr - 1) / nthr;
@@ -529,62 +530,64 @@ static hipError_t launch_chunk_sort(const BuildArgs& a, hipStream_t stream) {
   const size_t lds = chunk_sort_lds_bytes(a.stride_log2, a.K);
   hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(chunk_sort_kernel<NTHR>), lds);
   if (e != hipSuccess) return e;
-  return launch(kKChunkSort, chunk_sort_kernel<NTHR>, dim3(a.nJ, a.U * a.L), dim3(NTHR),
-                static_cast<unsigned>(lds), stream, static_cast<const uint16_t*>(a.codes), a.N, a.K, a.stride_log2,
-                a.nJ, a.offsets, a.indices);
+  return launch(kKChunkSort, chunk_sort_kernel<NTHR>, dim3(a.nJ - a.j0, a.U * a.L), dim3(NTHR),
+                static_cast<unsigned>(lds), stream, static_cast<const uint16_t*>(a.codes), a.N, a.P, a.K,
+                a.stride_log2, a.nJP, a.j0, a.offsets, a.indices);
 }
 
 // ---------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------
 template <typename T, int KB>
-static hipError_t launch_project_k(const void* keys, const void* WT, uint16_t* codes, int U, int N, int L,
-                                   int nslab, hipStream_t stream) {
+static hipError_t launch_project_k(const BuildArgs& a, int nslab, hipStream_t stream) {
   using S = typename T::storage;
-  return launch(kKProject, project_codes_kernel<T, KB>, dim3((N + kProjKeys - 1) / kProjKeys, U),
-                dim3(kProjThreads), 0, stream, static_cast<const S*>(keys), static_cast<const S*>(WT), codes, N,
-                L, nslab);
+  const int n_first = a.j0 << a.stride_log2;
+  return launch(kKProject, project_codes_kernel<T, KB>, dim3((a.N - n_first + kProjKeys - 1) / kProjKeys, a.U),
+                dim3(kProjThreads), 0, stream, static_cast<const S*>(a.keys), static_cast<const S*>(a.wt), a.codes,
+                a.N, a.P, n_first, a.L, nslab);
 }
 
 template <typename T>
-static hipError_t launch_project(const void* keys, const void* W, void* WT, uint16_t* codes,
-                                 int U, int N, int K, int L, hipStream_t stream) {
+static hipError_t launch_project(const BuildArgs& a, hipStream_t stream) {
   using S = typename T::storage;
+  const int K = a.K, L = a.L;
   if (K == 0) {
-    const size_t n = static_cast<size_t>(U) * L * N;
+    const int n_first = a.j0 << a.stride_log2;
+    const size_t rows = static_cast<size_t>(a.U) * L;
+    const size_t n = rows * static_cast<size_t>(a.N - n_first);
     return launch(kKProject, zero_codes_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
-                  codes, n);
+                  a.codes, rows, n_first, a.N, a.P);
   }
   const ProjShape ps = proj_shape(K);
   const int rows = proj_wt_rows(K, L);
   const int nslab = rows / (ps.nct * 16);
   hipError_t e = launch(kKTransposeW, transpose_w_kernel<T>, dim3((rows * kHeadDim + 255) / 256), dim3(256), 0,
-                        stream, static_cast<const S*>(W), static_cast<S*>(WT), K, L, ps.nct, ps.tpg, rows);
+                        stream, static_cast<const S*>(a.W), static_cast<S*>(a.wt), K, L, ps.nct, ps.tpg, rows);
   if (e != hipSuccess) return e;
   switch (K) {
-    case 1: return launch_project_k<T, 1>(keys, WT, codes, U, N, L, nslab, stream);
-    case 2: return launch_project_k<T, 2>(keys, WT, codes, U, N, L, nslab, stream);
-    case 3: return launch_project_k<T, 3>(keys, WT, codes, U, N, L, nslab, stream);
-    case 4: return launch_project_k<T, 4>(keys, WT, codes, U, N, L, nslab, stream);
-    case 5: return launch_project_k<T, 5>(keys, WT, codes, U, N, L, nslab, stream);
-    case 6: return launch_project_k<T, 6>(keys, WT, codes, U, N, L, nslab, stream);
-    case 7: return launch_project_k<T, 7>(keys, WT, codes, U, N, L, nslab, stream);
-    case 8: return launch_project_k<T, 8>(keys, WT, codes, U, N, L, nslab, stream);
-    case 9: return launch_project_k<T, 9>(keys, WT, codes, U, N, L, nslab, stream);
-    case 10: return launch_project_k<T, 10>(keys, WT, codes, U, N, L, nslab, stream);
-    case 11: return launch_project_k<T, 11>(keys, WT, codes, U, N, L, nslab, stream);
-    case 12: return launch_project_k<T, 12>(keys, WT, codes, U, N, L, nslab, stream);
-    case 13: return launch_project_k<T, 13>(keys, WT, codes, U, N, L, nslab, stream);
-    case 14: return launch_project_k<T, 14>(keys, WT, codes, U, N, L, nslab, stream);
-    case 15: return launch_project_k<T, 15>(keys, WT, codes, U, N, L, nslab, stream);
+    case 1: return launch_project_k<T, 1>(a, nslab, stream);
+    case 2: return launch_project_k<T, 2>(a, nslab, stream);
+    case 3: return launch_project_k<T, 3>(a, nslab, stream);
+    case 4: return launch_project_k<T, 4>(a, nslab, stream);
+    case 5: return launch_project_k<T, 5>(a, nslab, stream);
+    case 6: return launch_project_k<T, 6>(a, nslab, stream);
+    case 7: return launch_project_k<T, 7>(a, nslab, stream);
+    case 8: return launch_project_k<T, 8>(a, nslab, stream);
+    case 9: return launch_project_k<T, 9>(a, nslab, stream);
+    case 10: return launch_project_k<T, 10>(a, nslab, stream);
+    case 11: return launch_project_k<T, 11>(a, nslab, stream);
+    case 12: return launch_project_k<T, 12>(a, nslab, stream);
+    case 13: return launch_project_k<T, 13>(a, nslab, stream);
+    case 14: return launch_project_k<T, 14>(a, nslab, stream);
+    case 15: return launch_project_k<T, 15>(a, nslab, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream) {
   hipError_t e = (a.dtype == 1)
-      ? launch_project<BF16>(a.keys, a.W, a.wt, a.codes, a.U, a.N, a.K, a.L, stream)
-      : launch_project<F32>(a.keys, a.W, a.wt, a.codes, a.U, a.N, a.K, a.L, stream);
+      ? launch_project<BF16>(a, stream)
+      : launch_project<F32>(a, stream);
   if (e != hipSuccess) return e;
   switch (sort_threads(a.stride_log2)) {
     case 64: return launch_chunk_sort<64>(a, stream);

@@ -191,9 +191,9 @@ constexpr int kCountUnroll = 8;   // index loads each thread keeps in flight
 
 __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
     const uint16_t* __restrict__ qcodes,   // [BH][L]
-    const uint16_t* __restrict__ indices,  // [U][L][N] chunk-major, chunk-relative key indices
-    const uint16_t* __restrict__ offsets,  // [U][L][nJ][2^K] bucket starts inside each chunk
-    int Hq, int Hkv, int N, int K, int L, int T, int stride_log2, int nJ,
+    const uint16_t* __restrict__ indices,  // [U][L][P] chunk-major, chunk-relative key indices
+    const uint16_t* __restrict__ offsets,  // [U][L][nJP][2^K] bucket starts inside each chunk
+    int Hq, int Hkv, int N, int P, int K, int L, int T, int stride_log2, int nJ, int nJP,
     uint32_t* __restrict__ bitmask,        // [BH][Nw]
     int32_t* __restrict__ chunk_nsel,      // [BH][nJ]
     uint8_t* __restrict__ counts,          // optional [BH][N]
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
   int len = 0;
   if (tid < L) {
     const int qc = qcodes[static_cast<size_t>(bh) * L + tid];
-    const uint16_t* op = offsets + ((static_cast<size_t>(u) * L + tid) * nJ + J) * nb + qc;
+    const uint16_t* op = offsets + ((static_cast<size_t>(u) * L + tid) * nJP + J) * nb + qc;
     // clamped into the chunk: tables that do not match the stride cannot
     // send the walk outside the chunk's region
     const int s0 = min(static_cast<int>(op[0]), clen);
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
   constexpr int kWaves = kCountThreads / 64;
   const int per = ((total + kWaves - 1) / kWaves + 63) & ~63;
   const int wstart = wave * per, wend = min(total, wstart + per);
-  const uint16_t* ib = indices + static_cast<size_t>(u) * L * N;
+  const uint16_t* ib = indices + static_cast<size_t>(u) * L * P;
   int l = 0;                                      // last segment starting at or before wstart
   {
     int lo = 0, hi = L - 1;
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
       loc[k] = -1;
       if (v < wend) {
         while (v >= seg_v[l + 1]) ++l;
-        loc[k] = ib[static_cast<size_t>(l) * N + seg_start[l] + (v - seg_v[l])];
+        loc[k] = ib[static_cast<size_t>(l) * P + seg_start[l] + (v - seg_v[l])];
       }
     }
 #pragma unroll
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
     const typename T::storage* __restrict__ values,  // [U][N][128]
     const uint32_t* __restrict__ bitmask,            // [BH][Nw]
     const float* __restrict__ lnu_tab,               // [kLnuTable + 1]
-    int Hq, int Hkv, int N, int K, int Tth, float scale, int split_len, int nsplit,
+    int Hq, int Hkv, int N, int P, int K, int Tth, float scale, int split_len, int nsplit,
     int exact_head, int exact_tail, int exact_len, int nexact,
     float* __restrict__ partials) {                  // [BH][nsplit + nexact][130]
   using S = typename T::storage;
@@ -395,8 +395,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
   const int b = u / Hkv, g = u % Hkv;
   const int bh0 = b * Hq + g * G;
   const int Nw = (N + 31) >> 5;
-  const S* kb = keys + static_cast<size_t>(u) * N * kHeadDim;
-  const S* vb = values + static_cast<size_t>(u) * N * kHeadDim;
+  const S* kb = keys + static_cast<size_t>(u) * P * kHeadDim;
+  const S* vb = values + static_cast<size_t>(u) * P * kHeadDim;
   const bool k0 = (K == 0);
   const bool exact = s >= nsplit;     // a piece of the exact set (all heads, u = 1)
   const bool nolnu = k0 || exact;
@@ -650,7 +650,7 @@ static hipError_t launch_attend(const DecodeArgs& a, hipStream_t stream) {
   return launch(kKAttend, attend_kernel<T, GM>, dim3(a.nsplit + a.nexact, a.B * a.Hkv), dim3(kAttThreads), 0, stream,
                 static_cast<const S*>(a.q), static_cast<const S*>(a.keys), static_cast<const S*>(a.values),
                 static_cast<const uint32_t*>(a.bitmask), static_cast<const float*>(a.lnu_table), a.Hq, a.Hkv,
-                a.N, a.K, a.T, a.scale, a.split_len, a.nsplit, a.exact_head, a.exact_tail, a.exact_len, a.nexact,
+                a.N, a.P, a.K, a.T, a.scale, a.split_len, a.nsplit, a.exact_head, a.exact_tail, a.exact_len, a.nexact,
                 a.partials);
 }
 
@@ -671,7 +671,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   e = launch(kKCountSelect, count_select_kernel, dim3(a.nJ, BH), dim3(kCountThreads),
              static_cast<unsigned>(lds), stream, static_cast<const uint16_t*>(a.qcodes),
-             a.indices, a.offsets, a.Hq, a.Hkv, a.N, a.K, a.L, a.T, a.stride_log2, a.nJ, a.bitmask,
+             a.indices, a.offsets, a.Hq, a.Hkv, a.N, a.P, a.K, a.L, a.T, a.stride_log2, a.nJ, a.nJP, a.bitmask,
              a.chunk_nsel, a.counts, a.exact_head, a.exact_tail);
   if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;

@@ -88,8 +88,13 @@ DecodeLayout decode_layout(int B, int Hq, int Hkv, int N, int L, const Geometry&
   w.chunk_nsel = off; off = align_up(off + BH * g.nJ * sizeof(int32_t));
   w.lnu = off;        off = align_up(off + (lsh::kLnuTable + 1) * sizeof(float));
   // one partial per head and context split, plus the exact set's pieces
+  // partial slots: nsplit <= min(ceil(N / 256), ceil(512 / units)), a bound
+  // that grows with N, so the workspace size at a cache's capacity covers
+  // every shorter length; plus the exact set's pieces
+  const long long slots = std::max<long long>(
+      w.nsplit, std::min((static_cast<long long>(N) + 255) / 256, (511 + units) / units));
   w.partials = off;
-  off = align_up(off + BH * (w.nsplit + lsh::kMaxExactSplits) * lsh::kPartialStride * sizeof(float));
+  off = align_up(off + BH * static_cast<size_t>(slots + lsh::kMaxExactSplits) * lsh::kPartialStride * sizeof(float));
   w.total = off;
   return w;
 }
@@ -219,15 +224,17 @@ size_t lsh_build_workspace_size(int B, int Hkv, int N, int d, int K, int L, int 
   return build_layout(B, Hkv, N, L, dtype, g, true).total;
 }
 
-lsh_status lsh_build_tables(const void* keys, const void* W, int B, int Hkv, int N, int d, int K, int L,
-                            int stride, int dtype, uint16_t* offsets, uint16_t* indices, uint16_t* key_codes,
-                            void* workspace, size_t workspace_bytes, void* stream) {
-  Geometry g;
-  lsh_status st = check_common(B, Hkv, N, d, K, L, stride, dtype, &g);
+lsh_status lsh_update_tables(const void* keys, const void* W, int B, int Hkv, int n_old, int n_new, int n_cap,
+                             int d, int K, int L, int stride, int dtype, uint16_t* offsets, uint16_t* indices,
+                             uint16_t* key_codes, void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry g;   // at capacity: the pitch of every per-key array and the offsets' chunk slots
+  lsh_status st = check_common(B, Hkv, n_cap, d, K, L, stride, dtype, &g);
   if (st != LSH_OK) return st;
+  if (n_old < 0 || n_old > n_new || n_new > n_cap) return LSH_ERR_INVALID_ARG;
   if (!keys || !offsets || !indices || !workspace || (K > 0 && !W)) return LSH_ERR_INVALID_ARG;
-  const BuildLayout w = build_layout(B, Hkv, N, L, dtype, g, key_codes == nullptr);
+  const BuildLayout w = build_layout(B, Hkv, n_cap, L, dtype, g, key_codes == nullptr);
   if (workspace_bytes < w.total) return LSH_ERR_WORKSPACE;
+  if (n_old == n_new) return LSH_OK;
   char* ws = static_cast<char*>(workspace);
   lsh::BuildArgs a;
   a.keys = keys;
@@ -237,13 +244,25 @@ lsh_status lsh_build_tables(const void* keys, const void* W, int B, int Hkv, int
   a.offsets = offsets;
   a.indices = indices;
   a.U = B * Hkv;
-  a.N = N;
+  a.N = n_new;
   a.K = K;
   a.L = L;
+  a.P = n_cap;
+  a.nJP = g.nJ;
+  // the chunk that key n_old falls into and every later one are rebuilt
+  // from their keys; earlier chunks are complete and left as they are
+  a.j0 = n_old >> g.stride_log2;
   a.stride_log2 = g.stride_log2;
-  a.nJ = g.nJ;
+  a.nJ = lsh_num_chunks(n_new, stride);
   a.dtype = dtype;
   return hip_status(lsh::launch_build(a, static_cast<hipStream_t>(stream)));
+}
+
+lsh_status lsh_build_tables(const void* keys, const void* W, int B, int Hkv, int N, int d, int K, int L,
+                            int stride, int dtype, uint16_t* offsets, uint16_t* indices, uint16_t* key_codes,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return lsh_update_tables(keys, W, B, Hkv, 0, N, N, d, K, L, stride, dtype, offsets, indices, key_codes,
+                           workspace, workspace_bytes, stream);
 }
 
 size_t lsh_decode_workspace_size(int B, int Hq, int Hkv, int N, int d, int K, int L, int stride) {
@@ -253,14 +272,17 @@ size_t lsh_decode_workspace_size(int B, int Hq, int Hkv, int N, int d, int K, in
   return decode_layout(B, Hq, Hkv, N, L, g).total;
 }
 
-lsh_status lsh_decode_attention_hybrid(const void* q, const void* keys, const void* values, const void* W,
+lsh_status lsh_decode_attention_cached(const void* q, const void* keys, const void* values, const void* W,
                                        const uint16_t* indices, const uint16_t* offsets, int B, int Hq, int Hkv,
-                                       int N, int d, int K, int L, int T, int stride, float sm_scale, int dtype,
-                                       int n_sink, int n_window, float* out, float* lse, int32_t* nsel,
+                                       int N, int n_cap, int d, int K, int L, int T, int stride, float sm_scale,
+                                       int dtype, int n_sink, int n_window, float* out, float* lse, int32_t* nsel,
                                        uint16_t* q_codes, uint8_t* counts, void* workspace, size_t workspace_bytes,
                                        void* stream) {
-  Geometry g;
+  Geometry g, gcap;
   lsh_status st = check_common(B, Hkv, N, d, K, L, stride, dtype, &g);
+  if (st != LSH_OK) return st;
+  if (n_cap < N) return LSH_ERR_INVALID_ARG;
+  st = check_common(B, Hkv, n_cap, d, K, L, stride, dtype, &gcap);
   if (st != LSH_OK) return st;
   if (Hq < 1 || Hq % Hkv != 0 || T < 1 || T > L || !std::isfinite(sm_scale)) return LSH_ERR_INVALID_ARG;
   if (n_sink < 0 || n_window < 0) return LSH_ERR_INVALID_ARG;
@@ -293,6 +315,8 @@ lsh_status lsh_decode_attention_hybrid(const void* q, const void* keys, const vo
   a.K = K;
   a.L = L;
   a.T = T;
+  a.P = n_cap;
+  a.nJP = gcap.nJ;
   a.stride_log2 = g.stride_log2;
   a.nJ = g.nJ;
   a.split_len = w.split_len;
@@ -309,6 +333,17 @@ lsh_status lsh_decode_attention_hybrid(const void* q, const void* keys, const vo
   a.exact_len = std::max(128, (per_piece + 127) / 128 * 128);
   a.nexact = (ne + a.exact_len - 1) / a.exact_len;
   return hip_status(lsh::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+lsh_status lsh_decode_attention_hybrid(const void* q, const void* keys, const void* values, const void* W,
+                                       const uint16_t* indices, const uint16_t* offsets, int B, int Hq, int Hkv,
+                                       int N, int d, int K, int L, int T, int stride, float sm_scale, int dtype,
+                                       int n_sink, int n_window, float* out, float* lse, int32_t* nsel,
+                                       uint16_t* q_codes, uint8_t* counts, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  return lsh_decode_attention_cached(q, keys, values, W, indices, offsets, B, Hq, Hkv, N, N, d, K, L, T, stride,
+                                     sm_scale, dtype, n_sink, n_window, out, lse, nsel, q_codes, counts, workspace,
+                                     workspace_bytes, stream);
 }
 
 lsh_status lsh_decode_attention(const void* q, const void* keys, const void* values, const void* W,

@@ -8,25 +8,30 @@
 
 namespace lsh {
 
+// Arrays over keys have a row pitch P >= N (the capacity of a growing
+// cache); offsets have nJP >= nJ chunk slots per table.  The build covers the
+// keys of chunks j0 .. nJ - 1 (keys j0 * stride .. N - 1): j0 = 0 is a full
+// build, a larger j0 rebuilds only the chunks that new keys fall into.
 struct BuildArgs {
-  const void* keys;      // [U][N][128]
+  const void* keys;      // [U][P][128]
   const void* W;         // [128][L*K]
   void* wt;              // workspace: [proj_wt_rows(K, L)][128]
-  uint16_t* codes;       // [U][L][N] (caller's key_codes or workspace)
-  uint16_t* offsets;     // [U][L][nJ][2^K] bucket starts inside each chunk
-  uint16_t* indices;     // [U][L][N] chunk-major, key - chunk start
+  uint16_t* codes;       // [U][L][P] (caller's key_codes or workspace)
+  uint16_t* offsets;     // [U][L][nJP][2^K] bucket starts inside each chunk
+  uint16_t* indices;     // [U][L][P] chunk-major, key - chunk start
   int U, N, K, L;
+  int P, nJP, j0;
   int stride_log2, nJ;
   int dtype;             // 0 = f32, 1 = bf16
 };
 
 struct DecodeArgs {
   const void* q;         // [B][Hq][128]
-  const void* keys;      // [U][N][128]
-  const void* values;    // [U][N][128]
+  const void* keys;      // [U][P][128], keys 0 .. N - 1 valid
+  const void* values;    // [U][P][128]
   const void* W;         // [128][L*K]
-  const uint16_t* indices;   // [U][L][N] chunk-major
-  const uint16_t* offsets;   // [U][L][nJ][2^K]
+  const uint16_t* indices;   // [U][L][P] chunk-major
+  const uint16_t* offsets;   // [U][L][nJP][2^K]
   uint16_t* qcodes;      // [B*Hq][L]
   uint32_t* bitmask;     // [B*Hq][Nw]
   int32_t* chunk_nsel;   // [B*Hq][nJ]
@@ -37,6 +42,7 @@ struct DecodeArgs {
   int32_t* nsel;         // optional [B*Hq]
   uint8_t* counts;       // optional [B*Hq][N]
   int B, Hq, Hkv, N, K, L, T;
+  int P, nJP;                // row pitch of keys / values / indices, chunk slots of offsets
   int stride_log2, nJ;
   int split_len, nsplit;
   float scale;

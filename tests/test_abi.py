@@ -151,6 +151,67 @@ def test_hybrid_rejects(n_sink, n_window, kw, status):
     assert _hybrid(n_sink, n_window, **kw) == status
 
 
+def _update(**kw):
+    a = dict(keys=1, W=1, B=1, Hkv=1, n_old=100, n_new=200, n_cap=4096, d=128, K=8, L=32, stride=1024, dtype=1,
+             offsets=1, indices=1, codes=None, ws=1, ws_bytes=1 << 40)
+    a.update(kw)
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    return lsh.lib().lsh_update_tables(p(a["keys"]), p(a["W"]), a["B"], a["Hkv"], a["n_old"], a["n_new"],
+                                       a["n_cap"], a["d"], a["K"], a["L"], a["stride"], a["dtype"],
+                                       p(a["offsets"]), p(a["indices"]), p(a["codes"]), p(a["ws"]),
+                                       a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_old=-1), lsh.LSH_ERR_INVALID_ARG),
+    (dict(n_old=300), lsh.LSH_ERR_INVALID_ARG),          # n_old > n_new
+    (dict(n_new=5000), lsh.LSH_ERR_INVALID_ARG),         # n_new > n_cap
+    (dict(n_cap=0, n_old=0, n_new=0), lsh.LSH_ERR_INVALID_ARG),
+    (dict(keys=None), lsh.LSH_ERR_INVALID_ARG),
+    (dict(stride=100), lsh.LSH_ERR_INVALID_ARG),
+    (dict(d=64), lsh.LSH_ERR_UNSUPPORTED),
+    (dict(ws_bytes=16), lsh.LSH_ERR_WORKSPACE),
+    (dict(n_old=200), lsh.LSH_OK),                       # nothing new: launches nothing
+])
+def test_update_rejects(kw, status):
+    assert _update(**kw) == status
+
+
+def _cached(**kw):
+    a = dict(q=1, keys=1, values=1, W=1, indices=1, offsets=1, B=1, Hq=4, Hkv=1, N=3000, n_cap=4096, d=128, K=8,
+             L=32, T=2, stride=1024, scale=0.088, dtype=1, n_sink=0, n_window=0, out=1, ws=1, ws_bytes=1 << 40)
+    a.update(kw)
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    return lsh.lib().lsh_decode_attention_cached(
+        p(a["q"]), p(a["keys"]), p(a["values"]), p(a["W"]), p(a["indices"]), p(a["offsets"]),
+        a["B"], a["Hq"], a["Hkv"], a["N"], a["n_cap"], a["d"], a["K"], a["L"], a["T"], a["stride"],
+        ctypes.c_float(a["scale"]), a["dtype"], a["n_sink"], a["n_window"], p(a["out"]), None, None, None, None,
+        p(a["ws"]), a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_cap=2999), lsh.LSH_ERR_INVALID_ARG),         # N > n_cap
+    (dict(N=0), lsh.LSH_ERR_INVALID_ARG),
+    (dict(n_sink=-2), lsh.LSH_ERR_INVALID_ARG),
+    (dict(values=None), lsh.LSH_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), lsh.LSH_ERR_INVALID_ARG),
+    (dict(ws_bytes=100), lsh.LSH_ERR_WORKSPACE),
+])
+def test_cached_decode_rejects(kw, status):
+    assert _cached(**kw) == status
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,L,stride", [(1, 32, 4, 150, 8192), (1, 32, 8, 150, 1024), (64, 32, 8, 150, 8192),
+                                                (2, 6, 2, 20, 256)])
+def test_decode_workspace_grows_with_n(B, Hq, Hkv, L, stride):
+    # the size at a cache's capacity covers every shorter prefix
+    prev = 0
+    for N in list(range(1, 3000, 97)) + list(range(3000, 300000, 4093)):
+        w = lsh.lsh_decode_workspace_size(B, Hq, Hkv, N, 128, 10, L, stride)
+        assert w >= prev, (N, w, prev)
+        prev = w
+
+
 def test_binding_raises_without_gpu_work():
     with pytest.raises(lsh.LshError) as e:
         lsh.lib()  # loads fine
