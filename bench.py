@@ -309,6 +309,39 @@ def main():
         "kernels": {k: v["avg_us"] for k, v in hk.items()},
     }
 
+    # multi-step decode over a growing cache: each step appends one key (the
+    # chunk it falls into is rebuilt) and runs the hybrid decode over the
+    # keys held.  The cache starts half-way into its last chunk, the average
+    # rebuild size; the tables of the first chunks stay as built.
+    c0 = copies[0]
+    n_start = max(1, N - stride // 2)
+    lsh.lsh_timing_begin()
+    ta0 = time.perf_counter()
+    for i in range(args.steps):
+        n = n_start + i
+        lsh.lsh_update_tables(c0["keys"], c0["W"], K, L, stride, n, n + 1, c0["offsets"], c0["indices"], None,
+                              c0["bws"])
+        lsh.lsh_decode_attention_cached(c0["q"], c0["keys"], c0["values"], c0["W"], c0["indices"], c0["offsets"],
+                                        n + 1, K, L, T, stride, cfg.scale, args.hybrid_sink, args.hybrid_window,
+                                        c0["out"], c0["lse"], c0["nsel"], None, None, c0["dws"])
+    torch.cuda.synchronize()
+    ta1 = time.perf_counter()
+    atimes = lsh.lsh_timing_end()
+    # back to the tables of all N keys
+    lsh.lsh_update_tables(c0["keys"], c0["W"], K, L, stride, n_start, N, c0["offsets"], c0["indices"], None,
+                          c0["bws"])
+    torch.cuda.synchronize()
+    ak = kernel_table(atimes)
+    append_ms = sum(v[0] for v in atimes.values()) / args.steps
+    append_decode = {
+        "keys_held": [n_start + 1, n_start + args.steps],
+        "ms": round(append_ms, 5),
+        "wall_ms_per_step": round((ta1 - ta0) * 1e3 / args.steps, 5),
+        "update_ms": round(sum(atimes[k][0] for k in BUILD_KERNELS) / args.steps, 5),
+        "qh_per_s": round(qh / (append_ms * 1e-3), 1),
+        "kernels": {k: v["avg_us"] for k, v in ak.items()},
+    }
+
     build_ms = sum(ktimes[k][0] for k in BUILD_KERNELS) / args.steps
     decode_ms = sum(ktimes[k][0] for k in DECODE_KERNELS) / args.steps
     dec_bytes = E_idx * 2 + qh * L * 8 + kv_bytes + qh * d * (esz + 4) + d * L * K * esz
@@ -352,6 +385,7 @@ def main():
             "kernels": kernels,
             "decode_steady": decode_steady,
             "decode_hybrid_steady": decode_hybrid_steady,
+            "append_decode_steady": append_decode,
         },
     }
 

@@ -11,6 +11,8 @@
 //   chunk_sort      per (table, key chunk): a stable LSD radix sort of the
 //                   chunk's keys by code into the chunk's own region of the
 //                   index array, with the chunk's bucket offsets
+#include <algorithm>
+
 #include "lsh_device.h"
 #include "lsh_kernels.h"
 
@@ -155,7 +157,8 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
     const typename T::storage* __restrict__ keys,   // [U][P][128]
     const typename T::storage* __restrict__ WT,     // [nslab * NCT * 16][128], permuted
     uint16_t* __restrict__ codes,                   // [U][L][P]
-    int N, int P, int n_first, int L, int nslab) {  // keys n_first .. N - 1
+    int N, int P, int n_first, int L, int nslab,    // keys n_first .. N - 1
+    int spz) {                                      // slabs per blockIdx.z
   using S = typename T::storage;
   constexpr ProjShape PS = proj_shape(KB);
   constexpr int NCT = PS.nct, TPG = PS.tpg, TPS = 4 * TPG;
@@ -201,17 +204,21 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
                                           (chunk % kChunksPerRow) * (16 / T::bytes)]) = pre[k];
     }
   };
-  // workgroups walk the slabs from different starting points, so that the
-  // CUs sharing an L2 do not all read the same slab of WT at once
-  const int s0 = static_cast<int>((blockIdx.x + 5u * blockIdx.y) % static_cast<unsigned>(nslab));
-  auto slab_of = [&](int s) { return s0 + s < nslab ? s0 + s : s0 + s - nslab; };
+  // this workgroup's slabs: zb .. zb + ns - 1 (all of them unless a short
+  // key range is spread over more workgroups by slab).  Workgroups walk
+  // their slabs from different starting points, so that the CUs sharing an
+  // L2 do not all read the same slab of WT at once
+  const int zb = static_cast<int>(blockIdx.z) * spz;
+  const int ns = min(spz, nslab - zb);
+  const int s0 = static_cast<int>((blockIdx.x + 5u * blockIdx.y) % static_cast<unsigned>(ns));
+  auto slab_of = [&](int s) { return zb + (s0 + s < ns ? s0 + s : s0 + s - ns); };
   fetch(slab_of(0));
   stash(0);
   __syncthreads();
 
-  for (int s = 0; s < nslab; ++s) {
+  for (int s = 0; s < ns; ++s) {
     const int buf = s & 1;
-    if (s + 1 < nslab) fetch(slab_of(s + 1));
+    if (s + 1 < ns) fetch(slab_of(s + 1));
     uint32_t sg[4];
     slab_signs<T, NCT>(&wt[buf][(lane & 15) * kRow + (lane >> 4) * 32], kRow, A, sg);
     // codes of tables slab_of(s) * TPS + g * TPG + tt, staged per table row
@@ -222,7 +229,7 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
       for (int tt = 0; tt < TPG; ++tt)
         sb[(g * TPG + tt) * kStgRow + wave * 64 + a * 16 + (lane & 15)] =
             static_cast<uint16_t>((sg[a] >> (tt * KB)) & kMask);
-    if (s + 1 < nslab) stash(buf ^ 1);
+    if (s + 1 < ns) stash(buf ^ 1);
     __syncthreads();
     // write-out: 8 consecutive keys of one table per 16-byte piece
     for (int c = tid; c < TPS * (kProjKeys / 8); c += kProjThreads) {
@@ -542,9 +549,16 @@ template <typename T, int KB>
 static hipError_t launch_project_k(const BuildArgs& a, int nslab, hipStream_t stream) {
   using S = typename T::storage;
   const int n_first = a.j0 << a.stride_log2;
-  return launch(kKProject, project_codes_kernel<T, KB>, dim3((a.N - n_first + kProjKeys - 1) / kProjKeys, a.U),
-                dim3(kProjThreads), 0, stream, static_cast<const S*>(a.keys), static_cast<const S*>(a.wt), a.codes,
-                a.N, a.P, n_first, a.L, nslab);
+  const int gx = (a.N - n_first + kProjKeys - 1) / kProjKeys;
+  // a short key range (a table update) has too few key blocks to fill the
+  // chip: its slabs are then dealt over up to ~1024 workgroups in all
+  const long long gxy = static_cast<long long>(gx) * a.U;
+  const int zwant = static_cast<int>(std::min<long long>(nslab, std::max<long long>(1, (1023 + gxy) / gxy)));
+  const int spz = (nslab + zwant - 1) / zwant;
+  const int gz = (nslab + spz - 1) / spz;
+  return launch(kKProject, project_codes_kernel<T, KB>, dim3(gx, a.U, gz), dim3(kProjThreads), 0, stream,
+                static_cast<const S*>(a.keys), static_cast<const S*>(a.wt), a.codes, a.N, a.P, n_first, a.L,
+                nslab, spz);
 }
 
 template <typename T>
