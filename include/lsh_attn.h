@@ -128,35 +128,47 @@ lsh_status lsh_build_tables(const void* keys, const void* W,
  * construction) and say nothing of the keys a decode appends; MAC-Attention
  * updates its caches for the next token inside the decode step
  * ("MAC-Attention" README, "How It Works").  Here the tables of a cache with
- * room for n_cap keys per (sequence, kv head) hold its first n keys, and
+ * room for n_cap keys per (sequence, kv head) hold its first n_b keys
+ * (sequence b), and
  *
- *   after lsh_update_tables(n_old, n_new), the tables are exactly those that
- *   lsh_build_tables would produce from keys 0 .. n_new - 1
+ *   after lsh_update_tables, the tables of sequence b are exactly those that
+ *   lsh_build_tables would produce from its keys 0 .. new_b - 1
  *
  * (same codes, buckets, order and offsets), laid out with the pitch n_cap:
  *
- * keys     [B, Hkv, n_cap, d] dtype     keys 0 .. n_new - 1 written
+ * keys     [B, Hkv, n_cap, d] dtype     keys 0 .. new_b - 1 written
+ * W        [d, L*K], or [Hkv, d, L*K] with w_per_head = 1 (kv head g hashes
+ *          with W[g]; queries of head h with W[h / G])
  * offsets  [B, Hkv, L, lsh_num_chunks(n_cap, stride), 2^K] uint16
- *                                       in/out: chunks j < n_old / stride are
- *                                       kept; the rest are rewritten
+ *                                       in/out: chunks j < old_b / stride are
+ *                                       kept; the rest up to new_b rewritten
  * indices  [B, Hkv, L, n_cap] uint16    in/out: positions below
- *                                       (n_old / stride) * stride are kept
+ *                                       (old_b / stride) * stride are kept
  * key_codes [B, Hkv, L, n_cap] uint16   optional out: codes of the keys from
- *                                       (n_old / stride) * stride on
+ *                                       (old_b / stride) * stride to new_b
+ * old_lens, new_lens [B] int32          optional (device): old_b, new_b per
+ *                                       sequence; when NULL every old_b =
+ *                                       n_old, every new_b = n_new
  * workspace                             lsh_build_workspace_size(.., n_cap, ..)
  *
- * (n_old / stride rounds down.)  The inputs must hold the tables of keys
- * 0 .. n_old - 1 built with the same W, K, L, stride and n_cap (n_old = 0:
- * nothing); keys of positions >= n_new are never read.  The call rebuilds the
- * chunks from the one holding key n_old to the last, reading their keys: one
- * new key per step costs one chunk of keys per (sequence, kv head).
- * 0 <= n_old <= n_new <= n_cap, else LSH_ERR_INVALID_ARG; n_old == n_new
- * launches nothing.  Size limits as for lsh_build_tables with N = n_cap.
- * lsh_build_tables(.., N, ..) is this call with n_old = 0, n_new = n_cap = N.
+ * (x / stride rounds down.)  The inputs must hold the tables of keys
+ * 0 .. old_b - 1 built with the same W, K, L, stride and n_cap (old_b = 0:
+ * nothing); keys of positions >= new_b are never read.  The call rebuilds the
+ * chunks from the one holding key old_b to the one holding key new_b - 1,
+ * reading their keys: one new key per step costs one chunk of keys per
+ * (sequence, kv head).  The scalars bound the arrays: n_old <= old_b <= new_b
+ * <= n_new, with device values clamped into that range (the launch covers the
+ * chunks of keys n_old .. n_new - 1).  0 <= n_old <= n_new <= n_cap and
+ * w_per_head in {0, 1}, else LSH_ERR_INVALID_ARG; n_old == n_new launches
+ * nothing.  Size limits as for lsh_build_tables with N = n_cap.
+ * lsh_build_tables(.., N, ..) is this call with n_old = 0, n_new = n_cap = N,
+ * no length arrays and a shared W.
  */
 lsh_status lsh_update_tables(const void* keys, const void* W,
                              int B, int Hkv, int n_old, int n_new, int n_cap,
+                             const int32_t* old_lens, const int32_t* new_lens,
                              int d, int K, int L, int stride, int dtype,
+                             int w_per_head,
                              uint16_t* offsets, uint16_t* indices,
                              uint16_t* key_codes,
                              void* workspace, size_t workspace_bytes,
@@ -234,22 +246,33 @@ lsh_status lsh_decode_attention_hybrid(const void* q, const void* keys,
                                        void* stream);
 
 /*
- * Decode over the first N keys of a cache with room for n_cap keys: the
- * hybrid decode above with keys, values [B, Hkv, n_cap, d] and tables of the
- * pitch lsh_update_tables uses (indices [B, Hkv, L, n_cap], offsets
- * [B, Hkv, L, lsh_num_chunks(n_cap, stride), 2^K]) holding keys 0 .. N - 1.
- * Keys and values from position N on are never read.  counts, when given, is
- * [B, Hq, N].  N <= n_cap, else LSH_ERR_INVALID_ARG.  The recent window is the
- * last n_window of the N keys.  Workspace: lsh_decode_workspace_size at N (or
- * at n_cap, which is never smaller).  lsh_decode_attention_hybrid is this call
- * with n_cap = N.
+ * Decode over a cache with room for n_cap keys: the hybrid decode above, for
+ * sequence b over its first len_b keys, with keys, values [B, Hkv, n_cap, d]
+ * and tables of the pitch lsh_update_tables uses (indices [B, Hkv, L, n_cap],
+ * offsets [B, Hkv, L, lsh_num_chunks(n_cap, stride), 2^K]) holding exactly
+ * those keys (built or updated to len_b).
+ *
+ * seq_lens [B] int32   optional (device): len_b, clamped into [0, N]; NULL:
+ *                      every len_b = N.  N is the longest; the launch covers N.
+ * w_per_head           W as in lsh_update_tables (0 shared, 1 per kv head).
+ * counts               when given, [B, Hq, N]; 0 for keys at or past len_b.
+ *
+ * Keys and values of sequence b from position len_b on are never read.  The
+ * exact set of sequence b is its first min(n_sink, len_b) keys and the last
+ * n_window of the rest (E of the hybrid decode with N = len_b); a sequence
+ * with len_b = 0 gets out = 0, lse = -inf, nsel = 0.  N <= n_cap and
+ * w_per_head in {0, 1}, else LSH_ERR_INVALID_ARG.  Workspace:
+ * lsh_decode_workspace_size at N (or at n_cap, which is never smaller).
+ * lsh_decode_attention_hybrid is this call with n_cap = N, no lengths and a
+ * shared W.
  */
 lsh_status lsh_decode_attention_cached(const void* q, const void* keys,
                                        const void* values, const void* W,
                                        const uint16_t* indices, const uint16_t* offsets,
                                        int B, int Hq, int Hkv, int N, int n_cap,
+                                       const int32_t* seq_lens,
                                        int d, int K, int L, int T, int stride,
-                                       float sm_scale, int dtype,
+                                       float sm_scale, int dtype, int w_per_head,
                                        int n_sink, int n_window,
                                        float* out, float* lse, int32_t* nsel,
                                        uint16_t* q_codes, uint8_t* counts,

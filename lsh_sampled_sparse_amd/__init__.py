@@ -63,7 +63,8 @@ def lib():
         L.lsh_build_tables.restype = _i
         L.lsh_build_tables.argtypes = [_p, _p] + [_i] * 8 + [_p, _p, _p, _p, _sz, _p]
         L.lsh_update_tables.restype = _i
-        L.lsh_update_tables.argtypes = [_p, _p] + [_i] * 10 + [_p, _p, _p, _p, _sz, _p]
+        L.lsh_update_tables.argtypes = ([_p, _p] + [_i] * 5 + [_p, _p] + [_i] * 6
+                                        + [_p, _p, _p, _p, _sz, _p])
         L.lsh_decode_workspace_size.restype = _sz
         L.lsh_decode_workspace_size.argtypes = [_i] * 8
         L.lsh_decode_attention.restype = _i
@@ -73,8 +74,8 @@ def lib():
         L.lsh_decode_attention_hybrid.argtypes = ([_p] * 6 + [_i] * 9 + [ctypes.c_float, _i, _i, _i]
                                                   + [_p] * 6 + [_sz, _p])
         L.lsh_decode_attention_cached.restype = _i
-        L.lsh_decode_attention_cached.argtypes = ([_p] * 6 + [_i] * 10 + [ctypes.c_float, _i, _i, _i]
-                                                  + [_p] * 6 + [_sz, _p])
+        L.lsh_decode_attention_cached.argtypes = ([_p] * 6 + [_i] * 5 + [_p] + [_i] * 5
+                                                  + [ctypes.c_float] + [_i] * 4 + [_p] * 6 + [_sz, _p])
         L.lsh_kernel_count.restype = _i
         L.lsh_kernel_count.argtypes = []
         L.lsh_kernel_name.restype = ctypes.c_char_p
@@ -152,24 +153,30 @@ def lsh_build_tables(keys, W, K, L, stride, offsets, indices, key_codes=None, wo
         _ptr(workspace), workspace.numel(), _stream(keys.device)))
 
 
-def lsh_update_tables(keys, W, K, L, stride, n_old, n_new, offsets, indices, key_codes=None, workspace=None):
+def lsh_update_tables(keys, W, K, L, stride, n_old, n_new, offsets, indices, key_codes=None, workspace=None,
+                      old_lens=None, new_lens=None):
     """Marshal tensors to ``lsh_update_tables``; keys [B, Hkv, n_cap, d] is the
-    cache, offsets / indices are updated in place."""
+    cache, offsets / indices are updated in place.  W [d, L*K] is shared,
+    W [Hkv, d, L*K] is one per kv head; old_lens / new_lens are optional int32
+    device tensors [B] of per-sequence lengths."""
     B, Hkv, n_cap, d = keys.shape
     dt = _dtype_code(keys.dtype)
     if workspace is None:
         workspace = torch.empty(max(1, lsh_build_workspace_size(B, Hkv, n_cap, d, K, L, stride, dt)),
                                 dtype=torch.uint8, device=keys.device)
     _check(lib().lsh_update_tables(
-        _ptr(keys), _ptr(W), B, Hkv, int(n_old), int(n_new), n_cap, d, K, L, stride, dt,
+        _ptr(keys), _ptr(W), B, Hkv, int(n_old), int(n_new), n_cap, _ptr(old_lens), _ptr(new_lens),
+        d, K, L, stride, dt, 1 if W.dim() == 3 else 0,
         _ptr(offsets), _ptr(indices), _ptr(key_codes),
         _ptr(workspace), workspace.numel(), _stream(keys.device)))
 
 
 def lsh_decode_attention_cached(q, keys, values, W, indices, offsets, N, K, L, T, stride, sm_scale, n_sink,
-                                n_window, out, lse=None, nsel=None, q_codes=None, counts=None, workspace=None):
+                                n_window, out, lse=None, nsel=None, q_codes=None, counts=None, workspace=None,
+                                seq_lens=None):
     """Marshal tensors to ``lsh_decode_attention_cached``: keys / values
-    [B, Hkv, n_cap, d], of which the first N are attended."""
+    [B, Hkv, n_cap, d], of which the first N (or seq_lens[b], an int32 device
+    tensor [B]) are attended; W as in ``lsh_update_tables``."""
     B, Hq, d = q.shape
     _, Hkv, n_cap, _ = keys.shape
     dt = _dtype_code(keys.dtype)
@@ -178,7 +185,8 @@ def lsh_decode_attention_cached(q, keys, values, W, indices, offsets, N, K, L, T
                                 dtype=torch.uint8, device=keys.device)
     _check(lib().lsh_decode_attention_cached(
         _ptr(q), _ptr(keys), _ptr(values), _ptr(W), _ptr(indices), _ptr(offsets),
-        B, Hq, Hkv, int(N), n_cap, d, K, L, T, stride, ctypes.c_float(sm_scale), dt, int(n_sink), int(n_window),
+        B, Hq, Hkv, int(N), n_cap, _ptr(seq_lens), d, K, L, T, stride, ctypes.c_float(sm_scale), dt,
+        1 if W.dim() == 3 else 0, int(n_sink), int(n_window),
         _ptr(out), _ptr(lse), _ptr(nsel), _ptr(q_codes), _ptr(counts),
         _ptr(workspace), workspace.numel(), _stream(keys.device)))
 
@@ -278,7 +286,8 @@ def build_tables(keys, W, K, L, stride=None, return_codes=False):
 def alloc_tables(keys, K, L, stride=None, return_codes=False):
     """Empty tables for a key cache keys [B, Hkv, n_cap, d] that will grow to
     n_cap keys; fill them with ``update_tables``.  Returns the dict of
-    ``build_tables`` with the pitch n_cap and "n" = 0 keys held."""
+    ``build_tables`` with the pitch n_cap, "lens" (keys held per sequence,
+    all 0) and "n" (the longest)."""
     B, Hkv, n_cap, d = keys.shape
     if stride is None:
         stride = lsh_default_stride(n_cap, K)
@@ -286,22 +295,41 @@ def alloc_tables(keys, K, L, stride=None, return_codes=False):
     dev = keys.device
     res = {"offsets": torch.empty(B, Hkv, L, nch, 1 << K, dtype=torch.int16, device=dev),
            "indices": torch.empty(B, Hkv, L, n_cap, dtype=torch.int16, device=dev),
-           "stride": stride, "n": 0, "n_cap": n_cap}
+           "stride": stride, "n": 0, "n_cap": n_cap, "lens": [0] * B, "lens_dev": None}
     if return_codes:
         res["codes"] = torch.empty(B, Hkv, L, n_cap, dtype=torch.int16, device=dev)
     return res
 
 
+def _lens_tensor(lens, device):
+    return torch.tensor(lens, dtype=torch.int32, device=device)
+
+
 def update_tables(keys, W, tables, n_new, K, L, workspace=None):
     """Extend ``tables`` (from ``alloc_tables``) to hold keys 0 .. n_new - 1
-    of the cache ``keys``; afterwards they equal a build over those keys."""
+    of the cache ``keys``: n_new is one length for every sequence or a list
+    of B lengths.  Afterwards each sequence's tables equal a build over its
+    keys.  W [d, L*K] is shared by all heads, W [Hkv, d, L*K] one per kv head."""
     _require(keys, "keys")
     _require(W, "W", keys.dtype)
-    if keys.shape[2] != tables["n_cap"]:
+    B, Hkv, n_cap, d = keys.shape
+    if n_cap != tables["n_cap"]:
         raise ValueError("keys and tables disagree on the capacity")
-    lsh_update_tables(keys, W, K, L, tables["stride"], tables["n"], n_new, tables["offsets"], tables["indices"],
-                      tables.get("codes"), workspace)
-    tables["n"] = int(n_new)
+    if tuple(W.shape) not in ((d, L * K), (Hkv, d, L * K)):
+        raise ValueError(f"W must be [{d}, {L * K}] or [{Hkv}, {d}, {L * K}], got {tuple(W.shape)}")
+    old = list(tables["lens"])
+    new = [int(n_new)] * B if isinstance(n_new, int) else [int(x) for x in n_new]
+    if len(new) != B or any(nw < od or nw > n_cap for nw, od in zip(new, old)):
+        raise ValueError(f"new lengths {new} must lie between the held lengths {old} and {n_cap}")
+    uniform = len(set(old)) == 1 and len(set(new)) == 1
+    old_t = None if uniform else _lens_tensor(old, keys.device)
+    new_t = None if uniform else _lens_tensor(new, keys.device)
+    lsh_update_tables(keys, W, K, L, tables["stride"], min(old), max(new), tables["offsets"], tables["indices"],
+                      tables.get("codes"), workspace, old_t, new_t)
+    tables["lens"] = new
+    tables["n"] = max(new)
+    tables["lens_dev"] = None if len(set(new)) == 1 else (new_t if new_t is not None
+                                                          else _lens_tensor(new, keys.device))
     return tables
 
 
@@ -335,7 +363,7 @@ def decode_attention(q, keys, values, W, tables, K, L, T, sm_scale=None, return_
     if cached:
         lsh_decode_attention_cached(q, keys, values, W, tables["indices"], tables["offsets"], N, K, L, T,
                                     tables["stride"], sm_scale, n_sink, n_window, out, lse, nsel, qc, cnt,
-                                    workspace)
+                                    workspace, seq_lens=tables.get("lens_dev"))
     elif n_sink or n_window:
         lsh_decode_attention_hybrid(q, keys, values, W, tables["indices"], tables["offsets"], K, L, T,
                                     tables["stride"], sm_scale, n_sink, n_window, out, lse, nsel, qc, cnt,

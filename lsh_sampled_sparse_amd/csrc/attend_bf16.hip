@@ -19,8 +19,8 @@
 // The four waves' (max, sum, acc) states are merged through LDS into one
 // partial per query head and split, for the log-sum-exp merge that follows.
 // Workgroups past the context splits take the hybrid decode's exact set
-// (keys [0, exact_head) and [N - exact_tail, N), counted 0 .. ne - 1 across
-// both ranges), a piece of exact_len keys each: every key is taken for every
+// (for a sequence of n keys, keys [0, exact_head) and [n - exact_tail, n),
+// counted 0 .. ne - 1 across both ranges), a piece of exact_len keys each: every key is taken for every
 // head of the group and weighted 1 (u = 1), which is plain softmax attention
 // on the same tiles.
 #include <math.h>
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
     const uint32_t* __restrict__ bitmask,  // [B*Hq][Nw]
     const float* __restrict__ lnu_tab,     // [kLnuTable + 1]
     int Hq, int Hkv, int N, int P, int K, int Tth, float scale, int split_len, int nsplit,
-    int exact_head, int exact_tail, int exact_len, int nexact,
+    int n_sink, int n_window, int exact_len, int nexact, const int32_t* __restrict__ seq_lens,
     float* __restrict__ partials) {        // [B*Hq][nsplit + nexact][130]
   __shared__ float2 tab2[kLnuTable];      // (g_j, g_{j+1} - g_j)
   __shared__ int ring_idx[kWaves][kRingN];
@@ -156,6 +156,10 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
   const bool k0 = (K == 0);
   const bool exact = s >= nsplit;          // a piece of the exact set
   const bool nolnu = k0 || exact;
+  // this sequence's keys and exact set
+  const int Nb = seq_len_of(seq_lens, b, N);
+  int exact_head, exact_tail;
+  exact_range(n_sink, n_window, Nb, exact_head, exact_tail);
   const int ne = exact_head + exact_tail;
   const int npart = nsplit + nexact;
   const uint16_t gmask = static_cast<uint16_t>((1u << G) - 1u);
@@ -164,9 +168,10 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
   for (int i = tid; i < kLnuTable; i += 256)
     tab2[i] = k0 ? make_float2(0.f, 0.f) : make_float2(lnu_tab[i], lnu_tab[i + 1] - lnu_tab[i]);
 
-  // q fragments (MFMA A operand): lane holds head sl, dims [32 g4, 32 g4 + 32)
+  // q fragments (MFMA A operand): lane holds head sl, dims 32 k + 8 g4 + [0, 8)
+  // of k-step k (the K fragments use the same order)
   Frag<BF16> Qf;
-  Qf.load(q + static_cast<size_t>(bh0 + (sl < G ? sl : 0)) * kHeadDim + g4 * 32, sl < G);
+  Qf.load_interleaved(q + static_cast<size_t>(bh0 + (sl < G ? sl : 0)) * kHeadDim + g4 * 8, sl < G);
   float qss = sumsq(Qf);
   qss += __shfl_xor(qss, 16);
   qss += __shfl_xor(qss, 32);
@@ -182,7 +187,7 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
   // this wave's range: keys of the context split, or exact-set positions
   const int plen = exact ? exact_len : split_len;
   const int sb = exact ? (s - nsplit) * exact_len : s * split_len;
-  const int se = min(exact ? ne : N, sb + plen);
+  const int se = min(exact ? ne : Nb, sb + plen);
   const int wq = plen / kWaves;
   const int wb = min(se, sb + wave * wq), we = min(se, sb + (wave + 1) * wq);
 
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
         const uint64_t bal = ballot(any);
         if (any) {
           const int e = (rhead + rcnt + lane) & (kRingN - 1);
-          ridx[e] = i < exact_head ? i : i + (N - ne);
+          ridx[e] = i < exact_head ? i : i + (Nb - ne);
           rhm[e] = gmask;
         }
         rcnt += __builtin_popcountll(bal);
@@ -262,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
   };
 
   // ---- tile loads: K rows as two 16-key MFMA B fragments (lane = key sl of
-  // the group, dims [32 g4, +32)); V rows as 16-byte pieces (lane = piece sl of
+  // the group, dims 32 k + 8 g4 + [0, 8) for k-step k); V rows as 16-byte pieces (lane = piece sl of
   // rows g4 + 4 j)
   Frag<BF16> Kf[2];
   u32x4_t vr[8];
@@ -273,7 +278,7 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
       const int slot = 16 * gp + sl;
       const int e = (rhead + (slot < nt ? slot : 0)) & (kRingN - 1);
       hmk[gp] = slot < nt ? static_cast<int>(rhm[e]) : 0;
-      Kf[gp].load(kb + static_cast<size_t>(ridx[e]) * kHeadDim + g4 * 32, true);
+      Kf[gp].load_interleaved(kb + static_cast<size_t>(ridx[e]) * kHeadDim + g4 * 8, true);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -438,14 +443,14 @@ hipError_t launch_attend_bf16(const DecodeArgs& a, hipStream_t stream) {
   const float* lt = a.lnu_table;
   if (G <= 4)
     return launch(kKAttend, attend_bf16_kernel<1>, grid, dim3(256), 0, stream, qp, kp, vp, bm, lt, a.Hq,
-                  a.Hkv, a.N, a.P, a.K, a.T, a.scale, a.split_len, a.nsplit, a.exact_head, a.exact_tail, a.exact_len, a.nexact,
+                  a.Hkv, a.N, a.P, a.K, a.T, a.scale, a.split_len, a.nsplit, a.n_sink, a.n_window, a.exact_len, a.nexact, a.seq_lens,
                   a.partials);
   if (G <= 8)
     return launch(kKAttend, attend_bf16_kernel<2>, grid, dim3(256), 0, stream, qp, kp, vp, bm, lt, a.Hq,
-                  a.Hkv, a.N, a.P, a.K, a.T, a.scale, a.split_len, a.nsplit, a.exact_head, a.exact_tail, a.exact_len, a.nexact,
+                  a.Hkv, a.N, a.P, a.K, a.T, a.scale, a.split_len, a.nsplit, a.n_sink, a.n_window, a.exact_len, a.nexact, a.seq_lens,
                   a.partials);
   return launch(kKAttend, attend_bf16_kernel<4>, grid, dim3(256), 0, stream, qp, kp, vp, bm, lt, a.Hq, a.Hkv,
-                a.N, a.P, a.K, a.T, a.scale, a.split_len, a.nsplit, a.exact_head, a.exact_tail, a.exact_len, a.nexact,
+                a.N, a.P, a.K, a.T, a.scale, a.split_len, a.nsplit, a.n_sink, a.n_window, a.exact_len, a.nexact, a.seq_lens,
                   a.partials);
 }
 

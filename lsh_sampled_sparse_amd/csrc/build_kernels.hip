@@ -71,10 +71,11 @@ int proj_wt_rows(int K, int L) {
 template <typename T>
 __global__ void transpose_w_kernel(const typename T::storage* __restrict__ W,
                                    typename T::storage* __restrict__ WT, int K, int L, int nct, int tpg,
-                                   int rows) {
+                                   int rows, int w_heads) {   // one W (and WT) per kv head when w_heads > 1
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= rows * kHeadDim) return;
-  const int R = idx / kHeadDim, d = idx % kHeadDim;
+  if (idx >= w_heads * rows * kHeadDim) return;
+  const int hw = idx / (rows * kHeadDim), rem = idx % (rows * kHeadDim);
+  const int R = rem / kHeadDim, d = rem % kHeadDim;
   const int slab = R / (nct * 16), p = R % (nct * 16);
   const int ct = p / 16, r = p % 16;
   const int g = r / 4, j = ct * 4 + r % 4;
@@ -82,7 +83,7 @@ __global__ void transpose_w_kernel(const typename T::storage* __restrict__ W,
   const int tt = jr / K, b = jr % K;
   const int t = slab * 4 * tpg + g * tpg + tt;
   const bool valid = tt < tpg && t < L;
-  WT[idx] = valid ? negate(W[static_cast<size_t>(d) * L * K + t * K + b]) : typename T::storage(0);
+  WT[idx] = valid ? negate(W[(static_cast<size_t>(hw) * kHeadDim + d) * L * K + t * K + b]) : typename T::storage(0);
 }
 
 // (s << 1) | [k.w > 0] from y = k.(-w), the MFMA result against the negated
@@ -158,7 +159,10 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
     const typename T::storage* __restrict__ WT,     // [nslab * NCT * 16][128], permuted
     uint16_t* __restrict__ codes,                   // [U][L][P]
     int N, int P, int n_first, int L, int nslab,    // keys n_first .. N - 1
-    int spz) {                                      // slabs per blockIdx.z
+    int spz,                                        // slabs per blockIdx.z
+    int Hkv, size_t wt_head_stride,                 // WT of kv head g at g * wt_head_stride
+    const int32_t* __restrict__ old_lens,           // optional per-sequence ranges
+    const int32_t* __restrict__ new_lens, int stride_log2) {
   using S = typename T::storage;
   constexpr ProjShape PS = proj_shape(KB);
   constexpr int NCT = PS.nct, TPG = PS.tpg, TPS = 4 * TPG;
@@ -175,6 +179,15 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
 
   const int u = blockIdx.y;
   const int n0 = n_first + blockIdx.x * kProjKeys;
+  // this sequence's keys to (re)code: from the chunk holding its first new
+  // key (never below n_first) to its new length; 256-key blocks never
+  // straddle a chunk start, so a block is either wholly in or out
+  const int b = u / Hkv;
+  const int hi = seq_len_of(new_lens, b, N);
+  int lo = n_first;
+  if (old_lens) lo = max(lo, (seq_len_of(old_lens, b, hi) >> stride_log2) << stride_log2);
+  if (n0 >= hi || n0 < lo) return;
+  WT += static_cast<size_t>(u % Hkv) * wt_head_stride;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4;
   const S* kb = keys + static_cast<size_t>(u) * P * kHeadDim;
@@ -186,7 +199,7 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     const int key = n0 + wave * 64 + a * 16 + (lane & 15);
-    const bool valid = key < N;
+    const bool valid = key < hi;
     A[a].load(kb + static_cast<size_t>(valid ? key : 0) * kHeadDim + g * 32, valid);
   }
 
@@ -238,22 +251,32 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
       if (t < L) {
         const uint16_t* src = sb + r * kStgRow + k8;
         uint16_t* dst = cb + static_cast<size_t>(t) * P + key;
-        if (key + 8 <= N && (P & 7) == 0) {
+        if (key + 8 <= hi && (P & 7) == 0) {
           *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
         } else {
           for (int e = 0; e < 8; ++e)
-            if (key + e < N) dst[e] = src[e];
+            if (key + e < hi) dst[e] = src[e];
         }
       }
     }
   }
 }
 
-// K = 0: every code is 0 (keys n_first .. N - 1 of every [U][L] row of pitch P).
-__global__ void zero_codes_kernel(uint16_t* __restrict__ codes, size_t rows, int n_first, int N, int P) {
+// K = 0: every code is 0 (keys n_first .. N - 1 of every [U][L] row of
+// pitch P, within each sequence's own range as in project_codes_kernel).
+__global__ void zero_codes_kernel(uint16_t* __restrict__ codes, size_t rows, int n_first, int N, int P, int L,
+                                  int Hkv, const int32_t* __restrict__ old_lens,
+                                  const int32_t* __restrict__ new_lens, int stride_log2) {
   const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const size_t w = static_cast<size_t>(N - n_first);
-  if (i < rows * w) codes[(i / w) * P + n_first + i % w] = 0;
+  if (i >= rows * w) return;
+  const size_t row = i / w;
+  const int key = n_first + static_cast<int>(i % w);
+  const int b = static_cast<int>(row / L) / Hkv;
+  const int hi = seq_len_of(new_lens, b, N);
+  int lo = n_first;
+  if (old_lens) lo = max(lo, (seq_len_of(old_lens, b, hi) >> stride_log2) << stride_log2);
+  if (key >= lo && key < hi) codes[row * P + key] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -370,7 +393,8 @@ __global__ __launch_bounds__(NTHR, NTHR >= 256 ? 4 : 1) void chunk_sort_kernel(
     const uint16_t* __restrict__ codes,   // [U][L][P]
     int N, int P, int K, int stride_log2, int nJP, int j0,   // chunks j0 + blockIdx.x
     uint16_t* __restrict__ offsets,       // [U][L][nJP][2^K]
-    uint16_t* __restrict__ indices) {     // [U][L][P]
+    uint16_t* __restrict__ indices,       // [U][L][P]
+    int L, int Hkv, const int32_t* __restrict__ old_lens, const int32_t* __restrict__ new_lens) {
   constexpr int E = kSortE;
   extern __shared__ __attribute__((aligned(16))) uint32_t smem32[];
   __shared__ uint32_t wave_tot[NTHR / 64];
@@ -385,7 +409,12 @@ __global__ __launch_bounds__(NTHR, NTHR >= 256 ? 4 : 1) void chunk_sort_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = 1 << K;
   const int cbeg = j << stride_log2;
-  const int clen = min(1 << stride_log2, N - cbeg);
+  // this sequence's chunks to rebuild (the same ranges as the projection)
+  const int b = static_cast<int>(table / L) / Hkv;
+  const int hi = seq_len_of(new_lens, b, N);
+  const int jlo = old_lens ? max(j0, seq_len_of(old_lens, b, hi) >> stride_log2) : j0;
+  if (j < jlo || cbeg >= hi) return;
+  const int clen = min(1 << stride_log2, hi - cbeg);
   const int p0 = tid * E;
   const bool full = p0 + E <= clen;
   const bool vec = ((table * P) & 7) == 0;      // the chunk's codes are 16-byte aligned
@@ -539,7 +568,7 @@ static hipError_t launch_chunk_sort(const BuildArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   return launch(kKChunkSort, chunk_sort_kernel<NTHR>, dim3(a.nJ - a.j0, a.U * a.L), dim3(NTHR),
                 static_cast<unsigned>(lds), stream, static_cast<const uint16_t*>(a.codes), a.N, a.P, a.K,
-                a.stride_log2, a.nJP, a.j0, a.offsets, a.indices);
+                a.stride_log2, a.nJP, a.j0, a.offsets, a.indices, a.L, a.Hkv, a.old_lens, a.new_lens);
 }
 
 // ---------------------------------------------------------------------------
@@ -558,7 +587,8 @@ static hipError_t launch_project_k(const BuildArgs& a, int nslab, hipStream_t st
   const int gz = (nslab + spz - 1) / spz;
   return launch(kKProject, project_codes_kernel<T, KB>, dim3(gx, a.U, gz), dim3(kProjThreads), 0, stream,
                 static_cast<const S*>(a.keys), static_cast<const S*>(a.wt), a.codes, a.N, a.P, n_first, a.L,
-                nslab, spz);
+                nslab, spz, a.Hkv, a.w_heads > 1 ? static_cast<size_t>(nslab) * proj_shape(KB).nct * 16 * kHeadDim : size_t(0),
+                a.old_lens, a.new_lens, a.stride_log2);
 }
 
 template <typename T>
@@ -570,13 +600,14 @@ static hipError_t launch_project(const BuildArgs& a, hipStream_t stream) {
     const size_t rows = static_cast<size_t>(a.U) * L;
     const size_t n = rows * static_cast<size_t>(a.N - n_first);
     return launch(kKProject, zero_codes_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
-                  a.codes, rows, n_first, a.N, a.P);
+                  a.codes, rows, n_first, a.N, a.P, L, a.Hkv, a.old_lens, a.new_lens, a.stride_log2);
   }
   const ProjShape ps = proj_shape(K);
   const int rows = proj_wt_rows(K, L);
   const int nslab = rows / (ps.nct * 16);
-  hipError_t e = launch(kKTransposeW, transpose_w_kernel<T>, dim3((rows * kHeadDim + 255) / 256), dim3(256), 0,
-                        stream, static_cast<const S*>(a.W), static_cast<S*>(a.wt), K, L, ps.nct, ps.tpg, rows);
+  hipError_t e = launch(kKTransposeW, transpose_w_kernel<T>, dim3((a.w_heads * rows * kHeadDim + 255) / 256),
+                        dim3(256), 0, stream, static_cast<const S*>(a.W), static_cast<S*>(a.wt), K, L, ps.nct,
+                        ps.tpg, rows, a.w_heads);
   if (e != hipSuccess) return e;
   switch (K) {
     case 1: return launch_project_k<T, 1>(a, nslab, stream);

@@ -100,7 +100,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void qhash_kernel(const typename T::storage* __restrict__ q,
                                                     const typename T::storage* __restrict__ W,
                                                     uint16_t* __restrict__ qcodes, float* __restrict__ lnu_tab,
-                                                    int BH, int K, int L, int Tth, int head_blocks) {
+                                                    int BH, int K, int L, int Tth, int head_blocks,
+                                                    int G, int Hkv, size_t w_head_stride) {
   __shared__ __attribute__((aligned(16))) float qs[kQHeads][kHeadDim];
   __shared__ float part[4][kQHeads][64];
   __shared__ uint8_t sgn[kQHeads][64];
@@ -117,20 +118,24 @@ __global__ __launch_bounds__(256) void qhash_kernel(const typename T::storage* _
     if (j <= kLnuTable && lane == 0) lnu_tab[j] = static_cast<float>(g);
     return;
   }
-  const int h0 = blockIdx.y * kQHeads;
+  // a workgroup hashes hpb heads: 16 with one shared W, or the G heads of
+  // one (sequence, kv head) with a W per kv head
+  const int hpb = w_head_stride ? G : kQHeads;
+  const int h0 = blockIdx.y * hpb;
   if (K == 0) {
-    for (int e = blockIdx.x * 256 + tid; e < kQHeads * L; e += gridDim.x * 256) {
+    for (int e = blockIdx.x * 256 + tid; e < hpb * L; e += gridDim.x * 256) {
       const int h = h0 + e / L;
       if (h < BH) qcodes[static_cast<size_t>(h) * L + e % L] = 0;
     }
     return;
   }
+  W += static_cast<size_t>((h0 / G) % Hkv) * w_head_stride;
   const int tpw = 64 / K;               // whole tables per workgroup
   const int l0 = blockIdx.x * tpw;
   for (int e = tid; e < kQHeads * kHeadDim; e += 256) {
     const int h = h0 + e / kHeadDim;
     float v = 0.f;
-    if (h < BH) {
+    if (e / kHeadDim < hpb && h < BH) {
       if constexpr (sizeof(typename T::storage) == 2)
         v = bf16_to_f32(q[static_cast<size_t>(h) * kHeadDim + e % kHeadDim]);
       else
@@ -175,7 +180,7 @@ __global__ __launch_bounds__(256) void qhash_kernel(const typename T::storage* _
   for (int e = tid; e < kQHeads * tpw; e += 256) {
     const int hh = e / tpw, t = e % tpw;
     const int l = l0 + t, h = h0 + hh;
-    if (h < BH && l < L) {
+    if (hh < hpb && h < BH && l < L) {
       uint32_t code = 0;
       for (int b = 0; b < K; ++b) code |= static_cast<uint32_t>(sgn[hh][t * K + b]) << b;
       qcodes[static_cast<size_t>(h) * L + l] = static_cast<uint16_t>(code);
@@ -197,7 +202,8 @@ __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
     uint32_t* __restrict__ bitmask,        // [BH][Nw]
     int32_t* __restrict__ chunk_nsel,      // [BH][nJ]
     uint8_t* __restrict__ counts,          // optional [BH][N]
-    int exact_head, int exact_tail) {      // keys attended exactly, never sampled
+    int n_sink, int n_window,              // the exact set, attended exactly, never sampled
+    const int32_t* __restrict__ seq_lens) {  // optional [B] keys per sequence
   extern __shared__ __attribute__((aligned(16))) uint32_t cnt[];   // one byte per key of the chunk
   __shared__ int seg_start[256];
   __shared__ int seg_v[257];
@@ -208,15 +214,21 @@ __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
   const int u = b * Hkv + h / G;
   const int nb = 1 << K;
   const int cbeg = J << stride_log2;
-  const int clen = min(1 << stride_log2, N - cbeg);
-  const int cwords = (clen + 3) >> 2;
+  // cfull: the chunk's positions in the bitmask and counts; clen: the keys
+  // of this sequence among them (none when the sequence ends before it)
+  const int Nb = seq_len_of(seq_lens, b, N);
+  const int cfull = min(1 << stride_log2, N - cbeg);
+  const int clen = max(0, min(1 << stride_log2, Nb - cbeg));
+  const int cwords = (cfull + 3) >> 2;
+  int exact_head, exact_tail;
+  exact_range(n_sink, n_window, Nb, exact_head, exact_tail);
 
   for (int i = tid; i < cwords; i += kCountThreads) cnt[i] = 0;
 
   // segment of bucket qcode_l restricted to this chunk, for every table l
   // (L <= 255, so the first four waves hold one table per thread)
   int len = 0;
-  if (tid < L) {
+  if (tid < L && clen > 0) {
     const int qc = qcodes[static_cast<size_t>(bh) * L + tid];
     const uint16_t* op = offsets + ((static_cast<size_t>(u) * L + tid) * nJP + J) * nb + qc;
     // clamped into the chunk: tables that do not match the stride cannot
@@ -273,12 +285,12 @@ __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
     }
 #pragma unroll
     for (int k = 0; k < kCountUnroll; ++k)
-      if (loc[k] >= 0) atomicAdd(&cnt[loc[k] >> 2], 1u << ((loc[k] & 3) * 8));
+      if (loc[k] >= 0 && loc[k] < clen) atomicAdd(&cnt[loc[k] >> 2], 1u << ((loc[k] & 3) * 8));
   }
   __syncthreads();
 
   const int Nw = (N + 31) >> 5;
-  const int nwords = (clen + 31) >> 5;
+  const int nwords = (cfull + 31) >> 5;
   int mysel = 0;
   for (int w = tid; w < nwords; w += kCountThreads) {
     uint32_t m = 0;
@@ -290,7 +302,7 @@ __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
       for (int k = 0; k < 4; ++k) {
         const int key = w * 32 + j * 4 + k;
         const int n = cbeg + key;
-        const bool exact = n < exact_head || n >= N - exact_tail;
+        const bool exact = n < exact_head || n >= Nb - exact_tail;
         if (key < clen && !exact && static_cast<int>((c4 >> (8 * k)) & 0xffu) >= T) m |= 1u << (j * 4 + k);
       }
     }
@@ -300,7 +312,7 @@ __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
   if (counts) {
     const uint8_t* c8 = reinterpret_cast<const uint8_t*>(cnt);
     uint8_t* dst = counts + static_cast<size_t>(bh) * N + cbeg;
-    for (int i = tid; i < clen; i += kCountThreads) dst[i] = c8[i];
+    for (int i = tid; i < cfull; i += kCountThreads) dst[i] = c8[i];
   }
   mysel = wave_sum_int(mysel);
   __syncthreads();
@@ -377,7 +389,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
     const uint32_t* __restrict__ bitmask,            // [BH][Nw]
     const float* __restrict__ lnu_tab,               // [kLnuTable + 1]
     int Hq, int Hkv, int N, int P, int K, int Tth, float scale, int split_len, int nsplit,
-    int exact_head, int exact_tail, int exact_len, int nexact,
+    int n_sink, int n_window, int exact_len, int nexact, const int32_t* __restrict__ seq_lens,
     float* __restrict__ partials) {                  // [BH][nsplit + nexact][130]
   using S = typename T::storage;
   __shared__ float tab[kLnuTable + 1];
@@ -400,6 +412,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
   const bool k0 = (K == 0);
   const bool exact = s >= nsplit;     // a piece of the exact set (all heads, u = 1)
   const bool nolnu = k0 || exact;
+  // this sequence's keys and exact set
+  const int Nb = seq_len_of(seq_lens, b, N);
+  int exact_head, exact_tail;
+  exact_range(n_sink, n_window, Nb, exact_head, exact_tail);
   const int ne = exact_head + exact_tail;
   const int npart = nsplit + nexact;
   const float TK = static_cast<float>(Tth * K);
@@ -419,7 +435,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
 
   const int plen = exact ? exact_len : split_len;
   const int sb = exact ? (s - nsplit) * exact_len : s * split_len;
-  const int se = min(exact ? ne : N, sb + plen);
+  const int se = min(exact ? ne : Nb, sb + plen);
   const int wq = plen / 4;
   const int wb = min(se, sb + wave * wq), we = min(se, sb + (wave + 1) * wq);
 
@@ -503,7 +519,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
     const int i = blk + lane;           // key, or position in the exact set
     int n = i, hm = 0;
     if (exact) {
-      n = i < exact_head ? i : i + (N - ne);
+      n = i < exact_head ? i : i + (Nb - ne);
       hm = (1 << G) - 1;
     } else {
       const int w0 = blk >> 5;
@@ -650,7 +666,7 @@ static hipError_t launch_attend(const DecodeArgs& a, hipStream_t stream) {
   return launch(kKAttend, attend_kernel<T, GM>, dim3(a.nsplit + a.nexact, a.B * a.Hkv), dim3(kAttThreads), 0, stream,
                 static_cast<const S*>(a.q), static_cast<const S*>(a.keys), static_cast<const S*>(a.values),
                 static_cast<const uint32_t*>(a.bitmask), static_cast<const float*>(a.lnu_table), a.Hq, a.Hkv,
-                a.N, a.P, a.K, a.T, a.scale, a.split_len, a.nsplit, a.exact_head, a.exact_tail, a.exact_len, a.nexact,
+                a.N, a.P, a.K, a.T, a.scale, a.split_len, a.nsplit, a.n_sink, a.n_window, a.exact_len, a.nexact, a.seq_lens,
                 a.partials);
 }
 
@@ -658,13 +674,16 @@ template <typename T>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   using S = typename T::storage;
   const int BH = a.B * a.Hq;
-  const int head_blocks = (BH + kQHeads - 1) / kQHeads;
+  const int G = a.Hq / a.Hkv;
+  const int hpb = a.w_heads > 1 ? G : kQHeads;          // heads per qhash workgroup
+  const int head_blocks = (BH + hpb - 1) / hpb;
+  const size_t w_head_stride = a.w_heads > 1 ? static_cast<size_t>(kHeadDim) * a.L * a.K : 0;
   const int tpw = a.K > 0 ? 64 / a.K : 256;
   const int xblocks = (a.L + tpw - 1) / tpw;
   const int tab_blocks = (kLnuTable + 1 + xblocks * 4 - 1) / (xblocks * 4);   // 4 entries per workgroup
   hipError_t e = launch(kKQhash, qhash_kernel<T>, dim3(xblocks, head_blocks + tab_blocks), dim3(256), 0,
                         stream, static_cast<const S*>(a.q), static_cast<const S*>(a.W), a.qcodes,
-                        a.lnu_table, BH, a.K, a.L, a.T, head_blocks);
+                        a.lnu_table, BH, a.K, a.L, a.T, head_blocks, G, a.Hkv, w_head_stride);
   if (e != hipSuccess) return e;
   const size_t lds = ((static_cast<size_t>(1) << a.stride_log2) + 3) & ~static_cast<size_t>(3);
   e = ensure_lds_limit(reinterpret_cast<const void*>(count_select_kernel), lds);
@@ -672,9 +691,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   e = launch(kKCountSelect, count_select_kernel, dim3(a.nJ, BH), dim3(kCountThreads),
              static_cast<unsigned>(lds), stream, static_cast<const uint16_t*>(a.qcodes),
              a.indices, a.offsets, a.Hq, a.Hkv, a.N, a.P, a.K, a.L, a.T, a.stride_log2, a.nJ, a.nJP, a.bitmask,
-             a.chunk_nsel, a.counts, a.exact_head, a.exact_tail);
+             a.chunk_nsel, a.counts, a.n_sink, a.n_window, a.seq_lens);
   if (e != hipSuccess) return e;
-  const int G = a.Hq / a.Hkv;
   if constexpr (sizeof(S) == 2)
     e = launch_attend_bf16(a, stream);
   else if (G <= 4)

@@ -57,8 +57,9 @@ struct BuildLayout {
 BuildLayout build_layout(int B, int Hkv, int N, int L, int dtype, const Geometry& g, bool need_codes) {
   BuildLayout w;
   size_t off = 0;
+  // WT for every kv head (one W per kv head is the larger case)
   w.wt = off;
-  off = align_up(off + static_cast<size_t>(g.LKpad) * 128 * elem_bytes(dtype));
+  off = align_up(off + static_cast<size_t>(Hkv) * g.LKpad * 128 * elem_bytes(dtype));
   w.codes = off;
   if (need_codes) off = align_up(off + static_cast<size_t>(B) * Hkv * L * N * sizeof(uint16_t));
   w.total = off;
@@ -225,12 +226,14 @@ size_t lsh_build_workspace_size(int B, int Hkv, int N, int d, int K, int L, int 
 }
 
 lsh_status lsh_update_tables(const void* keys, const void* W, int B, int Hkv, int n_old, int n_new, int n_cap,
-                             int d, int K, int L, int stride, int dtype, uint16_t* offsets, uint16_t* indices,
-                             uint16_t* key_codes, void* workspace, size_t workspace_bytes, void* stream) {
+                             const int32_t* old_lens, const int32_t* new_lens, int d, int K, int L, int stride,
+                             int dtype, int w_per_head, uint16_t* offsets, uint16_t* indices, uint16_t* key_codes,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   Geometry g;   // at capacity: the pitch of every per-key array and the offsets' chunk slots
   lsh_status st = check_common(B, Hkv, n_cap, d, K, L, stride, dtype, &g);
   if (st != LSH_OK) return st;
   if (n_old < 0 || n_old > n_new || n_new > n_cap) return LSH_ERR_INVALID_ARG;
+  if (w_per_head != 0 && w_per_head != 1) return LSH_ERR_INVALID_ARG;
   if (!keys || !offsets || !indices || !workspace || (K > 0 && !W)) return LSH_ERR_INVALID_ARG;
   const BuildLayout w = build_layout(B, Hkv, n_cap, L, dtype, g, key_codes == nullptr);
   if (workspace_bytes < w.total) return LSH_ERR_WORKSPACE;
@@ -243,7 +246,11 @@ lsh_status lsh_update_tables(const void* keys, const void* W, int B, int Hkv, in
   a.codes = key_codes ? key_codes : reinterpret_cast<uint16_t*>(ws + w.codes);
   a.offsets = offsets;
   a.indices = indices;
+  a.old_lens = old_lens;
+  a.new_lens = new_lens;
   a.U = B * Hkv;
+  a.Hkv = Hkv;
+  a.w_heads = w_per_head ? Hkv : 1;
   a.N = n_new;
   a.K = K;
   a.L = L;
@@ -261,8 +268,8 @@ lsh_status lsh_update_tables(const void* keys, const void* W, int B, int Hkv, in
 lsh_status lsh_build_tables(const void* keys, const void* W, int B, int Hkv, int N, int d, int K, int L,
                             int stride, int dtype, uint16_t* offsets, uint16_t* indices, uint16_t* key_codes,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  return lsh_update_tables(keys, W, B, Hkv, 0, N, N, d, K, L, stride, dtype, offsets, indices, key_codes,
-                           workspace, workspace_bytes, stream);
+  return lsh_update_tables(keys, W, B, Hkv, 0, N, N, nullptr, nullptr, d, K, L, stride, dtype, 0, offsets, indices,
+                           key_codes, workspace, workspace_bytes, stream);
 }
 
 size_t lsh_decode_workspace_size(int B, int Hq, int Hkv, int N, int d, int K, int L, int stride) {
@@ -274,10 +281,10 @@ size_t lsh_decode_workspace_size(int B, int Hq, int Hkv, int N, int d, int K, in
 
 lsh_status lsh_decode_attention_cached(const void* q, const void* keys, const void* values, const void* W,
                                        const uint16_t* indices, const uint16_t* offsets, int B, int Hq, int Hkv,
-                                       int N, int n_cap, int d, int K, int L, int T, int stride, float sm_scale,
-                                       int dtype, int n_sink, int n_window, float* out, float* lse, int32_t* nsel,
-                                       uint16_t* q_codes, uint8_t* counts, void* workspace, size_t workspace_bytes,
-                                       void* stream) {
+                                       int N, int n_cap, const int32_t* seq_lens, int d, int K, int L, int T,
+                                       int stride, float sm_scale, int dtype, int w_per_head, int n_sink,
+                                       int n_window, float* out, float* lse, int32_t* nsel, uint16_t* q_codes,
+                                       uint8_t* counts, void* workspace, size_t workspace_bytes, void* stream) {
   Geometry g, gcap;
   lsh_status st = check_common(B, Hkv, N, d, K, L, stride, dtype, &g);
   if (st != LSH_OK) return st;
@@ -286,6 +293,7 @@ lsh_status lsh_decode_attention_cached(const void* q, const void* keys, const vo
   if (st != LSH_OK) return st;
   if (Hq < 1 || Hq % Hkv != 0 || T < 1 || T > L || !std::isfinite(sm_scale)) return LSH_ERR_INVALID_ARG;
   if (n_sink < 0 || n_window < 0) return LSH_ERR_INVALID_ARG;
+  if (w_per_head != 0 && w_per_head != 1) return LSH_ERR_INVALID_ARG;
   if (Hq / Hkv > 16) return LSH_ERR_UNSUPPORTED;
   if (!q || !keys || !values || !indices || !offsets || !out || !workspace || (K > 0 && !W))
     return LSH_ERR_INVALID_ARG;
@@ -323,12 +331,15 @@ lsh_status lsh_decode_attention_cached(const void* q, const void* keys, const vo
   a.nsplit = w.nsplit;
   a.scale = sm_scale;
   a.dtype = dtype;
-  a.exact_head = std::min(n_sink, N);
-  a.exact_tail = std::min(n_window, N - a.exact_head);
+  a.seq_lens = seq_lens;
+  a.w_heads = w_per_head ? Hkv : 1;
+  a.n_sink = n_sink;
+  a.n_window = n_window;
   // the exact set goes to the attention kernel as extra workgroups over
   // pieces of at least 128 keys (one 32-key tile per wave), at most
-  // kMaxExactSplits of them
-  const int ne = a.exact_head + a.exact_tail;
+  // kMaxExactSplits of them, sized for the longest sequence (a sequence's
+  // exact set, min(n, n_sink + n_window) keys, grows with its length n)
+  const int ne = static_cast<int>(std::min<long long>(N, static_cast<long long>(n_sink) + n_window));
   const int per_piece = (ne + lsh::kMaxExactSplits - 1) / lsh::kMaxExactSplits;
   a.exact_len = std::max(128, (per_piece + 127) / 128 * 128);
   a.nexact = (ne + a.exact_len - 1) / a.exact_len;
@@ -341,9 +352,9 @@ lsh_status lsh_decode_attention_hybrid(const void* q, const void* keys, const vo
                                        int n_sink, int n_window, float* out, float* lse, int32_t* nsel,
                                        uint16_t* q_codes, uint8_t* counts, void* workspace, size_t workspace_bytes,
                                        void* stream) {
-  return lsh_decode_attention_cached(q, keys, values, W, indices, offsets, B, Hq, Hkv, N, N, d, K, L, T, stride,
-                                     sm_scale, dtype, n_sink, n_window, out, lse, nsel, q_codes, counts, workspace,
-                                     workspace_bytes, stream);
+  return lsh_decode_attention_cached(q, keys, values, W, indices, offsets, B, Hq, Hkv, N, N, nullptr, d, K, L, T,
+                                     stride, sm_scale, dtype, 0, n_sink, n_window, out, lse, nsel, q_codes, counts,
+                                     workspace, workspace_bytes, stream);
 }
 
 lsh_status lsh_decode_attention(const void* q, const void* keys, const void* values, const void* W,

@@ -90,6 +90,16 @@ struct Frag<BF16> {
 #pragma unroll
     for (int k = 0; k < 4; ++k) v[k] = __builtin_bit_cast(bf16x8_t, valid ? q[k] : zero);
   }
+  // the four 16-byte pieces at p, p + 32, p + 64 and p + 96 (elements).  With
+  // p = row + 8 * (lane >> 4) for both operands, k-step k sums dims
+  // [32 k, 32 k + 32), and the four lanes that share a row read 64
+  // contiguous bytes of it per step (half the cache lines of load()'s order)
+  __device__ __forceinline__ void load_interleaved(const uint16_t* p, bool valid) {
+    const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = __builtin_bit_cast(bf16x8_t, valid ? q[4 * k] : zero);
+  }
   __device__ __forceinline__ floatx4_t mma(const Frag& b, floatx4_t acc) const {
 #pragma unroll
     for (int k = 0; k < 4; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[k], b.v[k], acc, 0, 0, 0);

@@ -12,26 +12,32 @@ namespace lsh {
 // cache); offsets have nJP >= nJ chunk slots per table.  The build covers the
 // keys of chunks j0 .. nJ - 1 (keys j0 * stride .. N - 1): j0 = 0 is a full
 // build, a larger j0 rebuilds only the chunks that new keys fall into.
+// Sequences may hold different numbers of keys: old_lens / new_lens (device,
+// optional) give sequence b's range, clamped into [j0 * stride, N].
 struct BuildArgs {
   const void* keys;      // [U][P][128]
-  const void* W;         // [128][L*K]
-  void* wt;              // workspace: [proj_wt_rows(K, L)][128]
+  const void* W;         // [w_heads][128][L*K]
+  void* wt;              // workspace: [w_heads][proj_wt_rows(K, L)][128]
   uint16_t* codes;       // [U][L][P] (caller's key_codes or workspace)
   uint16_t* offsets;     // [U][L][nJP][2^K] bucket starts inside each chunk
   uint16_t* indices;     // [U][L][P] chunk-major, key - chunk start
-  int U, N, K, L;
+  const int32_t* old_lens;   // optional [B]: keys each sequence's tables hold
+  const int32_t* new_lens;   // optional [B]: keys they hold afterwards
+  int U, Hkv, N, K, L;
   int P, nJP, j0;
   int stride_log2, nJ;
+  int w_heads;           // 1: one W for every head; Hkv: W per kv head
   int dtype;             // 0 = f32, 1 = bf16
 };
 
 struct DecodeArgs {
   const void* q;         // [B][Hq][128]
-  const void* keys;      // [U][P][128], keys 0 .. N - 1 valid
+  const void* keys;      // [U][P][128], keys 0 .. len_b - 1 valid
   const void* values;    // [U][P][128]
-  const void* W;         // [128][L*K]
+  const void* W;         // [w_heads][128][L*K]
   const uint16_t* indices;   // [U][L][P] chunk-major
   const uint16_t* offsets;   // [U][L][nJP][2^K]
+  const int32_t* seq_lens;   // optional [B]: keys of sequence b (clamped to [0, N]); N when null
   uint16_t* qcodes;      // [B*Hq][L]
   uint32_t* bitmask;     // [B*Hq][Nw]
   int32_t* chunk_nsel;   // [B*Hq][nJ]
@@ -46,10 +52,26 @@ struct DecodeArgs {
   int stride_log2, nJ;
   int split_len, nsplit;
   float scale;
+  int w_heads;
   int dtype;
-  int exact_head, exact_tail;  // exact set: keys [0, exact_head) and [N - exact_tail, N), disjoint
+  // exact set of sequence b (length n): keys [0, eh) and [n - et, n) with
+  // eh = min(n_sink, n), et = min(n_window, n - eh)
+  int n_sink, n_window;
   int exact_len, nexact;       // the exact set in nexact pieces of exact_len keys, one workgroup each
 };
+
+// Keys of sequence b: the given length clamped into [0, N], or N.
+__host__ __device__ inline int seq_len_of(const int32_t* lens, int b, int N) {
+  if (!lens) return N;
+  const int v = lens[b];
+  return v < 0 ? 0 : (v > N ? N : v);
+}
+
+// The exact set of a sequence of n keys: its first eh and its last et keys.
+__host__ __device__ inline void exact_range(int n_sink, int n_window, int n, int& eh, int& et) {
+  eh = n_sink < n ? n_sink : n;
+  et = n_window < n - eh ? n_window : n - eh;
+}
 
 constexpr int kLnuTable = 1024;   // ln-u correction table intervals over theta in [0, pi]
 constexpr int kPartialStride = 130;

@@ -153,13 +153,13 @@ def test_hybrid_rejects(n_sink, n_window, kw, status):
 
 def _update(**kw):
     a = dict(keys=1, W=1, B=1, Hkv=1, n_old=100, n_new=200, n_cap=4096, d=128, K=8, L=32, stride=1024, dtype=1,
-             offsets=1, indices=1, codes=None, ws=1, ws_bytes=1 << 40)
+             w_per_head=0, offsets=1, indices=1, codes=None, ws=1, ws_bytes=1 << 40)
     a.update(kw)
     p = lambda v: None if v is None else ctypes.c_void_p(v)
     return lsh.lib().lsh_update_tables(p(a["keys"]), p(a["W"]), a["B"], a["Hkv"], a["n_old"], a["n_new"],
-                                       a["n_cap"], a["d"], a["K"], a["L"], a["stride"], a["dtype"],
-                                       p(a["offsets"]), p(a["indices"]), p(a["codes"]), p(a["ws"]),
-                                       a["ws_bytes"], None)
+                                       a["n_cap"], None, None, a["d"], a["K"], a["L"], a["stride"], a["dtype"],
+                                       a["w_per_head"], p(a["offsets"]), p(a["indices"]), p(a["codes"]),
+                                       p(a["ws"]), a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -171,6 +171,7 @@ def _update(**kw):
     (dict(stride=100), lsh.LSH_ERR_INVALID_ARG),
     (dict(d=64), lsh.LSH_ERR_UNSUPPORTED),
     (dict(ws_bytes=16), lsh.LSH_ERR_WORKSPACE),
+    (dict(w_per_head=2), lsh.LSH_ERR_INVALID_ARG),
     (dict(n_old=200), lsh.LSH_OK),                       # nothing new: launches nothing
 ])
 def test_update_rejects(kw, status):
@@ -179,14 +180,15 @@ def test_update_rejects(kw, status):
 
 def _cached(**kw):
     a = dict(q=1, keys=1, values=1, W=1, indices=1, offsets=1, B=1, Hq=4, Hkv=1, N=3000, n_cap=4096, d=128, K=8,
-             L=32, T=2, stride=1024, scale=0.088, dtype=1, n_sink=0, n_window=0, out=1, ws=1, ws_bytes=1 << 40)
+             L=32, T=2, stride=1024, scale=0.088, dtype=1, w_per_head=0, n_sink=0, n_window=0, out=1, ws=1,
+             ws_bytes=1 << 40)
     a.update(kw)
     p = lambda v: None if v is None else ctypes.c_void_p(v)
     return lsh.lib().lsh_decode_attention_cached(
         p(a["q"]), p(a["keys"]), p(a["values"]), p(a["W"]), p(a["indices"]), p(a["offsets"]),
-        a["B"], a["Hq"], a["Hkv"], a["N"], a["n_cap"], a["d"], a["K"], a["L"], a["T"], a["stride"],
-        ctypes.c_float(a["scale"]), a["dtype"], a["n_sink"], a["n_window"], p(a["out"]), None, None, None, None,
-        p(a["ws"]), a["ws_bytes"], None)
+        a["B"], a["Hq"], a["Hkv"], a["N"], a["n_cap"], None, a["d"], a["K"], a["L"], a["T"], a["stride"],
+        ctypes.c_float(a["scale"]), a["dtype"], a["w_per_head"], a["n_sink"], a["n_window"], p(a["out"]), None,
+        None, None, None, p(a["ws"]), a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -195,6 +197,7 @@ def _cached(**kw):
     (dict(n_sink=-2), lsh.LSH_ERR_INVALID_ARG),
     (dict(values=None), lsh.LSH_ERR_INVALID_ARG),
     (dict(Hq=6, Hkv=4), lsh.LSH_ERR_INVALID_ARG),
+    (dict(w_per_head=-1), lsh.LSH_ERR_INVALID_ARG),
     (dict(ws_bytes=100), lsh.LSH_ERR_WORKSPACE),
 ])
 def test_cached_decode_rejects(kw, status):

@@ -36,25 +36,35 @@ def to_np(t):
     return t.detach().cpu().numpy()
 
 
-def check_prefix(cfg, data, tb, r, n, units, heads_per_unit=None, n_sink=0, n_window=0):
-    """Compare the tables (first n keys) and one decode over them with the oracle."""
+def check_prefix(cfg, data, tb, r, n, units, heads_per_unit=None, n_sink=0, n_window=0, W_heads=None):
+    """Compare the tables and one decode with the oracle: sequence b holds
+    n[b] keys (n may be one int for all), unit (b, g) hashes with W, or with
+    W_heads[g] when there is one W per kv head."""
     stride = tb["stride"]
-    nj = O.num_chunks(n, stride)
-    W = data["W"].float().cpu().numpy()
+    lens = [n] * cfg.B if isinstance(n, int) else list(n)
     q = data["q"][0].float().cpu().numpy()
     flips = bits = 0
     rels = []
     for (b, g) in units:
-        ku = data["keys"][b, g, :n].float().cpu().numpy()
-        vu = data["values"][b, g, :n].float().cpu().numpy()
-        ref = O.build_tables(ku, W, cfg.K, cfg.L, stride)
-        band = PAR.band_mask(ku, W) if cfg.K > 0 else np.zeros((n, 0), bool)
-        gcodes = to_np(tb["codes"][b, g, :, :n])
-        flips += PAR.compare_codes(gcodes, ref["codes"], band, cfg.K, cfg.L)
-        bits += n * cfg.L * cfg.K
-        PAR.check_tables(to_np(tb["offsets"][b, g, :, :nj]), to_np(tb["indices"][b, g, :, :n]), gcodes, ref,
-                         cfg.K, stride)
+        nb = lens[b]
         hs = list(range(g * cfg.G, (g + 1) * cfg.G))[:heads_per_unit]
+        if nb == 0:
+            # nothing held: empty estimate
+            for h in hs:
+                assert float(r["out"][b, h].abs().max()) == 0.0
+                assert float(r["lse"][b, h]) == -np.inf and int(r["nsel"][b, h]) == 0
+            continue
+        W = (W_heads[g] if W_heads is not None else data["W"]).float().cpu().numpy()
+        nj = O.num_chunks(nb, stride)
+        ku = data["keys"][b, g, :nb].float().cpu().numpy()
+        vu = data["values"][b, g, :nb].float().cpu().numpy()
+        ref = O.build_tables(ku, W, cfg.K, cfg.L, stride)
+        band = PAR.band_mask(ku, W) if cfg.K > 0 else np.zeros((nb, 0), bool)
+        gcodes = to_np(tb["codes"][b, g, :, :nb])
+        flips += PAR.compare_codes(gcodes, ref["codes"], band, cfg.K, cfg.L)
+        bits += nb * cfg.L * cfg.K
+        PAR.check_tables(to_np(tb["offsets"][b, g, :, :nj]), to_np(tb["indices"][b, g, :, :nb]), gcodes, ref,
+                         cfg.K, stride)
         for h in hs:
             if n_sink or n_window:
                 rr = O.hybrid_decode_head(q[b, h], ku, vu, W, ref["offsets"], ref["indices"], cfg.K, cfg.L, cfg.T,
@@ -63,8 +73,9 @@ def check_prefix(cfg, data, tb, r, n, units, heads_per_unit=None, n_sink=0, n_wi
                 rr = O.decode_head(q[b, h], ku, vu, W, ref["offsets"], ref["indices"], cfg.K, cfg.L, cfg.T,
                                    cfg.scale)
             qb = PAR.band_mask(q[b, h][None], W) if cfg.K > 0 else np.zeros((1, 0), bool)
-            gh = {"q_codes": to_np(r["q_codes"][b, h]), "counts": to_np(r["counts"][b, h]),
+            gh = {"q_codes": to_np(r["q_codes"][b, h]), "counts": to_np(r["counts"][b, h, :nb]),
                   "out": to_np(r["out"][b, h]), "lse": float(r["lse"][b, h]), "nsel": int(r["nsel"][b, h])}
+            assert not r["counts"][b, h, nb:].any(), "counts past the sequence's length"
             res = PAR.check_head(gh, rr, qb, gcodes, ref["codes"], cfg.K, cfg.L, cfg.T, exact=rr.get("exact"))
             flips += res["qflips"]
             bits += cfg.L * cfg.K
@@ -75,32 +86,38 @@ def check_prefix(cfg, data, tb, r, n, units, heads_per_unit=None, n_sink=0, n_wi
 
 
 def grow(cfg, schedule, stride=None, n_sink=0, n_window=0, check_units=None, heads_per_unit=None,
-         check_at=None, device="cpu"):
+         check_at=None, device="cpu", W_heads=None):
+    """Fill a NaN cache step by step; ``schedule`` lists the keys held after
+    each step, one int for every sequence or a list of B per-sequence
+    lengths.  Checks against the oracle after the steps in ``check_at``
+    (default: all)."""
     lsh = _lsh()
     dev = torch.device("cuda:0")
     data = workloads.generate(cfg, device=device)
-    n_cap = cfg.N
     keys = data["keys"].to(dev)
     vals = data["values"].to(dev)
-    W = data["W"].to(dev)
+    W = (W_heads if W_heads is not None else data["W"]).to(dev).contiguous()
     q = data["q"][0].to(dev).contiguous()
     # the cache: NaN past the keys it holds
     ck = torch.full_like(keys, float("nan"))
     cv = torch.full_like(vals, float("nan"))
     tb = lsh.alloc_tables(ck, cfg.K, cfg.L, stride=stride, return_codes=True)
     units = check_units or [(b, g) for b in range(cfg.B) for g in range(cfg.Hkv)]
-    for n in schedule:
-        n0 = tb["n"]
-        ck[:, :, n0:n] = keys[:, :, n0:n]
-        cv[:, :, n0:n] = vals[:, :, n0:n]
+    for step, n in enumerate(schedule):
+        lens = [n] * cfg.B if isinstance(n, int) else list(n)
+        for b in range(cfg.B):
+            n0 = tb["lens"][b]
+            ck[b, :, n0:lens[b]] = keys[b, :, n0:lens[b]]
+            cv[b, :, n0:lens[b]] = vals[b, :, n0:lens[b]]
         lsh.update_tables(ck, W, tb, n, cfg.K, cfg.L)
         r = lsh.decode_attention(q, ck, cv, W, tb, cfg.K, cfg.L, cfg.T, sm_scale=cfg.scale, return_codes=True,
                                  return_counts=True, n_sink=n_sink, n_window=n_window)
         torch.cuda.synchronize()
-        assert torch.isfinite(r["out"]).all()
-        if check_at is None or n in check_at:
-            rel = check_prefix(cfg, data, tb, r, n, units, heads_per_unit, n_sink, n_window)
-            say(f"[{cfg.name}] n={n} (from {n0}) stride={tb['stride']} max_rel={rel:.2e}")
+        assert not torch.isnan(r["out"]).any()
+        if check_at is None or step in check_at:
+            rel = check_prefix(cfg, data, tb, r, lens, units, heads_per_unit, n_sink, n_window,
+                               W_heads=W_heads)
+            say(f"[{cfg.name}] lens={lens} stride={tb['stride']} max_rel={rel:.2e}")
     return lsh, data, keys, vals, W, q, ck, cv, tb
 
 
@@ -183,6 +200,26 @@ def test_full_size_decode_steps_128k():
     say(f"case cache full {cfg.name}")
     N = cfg.N
     schedule = [N - 8 + i for i in range(9)]
-    grow(cfg, schedule, n_sink=4, n_window=64, check_units=[(0, 3)], heads_per_unit=2, check_at=(N,),
-         device="cuda")
+    grow(cfg, schedule, n_sink=4, n_window=64, check_units=[(0, 3)], heads_per_unit=2,
+         check_at=(len(schedule) - 1,), device="cuda")
     torch.cuda.empty_cache()
+
+
+def test_ragged_growth():
+    # three sequences growing at different rates, one of them empty at first
+    # and one that stops growing; hybrid decode over each sequence's own keys
+    cfg = workloads.Config("cache-ragged", B=3, Hq=8, Hkv=2, N=5000, d=128, K=8, L=20, T=2, dtype="bf16",
+                           planted=4, a=0.8, offset="per_head", seed=36)
+    say("case ragged growth")
+    schedule = [[1000, 0, 300], [1001, 2500, 1024], [3000, 2500, 1025], [3000, 4999, 4096], [5000, 5000, 4097]]
+    grow(cfg, schedule, stride=1024, n_sink=2, n_window=100)
+
+
+def test_per_head_projection():
+    # one SimHash projection per kv head: the tables of unit (b, g) and the
+    # query codes of head h use W[g], W[h / G]
+    cfg = workloads.Config("per-head-w", B=2, Hq=8, Hkv=2, N=3000, d=128, K=9, L=16, T=2, dtype="bf16",
+                           planted=4, a=0.8, offset="per_unit", seed=37)
+    say("case per-head W")
+    Wh = workloads.per_head_projections(cfg, seed=1037)
+    grow(cfg, [1500, [3000, 2200]], stride=1024, W_heads=Wh)

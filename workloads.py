@@ -143,3 +143,12 @@ def generate(cfg: Config, device="cpu"):
         del picked, r
     return {"W": W, "keys": keys, "values": values,
             "q": torch.stack(qs), "planted": torch.stack(planted)}
+
+
+def per_head_projections(cfg: Config, seed: int, device="cpu"):
+    """One SimHash projection per kv head: W [Hkv, d, L*K], i.i.d. N(0, 1)
+    from its own seeded generator, cast to the configuration's dtype."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    W = torch.randn(cfg.Hkv, cfg.d, cfg.L * cfg.K, generator=g, device=device, dtype=torch.float32)
+    return W.to(cfg.torch_dtype)
