@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--config", type=int, default=4, help="workload id in workloads.CONFIGS (default: 128K GQA-8)")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the hybrid and growing-cache sections (profiling runs: every launch of a "
+                         "kernel then has the headline workload's shape)")
     ap.add_argument("--hybrid-sink", type=int, default=4,
                     help="sink keys of the hybrid decode timed beside the plain one")
     ap.add_argument("--hybrid-window", type=int, default=1024,
@@ -290,57 +293,59 @@ def main():
     dkernels = kernel_table(dtimes)
     dec_ms_steady = sum(dtimes[k][0] for k in DECODE_KERNELS) / args.steps
 
-    # the hybrid decode in steady state: the exact sink + window part runs in
-    # the merge kernel, the selection leaves those keys out
-    lsh.lsh_timing_begin()
-    for i in range(args.steps):
-        decode_hybrid(copies[i % R])
-    htimes = lsh.lsh_timing_end()
-    hk = kernel_table(htimes)
-    n_exact = min(N, args.hybrid_sink + args.hybrid_window)
-    hyb_ms = sum(htimes[k][0] for k in DECODE_KERNELS) / args.steps
-    decode_hybrid_steady = {
-        "n_sink": args.hybrid_sink, "n_window": args.hybrid_window,
-        "ms": round(hyb_ms, 5),
-        "qh_per_s": round(qh / (hyb_ms * 1e-3), 1),
-        "merge_avg_us": hk["merge"]["avg_us"],
-        # keys and values of the exact set, once per (sequence, kv head)
-        "exact_kv_bytes": int(B * Hkv * n_exact * 2 * d * esz),
-        "kernels": {k: v["avg_us"] for k, v in hk.items()},
-    }
+    decode_hybrid_steady = append_decode = None
+    if not args.headline_only:
+        # the hybrid decode in steady state: the exact sink + window set runs as
+        # extra attention workgroups, the selection leaves those keys out
+        lsh.lsh_timing_begin()
+        for i in range(args.steps):
+            decode_hybrid(copies[i % R])
+        htimes = lsh.lsh_timing_end()
+        hk = kernel_table(htimes)
+        n_exact = min(N, args.hybrid_sink + args.hybrid_window)
+        hyb_ms = sum(htimes[k][0] for k in DECODE_KERNELS) / args.steps
+        decode_hybrid_steady = {
+            "n_sink": args.hybrid_sink, "n_window": args.hybrid_window,
+            "ms": round(hyb_ms, 5),
+            "qh_per_s": round(qh / (hyb_ms * 1e-3), 1),
+            "merge_avg_us": hk["merge"]["avg_us"],
+            # keys and values of the exact set, once per (sequence, kv head)
+            "exact_kv_bytes": int(B * Hkv * n_exact * 2 * d * esz),
+            "kernels": {k: v["avg_us"] for k, v in hk.items()},
+        }
 
-    # multi-step decode over a growing cache: each step appends one key (the
-    # chunk it falls into is rebuilt) and runs the hybrid decode over the
-    # keys held.  The cache starts half-way into its last chunk, the average
-    # rebuild size; the tables of the first chunks stay as built.
-    c0 = copies[0]
-    n_start = max(1, N - stride // 2)
-    lsh.lsh_timing_begin()
-    ta0 = time.perf_counter()
-    for i in range(args.steps):
-        n = n_start + i
-        lsh.lsh_update_tables(c0["keys"], c0["W"], K, L, stride, n, n + 1, c0["offsets"], c0["indices"], None,
+        # multi-step decode over a growing cache: each step appends one key (the
+        # chunk it falls into is rebuilt) and runs the hybrid decode over the
+        # keys held.  The cache starts half-way into its last chunk, the average
+        # rebuild size; the tables of the first chunks stay as built.
+        c0 = copies[0]
+        n_start = max(1, N - stride // 2)
+        lsh.lsh_timing_begin()
+        ta0 = time.perf_counter()
+        for i in range(args.steps):
+            n = n_start + i
+            lsh.lsh_update_tables(c0["keys"], c0["W"], K, L, stride, n, n + 1, c0["offsets"], c0["indices"], None,
+                                  c0["bws"])
+            lsh.lsh_decode_attention_cached(c0["q"], c0["keys"], c0["values"], c0["W"], c0["indices"], c0["offsets"],
+                                            n + 1, K, L, T, stride, cfg.scale, args.hybrid_sink, args.hybrid_window,
+                                            c0["out"], c0["lse"], c0["nsel"], None, None, c0["dws"])
+        torch.cuda.synchronize()
+        ta1 = time.perf_counter()
+        atimes = lsh.lsh_timing_end()
+        # back to the tables of all N keys
+        lsh.lsh_update_tables(c0["keys"], c0["W"], K, L, stride, n_start, N, c0["offsets"], c0["indices"], None,
                               c0["bws"])
-        lsh.lsh_decode_attention_cached(c0["q"], c0["keys"], c0["values"], c0["W"], c0["indices"], c0["offsets"],
-                                        n + 1, K, L, T, stride, cfg.scale, args.hybrid_sink, args.hybrid_window,
-                                        c0["out"], c0["lse"], c0["nsel"], None, None, c0["dws"])
-    torch.cuda.synchronize()
-    ta1 = time.perf_counter()
-    atimes = lsh.lsh_timing_end()
-    # back to the tables of all N keys
-    lsh.lsh_update_tables(c0["keys"], c0["W"], K, L, stride, n_start, N, c0["offsets"], c0["indices"], None,
-                          c0["bws"])
-    torch.cuda.synchronize()
-    ak = kernel_table(atimes)
-    append_ms = sum(v[0] for v in atimes.values()) / args.steps
-    append_decode = {
-        "keys_held": [n_start + 1, n_start + args.steps],
-        "ms": round(append_ms, 5),
-        "wall_ms_per_step": round((ta1 - ta0) * 1e3 / args.steps, 5),
-        "update_ms": round(sum(atimes[k][0] for k in BUILD_KERNELS) / args.steps, 5),
-        "qh_per_s": round(qh / (append_ms * 1e-3), 1),
-        "kernels": {k: v["avg_us"] for k, v in ak.items()},
-    }
+        torch.cuda.synchronize()
+        ak = kernel_table(atimes)
+        append_ms = sum(v[0] for v in atimes.values()) / args.steps
+        append_decode = {
+            "keys_held": [n_start + 1, n_start + args.steps],
+            "ms": round(append_ms, 5),
+            "wall_ms_per_step": round((ta1 - ta0) * 1e3 / args.steps, 5),
+            "update_ms": round(sum(atimes[k][0] for k in BUILD_KERNELS) / args.steps, 5),
+            "qh_per_s": round(qh / (append_ms * 1e-3), 1),
+            "kernels": {k: v["avg_us"] for k, v in ak.items()},
+        }
 
     build_ms = sum(ktimes[k][0] for k in BUILD_KERNELS) / args.steps
     decode_ms = sum(ktimes[k][0] for k in DECODE_KERNELS) / args.steps
