@@ -20,9 +20,9 @@
 // partial per query head and split, for the log-sum-exp merge that follows.
 // Workgroups past the context splits take the hybrid decode's exact set
 // (for a sequence of n keys, keys [0, exact_head) and [n - exact_tail, n),
-// counted 0 .. ne - 1 across both ranges), a piece of exact_len keys each: every key is taken for every
-// head of the group and weighted 1 (u = 1), which is plain softmax attention
-// on the same tiles.
+// counted 0 .. ne - 1 across both ranges), a piece of exact_len keys each:
+// every key is taken for every head of the group and weighted 1 (u = 1),
+// which is plain softmax attention on the same tiles.
 #include <math.h>
 
 #include "lsh_device.h"
@@ -298,11 +298,11 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
 #pragma unroll
   for (int t = 0; t < 8; ++t) O[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  __syncthreads();   // ln u table in LDS
-
+  // the first tile's loads go out before waiting for the ln u table
   fill();
   int nt = min(kTile, rcnt);
   if (nt > 0) issue(nt);
+  __syncthreads();   // ln u table in LDS
   while (nt > 0) {
     // V of this tile into LDS (row-major, padded rows)
 #pragma unroll
