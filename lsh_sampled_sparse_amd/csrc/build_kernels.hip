@@ -97,7 +97,7 @@ __device__ __forceinline__ uint32_t push_code_bit(uint32_t s, float y) {
 }
 
 // Sign bits of one slab (NCT column tiles of 16 projection columns) for this
-// lane's key in each of the four key tiles: sg[a] collects the P = 4 NCT rows
+// lane's key in each of the KT key tiles: sg[a] collects the P = 4 NCT rows
 // of lane group g in row order (s = 2 s + [x > 0]).  `wrow` points at this
 // lane's W row (tile 0, row lane % 16, dims [32 g, 32 g + 32)) in LDS; rows
 // are `row` elements apart.  Software pipelined over column tiles: each of the
@@ -105,28 +105,28 @@ __device__ __forceinline__ uint32_t push_code_bit(uint32_t s, float y) {
 // accumulator sets, two W fragments), and the pairs are fenced so that the
 // VALU work issues while the matrix pipe runs; the W fragment of tile ct + 1
 // is read during tile ct.
-template <typename T, int NCT>
-__device__ __forceinline__ void slab_signs(const typename T::storage* wrow, int row, const Frag<T> (&A)[4],
-                                           uint32_t (&sg)[4]) {
+template <typename T, int NCT, int KT>
+__device__ __forceinline__ void slab_signs(const typename T::storage* wrow, int row, const Frag<T> (&A)[KT],
+                                           uint32_t (&sg)[KT]) {
 #pragma unroll
-  for (int a = 0; a < 4; ++a) sg[a] = 0u;
-  floatx4_t accA[4], accB[4];
+  for (int a = 0; a < KT; ++a) sg[a] = 0u;
+  floatx4_t accA[KT], accB[KT];
   Frag<T> Wa, Wb;
   auto wtile = [&](int ct) { return wrow + min(ct, NCT - 1) * 16 * row; };
   // MFMAs of one tile (W -> acc), paired with the signs of the previous one
-  auto half = [&](const Frag<T>& W, floatx4_t (&acc)[4], const floatx4_t (&prev)[4], bool signs) {
+  auto half = [&](const Frag<T>& W, floatx4_t (&acc)[KT], const floatx4_t (&prev)[KT], bool signs) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) acc[a] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < KT; ++a) acc[a] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      W.mma_step(q >> 2, A[q & 3], acc[q & 3]);       // k-step q / 4 of key tile q % 4
+    for (int q = 0; q < 4 * KT; ++q) {
+      W.mma_step(q / KT, A[q % KT], acc[q % KT]);     // k-step q / KT of key tile q % KT
       if (signs) sg[q >> 2] = push_code_bit(sg[q >> 2], prev[q >> 2][q & 3]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto signs_of = [&](const floatx4_t (&acc)[4]) {
+  auto signs_of = [&](const floatx4_t (&acc)[KT]) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < KT; ++a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sg[a] = push_code_bit(sg[a], acc[a][i]);
   };
@@ -150,9 +150,10 @@ __device__ __forceinline__ void slab_signs(const typename T::storage* wrow, int 
 }
 
 constexpr int kProjThreads = 256;              // 4 waves
-constexpr int kProjKeys = 256;                 // 64 keys per wave = 4 tiles of 16
+constexpr int kProjKT = 4;                     // key tiles of 16 per wave
+constexpr int kProjKeys = 64 * kProjKT;        // keys per workgroup
 
-// codes[u][l][n] for this workgroup's 256 keys.
+// codes[u][l][n] for this workgroup's kProjKeys keys.
 template <typename T, int KB>
 __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_codes_kernel(
     const typename T::storage* __restrict__ keys,   // [U][P][128]
@@ -180,13 +181,12 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
   const int u = blockIdx.y;
   const int n0 = n_first + blockIdx.x * kProjKeys;
   // this sequence's keys to (re)code: from the chunk holding its first new
-  // key (never below n_first) to its new length; 256-key blocks never
-  // straddle a chunk start, so a block is either wholly in or out
+  // key (never below n_first) to its new length
   const int b = u / Hkv;
   const int hi = seq_len_of(new_lens, b, N);
   int lo = n_first;
   if (old_lens) lo = max(lo, (seq_len_of(old_lens, b, hi) >> stride_log2) << stride_log2);
-  if (n0 >= hi || n0 < lo) return;
+  if (n0 >= hi || n0 + kProjKeys <= lo) return;
   WT += static_cast<size_t>(u % Hkv) * wt_head_stride;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4;
@@ -195,11 +195,11 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
 
   // key fragments (MFMA B operand): lane holds key lane & 15 of tile a, dims
   // [32 g, 32 g + 32)
-  Frag<T> A[4];
+  Frag<T> A[kProjKT];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int key = n0 + wave * 64 + a * 16 + (lane & 15);
-    const bool valid = key < hi;
+  for (int a = 0; a < kProjKT; ++a) {
+    const int key = n0 + wave * 16 * kProjKT + a * 16 + (lane & 15);
+    const bool valid = key >= lo && key < hi;
     A[a].load(kb + static_cast<size_t>(valid ? key : 0) * kHeadDim + g * 32, valid);
   }
 
@@ -232,15 +232,15 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
   for (int s = 0; s < ns; ++s) {
     const int buf = s & 1;
     if (s + 1 < ns) fetch(slab_of(s + 1));
-    uint32_t sg[4];
-    slab_signs<T, NCT>(&wt[buf][(lane & 15) * kRow + (lane >> 4) * 32], kRow, A, sg);
+    uint32_t sg[kProjKT];
+    slab_signs<T, NCT, kProjKT>(&wt[buf][(lane & 15) * kRow + (lane >> 4) * 32], kRow, A, sg);
     // codes of tables slab_of(s) * TPS + g * TPG + tt, staged per table row
     uint16_t* sb = stg[s & 1];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < kProjKT; ++a)
 #pragma unroll
       for (int tt = 0; tt < TPG; ++tt)
-        sb[(g * TPG + tt) * kStgRow + wave * 64 + a * 16 + (lane & 15)] =
+        sb[(g * TPG + tt) * kStgRow + wave * 16 * kProjKT + a * 16 + (lane & 15)] =
             static_cast<uint16_t>((sg[a] >> (tt * KB)) & kMask);
     if (s + 1 < ns) stash(buf ^ 1);
     __syncthreads();
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
     for (int c = tid; c < TPS * (kProjKeys / 8); c += kProjThreads) {
       const int r = c / (kProjKeys / 8), k8 = (c % (kProjKeys / 8)) * 8;
       const int t = slab_of(s) * TPS + r, key = n0 + k8;
-      if (t < L) {
+      if (t < L && key >= lo) {                       // lo is a chunk start: a multiple of 8
         const uint16_t* src = sb + r * kStgRow + k8;
         uint16_t* dst = cb + static_cast<size_t>(t) * P + key;
         if (key + 8 <= hi && (P & 7) == 0) {
