@@ -220,3 +220,23 @@ def test_binding_raises_without_gpu_work():
         lsh.lib()  # loads fine
         raise lsh.LshError(lsh.LSH_ERR_WORKSPACE)
     assert "WORKSPACE" in str(e.value)
+
+
+def test_header_is_plain_c():
+    # the boundary header compiles as C99 and as C++ (no torch or HIP types)
+    import shutil
+    import subprocess
+    for cc, args in (("gcc", ["-std=c99", "-x", "c"]), ("g++", ["-std=c++11", "-x", "c++"])):
+        if shutil.which(cc) is None:
+            pytest.skip(f"{cc} not available")
+        r = subprocess.run([cc, "-fsyntax-only", "-Wall", "-Wextra", "-Werror", *args, HEADER],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
