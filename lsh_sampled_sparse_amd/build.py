@@ -57,7 +57,31 @@ def build(verbose: bool = True) -> str:
     shutil.move(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_c_consumer(verbose)
     return LIB
+
+
+ROOT = os.path.dirname(HERE)
+C_CONSUMER_SRC = os.path.join(ROOT, "tests", "c_consumer", "abi_smoke.c")
+C_CONSUMER = os.path.join(ROOT, "tests", "c_consumer", "abi_smoke")
+
+
+def build_c_consumer(verbose: bool = True) -> str | None:
+    """The plain-C test program that drives the library through its header
+    alone (gcc, HIP runtime API for device memory); None when absent."""
+    if not os.path.exists(C_CONSUMER_SRC):
+        return None
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           f"-I{rocm}/include", f"-I{os.path.join(ROOT, 'include')}", C_CONSUMER_SRC, f"-L{HERE}", "-llsh_attn",
+           f"-L{rocm}/lib", "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../lsh_sampled_sparse_amd",
+           f"-Wl,-rpath,{rocm}/lib", "-o", C_CONSUMER]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C consumer build failed:\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {C_CONSUMER}")
+    return C_CONSUMER
 
 
 if __name__ == "__main__":
