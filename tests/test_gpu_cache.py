@@ -223,3 +223,20 @@ def test_per_head_projection():
     say("case per-head W")
     Wh = workloads.per_head_projections(cfg, seed=1037)
     grow(cfg, [1500, [3000, 2200]], stride=1024, W_heads=Wh)
+
+
+def test_ragged_growth_fp32():
+    # the fp32 attention kernel over ragged lengths, with a per-head W
+    cfg = workloads.Config("cache-ragged-f32", B=2, Hq=4, Hkv=2, N=2500, d=128, K=7, L=12, T=2, dtype="f32",
+                           planted=3, a=0.8, offset="per_unit", seed=38)
+    say("case ragged growth fp32")
+    Wh = workloads.per_head_projections(cfg, seed=1038)
+    grow(cfg, [[300, 0], [1025, 700], [2500, 1800]], stride=512, n_sink=3, n_window=40, W_heads=Wh)
+
+
+def test_k15_growth():
+    # 2^15 bucket starts per chunk: every rebuilt chunk rewrites 64 KB of offsets
+    cfg = workloads.Config("cache-k15", B=1, Hq=2, Hkv=1, N=1200, d=128, K=15, L=3, T=1, dtype="bf16",
+                           planted=1, a=0.95, offset="none", seed=39)
+    say("case K15 growth")
+    grow(cfg, [500, 513, 1200], stride=256)
