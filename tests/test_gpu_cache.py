@@ -240,3 +240,17 @@ def test_k15_growth():
                            planted=1, a=0.95, offset="none", seed=39)
     say("case K15 growth")
     grow(cfg, [500, 513, 1200], stride=256)
+
+
+def test_full_size_ragged_batch64():
+    # the batch-64 32K workload as a ragged cache: sequences held at different
+    # lengths, two decode steps that each append a key to every sequence
+    # (hybrid decode), one (sequence, kv head) unit checked at the end
+    cfg = workloads.CONFIGS[5]
+    say(f"case cache full ragged {cfg.name}")
+    N = cfg.N
+    base = [N - 2 - 1000 * (b % 5) for b in range(cfg.B)]
+    schedule = [base, [n + 1 for n in base], [n + 2 for n in base]]
+    grow(cfg, schedule, n_sink=4, n_window=64, check_units=[(37, 6)], heads_per_unit=2,
+         check_at=(len(schedule) - 1,), device="cuda")
+    torch.cuda.empty_cache()
