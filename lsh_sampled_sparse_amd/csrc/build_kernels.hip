@@ -311,7 +311,6 @@ __global__ void zero_codes_kernel(uint16_t* __restrict__ codes, size_t rows, int
 // code 0xffff, whose every digit is the largest, so they stay behind all keys
 // in every pass and the loops need no validity tests.
 // ---------------------------------------------------------------------------
-constexpr int kSortMaxThreads = 512;
 constexpr int kSortE = 32;              // elements per thread
 constexpr int kDigitBits = 5;
 constexpr int kCntWords = 16;           // 32 digit counters of 16 bits per thread
