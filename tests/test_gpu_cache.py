@@ -254,3 +254,13 @@ def test_full_size_ragged_batch64():
     grow(cfg, schedule, n_sink=4, n_window=64, check_units=[(37, 6)], heads_per_unit=2,
          check_at=(len(schedule) - 1,), device="cuda")
     torch.cuda.empty_cache()
+
+
+def test_per_head_projection_gqa3_hybrid():
+    # per-head W with three query heads per kv head (the query hash then
+    # works one (sequence, kv head) group per workgroup) and a hybrid decode
+    cfg = workloads.Config("per-head-w-gqa3", B=2, Hq=9, Hkv=3, N=1800, d=128, K=10, L=12, T=2, dtype="bf16",
+                           planted=3, a=0.8, offset="per_head", seed=40)
+    say("case per-head W gqa3")
+    Wh = workloads.per_head_projections(cfg, seed=1040)
+    grow(cfg, [[1800, 900]], stride=512, n_sink=2, n_window=50, W_heads=Wh)
