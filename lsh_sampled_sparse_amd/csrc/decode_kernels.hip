@@ -189,12 +189,16 @@ __global__ __launch_bounds__(256) void qhash_kernel(const typename T::storage* _
 }
 
 // ---------------------------------------------------------------------------
-// count_select: one workgroup per (query head, key chunk).
+// count_select: one workgroup of NT threads per (query head, key chunk).
+// Every workgroup runs the same chain of dependent loads (query codes, bucket
+// starts, bucket entries), so when there are many (head, chunk) pairs smaller
+// workgroups let more of them be resident at once; with few pairs, large
+// workgroups spread each walk over more lanes.
 // ---------------------------------------------------------------------------
-constexpr int kCountThreads = 1024;
 constexpr int kCountUnroll = 8;   // index loads each thread keeps in flight
 
-__global__ __launch_bounds__(kCountThreads) void count_select_kernel(
+template <int NT>
+__global__ __launch_bounds__(NT) void count_select_kernel(
     const uint16_t* __restrict__ qcodes,   // [BH][L]
     const uint16_t* __restrict__ indices,  // [U][L][P] chunk-major, chunk-relative key indices
     const uint16_t* __restrict__ offsets,  // [U][L][nJP][2^K] bucket starts inside each chunk
@@ -207,6 +211,8 @@ __global__ __launch_bounds__(kCountThreads) void count_select_kernel(
   extern __shared__ __attribute__((aligned(16))) uint32_t cnt[];   // one byte per key of the chunk
   __shared__ int seg_start[256];
   __shared__ int seg_v[257];
+  constexpr int kCountThreads = NT;
+  static_assert(NT >= 256, "the first four waves hold one table per thread");
   __shared__ int wave_tot[kCountThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int J = blockIdx.x, bh = blockIdx.y;
@@ -686,12 +692,23 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
                         a.lnu_table, BH, a.K, a.L, a.T, head_blocks, G, a.Hkv, w_head_stride);
   if (e != hipSuccess) return e;
   const size_t lds = ((static_cast<size_t>(1) << a.stride_log2) + 3) & ~static_cast<size_t>(3);
-  e = ensure_lds_limit(reinterpret_cast<const void*>(count_select_kernel), lds);
+  // 1024-thread workgroups while the (head, chunk) pairs fit in about two
+  // per CU, 256-thread ones beyond that
+  const bool small_wg = static_cast<long long>(a.nJ) * BH > 1024;
+  const void* cs = small_wg ? reinterpret_cast<const void*>(count_select_kernel<256>)
+                            : reinterpret_cast<const void*>(count_select_kernel<1024>);
+  e = ensure_lds_limit(cs, lds);
   if (e != hipSuccess) return e;
-  e = launch(kKCountSelect, count_select_kernel, dim3(a.nJ, BH), dim3(kCountThreads),
-             static_cast<unsigned>(lds), stream, static_cast<const uint16_t*>(a.qcodes),
-             a.indices, a.offsets, a.Hq, a.Hkv, a.N, a.P, a.K, a.L, a.T, a.stride_log2, a.nJ, a.nJP, a.bitmask,
-             a.chunk_nsel, a.counts, a.n_sink, a.n_window, a.seq_lens);
+  if (small_wg)
+    e = launch(kKCountSelect, count_select_kernel<256>, dim3(a.nJ, BH), dim3(256), static_cast<unsigned>(lds),
+               stream, static_cast<const uint16_t*>(a.qcodes), a.indices, a.offsets, a.Hq, a.Hkv, a.N, a.P, a.K,
+               a.L, a.T, a.stride_log2, a.nJ, a.nJP, a.bitmask, a.chunk_nsel, a.counts, a.n_sink, a.n_window,
+               a.seq_lens);
+  else
+    e = launch(kKCountSelect, count_select_kernel<1024>, dim3(a.nJ, BH), dim3(1024), static_cast<unsigned>(lds),
+               stream, static_cast<const uint16_t*>(a.qcodes), a.indices, a.offsets, a.Hq, a.Hkv, a.N, a.P, a.K,
+               a.L, a.T, a.stride_log2, a.nJ, a.nJP, a.bitmask, a.chunk_nsel, a.counts, a.n_sink, a.n_window,
+               a.seq_lens);
   if (e != hipSuccess) return e;
   if constexpr (sizeof(S) == 2)
     e = launch_attend_bf16(a, stream);
