@@ -3,11 +3,13 @@
 // MagicPIG builds per-table hash buckets of the keys at prefill and names an
 // optimised hash-table construction (MagicPIG project summary on sourcepulse,
 // "Highlighted Details").  Here the build is:
-//   transpose_w     W [d, L*K] -> WT [LKpad, d] (zero-padded columns), so that
-//                   a projection column is one contiguous row
+//   transpose_w     W [d, L*K] -> -WT [LKpad, d] (negated, rows permuted,
+//                   zero rows for padding), so that a projection column is
+//                   one contiguous row
 //   project_codes   SimHash codes of every key: a dense bf16 (or fp32) MFMA
-//                   contraction keys x W with fp32 accumulation, sign bits
-//                   packed with wave ballots, codes written table-major
+//                   contraction keys x W with fp32 accumulation, each lane
+//                   packing its own key's code bits from its accumulators (one
+//                   funnel shift per bit), codes written table-major
 //   chunk_sort      per (table, key chunk): a stable LSD radix sort of the
 //                   chunk's keys by code into the chunk's own region of the
 //                   index array, with the chunk's bucket offsets

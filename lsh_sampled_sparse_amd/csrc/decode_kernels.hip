@@ -10,10 +10,12 @@
 //                  count collisions in LDS byte counters, and emit the
 //                  selection bitmask (count >= T)
 //   attend         per (sequence, kv head, context split): union of the
-//                  group's selections, ballot compaction, gathered K rows,
-//                  q.k on MFMA, 1/u weights, online softmax and P.V in fp32,
-//                  partial state (m, l, acc) per query head
-//   merge          log-sum-exp merge of the split partials (the stable merge
+//                  group's selections, ballot compaction, gathered K/V rows,
+//                  q.k on MFMA, 1/u weights, online softmax in fp32 and P.V
+//                  (MFMA with P in bf16 high + low parts for bf16 K/V, FMAs
+//                  for fp32), partial state (m, l, acc) per query head; with
+//                  an exact set, extra workgroups attend it with unit weights
+//   merge          log-sum-exp merge of the partials (the stable merge
 //                  MAC-Attention also uses, "MAC-Attention" README,
 //                  "How It Works")
 #include <math.h>
