@@ -14,9 +14,12 @@ eager`` launches them one by one instead); the decode alone is reported under
 ``breakdown``.  The ``roofline`` object is for the kernel with the largest
 total time, from the library's per-dispatch timing events in a separate eager
 pass over the same steps; ``cpu_baseline`` times the fp64 CPU oracle on a
-bounded sample of the same workload.
+bounded sample of the same workload.  Two more sections time consecutive
+hybrid decodes (exact sinks + recent window) and decode steps that append one
+key to a growing cache and update its tables (``--headline-only`` skips them).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4] [--launch graph|eager]
+                       [--hybrid-sink S] [--hybrid-window W] [--headline-only] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
