@@ -60,11 +60,11 @@ struct Bf16Pairs {
   bf16x2_t p[4];
 };
 
-// arccos on [-1, 1] from the approximation of Abramowitz & Stegun 4.4.46
-// (Hastings): acos(x) = sqrt(1 - x) * sum_{i<8} a_i x^i for 0 <= x <= 1 with
-// |error| <= 2e-8, and acos(-x) = pi - acos(x).  In fp32 the error is about
-// 3e-7 rad, i.e. a few 1e-6 in ln u.
-__device__ __forceinline__ float acos_as(float c) {
+// arccos of |c| in [0, 1] from the approximation of Abramowitz & Stegun
+// 4.4.46 (Hastings): acos(x) = sqrt(1 - x) * sum_{i<8} a_i x^i with
+// |error| <= 2e-8 in exact arithmetic (about 3e-7 rad in fp32).  The angle
+// itself is theta = r for c >= 0 and pi - r for c < 0.
+__device__ __forceinline__ float acos_abs_as(float c) {
   const float x = fabsf(c);
   float p = -0.0012624911f;
   p = fmaf(p, x, 0.0066700901f);
@@ -74,20 +74,27 @@ __device__ __forceinline__ float acos_as(float c) {
   p = fmaf(p, x, 0.0889789874f);
   p = fmaf(p, x, -0.2145988016f);
   p = fmaf(p, x, 1.5707963050f);
-  const float r = __builtin_amdgcn_sqrtf(1.f - x) * p;
-  return c < 0.f ? kPiF - r : r;
+  return __builtin_amdgcn_sqrtf(1.f - x) * p;
 }
 
-// ln u of a key at cosine c with the query: T K ln(1 - theta / pi) + g(theta),
-// g interpolated from the (value, slope) table; clamped at ln(1e-30).
-__device__ __forceinline__ float lnu_of_cos(float c, const float2* tab2, float TKln2) {
-  const float th = acos_as(fminf(1.f, fmaxf(-1.f, c)));
+// ln u of a key at cosine c with the query: T K ln p + g(theta) with
+// p = 1 - theta / pi, g from the interval quadratics (lnu_interval); clamped
+// at ln(1e-30).  For c < 0, p = r / pi straight from r = acos(|c|), so the
+// keys nearly opposite the query (theta -> pi, the largest 1/u) keep the
+// relative accuracy of r instead of the cancellation in 1 - theta / pi.
+__device__ __forceinline__ float lnu_of_cos(float c, const float4* tab4, float TKln2) {
+  const float cc = fminf(1.f, fmaxf(-1.f, c));
+  const float r = acos_abs_as(cc);
+  const bool neg = cc < 0.f;
+  const float th = neg ? kPiF - r : r;
   const float x = th * (static_cast<float>(kLnuTable) / kPiF);
   const int j = min(static_cast<int>(x), kLnuTable - 1);
-  const float2 e = tab2[j];
-  const float g = fmaf(x - static_cast<float>(j), e.y, e.x);
-  // log2 of p = 1 - theta / pi with the hardware log (absolute error ~1e-7)
-  const float l2p = __builtin_amdgcn_logf(fmaxf(0.f, 1.f - th * (1.0f / kPiF)));
+  const float4 e = tab4[j];
+  const float f = x - static_cast<float>(j);
+  const float g = fmaf(f, fmaf(f, e.z, e.y), e.x);
+  // log2 p with the hardware log (absolute error ~1e-7)
+  const float rp = r * (1.0f / kPiF);
+  const float l2p = __builtin_amdgcn_logf(neg ? rp : 1.f - rp);
   return fmaxf(fmaf(TKln2, l2p, g), kLnUFloorF);
 }
 
@@ -133,11 +140,11 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
     const uint16_t* __restrict__ keys,     // [U][N][128]
     const uint16_t* __restrict__ values,   // [U][N][128]
     const uint32_t* __restrict__ bitmask,  // [B*Hq][Nw]
-    const float* __restrict__ lnu_tab,     // [kLnuTable + 1]
+    const double* __restrict__ lnu_samples,   // [kLnuSamples]
     int Hq, int Hkv, int N, int P, int K, int Tth, float scale, int split_len, int nsplit,
     int n_sink, int n_window, int exact_len, int nexact, const int32_t* __restrict__ seq_lens,
     float* __restrict__ partials) {        // [B*Hq][nsplit + nexact][130]
-  __shared__ float2 tab2[kLnuTable];      // (g_j, g_{j+1} - g_j)
+  __shared__ float4 tab4[kLnuTable];      // interval quadratics of g
   __shared__ int ring_idx[kWaves][kRingN];
   __shared__ uint16_t ring_hm[kWaves][kRingN];
   __shared__ __attribute__((aligned(16))) uint16_t vt[kWaves][kTile * kVRow];
@@ -166,7 +173,7 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
   const float TKln2 = static_cast<float>(Tth * K) * 0.69314718055994531f;
 
   for (int i = tid; i < kLnuTable; i += 256)
-    tab2[i] = k0 ? make_float2(0.f, 0.f) : make_float2(lnu_tab[i], lnu_tab[i + 1] - lnu_tab[i]);
+    tab4[i] = nolnu ? make_float4(0.f, 0.f, 0.f, 0.f) : lnu_interval(lnu_samples, i);
 
   // q fragments (MFMA A operand): lane holds head sl, dims 32 k + 8 g4 + [0, 8)
   // of k-step k (the K fragments use the same order)
@@ -334,8 +341,8 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float x0 = S0[i], x1 = S1[i];
-      const float u0 = nolnu ? 0.f : lnu_of_cos(x0 * rq[i] * rk0, tab2, TKln2);
-      const float u1 = nolnu ? 0.f : lnu_of_cos(x1 * rq[i] * rk1, tab2, TKln2);
+      const float u0 = nolnu ? 0.f : lnu_of_cos(x0 * rq[i] * rk0, tab4, TKln2);
+      const float u1 = nolnu ? 0.f : lnu_of_cos(x1 * rq[i] * rk1, tab4, TKln2);
       const int hh = 4 * g4 + i;
       const bool ok = hh < G;
       lg[0][i] = (ok && ((hm0 >> hh) & 1)) ? fmaf(scale, x0, -u0) : -INFINITY;
@@ -440,7 +447,7 @@ hipError_t launch_attend_bf16(const DecodeArgs& a, hipStream_t stream) {
   const uint16_t* kp = static_cast<const uint16_t*>(a.keys);
   const uint16_t* vp = static_cast<const uint16_t*>(a.values);
   const uint32_t* bm = a.bitmask;
-  const float* lt = a.lnu_table;
+  const double* lt = a.lnu_samples;
   if (G <= 4)
     return launch(kKAttend, attend_bf16_kernel<1>, grid, dim3(256), 0, stream, qp, kp, vp, bm, lt, a.Hq,
                   a.Hkv, a.N, a.P, a.K, a.T, a.scale, a.split_len, a.nsplit, a.n_sink, a.n_window, a.exact_len, a.nexact, a.seq_lens,

@@ -33,9 +33,10 @@ constexpr float kLnUFloor = -69.07755278982137f;   // ln(1e-30)
 //
 // u(theta) = P[Binomial(L, P) >= T] with P = (1 - theta/pi)^K.  Writing
 // ln u = T ln P + g(P),  g(P) = ln sum_{i>=T} C(L,i) P^(i-T) (1-P)^(L-i),
-// g is smooth on [0, 1] (g(0) = ln C(L,T), g(1) = 0), so it is tabulated in
-// fp64 at theta_j = j pi / kLnuTable and interpolated linearly; T ln P is
-// evaluated exactly from ln p = log1p(-theta/pi).
+// g is smooth on [0, 1] (g(0) = ln C(L,T), g(1) = 0), so it is sampled in
+// fp64 at theta_t = t pi / (2 kLnuTable) and interpolated by one quadratic per
+// interval of width pi / kLnuTable (through its start, middle and end); T ln P
+// = T K ln p is evaluated from p itself.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double wave_max_f64(double v) {
 #pragma unroll
@@ -78,14 +79,21 @@ __device__ double lnu_correction_wave(double theta, int K, int L, int T, const d
   return m + log(sum);
 }
 
-__device__ __forceinline__ float log_inclusion(float cosv, const float* tab, float TK) {
+// ln u at cosine cosv (fp32 K/V path).  r = acos(|c|); theta = r for c >= 0
+// and pi - r for c < 0, where p = 1 - theta / pi = r / pi is taken from r
+// directly so that it keeps r's relative accuracy as theta -> pi.
+__device__ __forceinline__ float log_inclusion(float cosv, const float4* tab, float TK) {
   const float c = fminf(1.f, fmaxf(-1.f, cosv));
-  const float th = acosf(c);
+  const float r = acosf(fabsf(c));
+  const bool neg = c < 0.f;
+  const float th = neg ? kPi - r : r;
   const float x = th * (static_cast<float>(kLnuTable) / kPi);
   const int j = min(static_cast<int>(x), kLnuTable - 1);
   const float fr = x - static_cast<float>(j);
-  const float g = fmaf(fr, tab[j + 1] - tab[j], tab[j]);
-  const float lnp = log1pf(-th * (1.0f / kPi));
+  const float4 e = tab[j];
+  const float g = fmaf(fr, fmaf(fr, e.z, e.y), e.x);
+  const float rp = r * (1.0f / kPi);
+  const float lnp = neg ? logf(rp) : log1pf(-rp);
   return fmaxf(fmaf(TK, lnp, g), kLnUFloor);
 }
 
@@ -101,7 +109,7 @@ constexpr int kQHeads = 16;
 template <typename T>
 __global__ __launch_bounds__(256) void qhash_kernel(const typename T::storage* __restrict__ q,
                                                     const typename T::storage* __restrict__ W,
-                                                    uint16_t* __restrict__ qcodes, float* __restrict__ lnu_tab,
+                                                    uint16_t* __restrict__ qcodes, double* __restrict__ lnu_samples,
                                                     int BH, int K, int L, int Tth, int head_blocks,
                                                     int G, int Hkv, size_t w_head_stride) {
   __shared__ __attribute__((aligned(16))) float qs[kQHeads][kHeadDim];
@@ -116,8 +124,8 @@ __global__ __launch_bounds__(256) void qhash_kernel(const typename T::storage* _
                 lgamma(static_cast<double>(L - tid) + 1.0);
     __syncthreads();
     const int j = ((blockIdx.y - head_blocks) * gridDim.x + blockIdx.x) * 4 + wave;
-    const double g = lnu_correction_wave(j * (3.14159265358979323846 / kLnuTable), K, L, Tth, lc, lane);
-    if (j <= kLnuTable && lane == 0) lnu_tab[j] = static_cast<float>(g);
+    const double g = lnu_correction_wave(j * (3.14159265358979323846 / (2 * kLnuTable)), K, L, Tth, lc, lane);
+    if (j < kLnuSamples && lane == 0) lnu_samples[j] = g;
     return;
   }
   // a workgroup hashes hpb heads: 16 with one shared W, or the G heads of
@@ -395,12 +403,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
     const typename T::storage* __restrict__ keys,    // [U][N][128]
     const typename T::storage* __restrict__ values,  // [U][N][128]
     const uint32_t* __restrict__ bitmask,            // [BH][Nw]
-    const float* __restrict__ lnu_tab,               // [kLnuTable + 1]
+    const double* __restrict__ lnu_samples,          // [kLnuSamples]
     int Hq, int Hkv, int N, int P, int K, int Tth, float scale, int split_len, int nsplit,
     int n_sink, int n_window, int exact_len, int nexact, const int32_t* __restrict__ seq_lens,
     float* __restrict__ partials) {                  // [BH][nsplit + nexact][130]
   using S = typename T::storage;
-  __shared__ float tab[kLnuTable + 1];
+  __shared__ float4 tab[kLnuTable];
   __shared__ float qn[16];
   __shared__ int sidx[4][kRing];
   __shared__ uint16_t shm[4][kRing];
@@ -428,7 +436,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
   const int npart = nsplit + nexact;
   const float TK = static_cast<float>(Tth * K);
 
-  for (int i = tid; i <= kLnuTable; i += kAttThreads) tab[i] = k0 ? 0.f : lnu_tab[i];
+  for (int i = tid; i < kLnuTable; i += kAttThreads)
+    tab[i] = nolnu ? make_float4(0.f, 0.f, 0.f, 0.f) : lnu_interval(lnu_samples, i);
   // query fragments: lane holds head (lane & 15), dims [32 (lane >> 4), +32)
   const int qh = lane & 15;
   Frag<T> Qf;
@@ -673,7 +682,7 @@ static hipError_t launch_attend(const DecodeArgs& a, hipStream_t stream) {
   using S = typename T::storage;
   return launch(kKAttend, attend_kernel<T, GM>, dim3(a.nsplit + a.nexact, a.B * a.Hkv), dim3(kAttThreads), 0, stream,
                 static_cast<const S*>(a.q), static_cast<const S*>(a.keys), static_cast<const S*>(a.values),
-                static_cast<const uint32_t*>(a.bitmask), static_cast<const float*>(a.lnu_table), a.Hq, a.Hkv,
+                static_cast<const uint32_t*>(a.bitmask), static_cast<const double*>(a.lnu_samples), a.Hq, a.Hkv,
                 a.N, a.P, a.K, a.T, a.scale, a.split_len, a.nsplit, a.n_sink, a.n_window, a.exact_len, a.nexact, a.seq_lens,
                 a.partials);
 }
@@ -688,10 +697,10 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const size_t w_head_stride = a.w_heads > 1 ? static_cast<size_t>(kHeadDim) * a.L * a.K : 0;
   const int tpw = a.K > 0 ? 64 / a.K : 256;
   const int xblocks = (a.L + tpw - 1) / tpw;
-  const int tab_blocks = (kLnuTable + 1 + xblocks * 4 - 1) / (xblocks * 4);   // 4 entries per workgroup
+  const int tab_blocks = (kLnuSamples + xblocks * 4 - 1) / (xblocks * 4);   // 4 samples per workgroup
   hipError_t e = launch(kKQhash, qhash_kernel<T>, dim3(xblocks, head_blocks + tab_blocks), dim3(256), 0,
                         stream, static_cast<const S*>(a.q), static_cast<const S*>(a.W), a.qcodes,
-                        a.lnu_table, BH, a.K, a.L, a.T, head_blocks, G, a.Hkv, w_head_stride);
+                        a.lnu_samples, BH, a.K, a.L, a.T, head_blocks, G, a.Hkv, w_head_stride);
   if (e != hipSuccess) return e;
   const size_t lds = ((static_cast<size_t>(1) << a.stride_log2) + 3) & ~static_cast<size_t>(3);
   // 1024-thread workgroups while the (head, chunk) pairs fit in about two

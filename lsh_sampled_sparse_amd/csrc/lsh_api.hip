@@ -87,7 +87,7 @@ DecodeLayout decode_layout(int B, int Hq, int Hkv, int N, int L, const Geometry&
   w.qcodes = off;     off = align_up(off + BH * L * sizeof(uint16_t));
   w.bitmask = off;    off = align_up(off + BH * ((N + 31) / 32) * sizeof(uint32_t));
   w.chunk_nsel = off; off = align_up(off + BH * g.nJ * sizeof(int32_t));
-  w.lnu = off;        off = align_up(off + (lsh::kLnuTable + 1) * sizeof(float));
+  w.lnu = off;        off = align_up(off + lsh::kLnuSamples * sizeof(double));
   // one partial per head and context split, plus the exact set's pieces
   // partial slots: nsplit <= min(ceil(N / 256), ceil(512 / units)), a bound
   // that grows with N, so the workspace size at a cache's capacity covers
@@ -310,7 +310,7 @@ lsh_status lsh_decode_attention_cached(const void* q, const void* keys, const vo
   a.qcodes = q_codes ? q_codes : reinterpret_cast<uint16_t*>(ws + w.qcodes);
   a.bitmask = reinterpret_cast<uint32_t*>(ws + w.bitmask);
   a.chunk_nsel = reinterpret_cast<int32_t*>(ws + w.chunk_nsel);
-  a.lnu_table = reinterpret_cast<float*>(ws + w.lnu);
+  a.lnu_samples = reinterpret_cast<double*>(ws + w.lnu);
   a.partials = reinterpret_cast<float*>(ws + w.partials);
   a.out = out;
   a.lse = lse;

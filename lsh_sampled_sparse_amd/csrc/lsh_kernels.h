@@ -41,7 +41,7 @@ struct DecodeArgs {
   uint16_t* qcodes;      // [B*Hq][L]
   uint32_t* bitmask;     // [B*Hq][Nw]
   int32_t* chunk_nsel;   // [B*Hq][nJ]
-  float* lnu_table;      // [kLnuTable + 1]
+  double* lnu_samples;   // [kLnuSamples]: g(theta) at theta_t = t pi / (2 kLnuTable)
   float* partials;       // [B*Hq][nsplit + nexact][130]
   float* out;            // [B*Hq][128]
   float* lse;            // optional [B*Hq]
@@ -74,6 +74,17 @@ __host__ __device__ inline void exact_range(int n_sink, int n_window, int n, int
 }
 
 constexpr int kLnuTable = 1024;   // ln-u correction table intervals over theta in [0, pi]
+constexpr int kLnuSamples = 2 * kLnuTable + 1;   // fp64 samples of g: both ends and the middle of every interval
+
+// Quadratic of ln-u correction interval j, from the fp64 samples of g at its
+// start, middle and end: g(theta_j + f h) ~ x + f (y + f z) for f in [0, 1]
+// (h = pi / kLnuTable).  The coefficients are formed in fp64 and rounded
+// once, so the small y and z keep their relative precision.
+__device__ __forceinline__ float4 lnu_interval(const double* s, int j) {
+  const double g0 = s[2 * j], gm = s[2 * j + 1], g1 = s[2 * j + 2];
+  return make_float4(static_cast<float>(g0), static_cast<float>(-3.0 * g0 + 4.0 * gm - g1),
+                     static_cast<float>(2.0 * g0 - 4.0 * gm + 2.0 * g1), 0.f);
+}
 constexpr int kPartialStride = 130;
 constexpr int kMaxExactSplits = 16;   // partial slots per head reserved for the exact set
 
