@@ -245,13 +245,14 @@ def test_k15_growth():
 def test_full_size_ragged_batch64():
     # the batch-64 32K workload as a ragged cache: sequences held at different
     # lengths, two decode steps that each append a key to every sequence
-    # (hybrid decode), one (sequence, kv head) unit checked at the end
+    # (hybrid decode), two (sequence, kv head) units checked at the end: unit
+    # 511 = (63, 7) sits past 2^31 elements of the [units, L, n_cap] arrays
     cfg = workloads.CONFIGS[5]
     say(f"case cache full ragged {cfg.name}")
     N = cfg.N
     base = [N - 2 - 1000 * (b % 5) for b in range(cfg.B)]
     schedule = [base, [n + 1 for n in base], [n + 2 for n in base]]
-    grow(cfg, schedule, n_sink=4, n_window=64, check_units=[(37, 6)], heads_per_unit=2,
+    grow(cfg, schedule, n_sink=4, n_window=64, check_units=[(37, 6), (63, 7)], heads_per_unit=2,
          check_at=(len(schedule) - 1,), device="cuda")
     torch.cuda.empty_cache()
 

@@ -76,8 +76,9 @@ def check_case(cfg, data, units=None, heads_per_unit=None, stride=None, step=0, 
         bad_tables += PAR.check_tables(to_np(tb["offsets"][b, g]), to_np(tb["indices"][b, g]),
                                        gcodes, ref, cfg.K, stride)
         hs = list(range(g * G, (g + 1) * G))
-        if heads_per_unit is not None:
-            hs = hs[:heads_per_unit]
+        nh = heads_per_unit.get((b, g)) if isinstance(heads_per_unit, dict) else heads_per_unit
+        if nh is not None:
+            hs = hs[:nh]
         for h in hs:
             if hybrid:
                 rr = O.hybrid_decode_head(q[b, h], ku, vu, W, ref["offsets"], ref["indices"],
@@ -192,11 +193,16 @@ def test_deterministic():
 
 # ----------------------------------------------------------------- full sizes
 
+# Sampled units.  Per-key arrays are [units, L, N] (codes, indices) and
+# [units, N, d] (keys, values): at 64 x 8 units of 32K keys and L = 150 the
+# codes and indices of unit u start at element u * L * N = u * 4.9e6, so the
+# units from 437 on lie past 2^31 elements; (63, 7) is unit 511 (2.5e9).
+# Heads per unit: an int for every unit, or a dict per unit (None = all).
 FULL = {
     2: dict(units=None, heads=None, steps=[0]),
     3: dict(units=[(0, 0), (11, 5)], heads=4, steps=[0]),
-    4: dict(units=[(0, 1)], heads=3, steps=[0]),
-    5: dict(units=[(37, 6)], heads=2, steps=[0, 7]),
+    4: dict(units=[(0, 1), (0, 3)], heads={(0, 1): 3, (0, 3): None}, steps=[0]),
+    5: dict(units=[(37, 6), (63, 7)], heads=2, steps=[0, 7]),
 }
 
 
@@ -283,5 +289,23 @@ def test_hybrid_full_size_128k():
     say(f"case hybrid full {cfg.name}")
     data = workloads.generate(cfg, device="cuda")
     check_case(cfg, data, units=[(0, 2)], heads_per_unit=2, n_sink=4, n_window=1024)
+    del data
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------ centred-plant variant
+# queries planted on the keys less their shared offset: the selection is then
+# sparse (a few percent of the keys per head), the regime the pages argue
+# sampling is for
+
+@pytest.mark.parametrize("cfg_id,units,heads", [(4, [(0, 2)], 4), (2, [(0, 0), (0, 5)], None)])
+def test_full_size_centred_plant(cfg_id, units, heads):
+    cfg = workloads.CONFIGS[cfg_id].with_(plant="centred")
+    say(f"case full centred cfg{cfg_id} {cfg.name}")
+    data = workloads.generate(cfg, device="cuda")
+    tb, r = check_case(cfg, data, units=units, heads_per_unit=heads)
+    frac = float(r["nsel"].float().mean()) / cfg.N
+    say(f"  centred plant: mean selected fraction per head {frac:.4f}")
+    assert frac < 0.2
     del data
     torch.cuda.empty_cache()
