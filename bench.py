@@ -1,22 +1,26 @@
 """Throughput of LSH-sampled decode attention on one MI355X.
 
-One step is one pass of the whole path over one batch of synthetic input:
-the table build of the batch's keys (SimHash projection, bucket build) and
-one decode step (query hash, probe and count, selection, weighted attention,
-log-sum-exp merge).  Steps rotate over ``--copies`` independent input copies;
-step i builds the tables of copy i mod R and decodes copy (i - 1) mod R, whose
-tables were built one step earlier, so the decode does not read tables that
-the build just left in the 256 MB last-level cache.
+The metric is decode query-heads per second: one step is one decode step of
+every query head of the batch (query hash, bucket probe and collision count,
+selection, 1/u-weighted attention over the selected keys, log-sum-exp merge)
+against tables built at prefill.  The tables of every input copy are built
+before the timed region, as prefill does; the build is timed on its own and
+reported under ``breakdown.build`` (with the build + decode step), since it
+runs once per sequence, not once per generated token.
 
-Prints ONE JSON line.  ``value`` is query-heads per second of whole steps
-(build + decode), timed over steps replayed from HIP graphs (``--launch
-eager`` launches them one by one instead); the decode alone is reported under
-``breakdown``.  The ``roofline`` object is for the kernel with the largest
-total time, from the library's per-dispatch timing events in a separate eager
-pass over the same steps; ``cpu_baseline`` times the fp64 CPU oracle on a
-bounded sample of the same workload.  Two more sections time consecutive
-hybrid decodes (exact sinks + recent window) and decode steps that append one
-key to a growing cache and update its tables (``--headline-only`` skips them).
+Steps rotate over ``--copies`` independent input copies (keys, values,
+tables, queries), so the decode never finds the previous step's K/V rows in
+the 256 MB last-level cache.  ``value`` comes from steps replayed from HIP
+graphs (one per copy); eager launches of the same steps are timed too.
+``roofline`` is the dominant decode kernel's fraction of the HBM peak on its
+algorithmic bytes (per-dispatch HIP events on the library's stream, in a
+separate eager pass) and, under ``roofline.decode``, the whole decode's.
+``breakdown`` carries every kernel's figures, the measured selection, the
+estimate's relative L2 error against exact attention (computed on the GPU by
+the same kernels with every key in the exact set), the table build, a
+centred-plant variant of the workload (sparse selection), the hybrid decode
+and decode steps over a growing cache.  ``cpu_baseline`` times the fp64 CPU
+oracle's decode on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4] [--launch graph|eager]
                        [--hybrid-sink S] [--hybrid-window W] [--headline-only] [--no-cpu-baseline]
@@ -59,14 +63,14 @@ def parse():
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
-                    help="skip the hybrid and growing-cache sections (profiling runs: every launch of a "
-                         "kernel then has the headline workload's shape)")
+                    help="time only the headline decode (profiling runs: every decode launch then has the "
+                         "headline workload's shape and selection)")
     ap.add_argument("--hybrid-sink", type=int, default=4,
                     help="sink keys of the hybrid decode timed beside the plain one")
     ap.add_argument("--hybrid-window", type=int, default=1024,
                     help="recent-window keys of the hybrid decode timed beside the plain one")
     ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
-                    help="replay each step from a HIP graph (default) or launch it eagerly")
+                    help="launch mode behind `value` (both are timed and reported)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -108,6 +112,25 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": 4 * n, "launches": 5, "kernel": "torch.neg fp32"}), flush=True)
 
 
+def kernel_table(times, alg):
+    """Per-kernel averages from a timing window, with achieved rates on the
+    algorithmic bytes or flops of one launch."""
+    out = {}
+    for name, (tot_ms, n) in times.items():
+        if n == 0:
+            continue
+        avg_ms = tot_ms / n
+        bound, amount = alg.get(name, ("hbm", 0.0))
+        rec = {"avg_us": round(avg_ms * 1e3, 3), "launches": n, "total_ms": round(tot_ms, 4), "bound": bound}
+        if bound == "mfma":
+            rec["achieved_tflops"] = round(amount / (avg_ms * 1e-3) / 1e12, 2)
+        elif amount > 0:
+            rec["achieved_gbs"] = round(amount / (avg_ms * 1e-3) / 1e9, 2)
+            rec["alg_bytes"] = int(amount)
+        out[name] = rec
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -137,181 +160,269 @@ def main():
     nch = lsh.lsh_num_chunks(N, stride)
     dt = lsh.LSH_BF16 if cfg.dtype == "bf16" else lsh.LSH_F32
     esz = 2 if cfg.dtype == "bf16" else 4
+    qh = B * Hq
+    full = not args.headline_only
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     # ---------------------------------------------------------------- inputs
     copies = []
     for r in range(R):
-        data = workloads.generate(cfg.with_(seed=cfg.seed + 1000 * r), device=dev)
-        c = {"keys": data["keys"], "values": data["values"], "W": data["W"],
-             "q": data["q"][0].contiguous()}
+        seed = cfg.seed + 1000 * r
+        data = workloads.generate(cfg.with_(seed=seed), device=dev)
+        c = {"keys": data["keys"], "values": data["values"], "W": data["W"], "q": data["q"][0].contiguous()}
+        del data
+        if full:
+            # the same keys, values and W; queries planted on the centred keys
+            c["q_centred"] = workloads.generate(cfg.with_(seed=seed, plant="centred"), device=dev)["q"][0].contiguous()
         c["offsets"] = torch.empty(B, Hkv, L, nch, 1 << K, dtype=torch.int16, device=dev)
         c["indices"] = torch.empty(B, Hkv, L, N, dtype=torch.int16, device=dev)
         c["bws"] = torch.empty(max(1, lsh.lsh_build_workspace_size(B, Hkv, N, d, K, L, stride, dt)),
                                dtype=torch.uint8, device=dev)
         c["dws"] = torch.empty(max(1, lsh.lsh_decode_workspace_size(B, Hq, Hkv, N, d, K, L, stride)),
                                dtype=torch.uint8, device=dev)
-        c["out"] = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+        for k in ("out", "out_exact"):
+            c[k] = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
         c["lse"] = torch.empty(B, Hq, dtype=torch.float32, device=dev)
         c["nsel"] = torch.empty(B, Hq, dtype=torch.int32, device=dev)
         copies.append(c)
-        del data
+        torch.cuda.empty_cache()
     torch.cuda.synchronize()
+    log(f"inputs ready: {cfg.name}, {R} copies")
 
     def build(c):
         lsh.lsh_build_tables(c["keys"], c["W"], K, L, stride, c["offsets"], c["indices"], None, c["bws"])
 
-    def decode(c, counts=None):
-        lsh.lsh_decode_attention(c["q"], c["keys"], c["values"], c["W"], c["indices"], c["offsets"], K, L, T,
-                                 stride, cfg.scale, c["out"], c["lse"], c["nsel"], None, counts, c["dws"])
+    def decode(c, q=None, counts=None, out=None):
+        lsh.lsh_decode_attention(c["q"] if q is None else q, c["keys"], c["values"], c["W"], c["indices"],
+                                 c["offsets"], K, L, T, stride, cfg.scale, c["out"] if out is None else out,
+                                 c["lse"], c["nsel"], None, counts, c["dws"])
 
-    def decode_hybrid(c):
-        lsh.lsh_decode_attention_hybrid(c["q"], c["keys"], c["values"], c["W"], c["indices"], c["offsets"], K, L,
-                                        T, stride, cfg.scale, args.hybrid_sink, args.hybrid_window, c["out"],
-                                        c["lse"], c["nsel"], None, None, c["dws"])
+    def decode_hybrid(c, n_sink, n_window, q=None, out=None):
+        lsh.lsh_decode_attention_hybrid(c["q"] if q is None else q, c["keys"], c["values"], c["W"], c["indices"],
+                                        c["offsets"], K, L, T, stride, cfg.scale, n_sink, n_window,
+                                        c["out"] if out is None else out, c["lse"], c["nsel"], None, None, c["dws"])
 
+    def capture(fn):
+        """One HIP graph per input copy of fn(copy); None where capture fails."""
+        try:
+            gs = []
+            for r in range(R):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    fn(copies[r])
+                gs.append(g)
+            for g in gs:
+                g.replay()
+            torch.cuda.synchronize()
+            return gs
+        except Exception as exc:  # capture unsupported here: eager only
+            log(f"graph capture failed ({exc})")
+            return None
+
+    def timed(fn, graphs, steps, warmup, offset=0):
+        """Wall ms per step over `steps` steps after `warmup`, rotating copies."""
+        run = (lambda i: graphs[i % R].replay()) if graphs else (lambda i: fn(copies[i % R]))
+        for i in range(warmup):
+            run(offset + i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            run(offset + warmup + i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    def kernel_times(fn, steps, offset=0):
+        lsh.lsh_timing_begin()
+        for i in range(steps):
+            fn(copies[(offset + i) % R])
+        return lsh.lsh_timing_end()
+
+    # prefill: the tables of every copy (untimed; the build is timed below)
+    for c in copies:
+        build(c)
+        decode(c)      # one eager decode per copy: every kernel's one-time set-up before any capture
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------- headline: decode steps
+    dec_graphs = capture(decode)
+    ms_graph = timed(decode, dec_graphs, args.steps, args.warmup) if dec_graphs else None
+    ms_eager = timed(decode, None, args.steps, args.warmup)
+    launch_mode = args.launch if dec_graphs else "eager"
+    ms_per_step = ms_graph if launch_mode == "graph" else ms_eager
+    log(f"decode: graph {ms_graph} ms, eager {ms_eager:.4f} ms per step")
+    dtimes = kernel_times(decode, args.steps)
+
+    # ------------------------------------------- measured selection statistics
+    # (untimed) one decode per copy with the collision counts returned, and
+    # the estimate's error against exact attention: the hybrid decode with
+    # every key in the exact set is exact softmax attention on the same kernels
+    counts = torch.empty(B, Hq, N, dtype=torch.uint8, device=dev)
+
+    def selection_stats(qkey):
+        sel_rows, idx_entries, nsel_tot, errs = [], [], [], []
+        for c in copies:
+            q = c[qkey]
+            decode(c, q=q, counts=counts)
+            decode_hybrid(c, N, 0, q=q, out=c["out_exact"])
+            decode(c, q=q)
+            torch.cuda.synchronize()
+            m = (counts >= T).view(B, Hkv, G, N)
+            sel_rows.append(int(m.any(dim=2).sum().item()))
+            idx_entries.append(int(counts.sum(dtype=torch.int64).item()))
+            nsel_tot.append(int(c["nsel"].sum().item()))
+            num = (c["out"] - c["out_exact"]).norm(dim=-1)
+            den = c["out_exact"].norm(dim=-1).clamp_min(1e-30)
+            errs.append((num / den).flatten().cpu().numpy())
+        e = np.concatenate(errs)
+        U_rows, E_idx = float(np.mean(sel_rows)), float(np.mean(idx_entries))
+        return {
+            "U_rows": U_rows, "E_idx": E_idx,
+            "selected_union_rows": U_rows,
+            "selected_frac_of_keys": round(U_rows / (B * Hkv * N), 4),
+            "nsel_mean_per_head": round(float(np.mean(nsel_tot)) / qh, 1),
+            "nsel_frac_per_head": round(float(np.mean(nsel_tot)) / qh / N, 4),
+            "probed_index_entries": E_idx,
+            "estimate_rel_l2_vs_exact": {"mean": round(float(e.mean()), 4), "median": round(float(np.median(e)), 4),
+                                         "max": round(float(e.max()), 4), "heads": int(e.size)},
+        }
+
+    sel = selection_stats("q")
+
+    def decode_alg(s):
+        """Algorithmic bytes of one decode launch per kernel and in all: probed
+        bucket entries (uint16), two uint16 bucket offsets per (head, table,
+        chunk), the union of the group's selected K/V rows once per (sequence,
+        kv head), q in and fp32 out, W once."""
+        kv = s["U_rows"] * 2 * d * esz
+        idx = s["E_idx"] * 2
+        offs = qh * L * nch * 2 * 2
+        qio = qh * d * (esz + 4)
+        w = d * L * K * esz
+        per = {
+            "qhash": ("hbm", qh * d * esz + w + qh * L * 2),
+            "count_select": ("hbm", idx + offs + qh * L * 2 + qh * N / 8),
+            "attend": ("hbm", kv + qh * d * esz + qh * N / 8),
+            "merge": ("hbm", 0.0),
+        }
+        return per, kv + idx + offs + qio + w
+
+    dalg, dec_bytes = decode_alg(sel)
+    dkernels = kernel_table(dtimes, dalg)
+    dec_kernel_us = sum(dkernels[k]["avg_us"] for k in DECODE_KERNELS if k in dkernels)
+    dom = max((k for k in DECODE_KERNELS if k in dkernels), key=lambda k: dkernels[k]["total_ms"])
+    drec = dkernels[dom]
+    roof = {"kernel": dom, "bound": "hbm", "achieved": drec["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(drec["achieved_gbs"] / HBM_PEAK_GBS, 4), "avg_us": drec["avg_us"],
+            "alg_bytes": drec["alg_bytes"], "traffic": measured_traffic(cfg.name, dom),
+            "decode": {"kernels": [k for k in DECODE_KERNELS if k in dkernels], "kernel_sum_us": round(dec_kernel_us, 3),
+                       "alg_bytes": int(dec_bytes),
+                       "achieved": round(dec_bytes / (dec_kernel_us * 1e-6) / 1e9, 2),
+                       "frac": round(dec_bytes / (dec_kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                       "wall_frac": round(dec_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+    value = qh / (ms_per_step * 1e-3)
+
+    # -------------------------------------------------------------- the build
+    tables = B * Hkv * L
+    build_bytes = B * Hkv * N * d * esz + tables * (N * 2 + nch * (1 << K) * 2)
+    balg = {
+        "project_codes": ("mfma", 2.0 * d * K * L * B * Hkv * N),
+        # the codes workspace: read once (written by the projection)
+        "chunk_sort": ("hbm", tables * N * 2 + tables * (N * 2 + nch * (1 << K) * 2)),
+        "transpose_w": ("hbm", 2.0 * d * L * K * esz),
+    }
+    build_graphs = capture(build)
+    ms_build_graph = timed(build, build_graphs, args.steps, 2) if build_graphs else None
+    btimes = kernel_times(build, args.steps)
+    bkernels = kernel_table(btimes, balg)
+    build_kernel_ms = sum(btimes[k][0] for k in BUILD_KERNELS) / args.steps
+    build_ms = ms_build_graph if ms_build_graph else build_kernel_ms
+    proj = bkernels.get("project_codes")
+    peak_mfma = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    build_rec = {
+        "ms": round(build_ms, 5), "launch": "graph" if ms_build_graph else "eager",
+        "kernel_sum_ms": round(build_kernel_ms, 5),
+        "alg_bytes": int(build_bytes),
+        "hbm_frac": round(build_bytes / (build_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "keys_per_s": round(B * Hkv * N / (build_ms * 1e-3), 1),
+        "flops": 2.0 * d * K * L * B * Hkv * N,
+        "project_mfma_frac": round(proj["achieved_tflops"] / peak_mfma, 4) if proj else None,
+        "project_traffic": measured_traffic(cfg.name, "project_codes"),
+        "chunk_sort_traffic": measured_traffic(cfg.name, "chunk_sort"),
+        "kernels": bkernels,
+    }
+    log(f"build: {build_ms:.4f} ms")
+
+    # the whole path: build the batch's tables, then decode one step over the
+    # tables built one step earlier (another copy)
     def step(i):
         build(copies[i % R])
         decode(copies[(i - 1) % R])
 
-    for c in copies:
-        build(c)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # ---------------------------------------------------------------- timed
-    # Steps are replayed from HIP graphs (one per input copy) unless --launch
-    # eager; the kernels and their arguments are those of the eager step.
-    launch_mode = args.launch
-    graphs = []
-    if launch_mode == "graph":
+    step_rec = None
+    if full:
+        step_graphs = []
         try:
             for r in range(R):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g):
                     step(r)
-                graphs.append(g)
-            for i in range(R):
-                graphs[i].replay()
-            torch.cuda.synchronize()
-        except Exception as exc:  # capture unsupported here: time eager launches instead
-            print(f"graph capture failed ({exc}); timing eager launches", file=sys.stderr)
-            launch_mode, graphs = "eager", []
-
-    def run(i):
-        if graphs:
-            graphs[i % R].replay()
-        else:
-            step(i)
-
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.warmup, args.warmup + args.steps):
-        run(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    # per-dispatch kernel times from a second, eager pass (events ride on the
-    # dispatch packets, so they are not part of the timed steps above)
-    lsh.lsh_timing_begin()
-    for i in range(args.warmup, args.warmup + args.steps):
-        step(i)
-    ktimes = lsh.lsh_timing_end()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    qh = B * Hq
-    value = qh / (ms_per_step * 1e-3)
-
-    # ------------------------------------------- measured selection statistics
-    # (untimed) one decode per copy with the collision counts returned
-    counts = torch.empty(B, Hq, N, dtype=torch.uint8, device=dev)
-    sel_rows = []    # sum over (b, g) of |union of the group's selections|
-    idx_entries = []  # sum over heads of probed-bucket entries = sum of counts
-    nsel_tot = []
-    for c in copies:
-        decode(c, counts)
+                step_graphs.append(g)
+        except Exception as exc:
+            log(f"graph capture of the step failed ({exc})")
+            step_graphs = None
+        for i in range(args.warmup):
+            step_graphs[i % R].replay() if step_graphs else step(i)
         torch.cuda.synchronize()
-        m = (counts >= T).view(B, Hkv, G, N)
-        sel_rows.append(int(m.any(dim=2).sum().item()))
-        idx_entries.append(int(counts.sum(dtype=torch.int64).item()))
-        nsel_tot.append(int(c["nsel"].sum().item()))
-    U_rows = float(np.mean(sel_rows))
-    E_idx = float(np.mean(idx_entries))
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step_graphs[i % R].replay() if step_graphs else step(i)
+        torch.cuda.synchronize()
+        step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        step_rec = {"ms": round(step_ms, 5), "qh_per_s": round(qh / (step_ms * 1e-3), 1),
+                    "launch": "graph" if step_graphs else "eager"}
+        del step_graphs
+        for c in copies:
+            build(c)
+        torch.cuda.synchronize()
 
-    # algorithmic bytes / flops per launch
-    kv_bytes = U_rows * 2 * d * esz
-    tables = B * Hkv * L
-    csr_out = tables * (N * 2 + nch * (1 << K) * 2)   # uint16 indices + per-chunk bucket offsets
-    alg = {
-        "project_codes": ("mfma", 2.0 * d * K * L * B * Hkv * N),
-        # codes read once, CSR written once
-        "chunk_sort": ("hbm", tables * N * 2 + csr_out),
-        "transpose_w": ("hbm", 2.0 * d * L * K * esz),
-        "qhash": ("hbm", qh * d * esz + d * L * K * esz + qh * L * 2),
-        # probed entries, query codes, two bucket offsets per (head, table, chunk), bitmask
-        "count_select": ("hbm", E_idx * 2 + qh * L * 2 + qh * L * nch * 4 + qh * N / 8),
-        "attend": ("hbm", kv_bytes + qh * d * esz + qh * N / 8),
-        "merge": ("hbm", 0.0),
-    }
-    def kernel_table(times):
-        out = {}
-        for name, (tot_ms, n) in times.items():
-            if n == 0:
-                continue
-            avg_ms = tot_ms / n
-            bound, amount = alg[name]
-            rec = {"avg_us": round(avg_ms * 1e3, 3), "launches": n, "total_ms": round(tot_ms, 4), "bound": bound}
-            if bound == "mfma":
-                rec["achieved_tflops"] = round(amount / (avg_ms * 1e-3) / 1e12, 2)
-            elif amount > 0:
-                rec["achieved_gbs"] = round(amount / (avg_ms * 1e-3) / 1e9, 2)
-            out[name] = rec
-        return out
-
-    def roofline_of(name, rec, traffic):
-        if rec["bound"] == "mfma":
-            peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
-            r = {"kernel": name, "bound": "mfma", "achieved": rec["achieved_tflops"], "peak": peak,
-                 "unit": "TFLOP/s", "frac": round(rec["achieved_tflops"] / peak, 4)}
-        else:
-            r = {"kernel": name, "bound": "hbm", "achieved": rec["achieved_gbs"], "peak": HBM_PEAK_GBS,
-                 "unit": "GB/s", "frac": round(rec["achieved_gbs"] / HBM_PEAK_GBS, 4)}
-        r["avg_us"] = rec["avg_us"]
-        r["traffic"] = traffic
-        return r
-
-    kernels = kernel_table(ktimes)
-    dom = max(kernels, key=lambda k: kernels[k]["total_ms"])
-    roof = roofline_of(dom, kernels[dom], measured_traffic(cfg.name, dom))
-
-    # decode alone in steady state: consecutive decode steps over the rotating
-    # copies with no table build in between (the build's ~0.5 GB of writes
-    # otherwise reach HBM while the next decode reads)
-    lsh.lsh_timing_begin()
-    torch.cuda.synchronize()
-    td0 = time.perf_counter()
-    for i in range(args.steps):
-        decode(copies[i % R])
-    torch.cuda.synchronize()
-    td1 = time.perf_counter()
-    dtimes = lsh.lsh_timing_end()
-    dkernels = kernel_table(dtimes)
-    dec_ms_steady = sum(dtimes[k][0] for k in DECODE_KERNELS) / args.steps
+    # ---------------------------------------------- centred-plant variant
+    centred = None
+    if full:
+        csel = selection_stats("q_centred")
+        cgraphs = capture(lambda c: decode(c, q=c["q_centred"]))
+        cms = timed(lambda c: decode(c, q=c["q_centred"]), cgraphs, args.steps, args.warmup)
+        ctimes = kernel_times(lambda c: decode(c, q=c["q_centred"]), args.steps)
+        calg, cbytes = decode_alg(csel)
+        ck = kernel_table(ctimes, calg)
+        c_us = sum(ck[k]["avg_us"] for k in DECODE_KERNELS if k in ck)
+        centred = {k: v for k, v in csel.items() if k not in ("U_rows", "E_idx")}
+        centred.update({
+            "plant": "q planted on k_j - mu (the keys' shared offset removed); same keys, values, W and tables",
+            "ms_per_step": round(cms, 5), "launch": "graph" if cgraphs else "eager",
+            "qh_per_s": round(qh / (cms * 1e-3), 1),
+            "alg_bytes": int(cbytes),
+            "hbm_frac": round(cbytes / (c_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "wall_hbm_frac": round(cbytes / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel_sum_us": round(c_us, 3),
+            "kernels": {k: v["avg_us"] for k, v in ck.items()},
+        })
+        del cgraphs
+        log(f"centred plant: {cms:.4f} ms, selected {centred['selected_frac_of_keys']}")
 
     decode_hybrid_steady = append_decode = None
-    if not args.headline_only:
-        # the hybrid decode in steady state: the exact sink + window set runs as
-        # extra attention workgroups, the selection leaves those keys out
-        lsh.lsh_timing_begin()
-        for i in range(args.steps):
-            decode_hybrid(copies[i % R])
-        htimes = lsh.lsh_timing_end()
-        hk = kernel_table(htimes)
+    if full:
+        # the hybrid decode: the exact sink + window set runs as extra
+        # attention workgroups, the selection leaves those keys out
+        htimes = kernel_times(lambda c: decode_hybrid(c, args.hybrid_sink, args.hybrid_window), args.steps)
+        hk = kernel_table(htimes, {})
         n_exact = min(N, args.hybrid_sink + args.hybrid_window)
         hyb_ms = sum(htimes[k][0] for k in DECODE_KERNELS) / args.steps
         decode_hybrid_steady = {
             "n_sink": args.hybrid_sink, "n_window": args.hybrid_window,
-            "ms": round(hyb_ms, 5),
+            "kernel_sum_ms": round(hyb_ms, 5),
             "qh_per_s": round(qh / (hyb_ms * 1e-3), 1),
-            "merge_avg_us": hk["merge"]["avg_us"],
             # keys and values of the exact set, once per (sequence, kv head)
             "exact_kv_bytes": int(B * Hkv * n_exact * 2 * d * esz),
             "kernels": {k: v["avg_us"] for k, v in hk.items()},
@@ -339,29 +450,18 @@ def main():
         lsh.lsh_update_tables(c0["keys"], c0["W"], K, L, stride, n_start, N, c0["offsets"], c0["indices"], None,
                               c0["bws"])
         torch.cuda.synchronize()
-        ak = kernel_table(atimes)
+        ak = kernel_table(atimes, {})
         append_ms = sum(v[0] for v in atimes.values()) / args.steps
         append_decode = {
             "keys_held": [n_start + 1, n_start + args.steps],
-            "ms": round(append_ms, 5),
+            "kernel_sum_ms": round(append_ms, 5),
             "wall_ms_per_step": round((ta1 - ta0) * 1e3 / args.steps, 5),
             "update_ms": round(sum(atimes[k][0] for k in BUILD_KERNELS) / args.steps, 5),
             "qh_per_s": round(qh / (append_ms * 1e-3), 1),
             "kernels": {k: v["avg_us"] for k, v in ak.items()},
         }
 
-    build_ms = sum(ktimes[k][0] for k in BUILD_KERNELS) / args.steps
-    decode_ms = sum(ktimes[k][0] for k in DECODE_KERNELS) / args.steps
-    dec_bytes = E_idx * 2 + qh * L * 8 + kv_bytes + qh * d * (esz + 4) + d * L * K * esz
-    decode_steady = {
-        "ms": round(dec_ms_steady, 5),
-        "wall_ms_per_step": round((td1 - td0) * 1e3 / args.steps, 5),
-        "qh_per_s": round(qh / (dec_ms_steady * 1e-3), 1),
-        "hbm_frac": round(dec_bytes / (dec_ms_steady * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "attend_roofline": roofline_of("attend", dkernels["attend"], measured_traffic(cfg.name, "attend")),
-        "kernels": dkernels,
-    }
-
+    headline = {k: v for k, v in sel.items() if k not in ("U_rows", "E_idx")}
     line = {
         "metric": "LSH-attn decode queries·heads/s at 32K–128K ctx; % of HBM roofline",
         "value": round(value, 1),
@@ -376,22 +476,23 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "K": K, "L": L, "T": T,
-                   "kv_dtype": cfg.dtype, "stride": stride, "step": "table build + 1 decode step", "launch": launch_mode,
-                   "input_copies": R},
+                   "kv_dtype": cfg.dtype, "stride": stride,
+                   "step": "one decode step of every query head over tables built at prefill",
+                   "launch": launch_mode, "input_copies": R},
         "roofline": roof,
         "breakdown": {
-            "build_ms": round(build_ms, 5),
-            "decode_ms": round(decode_ms, 5),
-            "decode_qh_per_s": round(qh / (decode_ms * 1e-3), 1),
+            "decode_graph_ms": round(ms_graph, 5) if ms_graph else None,
+            "decode_eager_ms": round(ms_eager, 5),
+            "decode_eager_qh_per_s": round(qh / (ms_eager * 1e-3), 1),
+            "decode_kernel_sum_us": round(dec_kernel_us, 3),
             "decode_alg_bytes": int(dec_bytes),
-            "decode_hbm_frac": round(dec_bytes / (decode_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "build_keys_per_s": round(B * Hkv * N / (build_ms * 1e-3), 1),
-            "selected_union_rows": U_rows,
-            "selected_frac_of_keys": round(U_rows / (B * Hkv * N), 4),
-            "nsel_mean_per_head": float(np.mean(nsel_tot)) / qh,
-            "probed_index_entries": E_idx,
-            "kernels": kernels,
-            "decode_steady": decode_steady,
+            "decode_hbm_frac": roof["decode"]["frac"],
+            "decode_wall_hbm_frac": roof["decode"]["wall_frac"],
+            **headline,
+            "kernels": dkernels,
+            "build": build_rec,
+            "step_build_plus_decode": step_rec,
+            "centred_plant": centred,
             "decode_hybrid_steady": decode_hybrid_steady,
             "append_decode_steady": append_decode,
         },
@@ -403,11 +504,10 @@ def main():
 
 
 def cpu_baseline(cfg, c, stride, budget_s=10.0):
-    """The fp64 oracle on (sequence, kv head) units in order, each unit's
-    table build plus the decode of its G query heads, until about
-    ``budget_s`` seconds of CPU work or the whole step is done; the rate is
-    query heads decoded (with their tables built) per second."""
-    import numpy as np
+    """The fp64 oracle's decode on (sequence, kv head) units in order: each
+    unit's tables are built first (untimed, as prefill), then the decode of
+    its G query heads is timed, until about ``budget_s`` seconds of decode or
+    the whole step is done; the rate is query heads decoded per second."""
     from threadpoolctl import threadpool_info
 
     from oracle import lsh_oracle as O
@@ -415,23 +515,25 @@ def cpu_baseline(cfg, c, stride, budget_s=10.0):
     W = c["W"].float().cpu().numpy()
     units = cfg.B * cfg.Hkv
     done = 0
-    t0 = time.perf_counter()
-    while done < units and (done == 0 or time.perf_counter() - t0 < budget_s):
+    spent = 0.0
+    while done < units and (done == 0 or spent < budget_s):
         b, g = divmod(done, cfg.Hkv)
         keys = c["keys"][b, g].float().cpu().numpy()
         vals = c["values"][b, g].float().cpu().numpy()
         q = c["q"][b].float().cpu().numpy()
         tb = O.build_tables(keys, W, cfg.K, cfg.L, stride)
+        t0 = time.perf_counter()
         for h in range(g * cfg.G, (g + 1) * cfg.G):
             O.decode_head(q[h], keys, vals, W, tb["offsets"], tb["indices"], cfg.K, cfg.L, cfg.T, cfg.scale)
+        spent += time.perf_counter() - t0
         done += 1
-    dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(done * cfg.G / dt, 3), "unit": "queries·heads/s", "cores": threads,
+    return {"value": round(done * cfg.G / spent, 3), "unit": "queries·heads/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{done} of {units} (sequence, kv head) units of one step: fp64 table build of {cfg.N} "
-                      f"keys + decode of the unit's {cfg.G} query heads each, {dt:.2f} s in all; BLAS threads "
-                      f"{threads} (matmuls), the rest single-threaded numpy"}
+            "sample": f"{done} of {units} (sequence, kv head) units of one step: fp64 decode of the unit's "
+                      f"{cfg.G} query heads over its {cfg.N} keys, {spent:.2f} s of decode in all (each unit's "
+                      f"tables built first, untimed); BLAS threads {threads} (matmuls), the rest "
+                      f"single-threaded numpy"}
 
 
 if __name__ == "__main__":

@@ -115,6 +115,48 @@ def _dtype_code(dt):
     raise TypeError(f"unsupported dtype {dt}; use bfloat16 or float32")
 
 
+def _require(t, name, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _check_decode_tensors(q, keys, values, W, indices, offsets, K, L, stride, n_cap, w_per_head_ok):
+    """Host-side checks of a decode call's tensors before any pointer crosses
+    the C ABI: every array on the GPU and contiguous, q / keys / values / W of
+    one dtype, W [d, L*K] (or [Hkv, d, L*K] where one W per kv head is
+    accepted), and tables of the shapes the kernels index with K, L, stride and
+    the cache capacity n_cap: offsets [B, Hkv, L, nchunks(n_cap), 2^K],
+    indices [B, Hkv, L, n_cap] (int16 holding uint16)."""
+    for name, t in (("q", q), ("keys", keys), ("values", values)):
+        _require(t, name, keys.dtype)
+    _require(W, "W", keys.dtype)
+    _require(indices, "indices", torch.int16)
+    _require(offsets, "offsets", torch.int16)
+    if q.dim() != 3 or keys.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and keys / values [B, Hkv, n_cap, d]")
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = keys.shape
+    if tuple(values.shape) != tuple(keys.shape) or keys.shape[0] != B or keys.shape[3] != d:
+        raise ValueError("q [B,Hq,d] and keys/values [B,Hkv,n_cap,d] disagree")
+    if cap != n_cap:
+        raise ValueError(f"keys hold {cap} positions per (sequence, kv head), the tables {n_cap}")
+    shapes = [(d, L * K)] + ([(Hkv, d, L * K)] if w_per_head_ok else [])
+    if tuple(W.shape) not in shapes:
+        raise ValueError(f"W must be {' or '.join(str(list(x)) for x in shapes)}, got {list(W.shape)}")
+    nch = lsh_num_chunks(n_cap, stride)
+    if nch < 1:
+        raise ValueError(f"invalid stride {stride} for {n_cap} keys")
+    if tuple(offsets.shape) != (B, Hkv, L, nch, 1 << K):
+        raise ValueError(f"offsets must be {[B, Hkv, L, nch, 1 << K]} for K={K}, L={L}, stride={stride}, "
+                         f"got {list(offsets.shape)}")
+    if tuple(indices.shape) != (B, Hkv, L, n_cap):
+        raise ValueError(f"indices must be {[B, Hkv, L, n_cap]}, got {list(indices.shape)}")
+
+
 # ------------------------------------------------------------------ C-ABI names
 
 def lsh_status_string(status: int) -> str:
@@ -177,6 +219,7 @@ def lsh_decode_attention_cached(q, keys, values, W, indices, offsets, N, K, L, T
     """Marshal tensors to ``lsh_decode_attention_cached``: keys / values
     [B, Hkv, n_cap, d], of which the first N (or seq_lens[b], an int32 device
     tensor [B]) are attended; W as in ``lsh_update_tables``."""
+    _check_decode_tensors(q, keys, values, W, indices, offsets, K, L, stride, keys.shape[2], True)
     B, Hq, d = q.shape
     _, Hkv, n_cap, _ = keys.shape
     dt = _dtype_code(keys.dtype)
@@ -194,6 +237,7 @@ def lsh_decode_attention_cached(q, keys, values, W, indices, offsets, N, K, L, T
 def lsh_decode_attention(q, keys, values, W, indices, offsets, K, L, T, stride, sm_scale, out,
                          lse=None, nsel=None, q_codes=None, counts=None, workspace=None):
     """Marshal tensors to ``lsh_decode_attention``; outputs are filled in place."""
+    _check_decode_tensors(q, keys, values, W, indices, offsets, K, L, stride, keys.shape[2], False)
     B, Hq, d = q.shape
     _, Hkv, N, _ = keys.shape
     dt = _dtype_code(keys.dtype)
@@ -210,6 +254,7 @@ def lsh_decode_attention(q, keys, values, W, indices, offsets, K, L, T, stride, 
 def lsh_decode_attention_hybrid(q, keys, values, W, indices, offsets, K, L, T, stride, sm_scale, n_sink,
                                 n_window, out, lse=None, nsel=None, q_codes=None, counts=None, workspace=None):
     """Marshal tensors to ``lsh_decode_attention_hybrid``; outputs are filled in place."""
+    _check_decode_tensors(q, keys, values, W, indices, offsets, K, L, stride, keys.shape[2], False)
     B, Hq, d = q.shape
     _, Hkv, N, _ = keys.shape
     dt = _dtype_code(keys.dtype)
@@ -246,14 +291,6 @@ def lsh_timing_end():
 
 
 # ------------------------------------------------------------------ convenience
-
-def _require(t, name, dtype=None):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if dtype is not None and t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
 def build_tables(keys, W, K, L, stride=None, return_codes=False):
@@ -345,12 +382,14 @@ def decode_attention(q, keys, values, W, tables, K, L, T, sm_scale=None, return_
         _require(t, name, keys.dtype)
     B, Hq, d = q.shape
     _, Hkv, N, _ = keys.shape
-    if tuple(values.shape) != tuple(keys.shape) or keys.shape[0] != B or keys.shape[3] != d:
-        raise ValueError("q [B,Hq,d] and keys/values [B,Hkv,N,d] disagree")
     cached = "n_cap" in tables
+    if cached and tables["n_cap"] != N:
+        raise ValueError("keys and tables disagree on the capacity")
+    # one W per kv head only goes with cache tables (the cached entry point
+    # takes the flag; the plain one would read a 3-D W as a shared one)
+    _check_decode_tensors(q, keys, values, W, tables["indices"], tables["offsets"], K, L, tables["stride"], N,
+                          cached)
     if cached:
-        if tables["n_cap"] != N:
-            raise ValueError("keys and tables disagree on the capacity")
         N = tables["n"]
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)

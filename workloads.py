@@ -23,6 +23,11 @@ seeded with ``seed``):
   4. per decode step: for every (b, h) a set J of ``planted`` distinct key
      indices of kv head h // G, uniform at random, and
        q = a * sum_{j in J} k_j / sqrt(|J|) + sqrt(1 - a^2) * eps.
+     With plant="centred" the planted term uses the keys less their offset
+     mean (k_j - mu; the rank-8 part of shared_lowrank stays): the queries
+     then no longer point along the offset that every key shares, and the
+     selection becomes sparse.  The draws are the same in both modes, so the
+     keys, values and W are identical and only q differs.
   5. keys, values, W and q are cast to the configuration's dtype last; q is
      built from the already-cast keys.
 """
@@ -52,6 +57,7 @@ class Config:
     offset: str
     steps: int = 1
     seed: int = 1234
+    plant: str = "raw"  # "raw": q planted on k_j; "centred": on k_j - mu
 
     @property
     def G(self):
@@ -107,19 +113,25 @@ def generate(cfg: Config, device="cpu"):
     W = torch.randn(d, cfg.L * cfg.K, generator=g, **f32)
 
     keys = torch.randn(B, Hkv, N, d, generator=g, **f32)
+    mean = torch.zeros(B, Hkv, d, **f32)   # the offset every key of a unit shares
     if cfg.offset == "per_head":
         mu = 8.0 * _unit(torch.randn(Hkv, d, generator=g, **f32))
         keys += mu[None, :, None, :]
+        mean += mu[None]
     elif cfg.offset == "per_unit":
         mu = 8.0 * _unit(torch.randn(B, Hkv, d, generator=g, **f32))
         keys += mu[:, :, None, :]
+        mean += mu
     elif cfg.offset == "shared_lowrank":
         mu = 8.0 * _unit(torch.randn(d, generator=g, **f32))
         basis = torch.linalg.qr(torch.randn(Hkv, d, 8, generator=g, **f32))[0]  # [Hkv, d, 8]
         coef = math.sqrt(8.0) * torch.randn(B, Hkv, N, 8, generator=g, **f32)
         keys += mu + torch.einsum("hdr,bhnr->bhnd", basis, coef)
+        mean += mu
     elif cfg.offset != "none":
         raise ValueError(cfg.offset)
+    if cfg.plant not in ("raw", "centred"):
+        raise ValueError(cfg.plant)
     values = torch.randn(B, Hkv, N, d, generator=g, **f32)
 
     dt = cfg.torch_dtype
@@ -136,6 +148,8 @@ def generate(cfg: Config, device="cpu"):
         b_idx = torch.arange(B, device=device)[:, None, None]
         g_idx = (torch.arange(Hq, device=device) // G)[None, :, None]
         picked = keys[b_idx, g_idx, J].float()                          # [B, Hq, P, d]
+        if cfg.plant == "centred":
+            picked = picked - mean[b_idx[..., 0], g_idx[..., 0]][:, :, None, :]
         eps = torch.randn(B, Hq, d, generator=g, **f32)
         q = cfg.a * picked.sum(2) / math.sqrt(cfg.planted) + math.sqrt(1.0 - cfg.a ** 2) * eps
         qs.append(q.to(dt))
