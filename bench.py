@@ -45,12 +45,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA, TFLOP/s
 
 BUILD_KERNELS = ("transpose_w", "project_codes", "chunk_sort")
-DECODE_KERNELS = ("qhash", "count_select", "attend", "merge")
+DECODE_KERNELS = ("qhash", "decode")
 KERNEL_SOURCES = {
-    "transpose_w": "build_kernels.hip", "project_codes": "build_kernels.hip",
-    "chunk_sort": "build_kernels.hip", "qhash": "decode_kernels.hip",
-    "count_select": "decode_kernels.hip", "attend": "attend_bf16.hip",
-    "merge": "decode_kernels.hip",
+    "transpose_w": ("build_kernels.hip",), "project_codes": ("build_kernels.hip",),
+    "chunk_sort": ("build_kernels.hip",), "qhash": ("decode_kernels.hip",),
+    "decode": ("attend_bf16.hip", "decode_roles.h"),
 }
 
 
@@ -78,7 +77,7 @@ def parse():
 
 def source_digest(kernel):
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "lsh_device.h", "lsh_kernels.h"):
+    for f in KERNEL_SOURCES[kernel] + ("lsh_device.h", "lsh_kernels.h"):
         with open(os.path.join(ROOT, "lsh_sampled_sparse_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -301,10 +300,10 @@ def main():
         qio = qh * d * (esz + 4)
         w = d * L * K * esz
         per = {
+            # q in, W, query codes out
             "qhash": ("hbm", qh * d * esz + w + qh * L * 2),
-            "count_select": ("hbm", idx + offs + qh * L * 2 + qh * N / 8),
-            "attend": ("hbm", kv + qh * d * esz + qh * N / 8),
-            "merge": ("hbm", 0.0),
+            # query codes, probed entries, bucket offsets, selected K/V rows, q, fp32 out
+            "decode": ("hbm", qh * L * 2 + idx + offs + kv + qio),
         }
         return per, kv + idx + offs + qio + w
 

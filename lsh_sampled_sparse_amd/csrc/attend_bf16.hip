@@ -25,6 +25,7 @@
 // which is plain softmax attention on the same tiles.
 #include <math.h>
 
+#include "decode_roles.h"
 #include "lsh_device.h"
 #include "lsh_kernels.h"
 
@@ -132,29 +133,38 @@ __device__ __forceinline__ float row_sum16(float v) {
 
 }  // namespace
 
-// GW = number of 64-lane mask words per head and 512-key block that a lane
-// holds: the G heads' 16 words per block are spread over GW loads.
-template <int GW>
-__global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
-    const uint16_t* __restrict__ q,        // [B][Hq][128]
-    const uint16_t* __restrict__ keys,     // [U][N][128]
-    const uint16_t* __restrict__ values,   // [U][N][128]
-    const uint32_t* __restrict__ bitmask,  // [B*Hq][Nw]
-    const double* __restrict__ lnu_samples,   // [kLnuSamples]
-    int Hq, int Hkv, int N, int P, int K, int Tth, float scale, int split_len, int nsplit,
-    int n_sink, int n_window, int exact_len, int nexact, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ partials) {        // [B*Hq][nsplit + nexact][130]
-  __shared__ float4 tab4[kLnuTable];      // interval quadratics of g
-  __shared__ int ring_idx[kWaves][kRingN];
-  __shared__ uint16_t ring_hm[kWaves][kRingN];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kWaves][kTile * kVRow];
-  __shared__ __attribute__((aligned(16))) uint16_t pt[kWaves][2][kTile * 16];
-  __shared__ float ep_m[kWaves][16], ep_l[kWaves][16];
+// LDS of the attention role (the other roles of the launch reuse the same bytes).
+struct AttendLds {
+  float4 tab4[kLnuTable];                                    // interval quadratics of g
+  int ring_idx[kWaves][kRingN];
+  uint16_t ring_hm[kWaves][kRingN];
+  __attribute__((aligned(16))) uint16_t vt[kWaves][kTile * kVRow];
+  __attribute__((aligned(16))) uint16_t pt[kWaves][2][kTile * 16];
+  float ep_m[kWaves][16], ep_l[kWaves][16];
+  int flag;
+};
+constexpr size_t kFusedLdsBytes = cmax(sizeof(AttendLds), kRolesLdsBytes);
 
+// The attention role: partial slot s (a context split, or past nsplit a
+// piece of the exact set) of unit u.  GW = number of 64-lane mask words per
+// head and 512-key block that a lane holds: the G heads' 16 words per block
+// are spread over GW loads.
+template <int GW>
+__device__ __forceinline__ void attend_bf16_role(const FusedParams& p, int s, int u, unsigned char* smem) {
+  AttendLds& A = *reinterpret_cast<AttendLds*>(smem);
+  LSH_STAMP(p, 0);
+  const uint16_t* __restrict__ q = static_cast<const uint16_t*>(p.q);
+  const uint16_t* __restrict__ keys = static_cast<const uint16_t*>(p.keys);
+  const uint16_t* __restrict__ values = static_cast<const uint16_t*>(p.values);
+  const uint32_t* bitmask = p.bitmask;
+  const int Hq = p.Hq, Hkv = p.Hkv, N = p.N, P = p.P, K = p.K, Tth = p.T;
+  const float scale = p.scale;
+  const int split_len = p.split_len, nsplit = p.nsplit, exact_len = p.exact_len;
+  const int npart = p.npart;
+  float4* tab4 = A.tab4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, sl = lane & 15;
-  const int s = blockIdx.x, u = blockIdx.y;
-  const int G = Hq / Hkv;
+  const int G = p.G;
   const int b = u / Hkv, g = u % Hkv;
   const int bh0 = b * Hq + g * G;
   const int Nw = (N + 31) >> 5;
@@ -164,16 +174,12 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
   const bool exact = s >= nsplit;          // a piece of the exact set
   const bool nolnu = k0 || exact;
   // this sequence's keys and exact set
-  const int Nb = seq_len_of(seq_lens, b, N);
+  const int Nb = seq_len_of(p.seq_lens, b, N);
   int exact_head, exact_tail;
-  exact_range(n_sink, n_window, Nb, exact_head, exact_tail);
+  exact_range(p.n_sink, p.n_window, Nb, exact_head, exact_tail);
   const int ne = exact_head + exact_tail;
-  const int npart = nsplit + nexact;
   const uint16_t gmask = static_cast<uint16_t>((1u << G) - 1u);
   const float TKln2 = static_cast<float>(Tth * K) * 0.69314718055994531f;
-
-  for (int i = tid; i < kLnuTable; i += 256)
-    tab4[i] = nolnu ? make_float4(0.f, 0.f, 0.f, 0.f) : lnu_interval(lnu_samples, i);
 
   // q fragments (MFMA A operand): lane holds head sl, dims 32 k + 8 g4 + [0, 8)
   // of k-step k (the K fragments use the same order)
@@ -191,6 +197,10 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
     rq[i] = x > 0.f ? __builtin_amdgcn_rsqf(x) : 0.f;
   }
 
+  // the ln-u table's samples, in flight during the wait for the selection
+  LnuFetch lf;
+  lnu_fetch(p, nolnu, lf);
+
   // this wave's range: keys of the context split, or exact-set positions
   const int plen = exact ? exact_len : split_len;
   const int sb = exact ? (s - nsplit) * exact_len : s * split_len;
@@ -198,12 +208,22 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
   const int wq = plen / kWaves;
   const int wb = min(se, sb + wave * wq), we = min(se, sb + (wave + 1) * wq);
 
-  int* ridx = ring_idx[wave];
-  uint16_t* rhm = ring_hm[wave];
-  uint16_t* V = vt[wave];
-  uint16_t* Phi = pt[wave][0];
-  uint16_t* Plo = pt[wave][1];
+  int* ridx = A.ring_idx[wave];
+  uint16_t* rhm = A.ring_hm[wave];
+  uint16_t* V = A.vt[wave];
+  uint16_t* Phi = A.pt[wave][0];
+  uint16_t* Plo = A.pt[wave][1];
 
+  // the selection of the split's key chunks must be complete (count
+  // workgroups of every query head of the group); a wait that does not end
+  // leaves a NaN partial
+  bool ok = true;
+  if (!exact && sb < se) {
+    const int j0 = sb >> p.stride_log2, j1 = (se - 1) >> p.stride_log2;
+    ok = wait_counters(p.ready + u * p.nJ + j0, j1 - j0 + 1, G, &A.flag);
+  }
+
+  LSH_STAMP(p, 1);
   // ---- selection masks: the 16 words (512 keys) of every head of the group
   // for one block; word w of head h sits in lane (h % 4) * 16 + w of load h / 4
   uint32_t mw[GW] = {}, mw_next[GW] = {};
@@ -212,7 +232,7 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
     for (int k = 0; k < GW; ++k) {
       const int hh = 4 * k + g4;
       const int wi = (blk0 >> 5) + sl;
-      dst[k] = (hh < G && blk0 < we && wi < Nw) ? bitmask[static_cast<size_t>(bh0 + hh) * Nw + wi] : 0u;
+      dst[k] = (hh < G && blk0 < we && wi < Nw) ? ld_agent(bitmask + static_cast<size_t>(bh0 + hh) * Nw + wi) : 0u;
     }
   };
   int blk = wb;                        // next window to compact
@@ -309,7 +329,9 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
   fill();
   int nt = min(kTile, rcnt);
   if (nt > 0) issue(nt);
+  lnu_store(lf, nolnu, tab4);
   __syncthreads();   // ln u table in LDS
+  LSH_STAMP(p, 2);
   while (nt > 0) {
     // V of this tile into LDS (row-major, padded rows)
 #pragma unroll
@@ -401,14 +423,15 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
     nt = nnext;
   }
 
+  LSH_STAMP(p, 3);
   // ---- merge the four waves' states per head; O[t][i] is head 4 g4 + i, dim 16 t + sl
   __syncthreads();
-  float* wacc = reinterpret_cast<float*>(&vt[0][0]);   // [kWaves][16][128]
+  float* wacc = reinterpret_cast<float*>(&A.vt[0][0]);   // [kWaves][16][128]
   if (sl == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ep_m[wave][4 * g4 + i] = m_run[i];
-      ep_l[wave][4 * g4 + i] = l_run[i];
+      A.ep_m[wave][4 * g4 + i] = m_run[i];
+      A.ep_l[wave][4 * g4 + i] = l_run[i];
     }
   }
 #pragma unroll
@@ -420,45 +443,58 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
     const int hh = e / kHeadDim, d = e % kHeadDim;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ep_m[w][hh]);
-    float A = 0.f, Lm = 0.f;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, A.ep_m[w][hh]);
+    float Acc = 0.f, Lm = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        if (ep_m[w][hh] == -INFINITY) continue;
-        const float f = __expf(ep_m[w][hh] - M);
-        A = fmaf(wacc[(w * 16 + hh) * kHeadDim + d], f, A);
-        Lm = fmaf(ep_l[w][hh], f, Lm);
+        if (A.ep_m[w][hh] == -INFINITY) continue;
+        const float f = __expf(A.ep_m[w][hh] - M);
+        Acc = fmaf(wacc[(w * 16 + hh) * kHeadDim + d], f, Acc);
+        Lm = fmaf(A.ep_l[w][hh], f, Lm);
       }
     }
-    float* dst = partials + (static_cast<size_t>(bh0 + hh) * npart + s) * kPartialStride;
-    dst[d] = A;
+    if (!ok) {   // a wait gave up: poison this partial
+      Acc = __builtin_nanf("");
+      M = 0.f;
+      Lm = 1.f;
+    }
+    float* dst = p.partials + (static_cast<size_t>(bh0 + hh) * npart + s) * kPartialStride;
+    st_agent(dst + d, Acc);
     if (d == 0) {
-      dst[kHeadDim] = M;
-      dst[kHeadDim + 1] = Lm;
+      st_agent(dst + kHeadDim, M);
+      st_agent(dst + kHeadDim + 1, Lm);
     }
   }
 }
 
-hipError_t launch_attend_bf16(const DecodeArgs& a, hipStream_t stream) {
-  const int G = a.Hq / a.Hkv;
-  const dim3 grid(a.nsplit + a.nexact, a.B * a.Hkv);
-  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
-  const uint16_t* kp = static_cast<const uint16_t*>(a.keys);
-  const uint16_t* vp = static_cast<const uint16_t*>(a.values);
-  const uint32_t* bm = a.bitmask;
-  const double* lt = a.lnu_samples;
-  if (G <= 4)
-    return launch(kKAttend, attend_bf16_kernel<1>, grid, dim3(256), 0, stream, qp, kp, vp, bm, lt, a.Hq,
-                  a.Hkv, a.N, a.P, a.K, a.T, a.scale, a.split_len, a.nsplit, a.n_sink, a.n_window, a.exact_len, a.nexact, a.seq_lens,
-                  a.partials);
-  if (G <= 8)
-    return launch(kKAttend, attend_bf16_kernel<2>, grid, dim3(256), 0, stream, qp, kp, vp, bm, lt, a.Hq,
-                  a.Hkv, a.N, a.P, a.K, a.T, a.scale, a.split_len, a.nsplit, a.n_sink, a.n_window, a.exact_len, a.nexact, a.seq_lens,
-                  a.partials);
-  return launch(kKAttend, attend_bf16_kernel<4>, grid, dim3(256), 0, stream, qp, kp, vp, bm, lt, a.Hq, a.Hkv,
-                a.N, a.P, a.K, a.T, a.scale, a.split_len, a.nsplit, a.n_sink, a.n_window, a.exact_len, a.nexact, a.seq_lens,
-                  a.partials);
+// The one-launch decode for bf16 K/V: count, exact and attend workgroups in
+// that order of id (see decode_roles.h).
+template <int GW>
+__global__ __launch_bounds__(kFusedThreads, 2) void decode_bf16_kernel(FusedParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kFusedLdsBytes];
+  int wid = blockIdx.x;
+  if (wid < p.n_count_wg) {
+    count_role(p, wid, smem);
+    return;
+  }
+  wid -= p.n_count_wg;
+  // unit by unit: the exact set's pieces, then the context splits (the
+  // finishers of a unit wait only for that unit's workgroups; see finish_slot)
+  const int per_unit = p.nexact + p.nsplit;
+  const int u = wid / per_unit, r = wid % per_unit;
+  const int slot = r < p.nexact ? p.nsplit + r : r - p.nexact;
+  attend_bf16_role<GW>(p, slot, u, smem);
+  __syncthreads();
+  LSH_STAMP(p, 4);
+  finish_slot(p, u, slot, smem);
+}
+
+hipError_t launch_decode_bf16(const FusedParams& p, hipStream_t stream) {
+  const dim3 grid(p.n_count_wg + p.n_exact_wg + p.n_attend_wg);
+  if (p.G <= 4) return launch(kKDecode, decode_bf16_kernel<1>, grid, dim3(kFusedThreads), 0, stream, p);
+  if (p.G <= 8) return launch(kKDecode, decode_bf16_kernel<2>, grid, dim3(kFusedThreads), 0, stream, p);
+  return launch(kKDecode, decode_bf16_kernel<4>, grid, dim3(kFusedThreads), 0, stream, p);
 }
 
 }  // namespace lsh

@@ -1,0 +1,708 @@
+// Workgroup roles of the one-launch decode (gfx950): the per-(query head,
+// key chunk) collision count and selection, and the log-sum-exp merges; the
+// attention role itself lives with its dtype's kernel.
+//
+// One grid holds, in this order of workgroup id,
+//   count    workgroups: one per (key chunk, query head), the selection bitmask
+//   exact    workgroups: the hybrid decode's exact set, in pieces
+//   attend   workgroups: one per (context split, sequence, kv head)
+// An attend workgroup waits, by polling a counter in the workspace, for the
+// count workgroups of its split's chunks, all of LOWER id.  Workgroups of a
+// launch are dispatched in id order (on each XCD in the order of the ids it
+// receives), so every producer has been dispatched before any workgroup that
+// waits for it, and producers never wait: the waits always end.  A bounded
+// poll count turns a wait that does not end into a NaN output instead of a
+// hang.
+//
+// Cross-workgroup data (bitmask words, chunk counts, partial states, the
+// counters) is written with agent-scope atomic stores, which write through
+// to memory and so stay coherent across the eight XCDs (whose L2s are not
+// coherent with each other for plain accesses).  A producer waits for its
+// stores to complete (s_waitcnt vmcnt(0)) before it bumps the counter a
+// consumer polls.  Consumers read small data (bitmask words) with
+// agent-scope atomic loads; the finishers, which read a unit's partial
+// states in bulk, issue one agent-scope acquire fence and then plain loads.
+// Fences in every workgroup are avoided: an L2 write-back or invalidate per
+// workgroup costs far more than these few coherent accesses.
+//
+// The merge: each attend / exact workgroup writes one partial state (acc,
+// max, sum) per query head of its group; the last workgroups of a (sequence,
+// kv head) to finish fold them into the outputs (finish_slot).  Folds run in
+// slot order, whoever runs them, so the result is deterministic.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "lsh_device.h"
+#include "lsh_kernels.h"
+
+namespace lsh {
+
+constexpr int kFusedThreads = 256;         // every role runs 4 waves
+constexpr int kSpinLimit = 1 << 18;        // polls before a wait gives up (a fraction of a second)
+
+// --------------------------------------------------------------------------
+// coherent accesses
+// --------------------------------------------------------------------------
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  st_agent(reinterpret_cast<uint32_t*>(p), __float_as_uint(v));
+}
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_agent(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __uint_as_float(ld_agent(reinterpret_cast<const uint32_t*>(p)));
+}
+__device__ __forceinline__ uint64_t ld_agent(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// every vector memory access of this wave has completed (gfx9: vmcnt counts stores too)
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Thread 0 polls *ctr until it reaches `target`; the workgroup then
+// proceeds.  Returns false (in every thread) when the poll limit ran out.
+__device__ __forceinline__ bool wait_counter(const int32_t* ctr, int target, int* flag_lds) {
+  if (threadIdx.x == 0) {
+    int ok = 1, it = 0;
+    while (ld_agent(ctr) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++it >= kSpinLimit) {
+        ok = 0;
+        break;
+      }
+    }
+    *flag_lds = ok;
+  }
+  __syncthreads();
+  const bool ok = *flag_lds != 0;
+  __syncthreads();
+  return ok;
+}
+
+// Every thread polls its share of ctr[0 .. n) until each reaches `target`.
+// Returns false (in every thread) when a poll limit ran out.
+__device__ __forceinline__ bool wait_counters(const int32_t* ctr, int n, int target, int* flag_lds) {
+  if (threadIdx.x == 0) *flag_lds = 1;
+  __syncthreads();
+  int ok = 1;
+  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+    int it = 0;
+    while (ld_agent(ctr + j) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++it >= kSpinLimit) {
+        ok = 0;
+        break;
+      }
+    }
+  }
+  if (!ok) *flag_lds = 0;
+  __syncthreads();
+  const bool all = *flag_lds != 0;
+  __syncthreads();
+  return all;
+}
+
+// This workgroup's stores are complete; thread 0 then adds 1 to *ctr and
+// returns the previous value (the same in every thread).
+__device__ __forceinline__ int arrive(int32_t* ctr, int* val_lds) {
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) *val_lds = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int v = *val_lds;
+  __syncthreads();
+  return v;
+}
+
+// --------------------------------------------------------------------------
+// Parameters of the one-launch decode
+// --------------------------------------------------------------------------
+struct FusedParams {
+  const void* q;               // [B][Hq][128]
+  const void* keys;            // [U][P][128]
+  const void* values;          // [U][P][128]
+  const uint16_t* indices;     // [U][L][P] chunk-major
+  const uint16_t* offsets;     // [U][L][nJP][2^K]
+  const int32_t* seq_lens;     // optional [B]
+  const uint16_t* qcodes;      // [BH][L] (written by the query-hash launch)
+  uint32_t* bitmask;           // [BH][Nw]
+  int32_t* chunk_nsel;         // [BH][nJ]
+  const double* lnu_samples;   // [kLnuSamples] g at theta_t = t pi / (2 kLnuTable) (query-hash launch)
+  float* partials;             // [BH][npart][kPartialStride]
+  int32_t* ready;              // [U][nJ] count workgroups done per (unit, chunk)
+  int32_t* arrive_unit;        // [U] partial slots written per unit
+  float* out;                  // [BH][128]
+  float* lse;                  // optional [BH]
+  int32_t* nsel;               // optional [BH]
+  uint8_t* counts;             // optional [BH][N]
+  int B, Hq, Hkv, G, N, P, K, L, T;
+  int stride_log2, nJ, nJP;
+  int split_len, nsplit, n_sink, n_window, exact_len, nexact;
+  int npart;
+  int n_count_wg, n_exact_wg, n_attend_wg;
+  float scale;
+#ifdef LSH_TRACE
+  unsigned long long* trace;   // [grid][16] phase timestamps (trace builds only)
+#endif
+};
+
+// Phase timestamps of a workgroup (s_memrealtime, 100 MHz), recorded only in
+// builds with LSH_TRACE defined; a profiling aid, compiled out otherwise.
+#ifdef LSH_TRACE
+#define LSH_STAMP(p, k) \
+  do { if (threadIdx.x == 0 && (p).trace) (p).trace[blockIdx.x * 16 + (k)] = __builtin_amdgcn_s_memrealtime(); } while (0)
+#else
+#define LSH_STAMP(p, k) do { } while (0)
+#endif
+
+// Sync words the query-hash launch zeroes before the decode launch.
+__host__ __device__ inline int fused_sync_words(int U, int nJ) { return U * nJ + U; }
+
+// --------------------------------------------------------------------------
+// The ln-u correction g(theta), sampled by the query-hash launch
+// --------------------------------------------------------------------------
+__device__ __forceinline__ double wave_max_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// g(theta) = ln sum_{i=T}^{L} C(L,i) P^(i-T) (1-P)^(L-i), P = (1 - theta/pi)^K,
+// by one wave: lane handles the terms i = T + lane + 64 k, whose log binomial
+// coefficients are lc[i] = ln C(L, i); a log-sum-exp over the wave.
+__device__ inline double lnu_correction_wave(double theta, int K, int L, int T, const double* lc, int lane) {
+  // the exponents are sums of large terms, so they are formed in fp64; the
+  // exponentials of their differences from the maximum lie in (0, 1] and a
+  // float keeps their relative precision, so those run in fp32
+  const double lp = log1p(-theta / 3.14159265358979323846);   // ln p
+  const double lP = (K == 0) ? 0.0 : K * lp;                      // ln P
+  const double lQ = (K == 0) ? -INFINITY : log(-expm1(lP));      // ln(1 - P)
+  double t[4];
+  double m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = T + lane + 64 * k;
+    double x = -INFINITY;
+    if (i <= L) {
+      x = lc[i];
+      if (i > T) x += (i - T) * lP;   // the zero power is 1: skip 0 * ln 0
+      if (L > i) x += (L - i) * lQ;
+    }
+    t[k] = x;
+    m = fmax(m, x);
+  }
+  m = wave_max_f64(m);
+  float sum = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (t[k] != -INFINITY) sum += __expf(static_cast<float>(t[k] - m));
+  sum = wave_sum(sum);
+  return m + static_cast<double>(__logf(sum));
+}
+
+// The ln-u interval quadratics for the attention role, from the fp64
+// samples the query-hash launch wrote (plain loads: that launch has
+// completed).  lnu_fetch issues this thread's loads (four intervals, three
+// samples each) so they can be in flight while the workgroup waits for its
+// selection; lnu_store forms the quadratics in LDS (zeros when no ln u is
+// needed).
+struct LnuFetch {
+  double g[kLnuTable / kFusedThreads][3];
+};
+__device__ __forceinline__ void lnu_fetch(const FusedParams& p, bool nolnu, LnuFetch& r) {
+  if (nolnu) return;
+#pragma unroll
+  for (int q = 0; q < kLnuTable / kFusedThreads; ++q) {
+    const int j = threadIdx.x + q * kFusedThreads;
+#pragma unroll
+    for (int t = 0; t < 3; ++t) r.g[q][t] = p.lnu_samples[2 * j + t];
+  }
+}
+__device__ __forceinline__ void lnu_store(const LnuFetch& r, bool nolnu, float4* tab) {
+#pragma unroll
+  for (int q = 0; q < kLnuTable / kFusedThreads; ++q) {
+    const int j = threadIdx.x + q * kFusedThreads;
+    float4 e = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!nolnu) {
+      const double g0 = r.g[q][0], gm = r.g[q][1], g1 = r.g[q][2];
+      e = make_float4(static_cast<float>(g0), static_cast<float>(-3.0 * g0 + 4.0 * gm - g1),
+                      static_cast<float>(2.0 * g0 - 4.0 * gm + 2.0 * g1), 0.f);
+    }
+    tab[j] = e;
+  }
+}
+
+// --------------------------------------------------------------------------
+// Count role: one workgroup per (key chunk J, query head bh).  For every table
+// the segment of the probed bucket inside chunk J is read in aligned 16-byte
+// blocks of 8 entries (entries outside the segment are skipped), and each
+// entry adds 1 to its key's byte counter in LDS.  Keys with count >= T, not in
+// the exact set and within the sequence, form the selection bitmask.
+//
+// The blocks of all tables are concatenated (a scan of the per-table block
+// counts) and every wave walks a contiguous range of them, 16 blocks in
+// flight per lane; each block's segment comes from a map of the segments'
+// first blocks (a bitmap, its per-row prefix counts and the list of
+// non-empty tables), or for very long walks from a binary search over the
+// scan.  Reading whole aligned blocks may read up to 14 bytes past a segment,
+// inside the 16-byte block that holds its first or last entry (never past the
+// 16-byte granule of the indices array's last entry).
+// --------------------------------------------------------------------------
+constexpr int kCountInflight = 16;
+
+constexpr int kSegMapRows = 512;   // walks of up to 512 x 64 blocks use the segment map
+
+struct CountLds {                  // laid out after the byte counters
+  long long fb[256];               // first block of each table's segment
+  uint64_t starts[kSegMapRows];    // segment map: bit v & 63 of row v >> 6 marks a segment's first block
+  int pre[kSegMapRows + 1];        // segment map: set bits in the rows before each row
+  short lo[256], hi[256];          // segment [lo, hi) in entries from 8 * fb
+  int segv[257];                   // exclusive scan of block counts
+  uint8_t seglist[256];            // segment map: the non-empty tables, in order
+  uint32_t spare[64];              // trace builds: keeps the traced loads alive
+  uint32_t wtot[kFusedThreads / 64];
+  int flag;
+};
+
+__device__ inline void count_role(const FusedParams& p, int wid, unsigned char* smem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int BH = p.B * p.Hq;
+  const int J = wid / BH, bh = wid % BH;
+  const int b = bh / p.Hq, h = bh % p.Hq;
+  const int u = b * p.Hkv + h / p.G;
+  const int nb = 1 << p.K;
+  const int sl = p.stride_log2;
+  const int cbeg = J << sl;
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(smem);                     // one byte per key of the chunk
+  CountLds& s = *reinterpret_cast<CountLds*>(smem + (1 << sl));
+  const int Nb = seq_len_of(p.seq_lens, b, p.N);
+  const int cfull = min(1 << sl, p.N - cbeg);
+  const int clen = max(0, min(1 << sl, Nb - cbeg));
+  const int cwords = (cfull + 3) >> 2;
+  int exact_head, exact_tail;
+  exact_range(p.n_sink, p.n_window, Nb, exact_head, exact_tail);
+
+  LSH_STAMP(p, 0);
+  for (int i = tid; i < cwords; i += kFusedThreads) cnt[i] = 0;
+
+  // segment of bucket qcode_l inside this chunk, in blocks, for table l = tid
+  int nblk = 0;
+  if (tid < p.L && clen > 0) {
+    const int qc = p.qcodes[static_cast<size_t>(bh) * p.L + tid];
+    const size_t row = static_cast<size_t>(u) * p.L + tid;
+    const uint16_t* op = p.offsets + (row * p.nJP + J) * nb + qc;
+    // clamped into the chunk: tables of another stride cannot send the walk out of it
+    const int s0 = min(static_cast<int>(op[0]), clen);
+    const int e0 = qc + 1 < nb ? min(static_cast<int>(op[1]), clen) : clen;
+    const size_t first = row * p.P + cbeg + s0;      // element index of the segment's first entry
+    const int lo = static_cast<int>(first & 7);
+    const int len = max(e0 - s0, 0);
+    nblk = len > 0 ? (lo + len + 7) >> 3 : 0;
+    s.fb[tid] = static_cast<long long>(first >> 3);
+    s.lo[tid] = static_cast<short>(lo);
+    s.hi[tid] = static_cast<short>(lo + len);
+  }
+  // one scan gives the block offsets (low 24 bits) and the rank of each
+  // non-empty segment among them (high 8 bits)
+  const uint32_t own = static_cast<uint32_t>(nblk) + (nblk > 0 ? (1u << 24) : 0u);
+  uint32_t incl = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) s.wtot[wave] = incl;
+  __syncthreads();
+  {
+    uint32_t wbase = 0;
+    for (int w = 0; w < wave; ++w) wbase += s.wtot[w];
+    incl += wbase;
+    s.segv[tid + 1] = static_cast<int>(incl & 0xffffffu);
+    if (tid == 0) s.segv[0] = 0;
+    if (nblk > 0) s.seglist[(incl - own) >> 24] = static_cast<uint8_t>(tid);
+  }
+  __syncthreads();
+  LSH_STAMP(p, 1);
+
+  const int total = s.segv[p.L];
+  // segment map (walks of at most kSegMapRows rows of 64 blocks): the
+  // segment of block v is seglist[(set bits of starts before v) - 1]
+  const int nrows = (total + 63) >> 6;
+  const bool mapped = nrows <= kSegMapRows;
+  if (mapped) {
+    for (int r = tid; r < nrows; r += kFusedThreads) s.starts[r] = 0ull;
+    __syncthreads();
+    if (nblk > 0) {
+      const int v = s.segv[tid];
+      atomicOr(reinterpret_cast<unsigned long long*>(&s.starts[v >> 6]), 1ull << (v & 63));
+    }
+    __syncthreads();
+    // exclusive scan of the rows' bit counts (two rows per thread)
+    const int r0 = 2 * tid;
+    const int c0 = r0 < nrows ? __popcll(s.starts[r0]) : 0;
+    const int c1 = r0 + 1 < nrows ? __popcll(s.starts[r0 + 1]) : 0;
+    int x = c0 + c1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(x, o);
+      if (lane >= o) x += v;
+    }
+    if (lane == 63) s.wtot[wave] = static_cast<uint32_t>(x);
+    __syncthreads();
+    int wb = 0;
+    for (int w = 0; w < wave; ++w) wb += static_cast<int>(s.wtot[w]);
+    x += wb;
+    if (r0 < nrows) s.pre[r0] = x - c0 - c1;
+    if (r0 + 1 < nrows) s.pre[r0 + 1] = x - c1;
+    __syncthreads();
+  }
+  constexpr int kW = kFusedThreads / 64;
+  const int per = ((total + kW - 1) / kW + 63) & ~63;
+  const int wstart = wave * per, wend = min(total, wstart + per);
+  const u32x4_t* ib = reinterpret_cast<const u32x4_t*>(p.indices);
+  LSH_STAMP(p, 4);
+  for (int w0 = wstart; w0 < wend; w0 += 64 * kCountInflight) {
+    const int v0 = w0 + lane;
+    // rows of 64 blocks this wave still has (wave-uniform): the unrolled
+    // steps below skip the others, so short walks cost little
+    const int nk = min(kCountInflight, (wend - w0 + 63) >> 6);
+    u32x4_t blk[kCountInflight];
+    int lo[kCountInflight], hi[kCountInflight];
+    // the segment of each block (past the wave's range: of its last block):
+    // from the segment map, or else by binary searches over the scan
+    int sg[kCountInflight];
+    if (mapped) {
+#pragma unroll
+      for (int k = 0; k < kCountInflight; ++k) {
+        if (k < nk) {
+          const int v = min(v0 + 64 * k, wend - 1);
+          const uint64_t below = s.starts[v >> 6] & ((2ull << (v & 63)) - 1ull);
+          sg[k] = s.seglist[s.pre[v >> 6] + __popcll(below) - 1];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kCountInflight; ++k) sg[k] = 0;
+#pragma unroll
+      for (int step = 128; step > 0; step >>= 1) {
+        int sv[kCountInflight];
+#pragma unroll
+        for (int k = 0; k < kCountInflight; ++k)
+          if (k < nk) sv[k] = s.segv[min(sg[k] + step, 256)];
+#pragma unroll
+        for (int k = 0; k < kCountInflight; ++k) {
+          const int c = sg[k] + step;
+          if (k < nk) sg[k] = (c < p.L && sv[k] <= min(v0 + 64 * k, wend - 1)) ? c : sg[k];
+        }
+      }
+    }
+    if (w0 == wstart) LSH_STAMP(p, 5);
+    // blocks past the wave's range load its last block again and take no entry
+#pragma unroll
+    for (int k = 0; k < kCountInflight; ++k) {
+      if (k < nk) {
+        const int v = v0 + 64 * k;
+        const bool in = v < wend;
+        const int l = sg[k];
+        const int i = min(v, wend - 1) - s.segv[l];
+        blk[k] = ib[s.fb[l] + i];
+        lo[k] = in ? s.lo[l] - 8 * i : 8;
+        hi[k] = in ? s.hi[l] - 8 * i : 0;
+      }
+    }
+#ifdef LSH_TRACE
+    if (w0 == wstart) {   // trace builds: the first row's blocks have arrived
+      uint32_t z = 0;
+#pragma unroll
+      for (int k = 0; k < kCountInflight; ++k)
+        if (k < nk) z ^= blk[k][0];
+      if (z == 0x9e3779b9u) s.spare[lane] = z;
+      LSH_STAMP(p, 6);
+    }
+#endif
+    // one LDS add per entry, without branches.  A key is masked into the
+    // chunk's range (the counter array holds one byte per position of a full
+    // chunk), so no access can leave the array whatever the table holds; an
+    // entry outside its segment adds 0.  Keys past the chunk's length (in a
+    // table of another layout) count positions the selection never reads.
+    const uint32_t kmask = (1u << sl) - 1u;
+#pragma unroll
+    for (int k = 0; k < kCountInflight; ++k) {
+      if (k < nk) {
+        const uint32_t inseg = (0xffu << max(lo[k], 0)) & (0xffu >> (8 - min(max(hi[k], 0), 8)));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t key = (blk[k][e >> 1] >> (16 * (e & 1))) & kmask;
+          const uint32_t inc = ((inseg >> e) & 1u) << ((key & 3u) * 8u);
+          __hip_atomic_fetch_add(&cnt[key >> 2], inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      }
+    }
+  }
+  LSH_STAMP(p, 7);
+  __syncthreads();
+  LSH_STAMP(p, 2);
+
+  const int Nw = (p.N + 31) >> 5;
+  const int nwords = (cfull + 31) >> 5;
+  int mysel = 0;
+  for (int w = tid; w < nwords; w += kFusedThreads) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int wi = w * 8 + j;
+      const uint32_t c4 = wi < cwords ? cnt[wi] : 0u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int key = w * 32 + j * 4 + k;
+        const int n = cbeg + key;
+        const bool ex = n < exact_head || n >= Nb - exact_tail;
+        if (key < clen && !ex && static_cast<int>((c4 >> (8 * k)) & 0xffu) >= p.T) m |= 1u << (j * 4 + k);
+      }
+    }
+    st_agent(p.bitmask + static_cast<size_t>(bh) * Nw + (cbeg >> 5) + w, m);
+    mysel += __builtin_popcount(m);
+  }
+  if (p.counts) {
+    const uint8_t* c8 = reinterpret_cast<const uint8_t*>(cnt);
+    uint8_t* dst = p.counts + static_cast<size_t>(bh) * p.N + cbeg;
+    for (int i = tid; i < cfull; i += kFusedThreads) dst[i] = c8[i];
+  }
+  mysel = wave_sum_int(mysel);
+  if (lane == 0) s.wtot[wave] = mysel;
+  __syncthreads();
+  if (tid == 0) {
+    int t = 0;
+    for (int w = 0; w < kW; ++w) t += s.wtot[w];
+    st_agent(p.chunk_nsel + static_cast<size_t>(bh) * p.nJ + J, t);
+  }
+  arrive(p.ready + u * p.nJ + J, &s.flag);
+  LSH_STAMP(p, 3);
+}
+
+// --------------------------------------------------------------------------
+// Merge
+//
+// Every attend / exact workgroup of unit u writes its partial slot and then
+// arrives at the unit's counter.  The last F = min(G, npart) arrivals are
+// the finishers: finisher f waits until all npart slots have arrived and
+// folds the slots of heads f, f + F, ... into out / lse / nsel.  Attend
+// workgroups are dispatched unit by unit (see the grids), so a finisher waits
+// only for workgroups that are running or will get a slot: every workgroup of
+// a lower unit has been dispatched, and none of a higher unit holds a slot
+// while one of its unit's is still waiting for dispatch.
+// --------------------------------------------------------------------------
+constexpr int kMergeBatch = 32;      // slot values a thread keeps in flight in a fold
+constexpr int kMergeMaxPairs = 2048; // (head, slot) pairs of a fold, in LDS
+
+struct MergeLds {
+  float m[kMergeMaxPairs];           // max, then the slot's weight exp(m - M)
+  float l[kMergeMaxPairs];
+  float M[16], Lm[16];
+  float red[kFusedThreads];          // column sums of the thread groups sharing a column
+  int nsel[16];
+  int flag;
+};
+
+// Fold all npart slots of heads f, f + F, ... of unit u (bh0 = its first
+// head) into the outputs.  The nh * 128 columns (head, dim) are spread over
+// the threads, R threads per column (R = 256 / columns when that is at least
+// 2), each R-th slot per thread.  The first batch of slot values goes out
+// together with the heads' max / sum and chunk-count loads, so a fold of up
+// to kMergeBatch slots per thread costs one round trip to memory.
+__device__ inline void fold_heads(const FusedParams& p, int bh0, int f, int F, unsigned char* smem) {
+  MergeLds& s = *reinterpret_cast<MergeLds*>(smem);
+  const int tid = threadIdx.x;
+  const int np = p.npart;
+  const int nh = (p.G - f + F - 1) / F;                         // heads of this finisher
+  const int C = nh * kHeadDim;
+  const int R = C >= kFusedThreads ? 1 : kFusedThreads / C;
+  const int cpt = (C + kFusedThreads - 1) / kFusedThreads;     // column blocks (R == 1 only)
+  if (tid < nh) s.nsel[tid] = 0;
+  // every slot has arrived (the finisher waited for the unit's counter), and
+  // each was written through to memory before its arrival; one acquire fence
+  // drops any stale copy from this XCD's caches, so the fold reads the slots
+  // with plain loads (a coherent load per value would be far slower in bulk)
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __syncthreads();
+  LSH_STAMP(p, 8);
+  // column block 0's first batch of slot values
+  const int c0 = R > 1 ? tid % C : tid;
+  const int r0 = R > 1 ? tid / C : 0;
+  const bool live0 = c0 < C && r0 < R;
+  const int hi0 = live0 ? c0 / kHeadDim : 0, d0 = c0 % kHeadDim;
+  const float* base0 = p.partials + static_cast<size_t>(bh0 + f + F * hi0) * np * kPartialStride + d0;
+  float x0[kMergeBatch];
+#pragma unroll
+  for (int i = 0; i < kMergeBatch; ++i) x0[i] = base0[static_cast<size_t>(min(r0 + i * R, np - 1)) * kPartialStride];
+  // max / sum of every (head, slot) pair and the heads' chunk selection
+  // counts: loads with clamped indices issue together, eight per thread at a time
+  for (int i0 = 0; i0 < nh * np; i0 += 8 * kFusedThreads) {
+    float mv[8], lv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int i = min(i0 + tid + q * kFusedThreads, nh * np - 1);
+      const float* ps = p.partials + (static_cast<size_t>(bh0 + f + F * (i / np)) * np + i % np) * kPartialStride;
+      mv[q] = ps[kHeadDim];
+      lv[q] = ps[kHeadDim + 1];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int i = i0 + tid + q * kFusedThreads;
+      if (i < nh * np) {
+        s.m[i] = mv[q];
+        s.l[i] = lv[q];
+      }
+    }
+  }
+  for (int i0 = 0; i0 < nh * p.nJ; i0 += 8 * kFusedThreads) {
+    int cv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int i = min(i0 + tid + q * kFusedThreads, nh * p.nJ - 1);
+      cv[q] = p.chunk_nsel[static_cast<size_t>(bh0 + f + F * (i / p.nJ)) * p.nJ + i % p.nJ];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int i = i0 + tid + q * kFusedThreads;
+      if (i < nh * p.nJ) atomicAdd(&s.nsel[i / p.nJ], cv[q]);
+    }
+  }
+  __syncthreads();
+  LSH_STAMP(p, 9);
+  // per head: the max over its slots, then each slot's weight exp(m - M)
+  // and the weighted sum of the slot sums; wave w takes heads w, w + 4, ...,
+  // its lanes the slots (reductions across the wave)
+  {
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int hi = wave; hi < nh; hi += kFusedThreads / 64) {
+      float M = -INFINITY;
+      for (int k = lane; k < np; k += 64) M = fmaxf(M, s.m[hi * np + k]);
+      M = wave_max(M);
+      float Lm = 0.f;
+      for (int k = lane; k < np; k += 64) {
+        const float mk = s.m[hi * np + k];
+        const float w = (M == -INFINITY || mk == -INFINITY) ? 0.f : __expf(mk - M);
+        Lm = fmaf(s.l[hi * np + k], w, Lm);
+        s.m[hi * np + k] = w;
+      }
+      Lm = wave_sum(Lm);
+      if (lane == 0) {
+        s.M[hi] = M;
+        s.Lm[hi] = Lm;
+      }
+    }
+  }
+  __syncthreads();
+  LSH_STAMP(p, 10);
+  for (int cb = 0; cb < cpt; ++cb) {
+    const int c = cb * kFusedThreads + (R > 1 ? tid % C : tid);
+    const int r = R > 1 ? tid / C : 0;
+    const bool live = c < C && r < R;
+    const int hi = live ? c / kHeadDim : 0, d = c % kHeadDim;
+    const float* base = p.partials + static_cast<size_t>(bh0 + f + F * hi) * np * kPartialStride + d;
+    float acc = 0.f;
+    for (int k0 = r; k0 < np; k0 += R * kMergeBatch) {
+      if (cb != 0 || k0 != r) {   // the first batch of block 0 is already in x0
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) {
+          const int k = min(k0 + i * R, np - 1);   // clamped: every load issues, the extra ones add nothing
+          x0[i] = base[static_cast<size_t>(k) * kPartialStride];
+        }
+      }
+      float* x = x0;
+      // the weights: clamped reads, so they issue together; past the last
+      // slot (and in dead columns) the weight is 0
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; i += 16) {
+        float w[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) w[q] = s.m[hi * np + min(k0 + (i + q) * R, np - 1)];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int k = k0 + (i + q) * R;
+          acc = fmaf(x[i + q], (live && k < np) ? w[q] : 0.f, acc);
+        }
+      }
+    }
+    // the R partial sums of each column
+    s.red[tid] = acc;
+    __syncthreads();
+    if (live && r == 0) {
+      for (int q = 1; q < R; ++q) acc += s.red[tid + q * C];
+      const int bh = bh0 + f + F * hi;
+      const float M = s.M[hi], Lm = s.Lm[hi];
+      p.out[static_cast<size_t>(bh) * kHeadDim + d] = (M == -INFINITY) ? 0.f : acc / Lm;
+      if (d == 0) {
+        if (p.lse) p.lse[bh] = (M == -INFINITY) ? -INFINITY : M + logf(Lm);
+        if (p.nsel) p.nsel[bh] = s.nsel[hi];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// After writing partial slot `slot` of unit u: arrive; the last F arrivals
+// fold the unit's heads.
+__device__ inline void finish_slot(const FusedParams& p, int u, int slot, unsigned char* smem) {
+  MergeLds& s = *reinterpret_cast<MergeLds*>(smem);
+  const int b = u / p.Hkv, g = u % p.Hkv;
+  const int bh0 = b * p.Hq + g * p.G;
+  const int F = min(p.G, p.npart);
+  const int c = arrive(p.arrive_unit + u, &s.flag);
+  if (c < p.npart - F) return;
+  LSH_STAMP(p, 5);
+  const int f = c - (p.npart - F);
+  // every slot of the unit has arrived, and the selection counts of every
+  // chunk of it are complete (chunks past a short sequence's end are waited
+  // for by no attend workgroup): thread 0 polls the first, the others the
+  // chunk counters, side by side
+  if (threadIdx.x == 0) s.flag = 1;
+  __syncthreads();
+  int ok = 1;
+  for (int j = static_cast<int>(threadIdx.x) - 1; j < p.nJ; j += kFusedThreads) {
+    const int32_t* ctr = j < 0 ? p.arrive_unit + u : p.ready + u * p.nJ + j;
+    const int target = j < 0 ? p.npart : p.G;
+    int it = 0;
+    while (ld_agent(ctr) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++it >= kSpinLimit) {
+        ok = 0;
+        break;
+      }
+    }
+  }
+  if (!ok) s.flag = 0;
+  __syncthreads();
+  const bool all = s.flag != 0;
+  __syncthreads();
+  LSH_STAMP(p, 6);
+  fold_heads(p, bh0, f, F, smem);
+  if (!all && threadIdx.x == 0) p.out[static_cast<size_t>(bh0 + f) * kHeadDim] = __builtin_nanf("");
+  LSH_STAMP(p, 7);
+}
+
+constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+// LDS the count and merge roles use (the attention roles add theirs)
+constexpr size_t kRolesLdsBytes = cmax((static_cast<size_t>(1) << 13) + sizeof(CountLds), sizeof(MergeLds));
+
+}  // namespace lsh

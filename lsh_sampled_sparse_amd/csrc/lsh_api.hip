@@ -67,7 +67,7 @@ BuildLayout build_layout(int B, int Hkv, int N, int L, int dtype, const Geometry
 }
 
 struct DecodeLayout {
-  size_t qcodes = 0, bitmask = 0, chunk_nsel = 0, lnu = 0, partials = 0, total = 0;
+  size_t qcodes = 0, bitmask = 0, chunk_nsel = 0, lnu = 0, partials = 0, sync = 0, total = 0;
   int split_len = 0, nsplit = 0;
 };
 
@@ -88,14 +88,16 @@ DecodeLayout decode_layout(int B, int Hq, int Hkv, int N, int L, const Geometry&
   w.bitmask = off;    off = align_up(off + BH * ((N + 31) / 32) * sizeof(uint32_t));
   w.chunk_nsel = off; off = align_up(off + BH * g.nJ * sizeof(int32_t));
   w.lnu = off;        off = align_up(off + lsh::kLnuSamples * sizeof(double));
-  // one partial per head and context split, plus the exact set's pieces
   // partial slots: nsplit <= min(ceil(N / 256), ceil(512 / units)), a bound
   // that grows with N, so the workspace size at a cache's capacity covers
   // every shorter length; plus the exact set's pieces
   const long long slots = std::max<long long>(
-      w.nsplit, std::min((static_cast<long long>(N) + 255) / 256, (511 + units) / units));
+      w.nsplit, std::min((static_cast<long long>(N) + 255) / 256, (511 + units) / units)) + lsh::kMaxExactSplits;
   w.partials = off;
-  off = align_up(off + BH * static_cast<size_t>(slots + lsh::kMaxExactSplits) * lsh::kPartialStride * sizeof(float));
+  off = align_up(off + BH * static_cast<size_t>(slots) * lsh::kPartialStride * sizeof(float));
+  // counters of the decode launch: per (unit, chunk) and per unit
+  w.sync = off;
+  off = align_up(off + static_cast<size_t>(units * g.nJ + units) * sizeof(int32_t));
   w.total = off;
   return w;
 }
@@ -120,7 +122,7 @@ namespace lsh {
 
 const char* kernel_name(int id) {
   static const char* const names[kKNumKernels] = {
-      "transpose_w", "project_codes", "chunk_sort", "qhash", "count_select", "attend", "merge"};
+      "transpose_w", "project_codes", "chunk_sort", "qhash", "decode"};
   return (id >= 0 && id < kKNumKernels) ? names[id] : nullptr;
 }
 
@@ -312,6 +314,7 @@ lsh_status lsh_decode_attention_cached(const void* q, const void* keys, const vo
   a.chunk_nsel = reinterpret_cast<int32_t*>(ws + w.chunk_nsel);
   a.lnu_samples = reinterpret_cast<double*>(ws + w.lnu);
   a.partials = reinterpret_cast<float*>(ws + w.partials);
+  a.sync = reinterpret_cast<int32_t*>(ws + w.sync);
   a.out = out;
   a.lse = lse;
   a.nsel = nsel;

@@ -41,8 +41,9 @@ struct DecodeArgs {
   uint16_t* qcodes;      // [B*Hq][L]
   uint32_t* bitmask;     // [B*Hq][Nw]
   int32_t* chunk_nsel;   // [B*Hq][nJ]
-  double* lnu_samples;   // [kLnuSamples]: g(theta) at theta_t = t pi / (2 kLnuTable)
+  double* lnu_samples;   // [kLnuSamples] the ln-u correction g at theta_t = t pi / (2 kLnuTable)
   float* partials;       // [B*Hq][nsplit + nexact][130]
+  int32_t* sync;         // the decode launch's counters (zeroed by the query-hash launch)
   float* out;            // [B*Hq][128]
   float* lse;            // optional [B*Hq]
   int32_t* nsel;         // optional [B*Hq]
@@ -73,19 +74,16 @@ __host__ __device__ inline void exact_range(int n_sink, int n_window, int n, int
   et = n_window < n - eh ? n_window : n - eh;
 }
 
-constexpr int kLnuTable = 1024;   // ln-u correction table intervals over theta in [0, pi]
-constexpr int kLnuSamples = 2 * kLnuTable + 1;   // fp64 samples of g: both ends and the middle of every interval
-
-// Quadratic of ln-u correction interval j, from the fp64 samples of g at its
-// start, middle and end: g(theta_j + f h) ~ x + f (y + f z) for f in [0, 1]
-// (h = pi / kLnuTable).  The coefficients are formed in fp64 and rounded
-// once, so the small y and z keep their relative precision.
-__device__ __forceinline__ float4 lnu_interval(const double* s, int j) {
-  const double g0 = s[2 * j], gm = s[2 * j + 1], g1 = s[2 * j + 2];
-  return make_float4(static_cast<float>(g0), static_cast<float>(-3.0 * g0 + 4.0 * gm - g1),
-                     static_cast<float>(2.0 * g0 - 4.0 * gm + 2.0 * g1), 0.f);
-}
-constexpr int kPartialStride = 130;
+// The ln-u correction g(theta) is kept as one quadratic per interval of
+// width pi / kLnuTable, g(theta_j + f h) ~ x + f (y + f z) for f in [0, 1],
+// through fp64 samples at the interval's start, middle and end; the
+// coefficients are formed in fp64 and rounded once, so the small y and z
+// keep their relative precision.
+constexpr int kLnuTable = 1024;
+constexpr int kLnuSamples = 2 * kLnuTable + 1;
+// A partial state (acc[128], max, sum) padded to five 128-byte lines, so no
+// cache line holds two workgroups' partials.
+constexpr int kPartialStride = 160;
 constexpr int kMaxExactSplits = 16;   // partial slots per head reserved for the exact set
 
 // Kernel kinds, in launch order; names for the timing interface.
@@ -94,9 +92,7 @@ enum KernelId {
   kKProject,
   kKChunkSort,
   kKQhash,
-  kKCountSelect,
-  kKAttend,
-  kKMerge,
+  kKDecode,
   kKNumKernels
 };
 const char* kernel_name(int id);
@@ -128,7 +124,8 @@ int proj_wt_rows(int K, int L);
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-// The bf16 weighted-attention kernel (MFMA for q.k and P.V).
-hipError_t launch_attend_bf16(const DecodeArgs& a, hipStream_t stream);
+// The one-launch decode over bf16 K/V (MFMA for q.k and P.V).
+struct FusedParams;
+hipError_t launch_decode_bf16(const FusedParams& p, hipStream_t stream);
 
 }  // namespace lsh
