@@ -34,10 +34,14 @@
  * Conventions for every entry point:
  *   - Every pointer argument is DEVICE memory owned by the caller, except
  *     `stream`, which is a hipStream_t handle (NULL = the null stream).  The
- *     library allocates no device memory and keeps no state between calls
- *     (the kernel-timing window at the end of this header is the one
- *     exception); calls on different streams may run concurrently if they use
- *     separate outputs and workspaces.
+ *     library allocates no device memory of its own at run time; the state it
+ *     keeps between calls is host-side bookkeeping that never changes a
+ *     result: the kernel-timing window at the end of this header, the record
+ *     of which kernels already had their LDS limit raised on which device, and
+ *     the per-device address of the static scratch array that
+ *     lsh_decode_attention_noalloc uses (the library's one device-side state,
+ *     loaded with the code object).  Calls on different streams may run
+ *     concurrently if they use separate outputs and workspaces.
  *   - All arrays are dense, row-major (last index fastest), 16-byte aligned.
  *   - Work is enqueued on `stream` and the call returns without waiting.
  *     The returned status covers argument checks (made before anything is
@@ -278,6 +282,40 @@ lsh_status lsh_decode_attention_cached(const void* q, const void* keys,
                                        uint16_t* q_codes, uint8_t* counts,
                                        void* workspace, size_t workspace_bytes,
                                        void* stream);
+
+/*
+ * The cached decode above with no workspace argument and no allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Arguments and
+ * results are those of lsh_decode_attention_cached without workspace and
+ * workspace_bytes.
+ *
+ * The workspace is a static device array of LSH_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * inside the library, one per device the library runs on, held until the
+ * process ends; its device address is looked up once per device, on the
+ * first call made with that device current.  A call that needs more
+ * (lsh_decode_workspace_size above the limit) returns LSH_ERR_WORKSPACE and
+ * launches nothing.  The call allocates nothing: no hipMalloc, no hipFree, no
+ * host allocation.  Its launches are never timed by the kernel-timing window
+ * below (taking events for them could allocate).
+ *
+ * Every call on a device shares that device's array, which keeps the last
+ * call's contents (the decode clears what must start at zero itself): calls
+ * that may overlap on one device (other streams, other threads) race, and
+ * must be ordered by the caller.
+ */
+#define LSH_NOALLOC_SCRATCH_BYTES (64u << 20)
+lsh_status lsh_decode_attention_noalloc(const void* q, const void* keys,
+                                        const void* values, const void* W,
+                                        const uint16_t* indices, const uint16_t* offsets,
+                                        int B, int Hq, int Hkv, int N, int n_cap,
+                                        const int32_t* seq_lens,
+                                        int d, int K, int L, int T, int stride,
+                                        float sm_scale, int dtype, int w_per_head,
+                                        int n_sink, int n_window,
+                                        float* out, float* lse, int32_t* nsel,
+                                        uint16_t* q_codes, uint8_t* counts,
+                                        void* stream);
 
 /* ------------------------------------------------------------------------
  * Kernel timing (a profiling aid; process-wide, one window at a time)

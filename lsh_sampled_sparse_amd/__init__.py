@@ -32,6 +32,7 @@ EXPORTS = (
     "lsh_decode_attention",
     "lsh_decode_attention_hybrid",
     "lsh_decode_attention_cached",
+    "lsh_decode_attention_noalloc",
     "lsh_kernel_count",
     "lsh_kernel_name",
     "lsh_timing_begin",
@@ -76,6 +77,9 @@ def lib():
         L.lsh_decode_attention_cached.restype = _i
         L.lsh_decode_attention_cached.argtypes = ([_p] * 6 + [_i] * 5 + [_p] + [_i] * 5
                                                   + [ctypes.c_float] + [_i] * 4 + [_p] * 6 + [_sz, _p])
+        L.lsh_decode_attention_noalloc.restype = _i
+        L.lsh_decode_attention_noalloc.argtypes = ([_p] * 6 + [_i] * 5 + [_p] + [_i] * 5
+                                                   + [ctypes.c_float] + [_i] * 4 + [_p] * 5 + [_p])
         L.lsh_kernel_count.restype = _i
         L.lsh_kernel_count.argtypes = []
         L.lsh_kernel_name.restype = ctypes.c_char_p
@@ -232,6 +236,25 @@ def lsh_decode_attention_cached(q, keys, values, W, indices, offsets, N, K, L, T
         1 if W.dim() == 3 else 0, int(n_sink), int(n_window),
         _ptr(out), _ptr(lse), _ptr(nsel), _ptr(q_codes), _ptr(counts),
         _ptr(workspace), workspace.numel(), _stream(keys.device)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def lsh_decode_attention_noalloc(q, keys, values, W, indices, offsets, N, K, L, T, stride, sm_scale, n_sink,
+                                 n_window, out, lse=None, nsel=None, q_codes=None, counts=None, seq_lens=None):
+    """Marshal tensors to ``lsh_decode_attention_noalloc``: the cached decode
+    with the library's static scratch as its workspace (nothing allocated);
+    arguments as ``lsh_decode_attention_cached`` without ``workspace``."""
+    _check_decode_tensors(q, keys, values, W, indices, offsets, K, L, stride, keys.shape[2], True)
+    B, Hq, d = q.shape
+    _, Hkv, n_cap, _ = keys.shape
+    dt = _dtype_code(keys.dtype)
+    _check(lib().lsh_decode_attention_noalloc(
+        _ptr(q), _ptr(keys), _ptr(values), _ptr(W), _ptr(indices), _ptr(offsets),
+        B, Hq, Hkv, int(N), n_cap, _ptr(seq_lens), d, K, L, T, stride, ctypes.c_float(sm_scale), dt,
+        1 if W.dim() == 3 else 0, int(n_sink), int(n_window),
+        _ptr(out), _ptr(lse), _ptr(nsel), _ptr(q_codes), _ptr(counts), _stream(keys.device)))
 
 
 def lsh_decode_attention(q, keys, values, W, indices, offsets, K, L, T, stride, sm_scale, out,

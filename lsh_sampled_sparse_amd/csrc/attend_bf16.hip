@@ -490,11 +490,11 @@ __global__ __launch_bounds__(kFusedThreads, 2) void decode_bf16_kernel(FusedPara
   finish_slot(p, u, slot, smem);
 }
 
-hipError_t launch_decode_bf16(const FusedParams& p, hipStream_t stream) {
+hipError_t launch_decode_bf16(const FusedParams& p, int kid, hipStream_t stream) {
   const dim3 grid(p.n_count_wg + p.n_exact_wg + p.n_attend_wg);
-  if (p.G <= 4) return launch(kKDecode, decode_bf16_kernel<1>, grid, dim3(kFusedThreads), 0, stream, p);
-  if (p.G <= 8) return launch(kKDecode, decode_bf16_kernel<2>, grid, dim3(kFusedThreads), 0, stream, p);
-  return launch(kKDecode, decode_bf16_kernel<4>, grid, dim3(kFusedThreads), 0, stream, p);
+  if (p.G <= 4) return launch(kid, decode_bf16_kernel<1>, grid, dim3(kFusedThreads), 0, stream, p);
+  if (p.G <= 8) return launch(kid, decode_bf16_kernel<2>, grid, dim3(kFusedThreads), 0, stream, p);
+  return launch(kid, decode_bf16_kernel<4>, grid, dim3(kFusedThreads), 0, stream, p);
 }
 
 }  // namespace lsh

@@ -461,7 +461,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_f32_kernel(FusedParams p
 // Host-side launcher
 // ---------------------------------------------------------------------------
 template <typename T>
-static hipError_t launch_qhash(const DecodeArgs& a, int nsync, hipStream_t stream) {
+static hipError_t launch_qhash(const DecodeArgs& a, int nsync, int kid, hipStream_t stream) {
   using S = typename T::storage;
   const int BH = a.B * a.Hq;
   const int G = a.Hq / a.Hkv;
@@ -471,7 +471,7 @@ static hipError_t launch_qhash(const DecodeArgs& a, int nsync, hipStream_t strea
   const int tpw = a.K > 0 ? 64 / a.K : 256;
   const int xblocks = (a.L + tpw - 1) / tpw;
   const int tab_rows = a.K > 0 ? (kLnuSamples + 4 * xblocks - 1) / (4 * xblocks) : 0;   // 4 samples per workgroup
-  return launch(kKQhash, qhash_kernel<T>, dim3(xblocks, head_blocks + 1 + tab_rows), dim3(256), 0, stream,
+  return launch(kid, qhash_kernel<T>, dim3(xblocks, head_blocks + 1 + tab_rows), dim3(256), 0, stream,
                 static_cast<const S*>(a.q), static_cast<const S*>(a.W), a.qcodes, a.sync, nsync, a.lnu_samples,
                 BH, a.K, a.L, a.T, head_blocks, G, a.Hkv, w_head_stride);
 }
@@ -534,13 +534,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int F = p.G < p.npart ? p.G : p.npart;
   if ((p.G + F - 1) / F * p.npart > kMergeMaxPairs || p.G > 16 || a.L > 255) return hipErrorInvalidValue;
   const int nsync = fused_sync_words(U, a.nJ);
-  hipError_t e = (a.dtype == 1) ? launch_qhash<BF16>(a, nsync, stream) : launch_qhash<F32>(a, nsync, stream);
+  const int kq = a.timed ? kKQhash : -1, kd = a.timed ? kKDecode : -1;
+  hipError_t e = (a.dtype == 1) ? launch_qhash<BF16>(a, nsync, kq, stream) : launch_qhash<F32>(a, nsync, kq, stream);
   if (e != hipSuccess) return e;
-  if (a.dtype == 1) return launch_decode_bf16(p, stream);
+  if (a.dtype == 1) return launch_decode_bf16(p, kd, stream);
   const dim3 grid(p.n_count_wg + p.n_exact_wg + p.n_attend_wg);
-  if (p.G <= 4) return launch(kKDecode, decode_f32_kernel<4>, grid, dim3(kFusedThreads), 0, stream, p);
-  if (p.G <= 8) return launch(kKDecode, decode_f32_kernel<8>, grid, dim3(kFusedThreads), 0, stream, p);
-  return launch(kKDecode, decode_f32_kernel<16>, grid, dim3(kFusedThreads), 0, stream, p);
+  if (p.G <= 4) return launch(kd, decode_f32_kernel<4>, grid, dim3(kFusedThreads), 0, stream, p);
+  if (p.G <= 8) return launch(kd, decode_f32_kernel<8>, grid, dim3(kFusedThreads), 0, stream, p);
+  return launch(kd, decode_f32_kernel<16>, grid, dim3(kFusedThreads), 0, stream, p);
 }
 
 }  // namespace lsh

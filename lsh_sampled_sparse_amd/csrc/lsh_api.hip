@@ -104,6 +104,13 @@ DecodeLayout decode_layout(int B, int Hq, int Hkv, int N, int L, const Geometry&
 
 lsh_status hip_status(hipError_t e) { return e == hipSuccess ? LSH_OK : LSH_ERR_HIP; }
 
+// Device address of each device's copy of `scratch` (below), taken once per
+// device with that device current; a fixed table, so the no-alloc entry point
+// allocates nothing, not even host memory.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 // Kernel timing.  While a timing window is open every launch takes a pair of
 // events from this pool (grown on demand, reused across windows); closing the
 // window waits for them and sums the elapsed times per kernel kind.
@@ -115,6 +122,29 @@ std::mutex g_timing_mu;
 bool g_timing_on = false;
 std::vector<TimingRecord> g_timing_pool;
 size_t g_timing_used = 0;
+
+}  // namespace
+
+// The workspace of lsh_decode_attention_noalloc: every device the library
+// runs on holds its own copy until the process ends.  In host code this name
+// is a host-side stand-in, never a device address: kernels receive the
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[LSH_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+lsh_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LSH_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LSH_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LSH_OK;
+}
 
 }  // namespace
 
@@ -142,6 +172,7 @@ hipError_t ensure_lds_limit(const void* kernel, size_t bytes) {
 
 void timing_events(int id, hipEvent_t* start, hipEvent_t* stop) {
   *start = *stop = nullptr;
+  if (id < 0) return;
   std::lock_guard<std::mutex> lk(g_timing_mu);
   if (!g_timing_on) return;
   if (g_timing_used == g_timing_pool.size()) {
@@ -168,7 +199,9 @@ const char* lsh_status_string(int status) {
     case LSH_OK: return "LSH_OK";
     case LSH_ERR_INVALID_ARG: return "LSH_ERR_INVALID_ARG: invalid argument";
     case LSH_ERR_UNSUPPORTED: return "LSH_ERR_UNSUPPORTED: valid but unsupported shape or parameter";
-    case LSH_ERR_WORKSPACE: return "LSH_ERR_WORKSPACE: workspace smaller than the size query";
+    case LSH_ERR_WORKSPACE:
+      return "LSH_ERR_WORKSPACE: workspace smaller than the size query (lsh_decode_attention_noalloc: the call "
+             "needs more than the library's static scratch holds)";
     case LSH_ERR_HIP: return "LSH_ERR_HIP: HIP runtime or launch error";
     default: return "unknown lsh_status";
   }
@@ -281,12 +314,12 @@ size_t lsh_decode_workspace_size(int B, int Hq, int Hkv, int N, int d, int K, in
   return decode_layout(B, Hq, Hkv, N, L, g).total;
 }
 
-lsh_status lsh_decode_attention_cached(const void* q, const void* keys, const void* values, const void* W,
-                                       const uint16_t* indices, const uint16_t* offsets, int B, int Hq, int Hkv,
-                                       int N, int n_cap, const int32_t* seq_lens, int d, int K, int L, int T,
-                                       int stride, float sm_scale, int dtype, int w_per_head, int n_sink,
-                                       int n_window, float* out, float* lse, int32_t* nsel, uint16_t* q_codes,
-                                       uint8_t* counts, void* workspace, size_t workspace_bytes, void* stream) {
+static lsh_status decode_cached(const void* q, const void* keys, const void* values, const void* W,
+                                const uint16_t* indices, const uint16_t* offsets, int B, int Hq, int Hkv, int N,
+                                int n_cap, const int32_t* seq_lens, int d, int K, int L, int T, int stride,
+                                float sm_scale, int dtype, int w_per_head, int n_sink, int n_window, float* out,
+                                float* lse, int32_t* nsel, uint16_t* q_codes, uint8_t* counts, void* workspace,
+                                size_t workspace_bytes, void* stream, bool noalloc) {
   Geometry g, gcap;
   lsh_status st = check_common(B, Hkv, N, d, K, L, stride, dtype, &g);
   if (st != LSH_OK) return st;
@@ -297,10 +330,15 @@ lsh_status lsh_decode_attention_cached(const void* q, const void* keys, const vo
   if (n_sink < 0 || n_window < 0) return LSH_ERR_INVALID_ARG;
   if (w_per_head != 0 && w_per_head != 1) return LSH_ERR_INVALID_ARG;
   if (Hq / Hkv > 16) return LSH_ERR_UNSUPPORTED;
-  if (!q || !keys || !values || !indices || !offsets || !out || !workspace || (K > 0 && !W))
+  if (!q || !keys || !values || !indices || !offsets || !out || (!noalloc && !workspace) || (K > 0 && !W))
     return LSH_ERR_INVALID_ARG;
   const DecodeLayout w = decode_layout(B, Hq, Hkv, N, L, g);
   if (workspace_bytes < w.total) return LSH_ERR_WORKSPACE;
+  if (noalloc) {
+    // every argument checked: only now the device's scratch address
+    st = scratch_address(&workspace);
+    if (st != LSH_OK) return st;
+  }
   char* ws = static_cast<char*>(workspace);
   lsh::DecodeArgs a;
   a.q = q;
@@ -338,6 +376,9 @@ lsh_status lsh_decode_attention_cached(const void* q, const void* keys, const vo
   a.w_heads = w_per_head ? Hkv : 1;
   a.n_sink = n_sink;
   a.n_window = n_window;
+  // the no-alloc path takes no timing events: the pool of events grows while
+  // a timing window is open
+  a.timed = !noalloc;
   // the exact set goes to the attention kernel as extra workgroups over
   // pieces of at least 128 keys (one 32-key tile per wave), at most
   // kMaxExactSplits of them, sized for the longest sequence (a sequence's
@@ -347,6 +388,30 @@ lsh_status lsh_decode_attention_cached(const void* q, const void* keys, const vo
   a.exact_len = std::max(128, (per_piece + 127) / 128 * 128);
   a.nexact = (ne + a.exact_len - 1) / a.exact_len;
   return hip_status(lsh::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+lsh_status lsh_decode_attention_cached(const void* q, const void* keys, const void* values, const void* W,
+                                       const uint16_t* indices, const uint16_t* offsets, int B, int Hq, int Hkv,
+                                       int N, int n_cap, const int32_t* seq_lens, int d, int K, int L, int T,
+                                       int stride, float sm_scale, int dtype, int w_per_head, int n_sink,
+                                       int n_window, float* out, float* lse, int32_t* nsel, uint16_t* q_codes,
+                                       uint8_t* counts, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_cached(q, keys, values, W, indices, offsets, B, Hq, Hkv, N, n_cap, seq_lens, d, K, L, T, stride,
+                       sm_scale, dtype, w_per_head, n_sink, n_window, out, lse, nsel, q_codes, counts, workspace,
+                       workspace_bytes, stream, false);
+}
+
+lsh_status lsh_decode_attention_noalloc(const void* q, const void* keys, const void* values, const void* W,
+                                        const uint16_t* indices, const uint16_t* offsets, int B, int Hq, int Hkv,
+                                        int N, int n_cap, const int32_t* seq_lens, int d, int K, int L, int T,
+                                        int stride, float sm_scale, int dtype, int w_per_head, int n_sink,
+                                        int n_window, float* out, float* lse, int32_t* nsel, uint16_t* q_codes,
+                                        uint8_t* counts, void* stream) {
+  // the scratch takes the workspace's part: a call that needs more than it
+  // holds is refused (LSH_ERR_WORKSPACE) before anything is launched
+  return decode_cached(q, keys, values, W, indices, offsets, B, Hq, Hkv, N, n_cap, seq_lens, d, K, L, T, stride,
+                       sm_scale, dtype, w_per_head, n_sink, n_window, out, lse, nsel, q_codes, counts, nullptr,
+                       LSH_NOALLOC_SCRATCH_BYTES, stream, true);
 }
 
 lsh_status lsh_decode_attention_hybrid(const void* q, const void* keys, const void* values, const void* W,

@@ -59,6 +59,7 @@ struct DecodeArgs {
   // eh = min(n_sink, n), et = min(n_window, n - eh)
   int n_sink, n_window;
   int exact_len, nexact;       // the exact set in nexact pieces of exact_len keys, one workgroup each
+  bool timed;                  // false: the launches never take timing events (no allocation)
 };
 
 // Keys of sequence b: the given length clamped into [0, N], or N.
@@ -98,7 +99,7 @@ enum KernelId {
 const char* kernel_name(int id);
 
 // Start/stop events for one launch of kernel `id` while timing is on; both
-// null otherwise.
+// null otherwise, and always for id < 0 (an untimed launch).
 void timing_events(int id, hipEvent_t* start, hipEvent_t* stop);
 
 // Every kernel goes through here: with timing on, the dispatch packet itself
@@ -126,6 +127,6 @@ hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // The one-launch decode over bf16 K/V (MFMA for q.k and P.V).
 struct FusedParams;
-hipError_t launch_decode_bf16(const FusedParams& p, hipStream_t stream);
+hipError_t launch_decode_bf16(const FusedParams& p, int kid, hipStream_t stream);
 
 }  // namespace lsh

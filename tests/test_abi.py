@@ -151,6 +151,33 @@ def test_hybrid_rejects(n_sink, n_window, kw, status):
     assert _hybrid(n_sink, n_window, **kw) == status
 
 
+def _noalloc(**kw):
+    a = dict(q=1, keys=1, values=1, W=1, indices=1, offsets=1, B=1, Hq=4, Hkv=1, N=4096, d=128, K=8,
+             L=32, T=2, stride=4096, scale=0.088, dtype=1, out=1)
+    a.update(kw)
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    return lsh.lib().lsh_decode_attention_noalloc(
+        p(a["q"]), p(a["keys"]), p(a["values"]), p(a["W"]), p(a["indices"]), p(a["offsets"]),
+        a["B"], a["Hq"], a["Hkv"], a["N"], a["N"], None, a["d"], a["K"], a["L"], a["T"], a["stride"],
+        ctypes.c_float(a["scale"]), a["dtype"], 0, 0, 0, p(a["out"]), None, None, None, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), lsh.LSH_ERR_INVALID_ARG),
+    (dict(out=None), lsh.LSH_ERR_INVALID_ARG),
+    (dict(T=0), lsh.LSH_ERR_INVALID_ARG),
+    (dict(Hq=17, Hkv=1), lsh.LSH_ERR_UNSUPPORTED),
+    # 256 x 32 heads of 128K keys need far more than the 64 MiB scratch
+    (dict(B=256, Hq=32, Hkv=8, N=131072, stride=8192, K=10, L=150), lsh.LSH_ERR_WORKSPACE),
+])
+def test_noalloc_rejects(kw, status):
+    """Argument checks and the scratch-size limit come before any HIP call."""
+    assert _noalloc(**kw) == status
+    size = lsh.lsh_decode_workspace_size(kw.get("B", 1), kw.get("Hq", 4), kw.get("Hkv", 1), kw.get("N", 4096),
+                                         128, kw.get("K", 8), kw.get("L", 32), kw.get("stride", 4096))
+    assert (size > lsh.NOALLOC_SCRATCH_BYTES) == (status == lsh.LSH_ERR_WORKSPACE)
+
+
 def _update(**kw):
     a = dict(keys=1, W=1, B=1, Hkv=1, n_old=100, n_new=200, n_cap=4096, d=128, K=8, L=32, stride=1024, dtype=1,
              w_per_head=0, offsets=1, indices=1, codes=None, ws=1, ws_bytes=1 << 40)
