@@ -72,6 +72,18 @@ def parse():
                     help="launch mode behind `value` (both are timed and reported)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--ingest-counters", metavar="DIR",
+                    help="no GPU work: read the rocprofv3 counter CSVs under DIR/fetch, DIR/write (FETCH_SIZE, "
+                         "WRITE_SIZE of a bench run) and DIR/calib_fetch, DIR/calib_write (the same counters of "
+                         "--copy-calibration) and write profiles/traffic_<workload>.json and .md")
+    ap.add_argument("--ingest-pmc", metavar="DIR",
+                    help="no GPU work: average every counter of the rocprofv3 --pmc CSVs under DIR (one pass per "
+                         "subdirectory) over the launches of --pmc-kernel and write "
+                         "profiles/pmc_<kernel>_<workload>.md")
+    ap.add_argument("--pmc-kernel", default="project_codes", help="kernel kind for --ingest-pmc")
+    ap.add_argument("--ingest-stats", metavar="DIR",
+                    help="no GPU work: read the rocprofv3 --stats kernel CSV under DIR and write "
+                         "profiles/kernel_stats_<workload>.md")
     return ap.parse_args()
 
 
@@ -111,6 +123,170 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": 4 * n, "launches": 5, "kernel": "torch.neg fp32"}), flush=True)
 
 
+# rocprofv3 kernel names -> the library's kernel kinds
+KERNEL_PATTERNS = (("qhash_kernel", "qhash"), ("decode_bf16_kernel", "decode"), ("decode_f32_kernel", "decode"),
+                   ("project_codes", "project_codes"), ("chunk_sort", "chunk_sort"), ("transpose_w", "transpose_w"))
+
+
+def _counter_values(d, counter):
+    """(kernel name, value) of every dispatch in the counter CSVs under d."""
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {d}")
+    return rows
+
+
+def ingest_counters(d, workload):
+    """HBM bytes per launch of every library kernel from two counter runs,
+    scaled by what the same counters read for the 1 GiB copy."""
+    calib = {}
+    for counter, sub in (("FETCH_SIZE", "calib_fetch"), ("WRITE_SIZE", "calib_write")):
+        vals = [v for name, v in _counter_values(os.path.join(d, sub), counter) if "neg" in name]
+        if not vals:
+            raise SystemExit(f"no copy kernel in {sub}")
+        calib[counter] = sum(vals) / len(vals)
+    scale = {"FETCH_SIZE": float(1 << 30) / calib["FETCH_SIZE"], "WRITE_SIZE": float(1 << 30) / calib["WRITE_SIZE"]}
+    per = {}
+    for counter, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        for name, v in _counter_values(os.path.join(d, sub), counter):
+            kind = next((k for pat, k in KERNEL_PATTERNS if pat in name), None)
+            if kind:
+                per.setdefault(kind, {}).setdefault(counter, []).append(v * scale[counter])
+    rec = {"_calibration": {
+        "kernel": "torch.neg fp32 over 2^28 elements (reads 1 GiB, writes 1 GiB)",
+        "FETCH_SIZE_KiB": round(calib["FETCH_SIZE"], 3), "WRITE_SIZE_KiB": round(calib["WRITE_SIZE"], 3),
+        "fetch_per_counted": scale["FETCH_SIZE"] / 1024.0, "write_per_counted": scale["WRITE_SIZE"] / 1024.0}}
+    for kind in sorted(per):
+        f, w = per[kind].get("FETCH_SIZE", [0.0]), per[kind].get("WRITE_SIZE", [0.0])
+        fb, wb = sum(f) / len(f), sum(w) / len(w)
+        rec[kind] = {"bytes_per_launch": int(fb + wb), "fetch_bytes": int(fb), "write_bytes": int(wb),
+                     "launches": len(f), "source_digest": source_digest(kind)}
+    base = os.path.join(ROOT, "profiles", f"traffic_{workload}")
+    with open(base + ".json", "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    lines = [f"# HBM traffic per launch: {workload}", "",
+             "Commands (from the repository root, one MI355X; one counter per run):", "", "```",
+             "rocprofv3 --pmc FETCH_SIZE -f csv -d <dir>/fetch -o run -- python3 bench.py --steps 3 --warmup 1 "
+             "--no-cpu-baseline --headline-only",
+             "rocprofv3 --pmc WRITE_SIZE -f csv -d <dir>/write -o run -- python3 bench.py --steps 3 --warmup 1 "
+             "--no-cpu-baseline --headline-only",
+             "rocprofv3 --pmc FETCH_SIZE -f csv -d <dir>/calib_fetch -o run -- python3 bench.py --copy-calibration",
+             "rocprofv3 --pmc WRITE_SIZE -f csv -d <dir>/calib_write -o run -- python3 bench.py --copy-calibration",
+             f"python3 bench.py --ingest-counters <dir>   # writes this file and traffic_{workload}.json",
+             "```", "",
+             f"Scaling: the 1 GiB elementwise copy reads {calib['FETCH_SIZE']:.4g} KiB of FETCH_SIZE and writes "
+             f"{calib['WRITE_SIZE']:.4g} KiB of WRITE_SIZE, so one counted KiB stands for "
+             f"{scale['FETCH_SIZE'] / 1024:.4g} KiB fetched and {scale['WRITE_SIZE'] / 1024:.4g} KiB written.", "",
+             "| kernel | launches | fetch MB | write MB | total MB per launch |", "|---|---|---|---|---|"]
+    for kind in sorted(per):
+        r = rec[kind]
+        lines.append(f"| {kind} | {r['launches']} | {r['fetch_bytes'] / 1e6:.1f} | {r['write_bytes'] / 1e6:.1f} | "
+                     f"{r['bytes_per_launch'] / 1e6:.1f} |")
+    with open(base + ".md", "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(json.dumps({k: v.get("bytes_per_launch") for k, v in rec.items() if k != "_calibration"}))
+
+
+def ingest_pmc(d, kind, workload):
+    """Per-launch averages of hardware counters for one kernel kind, with the
+    MFMA rate and utilisation they imply (MI355X: 1024 SIMDs)."""
+    import csv
+    import glob
+    vals, durs, passes = {}, [], []
+    for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        seen = set()
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if next((k for pat, k in KERNEL_PATTERNS if pat in r["Kernel_Name"]), None) != kind:
+                    continue
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                seen.add(r["Counter_Name"])
+                if r["Dispatch_Id"] not in {x[0] for x in durs}:
+                    durs.append((r["Dispatch_Id"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9))
+        if seen:
+            passes.append(sorted(seen))
+    if not vals:
+        raise SystemExit(f"no {kind} launches under {d}")
+    avg = {k: sum(v) / len(v) for k, v in vals.items()}
+    dur = sum(x[1] for x in durs) / len(durs)
+    lines = [f"# Hardware counters of {kind}: {workload}", "",
+             "Commands (from the repository root, one MI355X; one pass per run):", "", "```"]
+    for cs in passes:
+        lines.append(f"rocprofv3 --pmc {' '.join(cs)} --kernel-include-regex {kind} -f csv -d <dir>/<pass> -o run "
+                     "-- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --headline-only")
+    lines += [f"python3 bench.py --ingest-pmc <dir> --pmc-kernel {kind}   # writes this file", "```", "",
+              f"Averages over the launches of each pass; mean launch duration under counters {dur * 1e6:.1f} µs.",
+              "", "| counter | per launch |", "|---|---|"]
+    for k in sorted(avg):
+        lines.append(f"| {k} | {avg[k]:.6g} |")
+    derived = []
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg:
+        fl = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        derived.append(f"- bf16 MFMA work: {fl / 1e9:.1f} GFLOP per launch (512 FLOP per counted MOP), "
+                       f"{fl / dur / 1e12:.0f} TFLOP/s over the launch = "
+                       f"{fl / dur / 1e12 / MFMA_BF16_PEAK_TFLOPS:.1%} of the 2.5 PFLOP/s dense bf16 peak")
+    if "MfmaUtil" in avg:
+        derived.append(f"- MFMA busy (MfmaUtil: MFMA-busy cycles over GUI-active cycles x 1024 SIMDs): "
+                       f"{avg['MfmaUtil']:.1f}%")
+    if "SQ_LDS_BANK_CONFLICT" in avg and avg.get("SQ_LDS_IDX_ACTIVE"):
+        derived.append(f"- LDS bank-conflict cycles per active LDS cycle: "
+                       f"{avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_LDS_IDX_ACTIVE']:.3f}")
+    if "SQ_INSTS_VALU" in avg and avg.get("SQ_INSTS_MFMA"):
+        derived.append(f"- VALU instructions per MFMA instruction: {avg['SQ_INSTS_VALU'] / avg['SQ_INSTS_MFMA']:.2f}")
+    if derived:
+        lines += ["", "Derived:", ""] + derived
+    path = os.path.join(ROOT, "profiles", f"pmc_{kind}_{workload}.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(path)
+
+
+def ingest_stats(d, cfg):
+    """Per-kernel duration statistics of a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    import glob
+    paths = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
+    if not paths:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = []
+    with open(paths[0], newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append(r)
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = [f"# rocprofv3 kernel statistics: {cfg.name} (B={cfg.B}, Hq={cfg.Hq}, Hkv={cfg.Hkv}, N={cfg.N}, "
+             f"d={cfg.d}, K={cfg.K}, L={cfg.L}, T={cfg.T}, {cfg.dtype})", "",
+             "Commands (from the repository root, one MI355X):", "", "```",
+             "rocprofv3 --kernel-trace --stats -f csv -d <dir> -o run -- python3 bench.py --steps 20 --warmup 5 "
+             "--no-cpu-baseline --headline-only",
+             "python3 bench.py --ingest-stats <dir>   # writes this file", "```", "",
+             "The bench runs warmup + 20 graph-replayed steps, then 20 eager steps with per-dispatch events, "
+             "then the selection-statistics decodes (one per input copy with the collision counts returned, one "
+             "without), so the call counts differ per kernel. `--headline-only` leaves out every other section "
+             "(the build timing aside), so every decode launch has the workload's shape.", "",
+             "| kernel | calls | avg µs | min µs | max µs | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"]
+        kind = next((k for pat, k in KERNEL_PATTERNS if pat in name), None)
+        if kind is None:
+            continue
+        short = name.replace("void ", "").replace("lsh::", "").split("(")[0]
+        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{100.0 * float(r['TotalDurationNs']) / total:.2f}% |")
+    path = os.path.join(ROOT, "profiles", f"kernel_stats_{cfg.name}.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(path)
+
+
 def kernel_table(times, alg):
     """Per-kernel averages from a timing window, with achieved rates on the
     algorithmic bytes or flops of one launch."""
@@ -138,6 +314,18 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.ingest_counters:
+        import workloads
+        ingest_counters(args.ingest_counters, workloads.CONFIGS[args.config].name)
+        return
+    if args.ingest_pmc:
+        import workloads
+        ingest_pmc(args.ingest_pmc, args.pmc_kernel, workloads.CONFIGS[args.config].name)
+        return
+    if args.ingest_stats:
+        import workloads
+        ingest_stats(args.ingest_stats, workloads.CONFIGS[args.config])
         return
 
     import numpy as np
@@ -264,17 +452,19 @@ def main():
         for c in copies:
             q = c[qkey]
             decode(c, q=q, counts=counts)
-            decode_hybrid(c, N, 0, q=q, out=c["out_exact"])
+            if full:   # a profiling run (--headline-only) keeps every decode launch at the workload's shape
+                decode_hybrid(c, N, 0, q=q, out=c["out_exact"])
             decode(c, q=q)
             torch.cuda.synchronize()
             m = (counts >= T).view(B, Hkv, G, N)
             sel_rows.append(int(m.any(dim=2).sum().item()))
             idx_entries.append(int(counts.sum(dtype=torch.int64).item()))
             nsel_tot.append(int(c["nsel"].sum().item()))
-            num = (c["out"] - c["out_exact"]).norm(dim=-1)
-            den = c["out_exact"].norm(dim=-1).clamp_min(1e-30)
-            errs.append((num / den).flatten().cpu().numpy())
-        e = np.concatenate(errs)
+            if full:
+                num = (c["out"] - c["out_exact"]).norm(dim=-1)
+                den = c["out_exact"].norm(dim=-1).clamp_min(1e-30)
+                errs.append((num / den).flatten().cpu().numpy())
+        e = np.concatenate(errs) if errs else None
         U_rows, E_idx = float(np.mean(sel_rows)), float(np.mean(idx_entries))
         return {
             "U_rows": U_rows, "E_idx": E_idx,
@@ -283,8 +473,9 @@ def main():
             "nsel_mean_per_head": round(float(np.mean(nsel_tot)) / qh, 1),
             "nsel_frac_per_head": round(float(np.mean(nsel_tot)) / qh / N, 4),
             "probed_index_entries": E_idx,
-            "estimate_rel_l2_vs_exact": {"mean": round(float(e.mean()), 4), "median": round(float(np.median(e)), 4),
-                                         "max": round(float(e.max()), 4), "heads": int(e.size)},
+            "estimate_rel_l2_vs_exact": None if e is None else {
+                "mean": round(float(e.mean()), 4), "median": round(float(np.median(e)), 4),
+                "max": round(float(e.max()), 4), "heads": int(e.size)},
         }
 
     sel = selection_stats("q")
