@@ -468,26 +468,20 @@ __device__ __forceinline__ void attend_bf16_role(const FusedParams& p, int s, in
   }
 }
 
-// The one-launch decode for bf16 K/V: count, exact and attend workgroups in
-// that order of id (see decode_roles.h).
+// The one-launch decode for bf16 K/V: count, exact and attend workgroups,
+// unit by unit (decode_role).
 template <int GW>
 __global__ __launch_bounds__(kFusedThreads, 2) void decode_bf16_kernel(FusedParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kFusedLdsBytes];
-  int wid = blockIdx.x;
-  if (wid < p.n_count_wg) {
-    count_role(p, wid, smem);
+  const DecodeRole r = decode_role(p, blockIdx.x);
+  if (r.count) {
+    count_role(p, r.J, r.bh, smem);
     return;
   }
-  wid -= p.n_count_wg;
-  // unit by unit: the exact set's pieces, then the context splits (the
-  // finishers of a unit wait only for that unit's workgroups; see finish_slot)
-  const int per_unit = p.nexact + p.nsplit;
-  const int u = wid / per_unit, r = wid % per_unit;
-  const int slot = r < p.nexact ? p.nsplit + r : r - p.nexact;
-  attend_bf16_role<GW>(p, slot, u, smem);
+  attend_bf16_role<GW>(p, r.slot, r.u, smem);
   __syncthreads();
   LSH_STAMP(p, 4);
-  finish_slot(p, u, slot, smem);
+  finish_slot(p, r.u, r.slot, smem);
 }
 
 hipError_t launch_decode_bf16(const FusedParams& p, int kid, hipStream_t stream) {

@@ -441,20 +441,14 @@ __device__ __forceinline__ void attend_f32_role(const FusedParams& p, int s, int
 template <int GM>
 __global__ __launch_bounds__(kFusedThreads) void decode_f32_kernel(FusedParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[cmax(sizeof(AttendF32Lds<GM>), kRolesLdsBytes)];
-  int wid = blockIdx.x;
-  if (wid < p.n_count_wg) {
-    count_role(p, wid, smem);
+  const DecodeRole r = decode_role(p, blockIdx.x);
+  if (r.count) {
+    count_role(p, r.J, r.bh, smem);
     return;
   }
-  wid -= p.n_count_wg;
-  // unit by unit: the exact set's pieces, then the context splits (the
-  // finishers of a unit wait only for that unit's workgroups; see finish_slot)
-  const int per_unit = p.nexact + p.nsplit;
-  const int u = wid / per_unit, r = wid % per_unit;
-  const int slot = r < p.nexact ? p.nsplit + r : r - p.nexact;
-  attend_f32_role<GM>(p, slot, u, smem);
+  attend_f32_role<GM>(p, r.slot, r.u, smem);
   __syncthreads();
-  finish_slot(p, u, slot, smem);
+  finish_slot(p, r.u, r.slot, smem);
 }
 
 // ---------------------------------------------------------------------------

@@ -172,6 +172,35 @@ struct FusedParams {
 // Sync words the query-hash launch zeroes before the decode launch.
 __host__ __device__ inline int fused_sync_words(int U, int nJ) { return U * nJ + U; }
 
+// What workgroup `wid` of the decode launch does.  The grid holds every
+// count workgroup first (chunk by chunk, one per query head), then unit by
+// unit the exact-set pieces and the context splits.  Attention workgroups
+// wait for count workgroups, which come earlier in the grid and never wait.
+// (Placing each unit's count workgroups just before its attention
+// workgroups, so that later units count while earlier ones stream, measured
+// slower: the count workgroups of later units got their slots late and their
+// attention waited for them.)
+struct DecodeRole {
+  bool count;
+  int u;
+  int J, bh;       // count: key chunk and query head
+  int slot;        // attention: context split (< nsplit) or exact-set piece
+};
+
+__device__ inline DecodeRole decode_role(const FusedParams& p, int wid) {
+  DecodeRole r;
+  const int BH = p.B * p.Hq;
+  r.count = wid < p.n_count_wg;
+  r.J = wid / BH;
+  r.bh = wid % BH;
+  const int k = wid - p.n_count_wg;
+  const int per_unit = p.nexact + p.nsplit;
+  r.u = r.count ? r.bh / p.G : k / per_unit;   // count: the head's unit (bh / G = b * Hkv + h / G)
+  const int i = k % per_unit;
+  r.slot = i < p.nexact ? p.nsplit + i : i - p.nexact;
+  return r;
+}
+
 // --------------------------------------------------------------------------
 // The ln-u correction g(theta), sampled by the query-hash launch
 // --------------------------------------------------------------------------
@@ -283,10 +312,8 @@ struct CountLds {                  // laid out after the byte counters
   int flag;
 };
 
-__device__ inline void count_role(const FusedParams& p, int wid, unsigned char* smem) {
+__device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned char* smem) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int BH = p.B * p.Hq;
-  const int J = wid / BH, bh = wid % BH;
   const int b = bh / p.Hq, h = bh % p.Hq;
   const int u = b * p.Hkv + h / p.G;
   const int nb = 1 << p.K;
@@ -511,30 +538,33 @@ __device__ inline void count_role(const FusedParams& p, int wid, unsigned char* 
 // a lower unit has been dispatched, and none of a higher unit holds a slot
 // while one of its unit's is still waiting for dispatch.
 // --------------------------------------------------------------------------
-constexpr int kMergeBatch = 32;      // slot values a thread keeps in flight in a fold
+constexpr int kFoldRows = 16;        // float4 slot rows a thread keeps in flight in a fold
 constexpr int kMergeMaxPairs = 2048; // (head, slot) pairs of a fold, in LDS
 
 struct MergeLds {
   float m[kMergeMaxPairs];           // max, then the slot's weight exp(m - M)
   float l[kMergeMaxPairs];
   float M[16], Lm[16];
-  float red[kFusedThreads];          // column sums of the thread groups sharing a column
+  float4 red[kFusedThreads];         // column sums of the thread groups sharing a column
   int nsel[16];
   int flag;
 };
 
 // Fold all npart slots of heads f, f + F, ... of unit u (bh0 = its first
-// head) into the outputs.  The nh * 128 columns (head, dim) are spread over
-// the threads, R threads per column (R = 256 / columns when that is at least
-// 2), each R-th slot per thread.  The first batch of slot values goes out
-// together with the heads' max / sum and chunk-count loads, so a fold of up
-// to kMergeBatch slots per thread costs one round trip to memory.
+// head) into the outputs.  The nh * 32 float4 columns (head, 4 dims) are
+// spread over the threads, R threads per column (R = 256 / columns when that
+// is at least 2), each R-th slot per thread.  The first batch of slot values
+// (kFoldRows rows per thread: all 128 slots of a head at R = 8) goes out
+// together with the heads' max / sum and chunk-count loads, so a fold of up to
+// R * kFoldRows slots costs one round trip to memory.
 __device__ inline void fold_heads(const FusedParams& p, int bh0, int f, int F, unsigned char* smem) {
   MergeLds& s = *reinterpret_cast<MergeLds*>(smem);
   const int tid = threadIdx.x;
   const int np = p.npart;
+  constexpr int kQ = kHeadDim / 4;                              // float4 columns of a head
+  constexpr int kRowQ = kPartialStride / 4;                     // float4 pitch of the slots
   const int nh = (p.G - f + F - 1) / F;                         // heads of this finisher
-  const int C = nh * kHeadDim;
+  const int C = nh * kQ;
   const int R = C >= kFusedThreads ? 1 : kFusedThreads / C;
   const int cpt = (C + kFusedThreads - 1) / kFusedThreads;     // column blocks (R == 1 only)
   if (tid < nh) s.nsel[tid] = 0;
@@ -549,28 +579,29 @@ __device__ inline void fold_heads(const FusedParams& p, int bh0, int f, int F, u
   const int c0 = R > 1 ? tid % C : tid;
   const int r0 = R > 1 ? tid / C : 0;
   const bool live0 = c0 < C && r0 < R;
-  const int hi0 = live0 ? c0 / kHeadDim : 0, d0 = c0 % kHeadDim;
-  const float* base0 = p.partials + static_cast<size_t>(bh0 + f + F * hi0) * np * kPartialStride + d0;
-  float x0[kMergeBatch];
+  const int hi0 = live0 ? c0 / kQ : 0;
+  const float4* base0 =
+      reinterpret_cast<const float4*>(p.partials + static_cast<size_t>(bh0 + f + F * hi0) * np * kPartialStride) +
+      c0 % kQ;
+  float4 x[kFoldRows];
 #pragma unroll
-  for (int i = 0; i < kMergeBatch; ++i) x0[i] = base0[static_cast<size_t>(min(r0 + i * R, np - 1)) * kPartialStride];
+  for (int i = 0; i < kFoldRows; ++i) x[i] = base0[static_cast<size_t>(min(r0 + i * R, np - 1)) * kRowQ];
   // max / sum of every (head, slot) pair and the heads' chunk selection
   // counts: loads with clamped indices issue together, eight per thread at a time
   for (int i0 = 0; i0 < nh * np; i0 += 8 * kFusedThreads) {
-    float mv[8], lv[8];
+    float2 ml[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int i = min(i0 + tid + q * kFusedThreads, nh * np - 1);
       const float* ps = p.partials + (static_cast<size_t>(bh0 + f + F * (i / np)) * np + i % np) * kPartialStride;
-      mv[q] = ps[kHeadDim];
-      lv[q] = ps[kHeadDim + 1];
+      ml[q] = *reinterpret_cast<const float2*>(ps + kHeadDim);
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int i = i0 + tid + q * kFusedThreads;
       if (i < nh * np) {
-        s.m[i] = mv[q];
-        s.l[i] = lv[q];
+        s.m[i] = ml[q].x;
+        s.l[i] = ml[q].y;
       }
     }
   }
@@ -618,42 +649,51 @@ __device__ inline void fold_heads(const FusedParams& p, int bh0, int f, int F, u
     const int c = cb * kFusedThreads + (R > 1 ? tid % C : tid);
     const int r = R > 1 ? tid / C : 0;
     const bool live = c < C && r < R;
-    const int hi = live ? c / kHeadDim : 0, d = c % kHeadDim;
-    const float* base = p.partials + static_cast<size_t>(bh0 + f + F * hi) * np * kPartialStride + d;
-    float acc = 0.f;
-    for (int k0 = r; k0 < np; k0 += R * kMergeBatch) {
-      if (cb != 0 || k0 != r) {   // the first batch of block 0 is already in x0
+    const int hi = live ? c / kQ : 0, cq = c % kQ;
+    const float4* base =
+        reinterpret_cast<const float4*>(p.partials + static_cast<size_t>(bh0 + f + F * hi) * np * kPartialStride) +
+        cq;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k0 = r; k0 < np; k0 += R * kFoldRows) {
+      if (cb != 0 || k0 != r) {   // the first batch of block 0 is already in x
 #pragma unroll
-        for (int i = 0; i < kMergeBatch; ++i) {
+        for (int i = 0; i < kFoldRows; ++i) {
           const int k = min(k0 + i * R, np - 1);   // clamped: every load issues, the extra ones add nothing
-          x0[i] = base[static_cast<size_t>(k) * kPartialStride];
+          x[i] = base[static_cast<size_t>(k) * kRowQ];
         }
       }
-      float* x = x0;
-      // the weights: clamped reads, so they issue together; past the last
-      // slot (and in dead columns) the weight is 0
+      // the weights: clamped reads; past the last slot (and in dead columns)
+      // the weight is 0
 #pragma unroll
-      for (int i = 0; i < kMergeBatch; i += 16) {
-        float w[16];
-#pragma unroll
-        for (int q = 0; q < 16; ++q) w[q] = s.m[hi * np + min(k0 + (i + q) * R, np - 1)];
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int k = k0 + (i + q) * R;
-          acc = fmaf(x[i + q], (live && k < np) ? w[q] : 0.f, acc);
-        }
+      for (int i = 0; i < kFoldRows; ++i) {
+        const int k = k0 + i * R;
+        const float w = s.m[hi * np + min(k, np - 1)];
+        const float wk = (live && k < np) ? w : 0.f;
+        acc.x = fmaf(x[i].x, wk, acc.x);
+        acc.y = fmaf(x[i].y, wk, acc.y);
+        acc.z = fmaf(x[i].z, wk, acc.z);
+        acc.w = fmaf(x[i].w, wk, acc.w);
       }
     }
     // the R partial sums of each column
     s.red[tid] = acc;
     __syncthreads();
     if (live && r == 0) {
-      for (int q = 1; q < R; ++q) acc += s.red[tid + q * C];
+      for (int q = 1; q < R; ++q) {
+        const float4 o = s.red[tid + q * C];
+        acc.x += o.x;
+        acc.y += o.y;
+        acc.z += o.z;
+        acc.w += o.w;
+      }
       const int bh = bh0 + f + F * hi;
       const float M = s.M[hi], Lm = s.Lm[hi];
-      p.out[static_cast<size_t>(bh) * kHeadDim + d] = (M == -INFINITY) ? 0.f : acc / Lm;
-      if (d == 0) {
-        if (p.lse) p.lse[bh] = (M == -INFINITY) ? -INFINITY : M + logf(Lm);
+      const bool empty = (M == -INFINITY);
+      const float4 o = empty ? make_float4(0.f, 0.f, 0.f, 0.f)
+                             : make_float4(acc.x / Lm, acc.y / Lm, acc.z / Lm, acc.w / Lm);
+      reinterpret_cast<float4*>(p.out + static_cast<size_t>(bh) * kHeadDim)[cq] = o;
+      if (cq == 0) {
+        if (p.lse) p.lse[bh] = empty ? -INFINITY : M + logf(Lm);
         if (p.nsel) p.nsel[bh] = s.nsel[hi];
       }
     }
