@@ -128,6 +128,14 @@ __device__ __forceinline__ int arrive(int32_t* ctr, int* val_lds) {
   return v;
 }
 
+// This workgroup's stores are complete; thread 0 then adds 1 to *ctr
+// without waiting for the add to return (a workgroup that only signals).
+__device__ __forceinline__ void signal(int32_t* ctr) {
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) (void)__hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // --------------------------------------------------------------------------
 // Parameters of the one-launch decode
 // --------------------------------------------------------------------------
@@ -522,8 +530,8 @@ __device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned 
     for (int w = 0; w < kW; ++w) t += s.wtot[w];
     st_agent(p.chunk_nsel + static_cast<size_t>(bh) * p.nJ + J, t);
   }
-  arrive(p.ready + u * p.nJ + J, &s.flag);
   LSH_STAMP(p, 3);
+  signal(p.ready + u * p.nJ + J);
 }
 
 // --------------------------------------------------------------------------

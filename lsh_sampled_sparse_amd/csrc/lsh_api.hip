@@ -380,12 +380,16 @@ static lsh_status decode_cached(const void* q, const void* keys, const void* val
   // a timing window is open
   a.timed = !noalloc;
   // the exact set goes to the attention kernel as extra workgroups over
-  // pieces of at least 128 keys (one 32-key tile per wave), at most
-  // kMaxExactSplits of them, sized for the longest sequence (a sequence's
-  // exact set, min(n, n_sink + n_window) keys, grows with its length n)
+  // pieces of up to an eighth of a context split (short next to the splits,
+  // so they add no round of workgroups at the end, yet not so many that
+  // they crowd long splits out of their slots), at least 128 keys (one
+  // 32-key tile per wave), at most kMaxExactSplits of them, sized for the
+  // longest sequence (a sequence's exact set, min(n, n_sink + n_window)
+  // keys, grows with its length n)
   const int ne = static_cast<int>(std::min<long long>(N, static_cast<long long>(n_sink) + n_window));
   const int per_piece = (ne + lsh::kMaxExactSplits - 1) / lsh::kMaxExactSplits;
-  a.exact_len = std::max(128, (per_piece + 127) / 128 * 128);
+  const int ne128 = (ne + 127) / 128 * 128;
+  a.exact_len = std::max({128, (per_piece + 127) / 128 * 128, std::min(ne128, w.split_len / 8 / 128 * 128)});
   a.nexact = (ne + a.exact_len - 1) / a.exact_len;
   return hip_status(lsh::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
