@@ -183,6 +183,18 @@ lsh_status lsh_update_tables(const void* keys, const void* W,
  *
  * Size limits: those of the build, plus Hq >= 1, Hq % Hkv == 0,
  * G = Hq / Hkv <= 16, 1 <= T <= L and a finite sm_scale.
+ *
+ * Every decode entry point enqueues two launches on `stream`: the query hash
+ * (which also resets the decode's counters in the workspace), then one launch
+ * that counts collisions, selects, attends and merges.  Workgroups of that
+ * launch hand results to each other through the workspace and wait for each
+ * other with bounded polls; a wait that does not end (which correct use never
+ * causes) writes NaN into the affected outputs instead of hanging.  The
+ * workspace must not be used by another call that may run at the same time.
+ * The probe reads `indices` in aligned 16-byte blocks, so it may read up to
+ * 14 bytes before the first or after the last entry of a probed bucket (never
+ * outside the 16-byte-aligned block holding an entry of the array); those
+ * bytes are never used.
  * ---------------------------------------------------------------------- */
 
 /* Bytes of device workspace lsh_decode_attention needs (0 on invalid sizes).
