@@ -84,12 +84,14 @@ __global__ __launch_bounds__(256) void qhash_kernel(const typename T::storage* _
   }
   if (static_cast<int>(blockIdx.y) > head_blocks) {
     // the ln-u correction g(theta) at one sample angle per wave
-    if (K == 0) return;
-    if (tid <= L)
-      lc[tid] = lgamma(static_cast<double>(L) + 1.0) - lgamma(static_cast<double>(tid) + 1.0) -
-                lgamma(static_cast<double>(L - tid) + 1.0);
-    __syncthreads();
     const int j = ((blockIdx.y - head_blocks - 1) * gridDim.x + blockIdx.x) * 4 + wave;
+    if (K == 0 || j - wave >= kLnuSamples) return;   // (workgroup-uniform)
+    // ln C(L, i) = ln L! - ln i! - ln (L - i)!: one lgamma per thread
+    __shared__ double lf[256];
+    if (tid <= L) lf[tid] = lgamma(static_cast<double>(tid) + 1.0);
+    __syncthreads();
+    if (tid <= L) lc[tid] = lf[L] - lf[tid] - lf[L - tid];
+    __syncthreads();
     if (j >= kLnuSamples) return;
     const double g = lnu_correction_wave(j * (3.14159265358979323846 / (2 * kLnuTable)), K, L, Tth, lc, lane);
     if (lane == 0) lnu_samples[j] = g;

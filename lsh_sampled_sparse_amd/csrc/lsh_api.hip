@@ -73,10 +73,11 @@ struct DecodeLayout {
 
 DecodeLayout decode_layout(int B, int Hq, int Hkv, int N, int L, const Geometry& g) {
   DecodeLayout w;
-  // context split: about two resident workgroups per CU (512 over the 256
-  // CUs) over the (sequence, kv head) units, each split a multiple of 256 keys
+  // context split: about two resident workgroups per CU (kResidentWG over
+  // the 256 CUs) over the (sequence, kv head) units, each split a multiple
+  // of 256 keys
   const long long units = static_cast<long long>(B) * Hkv;
-  long long per = (units * N + 511) / 512;
+  long long per = (units * N + lsh::kResidentWG - 1) / lsh::kResidentWG;
   per = (per + 255) / 256 * 256;
   if (per < 256) per = 256;
   if (per > N) per = (static_cast<long long>(N) + 255) / 256 * 256;
@@ -88,11 +89,12 @@ DecodeLayout decode_layout(int B, int Hq, int Hkv, int N, int L, const Geometry&
   w.bitmask = off;    off = align_up(off + BH * ((N + 31) / 32) * sizeof(uint32_t));
   w.chunk_nsel = off; off = align_up(off + BH * g.nJ * sizeof(int32_t));
   w.lnu = off;        off = align_up(off + lsh::kLnuSamples * sizeof(double));
-  // partial slots: nsplit <= min(ceil(N / 256), ceil(512 / units)), a bound
+  // partial slots: nsplit <= min(ceil(N / 256), ceil(kResidentWG / units)), a bound
   // that grows with N, so the workspace size at a cache's capacity covers
   // every shorter length; plus the exact set's pieces
   const long long slots = std::max<long long>(
-      w.nsplit, std::min((static_cast<long long>(N) + 255) / 256, (511 + units) / units)) + lsh::kMaxExactSplits;
+      w.nsplit, std::min((static_cast<long long>(N) + 255) / 256, (lsh::kResidentWG - 1 + units) / units)) +
+      lsh::kMaxExactSplits;
   w.partials = off;
   off = align_up(off + BH * static_cast<size_t>(slots) * lsh::kPartialStride * sizeof(float));
   // counters of the decode launch: per (unit, chunk) and per unit

@@ -84,6 +84,7 @@ constexpr int kLnuTable = 1024;
 constexpr int kLnuSamples = 2 * kLnuTable + 1;
 // A partial state (acc[128], max, sum) padded to five 128-byte lines, so no
 // cache line holds two workgroups' partials.
+constexpr int kResidentWG = 512;   // decode workgroups resident at once: about two per CU on 256 CUs
 constexpr int kPartialStride = 160;
 constexpr int kMaxExactSplits = 16;   // partial slots per head reserved for the exact set
 

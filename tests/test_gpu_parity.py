@@ -242,6 +242,25 @@ def test_hybrid_parity(cfg, n_sink, n_window, stride):
     check_case(cfg, data, stride=stride, n_sink=n_sink, n_window=n_window)
 
 
+# more count workgroups (query heads x key chunks) than one round of resident
+# workgroups (512): counting takes several rounds before attention starts
+MANY_ROUNDS = [
+    (workloads.Config("rounds-bf16", B=3, Hq=12, Hkv=3, N=6000, d=128, K=8, L=16, T=2, dtype="bf16",
+                      planted=4, a=0.8, offset="per_unit", seed=41), 4, 300),
+    (workloads.Config("rounds-f32", B=2, Hq=16, Hkv=2, N=4200, d=128, K=7, L=12, T=2, dtype="f32",
+                      planted=3, a=0.8, offset="per_head", seed=42), 0, 0),
+]
+
+
+@pytest.mark.parametrize("cfg,n_sink,n_window", MANY_ROUNDS, ids=[c.name for c, _, _ in MANY_ROUNDS])
+def test_many_count_rounds(cfg, n_sink, n_window):
+    import lsh_sampled_sparse_amd as lsh
+    assert cfg.B * cfg.Hq * lsh.lsh_num_chunks(cfg.N, 256) > 512
+    say(f"case many count rounds {cfg.name} sink={n_sink} window={n_window}")
+    data = workloads.generate(cfg)
+    check_case(cfg, data, stride=256, n_sink=n_sink, n_window=n_window)
+
+
 def test_hybrid_all_exact_is_attention():
     # an exact set covering every key leaves nothing to sample: exact attention
     cfg = SMALL[1]
