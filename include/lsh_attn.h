@@ -90,7 +90,8 @@ int lsh_default_stride(int N, int K);
  *
  * Size limits: B, Hkv, N >= 1; d == 128 (else LSH_ERR_UNSUPPORTED);
  * 0 <= K <= 15; 1 <= L <= 255; stride a power of two in [256, 8192]
- * (else LSH_ERR_UNSUPPORTED); B*Hkv*L*N < 2^40 and B*Hkv*L < 2^31.
+ * (else LSH_ERR_UNSUPPORTED); N <= 2^30, B*Hkv*L*N < 2^40 and B*Hkv*L < 2^31
+ * (else LSH_ERR_UNSUPPORTED).
  *
  * Layout of the tables (two-level CSR, chunk-major).  The keys of a table are
  * cut into nchunks = lsh_num_chunks(N, stride) chunks of `stride` keys (the
@@ -328,6 +329,13 @@ lsh_status lsh_decode_attention_noalloc(const void* q, const void* keys,
                                         float* out, float* lse, int32_t* nsel,
                                         uint16_t* q_codes, uint8_t* counts,
                                         void* stream);
+
+/* ------------------------------------------------------------------------
+ * Launch printing (a debugging aid): with the environment variable
+ * LSH_DEBUG_LAUNCH set to anything but "" or "0" when the library first
+ * launches, every launch prints one line to stderr with the kernel's name,
+ * grid, block, dynamic LDS bytes and stream.
+ * ---------------------------------------------------------------------- */
 
 /* ------------------------------------------------------------------------
  * Kernel timing (a profiling aid; process-wide, one window at a time)

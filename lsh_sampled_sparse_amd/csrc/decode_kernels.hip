@@ -530,7 +530,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int F = p.G < p.npart ? p.G : p.npart;
   if ((p.G + F - 1) / F * p.npart > kMergeMaxPairs || p.G > 16 || a.L > 255) return hipErrorInvalidValue;
   const int nsync = fused_sync_words(U, a.nJ);
-  const int kq = a.timed ? kKQhash : -1, kd = a.timed ? kKDecode : -1;
+  const int untimed = a.timed ? 0 : kUntimed;
+  const int kq = kKQhash | untimed, kd = kKDecode | untimed;
   hipError_t e = (a.dtype == 1) ? launch_qhash<BF16>(a, nsync, kq, stream) : launch_qhash<F32>(a, nsync, kq, stream);
   if (e != hipSuccess) return e;
   if (a.dtype == 1) return launch_decode_bf16(p, kd, stream);

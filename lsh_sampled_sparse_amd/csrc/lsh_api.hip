@@ -5,6 +5,9 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <map>
 #include <mutex>
 #include <vector>
@@ -40,8 +43,13 @@ lsh_status check_common(int B, int Hkv, int N, int d, int K, int L, int stride, 
   if (sl < 0) return LSH_ERR_INVALID_ARG;
   if (d != 128) return LSH_ERR_UNSUPPORTED;
   if (sl < kMinStrideLog2 || sl > kMaxStrideLog2) return LSH_ERR_UNSUPPORTED;
+  // keys per sequence: up to 2^30, so that index arithmetic on N in int
+  // (rounding up to words, chunks or splits) cannot overflow
+  if (N > (1 << 30)) return LSH_ERR_UNSUPPORTED;
+  // each product is formed only once the one before it is known to be small
   const long long units = static_cast<long long>(B) * Hkv;
-  if (units * L * static_cast<long long>(N) >= (1ll << 40) || units * L >= (1ll << 31)) return LSH_ERR_UNSUPPORTED;
+  if (units >= (1ll << 31) || units * L >= (1ll << 31) || units * L * static_cast<long long>(N) >= (1ll << 40))
+    return LSH_ERR_UNSUPPORTED;
   g->stride_log2 = sl;
   g->nJ = lsh_num_chunks(N, stride);
   g->LKpad = lsh::proj_wt_rows(K, L);
@@ -86,7 +94,7 @@ DecodeLayout decode_layout(int B, int Hq, int Hkv, int N, int L, const Geometry&
   const size_t BH = static_cast<size_t>(B) * Hq;
   size_t off = 0;
   w.qcodes = off;     off = align_up(off + BH * L * sizeof(uint16_t));
-  w.bitmask = off;    off = align_up(off + BH * ((N + 31) / 32) * sizeof(uint32_t));
+  w.bitmask = off;    off = align_up(off + BH * ((static_cast<size_t>(N) + 31) / 32) * sizeof(uint32_t));
   w.chunk_nsel = off; off = align_up(off + BH * g.nJ * sizeof(int32_t));
   w.lnu = off;        off = align_up(off + lsh::kLnuSamples * sizeof(double));
   // partial slots: nsplit <= min(ceil(N / 256), ceil(kResidentWG / units)), a bound
@@ -172,9 +180,24 @@ hipError_t ensure_lds_limit(const void* kernel, size_t bytes) {
   return e;
 }
 
+bool debug_launch() {
+  static const bool on = [] {
+    const char* e = std::getenv("LSH_DEBUG_LAUNCH");
+    return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+void print_launch(int id, dim3 grid, dim3 block, unsigned lds, hipStream_t stream) {
+  const char* name = kernel_name(id & (kUntimed - 1));
+  std::fprintf(stderr, "[lsh] launch %s%s grid (%u, %u, %u) block (%u, %u, %u) dynamic lds %u stream %p\n",
+               name ? name : "?", (id & kUntimed) ? " (untimed)" : "", grid.x, grid.y, grid.z, block.x, block.y,
+               block.z, lds, static_cast<void*>(stream));
+}
+
 void timing_events(int id, hipEvent_t* start, hipEvent_t* stop) {
   *start = *stop = nullptr;
-  if (id < 0) return;
+  if (id & kUntimed) return;
   std::lock_guard<std::mutex> lk(g_timing_mu);
   if (!g_timing_on) return;
   if (g_timing_used == g_timing_pool.size()) {

@@ -99,15 +99,25 @@ enum KernelId {
 };
 const char* kernel_name(int id);
 
+// A launch id ORed with kUntimed never takes timing events.
+constexpr int kUntimed = 1 << 8;
+
 // Start/stop events for one launch of kernel `id` while timing is on; both
-// null otherwise, and always for id < 0 (an untimed launch).
+// null otherwise, and always for an untimed launch.
 void timing_events(int id, hipEvent_t* start, hipEvent_t* stop);
+
+// LSH_DEBUG_LAUNCH set (and not "0") in the environment when the library
+// first launches: every launch prints its kernel, grid, block and LDS bytes
+// to stderr (a debugging aid; the check itself is one load of a flag).
+bool debug_launch();
+void print_launch(int id, dim3 grid, dim3 block, unsigned lds, hipStream_t stream);
 
 // Every kernel goes through here: with timing on, the dispatch packet itself
 // carries the start and stop timestamps (no extra packets on the stream).
 template <typename F, typename... Args>
 inline hipError_t launch(int id, F kernel, dim3 grid, dim3 block, unsigned lds, hipStream_t stream,
                          Args... args) {
+  if (debug_launch()) print_launch(id, grid, block, lds, stream);
   hipEvent_t a = nullptr, b = nullptr;
   timing_events(id, &a, &b);
   hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, a, b, 0u, args...);

@@ -105,6 +105,7 @@ def _decode(**kw):
     (dict(stride=128), lsh.LSH_ERR_UNSUPPORTED),
     (dict(stride=16384), lsh.LSH_ERR_UNSUPPORTED),
     (dict(ws_bytes=16), lsh.LSH_ERR_WORKSPACE),
+    (dict(N=(1 << 30) + 1), lsh.LSH_ERR_UNSUPPORTED),
 ])
 def test_build_rejects(kw, status):
     assert _build(**kw) == status
