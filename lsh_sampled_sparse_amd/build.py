@@ -32,9 +32,16 @@ FLAGS = [
 EXTRA = {"build_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+# the checked build (kernels test their index arithmetic, see LSH_CHECKED in
+# csrc/lsh_kernels.h): a debugging library beside the shipped one
+CHECKED_LIB = os.path.join(HERE, "liblsh_attn_checked.so")
+CHECKED_OBJ = os.path.join(HERE, "_build_checked")
+
+
+def _compile(src: str, checked: bool = False) -> str:
+    obj = os.path.join(CHECKED_OBJ if checked else OBJ, src.replace(".hip", ".o"))
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *(["-DLSH_CHECKED"] if checked else []), "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -44,19 +51,30 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every HIP source and link the shared library; returns its path."""
-    os.makedirs(OBJ, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    shutil.move(tmp, LIB)
+    shutil.move(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {lib}")
+
+
+def build(verbose: bool = True, checked: bool = True) -> str:
+    """Compile every HIP source and link the shared library (and, with
+    `checked`, the checked debugging library); returns the library's path."""
+    os.makedirs(OBJ, exist_ok=True)
+    jobs = [(src, False) for src in SOURCES]
+    if checked:
+        os.makedirs(CHECKED_OBJ, exist_ok=True)
+        jobs += [(src, True) for src in SOURCES]
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    if checked:
+        _link(objs[len(SOURCES):], CHECKED_LIB, verbose)
     build_c_consumer(verbose)
     return LIB
 

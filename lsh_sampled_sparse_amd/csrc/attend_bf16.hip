@@ -151,6 +151,7 @@ constexpr size_t kFusedLdsBytes = cmax(sizeof(AttendLds), kRolesLdsBytes);
 // are spread over GW loads.
 template <int GW>
 __device__ __forceinline__ void attend_bf16_role(const FusedParams& p, int s, int u, unsigned char* smem) {
+  LSH_PCHECK(p, u < p.B * p.Hkv && s < p.npart, kChkSlot);
   AttendLds& A = *reinterpret_cast<AttendLds*>(smem);
   LSH_STAMP(p, 0);
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(p.q);

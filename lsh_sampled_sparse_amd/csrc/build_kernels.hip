@@ -395,7 +395,11 @@ __global__ __launch_bounds__(NTHR, NTHR >= 256 ? 4 : 1) void chunk_sort_kernel(
     int N, int P, int K, int stride_log2, int nJP, int j0,   // chunks j0 + blockIdx.x
     uint16_t* __restrict__ offsets,       // [U][L][nJP][2^K]
     uint16_t* __restrict__ indices,       // [U][L][P]
-    int L, int Hkv, const int32_t* __restrict__ old_lens, const int32_t* __restrict__ new_lens) {
+    int L, int Hkv, const int32_t* __restrict__ old_lens, const int32_t* __restrict__ new_lens
+#ifdef LSH_CHECKED
+    , uint32_t* check
+#endif
+    ) {
   constexpr int E = kSortE;
   extern __shared__ __attribute__((aligned(16))) uint32_t smem32[];
   __shared__ uint32_t wave_tot[NTHR / 64];
@@ -522,6 +526,7 @@ __global__ __launch_bounds__(NTHR, NTHR >= 256 ? 4 : 1) void chunk_sort_kernel(
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < E; ++i) {
+    LSH_CHECK(check, p0 + i >= clen || static_cast<int>(e[i] >> 16) < nb, kChkSortCode);
     const int c = min(static_cast<int>(e[i] >> 16), nb - 1);   // codes are < 2^K
     if (p0 + i < clen && c != prev) st[c] = static_cast<uint16_t>(p0 + i);
     prev = c;
@@ -569,7 +574,11 @@ static hipError_t launch_chunk_sort(const BuildArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   return launch(kKChunkSort, chunk_sort_kernel<NTHR>, dim3(a.nJ - a.j0, a.U * a.L), dim3(NTHR),
                 static_cast<unsigned>(lds), stream, static_cast<const uint16_t*>(a.codes), a.N, a.P, a.K,
-                a.stride_log2, a.nJP, a.j0, a.offsets, a.indices, a.L, a.Hkv, a.old_lens, a.new_lens);
+                a.stride_log2, a.nJP, a.j0, a.offsets, a.indices, a.L, a.Hkv, a.old_lens, a.new_lens
+#ifdef LSH_CHECKED
+                , g_check
+#endif
+                );
 }
 
 // ---------------------------------------------------------------------------

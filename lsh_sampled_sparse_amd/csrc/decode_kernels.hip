@@ -224,6 +224,7 @@ struct AttendF32Lds {
 
 template <int GM>
 __device__ __forceinline__ void attend_f32_role(const FusedParams& p, int s, int u, unsigned char* smem) {
+  LSH_PCHECK(p, u < p.B * p.Hkv && s < p.npart, kChkSlot);
   AttendF32Lds<GM>& A = *reinterpret_cast<AttendF32Lds<GM>*>(smem);
   const float* __restrict__ q = static_cast<const float*>(p.q);
   const float* __restrict__ keys = static_cast<const float*>(p.keys);
@@ -484,6 +485,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   FusedParams p{};
 #ifdef LSH_TRACE
   p.trace = g_trace;
+#endif
+#ifdef LSH_CHECKED
+  p.check = g_check;
 #endif
   p.q = a.q;
   p.keys = a.keys;

@@ -166,7 +166,15 @@ struct FusedParams {
 #ifdef LSH_TRACE
   unsigned long long* trace;   // [grid][16] phase timestamps (trace builds only)
 #endif
+#ifdef LSH_CHECKED
+  uint32_t* check;             // violation bits (checked builds only)
+#endif
 };
+#ifdef LSH_CHECKED
+#define LSH_PCHECK(p, cond, bit) LSH_CHECK((p).check, cond, bit)
+#else
+#define LSH_PCHECK(p, cond, bit) do { } while (0)
+#endif
 
 // Phase timestamps of a workgroup (s_memrealtime, 100 MHz), recorded only in
 // builds with LSH_TRACE defined; a profiling aid, compiled out otherwise.
@@ -344,8 +352,12 @@ __device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned 
   int nblk = 0;
   if (tid < p.L && clen > 0) {
     const int qc = p.qcodes[static_cast<size_t>(bh) * p.L + tid];
+    LSH_PCHECK(p, qc < nb, kChkQueryCode);
     const size_t row = static_cast<size_t>(u) * p.L + tid;
     const uint16_t* op = p.offsets + (row * p.nJP + J) * nb + qc;
+    LSH_PCHECK(p, static_cast<int>(op[0]) <= (qc + 1 < nb ? static_cast<int>(op[1]) : clen) &&
+                      (qc + 1 < nb ? static_cast<int>(op[1]) : static_cast<int>(op[0])) <= clen,
+               kChkSegment);
     // clamped into the chunk: tables of another stride cannot send the walk out of it
     const int s0 = min(static_cast<int>(op[0]), clen);
     const int e0 = qc + 1 < nb ? min(static_cast<int>(op[1]), clen) : clen;
@@ -487,6 +499,8 @@ __device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned 
         const uint32_t inseg = (0xffu << max(lo[k], 0)) & (0xffu >> (8 - min(max(hi[k], 0), 8)));
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
+          LSH_PCHECK(p, !((inseg >> e) & 1u) || ((blk[k][e >> 1] >> (16 * (e & 1))) & 0xffffu) <
+                            static_cast<uint32_t>(clen), kChkEntry);
           const uint32_t key = (blk[k][e >> 1] >> (16 * (e & 1))) & kmask;
           const uint32_t inc = ((inseg >> e) & 1u) << ((key & 3u) * 8u);
           __hip_atomic_fetch_add(&cnt[key >> 2], inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);

@@ -160,6 +160,10 @@ lsh_status scratch_address(void** out) {
 
 namespace lsh {
 
+#ifdef LSH_CHECKED
+uint32_t* g_check = nullptr;
+#endif
+
 const char* kernel_name(int id) {
   static const char* const names[kKNumKernels] = {
       "transpose_w", "project_codes", "chunk_sort", "qhash", "decode"};
@@ -218,6 +222,12 @@ void timing_events(int id, hipEvent_t* start, hipEvent_t* stop) {
 }  // namespace lsh
 
 extern "C" {
+
+#ifdef LSH_CHECKED
+// checked builds: the device word (uint32, caller-owned) that the next
+// launches OR their violation bits into; NULL turns the checks off
+void lsh_check_set(void* word) { lsh::g_check = static_cast<uint32_t*>(word); }
+#endif
 
 const char* lsh_status_string(int status) {
   switch (status) {

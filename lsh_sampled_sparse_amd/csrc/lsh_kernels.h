@@ -99,6 +99,25 @@ enum KernelId {
 };
 const char* kernel_name(int id);
 
+// Checked builds (LSH_CHECKED defined): kernels test their index arithmetic
+// against the bounds the arguments promise and OR a bit into a device word
+// on a violation (the access itself stays clamped as in every build).  The
+// word is set with lsh_check_set; unchecked builds compile the tests out.
+enum CheckBit : uint32_t {
+  kChkQueryCode = 1u,      // a query code >= 2^K
+  kChkSegment = 2u,        // a probed bucket's bounds outside its chunk
+  kChkEntry = 4u,          // a bucket entry >= the chunk's length
+  kChkSlot = 8u,           // an attention workgroup's unit or slot out of range
+  kChkSortCode = 16u,      // a key code >= 2^K in the sort
+};
+#ifdef LSH_CHECKED
+extern uint32_t* g_check;   // device word of the checked build (null: no checks)
+#define LSH_CHECK(ptr, cond, bit) \
+  do { if (!(cond) && (ptr) != nullptr) atomicOr((ptr), static_cast<unsigned>(bit)); } while (0)
+#else
+#define LSH_CHECK(ptr, cond, bit) do { } while (0)
+#endif
+
 // A launch id ORed with kUntimed never takes timing events.
 constexpr int kUntimed = 1 << 8;
 
