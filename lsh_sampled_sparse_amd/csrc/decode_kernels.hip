@@ -532,6 +532,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.n_attend_wg = U * a.nsplit;
   // a fold keeps the (head, slot) pairs of its heads in LDS
   const int F = p.G < p.npart ? p.G : p.npart;
+  // splits of up to 64 / F units at a time are dispatched interleaved: at
+  // most 64 finishers can then wait for workgroups that have no slot yet
+  p.unit_group = F > 0 && 64 / F > 1 ? 64 / F : 1;
   if ((p.G + F - 1) / F * p.npart > kMergeMaxPairs || p.G > 16 || a.L > 255) return hipErrorInvalidValue;
   const int nsync = fused_sync_words(U, a.nJ);
   const int untimed = a.timed ? 0 : kUntimed;

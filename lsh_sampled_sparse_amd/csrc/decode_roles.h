@@ -162,6 +162,7 @@ struct FusedParams {
   int split_len, nsplit, n_sink, n_window, exact_len, nexact;
   int npart;
   int n_count_wg, n_exact_wg, n_attend_wg;
+  int unit_group;              // units whose splits are dispatched interleaved (decode_role)
   float scale;
 #ifdef LSH_TRACE
   unsigned long long* trace;   // [grid][16] phase timestamps (trace builds only)
@@ -189,9 +190,19 @@ struct FusedParams {
 __host__ __device__ inline int fused_sync_words(int U, int nJ) { return U * nJ + U; }
 
 // What workgroup `wid` of the decode launch does.  The grid holds every
-// count workgroup first (chunk by chunk, one per query head), then unit by
-// unit the exact-set pieces and the context splits.  Attention workgroups
-// wait for count workgroups, which come earlier in the grid and never wait.
+// count workgroup first (chunk by chunk, one per query head), then the
+// attention workgroups of the units, a group of R units at a time
+// (R = unit_group): within a group, the exact-set pieces of its units, then
+// their context splits, split 0 of every unit of the group, then split 1,
+// and so on.  Attention workgroups that take the later slots of a CU stream
+// more slowly while the earlier ones run, so this gives every unit of a
+// group its share of early and late slots and the units end together,
+// instead of the last-dispatched unit ending last.
+// Progress: count workgroups come before every attention workgroup and never
+// wait; a unit's finishers wait only for workgroups of their own unit, and
+// only the R units of the group being dispatched can still have workgroups
+// waiting for a slot, so at most R * F finishers (F per unit, R * F <= 64)
+// wait while the rest of the resident workgroups run and leave.
 // (Placing each unit's count workgroups just before its attention
 // workgroups, so that later units count while earlier ones stream, measured
 // slower at every size tried, from 4 units of 128K keys to 512 units of 32K:
@@ -210,11 +221,26 @@ __device__ inline DecodeRole decode_role(const FusedParams& p, int wid) {
   r.count = wid < p.n_count_wg;
   r.J = wid / BH;
   r.bh = wid % BH;
-  const int k = wid - p.n_count_wg;
+  if (r.count) {
+    r.u = r.bh / p.G;   // the head's unit (bh / G = b * Hkv + h / G)
+    r.slot = 0;
+    return r;
+  }
+  const int U = p.B * p.Hkv;
   const int per_unit = p.nexact + p.nsplit;
-  r.u = r.count ? r.bh / p.G : k / per_unit;   // count: the head's unit (bh / G = b * Hkv + h / G)
-  const int i = k % per_unit;
-  r.slot = i < p.nexact ? p.nsplit + i : i - p.nexact;
+  const int k = wid - p.n_count_wg;
+  const int grp = k / (p.unit_group * per_unit);            // group of units
+  const int u0 = grp * p.unit_group;
+  const int R = min(p.unit_group, U - u0);                   // units in this group
+  const int i = k - u0 * per_unit;                           // position in the group
+  if (i < R * p.nexact) {                                    // exact-set pieces, unit by unit
+    r.u = u0 + i / max(p.nexact, 1);
+    r.slot = p.nsplit + i % max(p.nexact, 1);
+  } else {                                                   // splits, split by split
+    const int j = i - R * p.nexact;
+    r.u = u0 + j % R;
+    r.slot = j / R;
+  }
   return r;
 }
 
