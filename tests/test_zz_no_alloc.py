@@ -114,3 +114,48 @@ def test_noalloc_refuses_oversize():
     assert ei.value.status == lsh.LSH_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
+
+
+def test_noalloc_decode_in_a_graph():
+    # the callers it is for: a decode step captured into a HIP graph without a
+    # workspace.  Three replays, each followed by an eager no-alloc call on
+    # other inputs (which leaves its own data in the shared scratch); every
+    # replay equals the cached decode with its own workspace, bit for bit
+    import lsh_sampled_sparse_amd as lsh
+    lsh.lib()
+    dev = torch.device("cuda:0")
+    say("case noalloc graph")
+    cfg = workloads.Config("noalloc-graph", B=2, Hq=8, Hkv=2, N=5000, d=128, K=8, L=24, T=2, dtype="bf16",
+                           planted=4, a=0.8, offset="per_head", seed=73)
+    q, keys, vals, W, tb = _inputs(cfg, 5000, None, 1024, dev)
+    ref = _decode("cached", q, keys, vals, W, tb, cfg, 2, 64)
+    other_cfg = CALLS[1][0]
+    oq, okeys, ovals, oW, otb = _inputs(other_cfg, other_cfg.N, None, 1024, dev)
+    oref = _decode("cached", oq, okeys, ovals, oW, otb, other_cfg, 0, 0)
+
+    out = torch.full_like(ref["out"], float("nan"))
+    lse = torch.full_like(ref["lse"], float("nan"))
+    nsel = torch.full_like(ref["nsel"], -1)
+    args = (q, keys, vals, W, tb["indices"], tb["offsets"], tb["n"], cfg.K, cfg.L, cfg.T, tb["stride"], cfg.scale,
+            2, 64, out, lse, nsel)
+    lsh.lsh_decode_attention_noalloc(*args)   # once eagerly: every kernel's one-time set-up before capture
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            lsh.lsh_decode_attention_noalloc(*args)
+    torch.cuda.current_stream(dev).wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        nsel.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref["out"]) and torch.equal(lse, ref["lse"]) and torch.equal(nsel, ref["nsel"]), rep
+        got = _decode("noalloc", oq, okeys, ovals, oW, otb, other_cfg, 0, 0)
+        for k in oref:
+            assert torch.equal(got[k], oref[k]), (rep, k)
+        say(f"  replay {rep} equal")
