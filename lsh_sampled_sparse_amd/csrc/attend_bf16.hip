@@ -306,13 +306,13 @@ __device__ __forceinline__ void attend_bf16_role(const FusedParams& p, int s, in
       const int slot = 16 * gp + sl;
       const int e = (rhead + (slot < nt ? slot : 0)) & (kRingN - 1);
       hmk[gp] = slot < nt ? static_cast<int>(rhm[e]) : 0;
-      Kf[gp].load_interleaved(kb + static_cast<size_t>(ridx[e]) * kHeadDim + g4 * 8, true);
+      Kf[gp].load_interleaved_nt(kb + static_cast<size_t>(ridx[e]) * kHeadDim + g4 * 8);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = g4 + 4 * j;
       const int e = (rhead + (row < nt ? row : 0)) & (kRingN - 1);
-      vr[j] = *reinterpret_cast<const u32x4_t*>(vb + static_cast<size_t>(ridx[e]) * kHeadDim + sl * 8);
+      vr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + static_cast<size_t>(ridx[e]) * kHeadDim + sl * 8));
     }
   };
 

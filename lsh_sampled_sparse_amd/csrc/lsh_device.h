@@ -100,6 +100,12 @@ struct Frag<BF16> {
 #pragma unroll
     for (int k = 0; k < 4; ++k) v[k] = __builtin_bit_cast(bf16x8_t, valid ? q[4 * k] : zero);
   }
+  // load_interleaved's pieces through non-temporal loads, for rows read once
+  __device__ __forceinline__ void load_interleaved_nt(const uint16_t* p) {
+    const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = __builtin_bit_cast(bf16x8_t, __builtin_nontemporal_load(q + 4 * k));
+  }
   __device__ __forceinline__ floatx4_t mma(const Frag& b, floatx4_t acc) const {
 #pragma unroll
     for (int k = 0; k < 4; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[k], b.v[k], acc, 0, 0, 0);
