@@ -45,11 +45,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA, TFLOP/s
 
-BUILD_KERNELS = ("transpose_w", "project_codes", "chunk_sort")
+BUILD_KERNELS = ("transpose_w", "project_codes", "chunk_sort", "chunk_insert")
 DECODE_KERNELS = ("qhash", "decode")
 KERNEL_SOURCES = {
     "transpose_w": ("build_kernels.hip",), "project_codes": ("build_kernels.hip",),
-    "chunk_sort": ("build_kernels.hip",), "qhash": ("decode_kernels.hip",),
+    "chunk_sort": ("build_kernels.hip",), "chunk_insert": ("build_kernels.hip",), "qhash": ("decode_kernels.hip",),
     "decode": ("attend_bf16.hip", "decode_roles.h"),
 }
 
@@ -127,7 +127,8 @@ def copy_calibration():
 
 # rocprofv3 kernel names -> the library's kernel kinds
 KERNEL_PATTERNS = (("qhash_kernel", "qhash"), ("decode_bf16_kernel", "decode"), ("decode_f32_kernel", "decode"),
-                   ("project_codes", "project_codes"), ("chunk_sort", "chunk_sort"), ("transpose_w", "transpose_w"))
+                   ("project_codes", "project_codes"), ("chunk_sort", "chunk_sort"), ("chunk_insert", "chunk_insert"),
+                   ("transpose_w", "transpose_w"))
 
 
 def _counter_values(d, counter):
@@ -620,10 +621,10 @@ def main():
             "kernels": {k: v["avg_us"] for k, v in hk.items()},
         }
 
-        # multi-step decode over a growing cache: each step appends one key (the
-        # chunk it falls into is rebuilt) and runs the hybrid decode over the
-        # keys held.  The cache starts half-way into its last chunk, the average
-        # rebuild size; the tables of the first chunks stay as built.
+        # multi-step decode over a growing cache: each step appends one key
+        # (inserted into the chunk it falls into) and runs the hybrid decode
+        # over the keys held.  The cache starts half-way into its last chunk,
+        # so an insert moves half a chunk of entries on average.
         c0 = copies[0]
         n_start = max(1, N - stride // 2)
         lsh.lsh_timing_begin()

@@ -149,21 +149,26 @@ lsh_status lsh_build_tables(const void* keys, const void* W,
  *                                       kept; the rest up to new_b rewritten
  * indices  [B, Hkv, L, n_cap] uint16    in/out: positions below
  *                                       (old_b / stride) * stride are kept
- * key_codes [B, Hkv, L, n_cap] uint16   optional out: codes of the keys from
- *                                       (old_b / stride) * stride to new_b
+ * key_codes [B, Hkv, L, n_cap] uint16   optional out: codes of keys old_b ..
+ *                                       new_b - 1 (of the keys from
+ *                                       (old_b / stride) * stride when the
+ *                                       chunks are rebuilt, below)
  * old_lens, new_lens [B] int32          optional (device): old_b, new_b per
  *                                       sequence; when NULL every old_b =
  *                                       n_old, every new_b = n_new
  * workspace                             lsh_build_workspace_size(.., n_cap, ..)
  *
- * (x / stride rounds down.)  The inputs must hold the tables of keys
- * 0 .. old_b - 1 built with the same W, K, L, stride and n_cap (old_b = 0:
- * nothing); keys of positions >= new_b are never read.  The call rebuilds the
- * chunks from the one holding key old_b to the one holding key new_b - 1,
- * reading their keys: one new key per step costs one chunk of keys per
- * (sequence, kv head).  The scalars bound the arrays: n_old <= old_b <= new_b
- * <= n_new, with device values clamped into that range (the launch covers the
- * chunks of keys n_old .. n_new - 1).  0 <= n_old <= n_new <= n_cap and
+ * (x / stride rounds down.)  The inputs must hold the tables of exactly the
+ * keys 0 .. old_b - 1, built with the same W, K, L, stride and n_cap
+ * (old_b = 0: nothing); keys of positions >= new_b are never read.  A
+ * sequence that gains at most 256 keys onto tables holding some (old_b > 0,
+ * new_b - old_b <= 256) has them inserted: only the new keys are projected,
+ * and in the one or two chunks they fall into the entries after each
+ * insertion point move up and the bucket starts are raised.  Any other
+ * sequence has the chunks from the one holding key old_b to the one holding
+ * key new_b - 1 rebuilt from their keys.  The scalars bound the arrays:
+ * n_old <= old_b <= new_b <= n_new, with device values clamped into that
+ * range (the launch covers the chunks of keys n_old .. n_new - 1).  0 <= n_old <= n_new <= n_cap and
  * w_per_head in {0, 1}, else LSH_ERR_INVALID_ARG; n_old == n_new launches
  * nothing.  Size limits as for lsh_build_tables with N = n_cap.
  * lsh_build_tables(.., N, ..) is this call with n_old = 0, n_new = n_cap = N,

@@ -162,6 +162,7 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
     const typename T::storage* __restrict__ WT,     // [nslab * NCT * 16][128], permuted
     uint16_t* __restrict__ codes,                   // [U][L][P]
     int N, int P, int n_first, int L, int nslab,    // keys n_first .. N - 1
+    int n_old,                                      // the update's bound on the old lengths
     int spz,                                        // slabs per blockIdx.z
     int Hkv, size_t wt_head_stride,                 // WT of kv head g at g * wt_head_stride
     const int32_t* __restrict__ old_lens,           // optional per-sequence ranges
@@ -182,13 +183,13 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
 
   const int u = blockIdx.y;
   const int n0 = n_first + blockIdx.x * kProjKeys;
-  // this sequence's keys to (re)code: from the chunk holding its first new
-  // key (never below n_first) to its new length
-  const int b = u / Hkv;
-  const int hi = seq_len_of(new_lens, b, N);
-  int lo = n_first;
-  if (old_lens) lo = max(lo, (seq_len_of(old_lens, b, hi) >> stride_log2) << stride_log2);
-  if (n0 >= hi || n0 + kProjKeys <= lo) return;
+  // this sequence's keys to (re)code: every key from the start of the chunk
+  // that holds its first new key (none when its keys are inserted: the
+  // insert kernel codes them)
+  const SeqUpdate su = seq_update(old_lens, new_lens, u / Hkv, n_old, N);
+  const int hi = su.hi;
+  const int lo = su.insert ? hi : (su.old >> stride_log2) << stride_log2;
+  if (n0 >= hi || n0 + kProjKeys <= lo || lo >= hi) return;
   WT += static_cast<size_t>(u % Hkv) * wt_head_stride;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4;
@@ -267,18 +268,16 @@ __global__ __launch_bounds__(kProjThreads, T::bytes == 2 ? 3 : 1) void project_c
 // K = 0: every code is 0 (keys n_first .. N - 1 of every [U][L] row of
 // pitch P, within each sequence's own range as in project_codes_kernel).
 __global__ void zero_codes_kernel(uint16_t* __restrict__ codes, size_t rows, int n_first, int N, int P, int L,
-                                  int Hkv, const int32_t* __restrict__ old_lens,
+                                  int n_old, int Hkv, const int32_t* __restrict__ old_lens,
                                   const int32_t* __restrict__ new_lens, int stride_log2) {
   const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const size_t w = static_cast<size_t>(N - n_first);
   if (i >= rows * w) return;
   const size_t row = i / w;
   const int key = n_first + static_cast<int>(i % w);
-  const int b = static_cast<int>(row / L) / Hkv;
-  const int hi = seq_len_of(new_lens, b, N);
-  int lo = n_first;
-  if (old_lens) lo = max(lo, (seq_len_of(old_lens, b, hi) >> stride_log2) << stride_log2);
-  if (key >= lo && key < hi) codes[row * P + key] = 0;
+  const SeqUpdate su = seq_update(old_lens, new_lens, static_cast<int>(row / L) / Hkv, n_old, N);
+  const int lo = su.insert ? su.hi : (su.old >> stride_log2) << stride_log2;
+  if (key >= lo && key < su.hi) codes[row * P + key] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -395,7 +394,7 @@ __global__ __launch_bounds__(NTHR, NTHR >= 256 ? 4 : 1) void chunk_sort_kernel(
     int N, int P, int K, int stride_log2, int nJP, int j0,   // chunks j0 + blockIdx.x
     uint16_t* __restrict__ offsets,       // [U][L][nJP][2^K]
     uint16_t* __restrict__ indices,       // [U][L][P]
-    int L, int Hkv, const int32_t* __restrict__ old_lens, const int32_t* __restrict__ new_lens
+    int L, int Hkv, int n_old, const int32_t* __restrict__ old_lens, const int32_t* __restrict__ new_lens
 #ifdef LSH_CHECKED
     , uint32_t* check
 #endif
@@ -414,11 +413,11 @@ __global__ __launch_bounds__(NTHR, NTHR >= 256 ? 4 : 1) void chunk_sort_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = 1 << K;
   const int cbeg = j << stride_log2;
-  // this sequence's chunks to rebuild (the same ranges as the projection)
-  const int b = static_cast<int>(table / L) / Hkv;
-  const int hi = seq_len_of(new_lens, b, N);
-  const int jlo = old_lens ? max(j0, seq_len_of(old_lens, b, hi) >> stride_log2) : j0;
-  if (j < jlo || cbeg >= hi) return;
+  // this sequence's chunks to rebuild (the same ranges as the projection;
+  // none when its new keys are inserted instead)
+  const SeqUpdate su = seq_update(old_lens, new_lens, static_cast<int>(table / L) / Hkv, n_old, N);
+  const int hi = su.hi;
+  if (su.insert || j < (su.old >> stride_log2) || cbeg >= hi) return;
   const int clen = min(1 << stride_log2, hi - cbeg);
   const int p0 = tid * E;
   const bool full = p0 + E <= clen;
@@ -558,6 +557,337 @@ __global__ __launch_bounds__(NTHR, NTHR >= 256 ? 4 : 1) void chunk_sort_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Insertion of a few appended keys into built chunks (table updates).
+//
+// A sequence that gains m <= kInsertMax keys onto built tables has them
+// coded and inserted by one workgroup per table, with no projection of the
+// rest of the chunk and no sort:
+//   - codes: the table's K columns of W go through the same MFMA k-steps as
+//     in project_codes, each column in the operand row and each key in the
+//     column it takes there, so the codes are bit for bit the build's;
+//   - a chunk holding c_old keys gains keys k0 .. k1 - 1 (all larger than its
+//     old keys).  In the rebuilt chunk every bucket keeps its old entries in
+//     order and appends its new keys after them, so with the new keys ranked
+//     by (code, key):
+//       new key r lands at ins_r + r, ins_r being the end of its bucket's old
+//         segment (its insertion point among the old entries);
+//       old entry i moves up by the number of new keys with ins_r <= i;
+//       the start of bucket c grows by the number of new codes below c.
+//     This is the layout chunk_sort writes from all the chunk's codes.
+// The chunk's entries and bucket starts are staged in LDS in the same round
+// of loads as the keys and W, before anything is written back, so the shift
+// works in place; every write stays inside the chunk's region whatever the
+// offsets hold.
+// ---------------------------------------------------------------------------
+constexpr int kInsertThreads = 256;
+static_assert(kInsertMax <= kInsertThreads, "one thread per inserted key");
+
+// The W operand of one projection tile for this lane's row: -W[d][bit]
+// over the lane's 32 dims when the row is bit `bit` of the table, else zero
+// (the rows of other tables do not touch this table's outputs).  `col` points
+// at the lane's 32 dims of the table's column `bit` (any column when the row
+// is not the table's): four or eight 16-byte LDS reads, the sign flipped as
+// negate() flips it, the row masked afterwards, with no branch.
+__device__ __forceinline__ void wfrag_of(Frag<BF16>& f, const uint16_t* col, bool valid) {
+  const u32x4_t* q = reinterpret_cast<const u32x4_t*>(col);
+  const uint32_t m = valid ? 0xffffffffu : 0u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const u32x4_t x = q[k];
+    const u32x4_t y = {(x[0] ^ 0x80008000u) & m, (x[1] ^ 0x80008000u) & m, (x[2] ^ 0x80008000u) & m,
+                       (x[3] ^ 0x80008000u) & m};
+    f.v[k] = __builtin_bit_cast(bf16x8_t, y);
+  }
+}
+__device__ __forceinline__ void wfrag_of(Frag<F32>& f, const float* col, bool valid) {
+  const u32x4_t* q = reinterpret_cast<const u32x4_t*>(col);
+  const uint32_t m = valid ? 0xffffffffu : 0u;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const u32x4_t x = q[k];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) f.v[4 * k + e2] = __uint_as_float((x[e2] ^ 0x80000000u) & m);
+  }
+}
+
+// A key fragment from the raw 16-byte pieces Frag<T>::load would read (zero
+// when the key is not valid).
+__device__ __forceinline__ void frag_from_raw(Frag<BF16>& f, const u32x4_t (&r)[4], bool valid) {
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) f.v[k] = __builtin_bit_cast(bf16x8_t, valid ? r[k] : zero);
+}
+__device__ __forceinline__ void frag_from_raw(Frag<F32>& f, const u32x4_t (&r)[8], bool valid) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f.v[4 * k + e] = valid ? __uint_as_float(r[k][e]) : 0.f;
+}
+
+// Dynamic LDS: a chunk's old entries [2^stride_log2], then its bucket
+// starts [2^K].
+size_t chunk_insert_lds_bytes(int stride_log2, int K) {
+  return ((static_cast<size_t>(1) << stride_log2) + (static_cast<size_t>(1) << K)) * 2;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kInsertThreads) void chunk_insert_kernel(
+    const typename T::storage* __restrict__ keys,   // [U][P][128]
+    const typename T::storage* __restrict__ W,      // [w_heads][128][L*K]
+    uint16_t* __restrict__ codes,         // [U][L][P]: the new keys' codes are written
+    int N, int P, int K, int L, int stride_log2, int nJP,
+    uint16_t* __restrict__ offsets,       // [U][L][nJP][2^K]
+    uint16_t* __restrict__ indices,       // [U][L][P]
+    int Hkv, int w_heads, int n_old, const int32_t* __restrict__ old_lens, const int32_t* __restrict__ new_lens
+#ifdef LSH_CHECKED
+    , uint32_t* check
+#endif
+    ) {
+  using S = typename T::storage;
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_dyn[];
+  constexpr int kWRow = kHeadDim + 16 / T::bytes;  // padded LDS row (16-byte aligned)
+  __shared__ __attribute__((aligned(16))) S s_w[16][kWRow];   // the table's columns of W: [bit][dim]
+  __shared__ uint16_t s_new[kInsertMax];           // codes of the sequence's new keys, in key order
+  // a chunk's new keys in (code, key) order: code, key, position in the new chunk
+  __shared__ uint16_t s_code[kInsertMax], s_key[kInsertMax], s_pos[kInsertMax];
+  uint16_t* s_old = s_dyn;                         // a chunk's old entries
+  uint16_t* s_off = s_dyn + (1 << stride_log2);    // its bucket starts
+  const size_t table = blockIdx.x;                 // u * L + l
+  const int u = static_cast<int>(table / L), l = static_cast<int>(table % L);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nb = 1 << K;
+  const SeqUpdate su = seq_update(old_lens, new_lens, u / Hkv, n_old, N);
+  if (!su.insert || su.old >= su.hi) return;
+  const int old = su.old, hi = su.hi;
+
+  // ---- one round of loads: the table's W columns, this wave's first key
+  // tile, the first chunk's entries and bucket starts
+  const S* Wu = W + (w_heads > 1 ? static_cast<size_t>(u % Hkv) * kHeadDim * L * K : size_t(0));
+  S wv[8];                                         // 128 K <= 1920 values
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int i = tid + q * kInsertThreads;
+    wv[q] = i < kHeadDim * K ? Wu[static_cast<size_t>(i / K) * L * K + l * K + i % K] : S(0);
+  }
+  const S* ku = keys + static_cast<size_t>(u) * P * kHeadDim;
+  const int tb0 = old >> 4, ntile = ((hi - 1) >> 4) - tb0 + 1;   // 16-key tiles holding new keys
+  const int g = lane >> 4, col = lane & 15;
+  // key n in column n % 16, as in project_codes: the lane's 32 dims as raw
+  // 16-byte pieces, masked only when the fragment is formed, so that the
+  // loads stay in flight with the others until the barrier
+  constexpr int kKeyQ = 2 * T::bytes;              // 16-byte pieces per lane
+  u32x4_t kraw[kKeyQ];
+  auto key_of = [&](int kt) { return (tb0 + kt) * 16 + col; };
+  auto load_keys = [&](int kt) {
+    const int n = key_of(kt);
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
+        ku + static_cast<size_t>(n >= old && n < hi ? n : old) * kHeadDim + g * 32);
+#pragma unroll
+    for (int k = 0; k < kKeyQ; ++k) kraw[k] = src[k];
+  };
+  if (K > 0 && wave < ntile) load_keys(wave);
+  // a chunk's old entries and bucket starts go to LDS in 16-byte pieces
+  // where aligned: the first four pieces per thread of each (all entries of
+  // a chunk, the bucket starts up to K = 13) are loaded straight-line, with
+  // no loop whose head would wait for the loads before it
+  const int j1 = old >> stride_log2;
+  auto chunk_old = [&](int j) { return max(0, min(old, (j + 1) << stride_log2) - (j << stride_log2)); };
+  auto ib_of = [&](int j) { return indices + table * P + (j << stride_log2); };
+  auto ob_of = [&](int j) { return offsets + (table * nJP + j) * static_cast<size_t>(nb); };
+  auto pieces = [&](const uint16_t* p, int n) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0 ? n >> 3 : 0; };
+  u32x4_t ev[4], ov[4];
+  auto stage_issue = [&](int j) {
+    const int c_old = chunk_old(j);
+    const int ne8 = pieces(ib_of(j), c_old), no8 = c_old > 0 ? pieces(ob_of(j), nb) : 0;
+    const u32x4_t* e4 = reinterpret_cast<const u32x4_t*>(ib_of(j));
+    const u32x4_t* o4 = reinterpret_cast<const u32x4_t*>(ob_of(j));
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = tid + q * kInsertThreads;
+      ev[q] = i < ne8 ? e4[i] : zero;
+      ov[q] = i < no8 ? o4[i] : zero;
+    }
+  };
+  auto stage_commit = [&](int j) {
+    const int c_old = chunk_old(j);
+    const uint16_t* ib = ib_of(j);
+    const uint16_t* ob = ob_of(j);
+    const int ne8 = pieces(ib, c_old), no8 = c_old > 0 ? pieces(ob, nb) : 0;
+    u32x4_t* so4 = reinterpret_cast<u32x4_t*>(s_old);
+    u32x4_t* sf4 = reinterpret_cast<u32x4_t*>(s_off);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = tid + q * kInsertThreads;
+      if (i < ne8) so4[i] = ev[q];
+      if (i < no8) sf4[i] = ov[q];
+    }
+    // the rest: bucket starts past the first pieces (K >= 14), the last
+    // entries or starts short of a piece, unaligned regions
+    for (int i = 4 * kInsertThreads + tid; i < no8; i += kInsertThreads)
+      sf4[i] = reinterpret_cast<const u32x4_t*>(ob)[i];
+    for (int i = 8 * ne8 + tid; i < c_old; i += kInsertThreads) s_old[i] = ib[i];
+    if (c_old > 0)
+      for (int i = 8 * no8 + tid; i < nb; i += kInsertThreads) s_off[i] = ob[i];
+  };
+  stage_issue(j1);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int i = tid + q * kInsertThreads;
+    if (i < kHeadDim * K) s_w[i % K][i / K] = wv[q];
+  }
+  stage_commit(j1);
+  __syncthreads();
+
+  // ---- codes of the new keys.  Table l is table tt of lane group gl of its
+  // slab; its bit b is row position jr = P - 1 - j = tt K + b of that group
+  // (j = 4 ct + i: tile ct, row 4 gl + i), as laid out by transpose_w_kernel
+  if (K > 0) {
+    const ProjShape ps = proj_shape(K);
+    const int P4 = 4 * ps.nct;
+    const int tt = l % ps.tpg, gl = (l / ps.tpg) % 4;
+    const int jlo = P4 - tt * K - K;                 // the table's bits: positions jlo .. jlo + K - 1
+    // this lane's operand row in tile ct: bit of the table, or -1
+    auto row_bit = [&](int ct) {
+      const int r = col, jr = P4 - 1 - (4 * ct + (r & 3));
+      return ((r >> 2) == gl && jr >= tt * K && jr < tt * K + K) ? jr - tt * K : -1;
+    };
+    static_assert(kWRow * T::bytes % 16 == 0, "16-byte LDS rows");
+    for (int kt = wave; kt < ntile; kt += kInsertThreads / 64) {
+      if (kt != wave) load_keys(kt);
+      const bool kvalid = key_of(kt) >= old && key_of(kt) < hi;
+      Frag<T> Kf;
+      frag_from_raw(Kf, kraw, kvalid);
+      uint32_t code = 0;
+      for (int ct = jlo >> 2; ct <= (jlo + K - 1) >> 2; ++ct) {
+        Frag<T> Wf;
+        const int bit = row_bit(ct);
+        wfrag_of(Wf, &s_w[bit < 0 ? 0 : bit][32 * g], bit >= 0);
+        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) Wf.mma_step(k, Kf, acc);
+        // lane (g, col) holds rows 4 g + i: bit jr - tt K of the code
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int jr = P4 - 1 - (4 * ct + i);
+          if (g == gl && jr >= tt * K && jr < tt * K + K)
+            code |= (__float_as_uint(acc[i]) >> 31) << (jr - tt * K);
+        }
+      }
+      const int n = (tb0 + kt) * 16 + col;
+      if (g == gl && n >= old && n < hi) {
+        s_new[n - old] = static_cast<uint16_t>(code);
+        codes[table * P + n] = static_cast<uint16_t>(code);
+      }
+    }
+  } else {
+    for (int n = old + tid; n < hi; n += kInsertThreads) {
+      s_new[n - old] = 0;
+      codes[table * P + n] = 0;
+    }
+  }
+  __syncthreads();
+
+  // ---- insertion, chunk by chunk (one or two chunks)
+  for (int j = j1; j <= (hi - 1) >> stride_log2; ++j) {
+    const int cbeg = j << stride_log2, cend = cbeg + (1 << stride_log2);
+    const int k0 = max(old, cbeg), k1 = min(hi, cend);
+    const int m = min(k1 - k0, kInsertMax);          // >= 1
+    const int c_old = max(0, min(old, cend) - cbeg);   // old entries of the chunk
+    uint16_t* ob = offsets + (table * nJP + j) * static_cast<size_t>(nb);
+    uint16_t* ib = indices + table * P + cbeg;
+    if (j != j1) {
+      stage_issue(j);
+      stage_commit(j);
+      __syncthreads();
+    }
+    if (tid < m) {
+      const int c = s_new[k0 - old + tid];
+      LSH_CHECK(check, c < nb, kChkInsert);
+      int r = 0;                                     // rank by (code, key)
+      for (int s = 0; s < m; ++s) {
+        const int cs = s_new[k0 - old + s];
+        r += (cs < c || (cs == c && s < tid)) ? 1 : 0;
+      }
+      // insertion point: the end of bucket c's old segment
+      const int end = c_old == 0 ? 0 : (c + 1 < nb ? static_cast<int>(s_off[c + 1]) : c_old);
+      LSH_CHECK(check, end <= c_old, kChkInsert);
+      s_code[r] = static_cast<uint16_t>(c);
+      s_key[r] = static_cast<uint16_t>(k0 + tid - cbeg);
+      s_pos[r] = static_cast<uint16_t>(min(end, c_old) + r);
+    }
+    __syncthreads();
+    // the rewritten span [a0, c_old + m), a0 = the first insertion point
+    // rounded down to 8 entries, in 16-byte pieces: a thread forms each of
+    // its pieces in registers, walking the new keys' positions (old entry
+    // i moves up by the new keys placed before it), and stores it at once
+    const int a0 = s_pos[0] & ~7, e1 = c_old + m;
+    const bool vec = (reinterpret_cast<uintptr_t>(ib) & 15) == 0;
+    for (int o0 = a0 + 8 * tid; o0 < e1; o0 += 8 * kInsertThreads) {
+      int lo = 0, hi2 = m;                           // new keys placed before o0
+      while (lo < hi2) {
+        const int mid = (lo + hi2) >> 1;
+        if (static_cast<int>(s_pos[mid]) < o0) lo = mid + 1;
+        else hi2 = mid;
+      }
+      int nx = lo, npos = nx < m ? static_cast<int>(s_pos[nx]) : INT_MAX;
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int o = o0 + q;
+        uint32_t v;
+        if (o == npos) {
+          v = s_key[nx];
+          ++nx;
+          npos = nx < m ? static_cast<int>(s_pos[nx]) : INT_MAX;
+        } else {
+          v = s_old[min(max(o - nx, 0), max(c_old - 1, 0))];
+        }
+        if (q & 1) w[q >> 1] |= v << 16;
+        else w[q >> 1] = v;
+      }
+      if (vec && o0 + 8 <= e1) {
+        *reinterpret_cast<u32x4_t*>(ib + o0) = u32x4_t{w[0], w[1], w[2], w[3]};
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (o0 + q < e1) ib[o0 + q] = static_cast<uint16_t>(w[q >> 1] >> (16 * (q & 1)));
+      }
+    }
+    // bucket starts: + the new codes below c (a chunk without old keys is
+    // written whole; otherwise pieces past the smallest new code's), eight
+    // per 16-byte piece
+    const int cs = c_old == 0 ? 0 : (s_code[0] + 1) & ~7;
+    const bool ovec = nb >= 8 && (reinterpret_cast<uintptr_t>(ob) & 15) == 0;
+    for (int c0 = cs + 8 * tid; c0 < nb; c0 += 8 * kInsertThreads) {
+      int lt = 0, hi2 = m;                           // new codes below c0
+      while (lt < hi2) {
+        const int mid = (lt + hi2) >> 1;
+        if (static_cast<int>(s_code[mid]) < c0) lt = mid + 1;
+        else hi2 = mid;
+      }
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int c = c0 + q;
+        while (lt < m && static_cast<int>(s_code[lt]) < c) ++lt;
+        const uint32_t v = static_cast<uint32_t>((c_old == 0 || c >= nb ? 0 : static_cast<int>(s_off[c])) + lt) & 0xffffu;
+        if (q & 1) w[q >> 1] |= v << 16;
+        else w[q >> 1] = v;
+      }
+      if (ovec) {
+        *reinterpret_cast<u32x4_t*>(ob + c0) = u32x4_t{w[0], w[1], w[2], w[3]};
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (c0 + q < nb) ob[c0 + q] = static_cast<uint16_t>(w[q >> 1] >> (16 * (q & 1)));
+      }
+    }
+    __syncthreads();                                 // LDS reused by the next chunk
+  }
+}
+
 // Block size for a chunk of 2^stride_log2 keys, and the LDS it needs.
 static int sort_threads(int stride_log2) { return max(64, (1 << stride_log2) / kSortE); }
 
@@ -574,7 +904,7 @@ static hipError_t launch_chunk_sort(const BuildArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   return launch(kKChunkSort, chunk_sort_kernel<NTHR>, dim3(a.nJ - a.j0, a.U * a.L), dim3(NTHR),
                 static_cast<unsigned>(lds), stream, static_cast<const uint16_t*>(a.codes), a.N, a.P, a.K,
-                a.stride_log2, a.nJP, a.j0, a.offsets, a.indices, a.L, a.Hkv, a.old_lens, a.new_lens
+                a.stride_log2, a.nJP, a.j0, a.offsets, a.indices, a.L, a.Hkv, a.n_old, a.old_lens, a.new_lens
 #ifdef LSH_CHECKED
                 , g_check
 #endif
@@ -584,6 +914,7 @@ static hipError_t launch_chunk_sort(const BuildArgs& a, hipStream_t stream) {
 // ---------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------
+
 template <typename T, int KB>
 static hipError_t launch_project_k(const BuildArgs& a, int nslab, hipStream_t stream) {
   using S = typename T::storage;
@@ -597,7 +928,8 @@ static hipError_t launch_project_k(const BuildArgs& a, int nslab, hipStream_t st
   const int gz = (nslab + spz - 1) / spz;
   return launch(kKProject, project_codes_kernel<T, KB>, dim3(gx, a.U, gz), dim3(kProjThreads), 0, stream,
                 static_cast<const S*>(a.keys), static_cast<const S*>(a.wt), a.codes, a.N, a.P, n_first, a.L,
-                nslab, spz, a.Hkv, a.w_heads > 1 ? static_cast<size_t>(nslab) * proj_shape(KB).nct * 16 * kHeadDim : size_t(0),
+                nslab, a.n_old, spz, a.Hkv,
+                a.w_heads > 1 ? static_cast<size_t>(nslab) * proj_shape(KB).nct * 16 * kHeadDim : size_t(0),
                 a.old_lens, a.new_lens, a.stride_log2);
 }
 
@@ -610,7 +942,7 @@ static hipError_t launch_project(const BuildArgs& a, hipStream_t stream) {
     const size_t rows = static_cast<size_t>(a.U) * L;
     const size_t n = rows * static_cast<size_t>(a.N - n_first);
     return launch(kKProject, zero_codes_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
-                  a.codes, rows, n_first, a.N, a.P, L, a.Hkv, a.old_lens, a.new_lens, a.stride_log2);
+                  a.codes, rows, n_first, a.N, a.P, L, a.n_old, a.Hkv, a.old_lens, a.new_lens, a.stride_log2);
   }
   const ProjShape ps = proj_shape(K);
   const int rows = proj_wt_rows(K, L);
@@ -639,10 +971,32 @@ static hipError_t launch_project(const BuildArgs& a, hipStream_t stream) {
   }
 }
 
+template <typename T>
+static hipError_t launch_insert(const BuildArgs& a, hipStream_t stream) {
+  using S = typename T::storage;
+  if (a.stride_log2 > 13) return hipErrorInvalidValue;
+  const size_t lds = chunk_insert_lds_bytes(a.stride_log2, a.K);
+  hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(chunk_insert_kernel<T>), lds);
+  if (e != hipSuccess) return e;
+  return launch(kKChunkInsert, chunk_insert_kernel<T>, dim3(static_cast<unsigned>(a.U * a.L)),
+                dim3(kInsertThreads), static_cast<unsigned>(lds), stream, static_cast<const S*>(a.keys),
+                static_cast<const S*>(a.W), a.codes, a.N, a.P, a.K, a.L, a.stride_log2, a.nJP, a.offsets, a.indices,
+                a.Hkv, a.w_heads, a.n_old, a.old_lens, a.new_lens
+#ifdef LSH_CHECKED
+                , g_check
+#endif
+                );
+}
+
+// A build, or an update: sequences whose new keys are inserted go through
+// chunk_insert alone; the others through the projection and chunk_sort.
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream) {
-  hipError_t e = (a.dtype == 1)
-      ? launch_project<BF16>(a, stream)
-      : launch_project<F32>(a, stream);
+  hipError_t e = hipSuccess;
+  if (a.mode & kUpdateInsert) {
+    e = (a.dtype == 1) ? launch_insert<BF16>(a, stream) : launch_insert<F32>(a, stream);
+    if (e != hipSuccess || !(a.mode & kUpdateSort)) return e;
+  }
+  e = (a.dtype == 1) ? launch_project<BF16>(a, stream) : launch_project<F32>(a, stream);
   if (e != hipSuccess) return e;
   switch (sort_threads(a.stride_log2)) {
     case 64: return launch_chunk_sort<64>(a, stream);

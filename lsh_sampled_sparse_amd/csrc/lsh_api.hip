@@ -166,7 +166,7 @@ uint32_t* g_check = nullptr;
 
 const char* kernel_name(int id) {
   static const char* const names[kKNumKernels] = {
-      "transpose_w", "project_codes", "chunk_sort", "qhash", "decode"};
+      "transpose_w", "project_codes", "chunk_sort", "chunk_insert", "qhash", "decode"};
   return (id >= 0 && id < kKNumKernels) ? names[id] : nullptr;
 }
 
@@ -332,6 +332,14 @@ lsh_status lsh_update_tables(const void* keys, const void* W, int B, int Hkv, in
   a.stride_log2 = g.stride_log2;
   a.nJ = lsh_num_chunks(n_new, stride);
   a.dtype = dtype;
+  // a few keys appended to built tables are inserted into their chunks, the
+  // rest re-sorted with their chunks; each sequence's kernels take the same
+  // choice from its lengths, so only when the bounds settle it for every
+  // sequence is one of the two launches left out
+  a.n_old = n_old;
+  if (n_old > 0 && n_new - n_old <= lsh::kInsertMax) a.mode = lsh::kUpdateInsert;
+  else if (!old_lens && !new_lens) a.mode = lsh::kUpdateSort;
+  else a.mode = lsh::kUpdateSort | lsh::kUpdateInsert;
   return hip_status(lsh::launch_build(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -28,7 +28,10 @@ struct BuildArgs {
   int stride_log2, nJ;
   int w_heads;           // 1: one W for every head; Hkv: W per kv head
   int dtype;             // 0 = f32, 1 = bf16
+  int n_old;             // the bound n_old of lsh_update_tables
+  int mode;              // kUpdateSort, kUpdateInsert or both (chosen per sequence, seq_update)
 };
+constexpr int kUpdateSort = 1, kUpdateInsert = 2;
 
 struct DecodeArgs {
   const void* q;         // [B][Hq][128]
@@ -69,6 +72,29 @@ __host__ __device__ inline int seq_len_of(const int32_t* lens, int b, int N) {
   return v < 0 ? 0 : (v > N ? N : v);
 }
 
+// A table update appends at most this many keys per sequence by insertion.
+constexpr int kInsertMax = 256;
+
+// Sequence b's part of a table update from n_old .. n_new (= N) keys: the
+// keys its tables hold before (old) and after (hi), both clamped into
+// [n_old, N], and whether its new keys are inserted into the built chunks
+// (at most kInsertMax keys onto tables that hold some) rather than re-sorted
+// with the chunks that hold them.
+struct SeqUpdate {
+  int old, hi;
+  bool insert;
+};
+__host__ __device__ inline SeqUpdate seq_update(const int32_t* old_lens, const int32_t* new_lens, int b, int n_old,
+                                                int N) {
+  SeqUpdate s;
+  const int h = seq_len_of(new_lens, b, N);
+  s.hi = h < n_old ? n_old : h;
+  const int o = old_lens ? seq_len_of(old_lens, b, s.hi) : n_old;
+  s.old = o < n_old ? n_old : o;
+  s.insert = s.old > 0 && s.hi - s.old <= kInsertMax;
+  return s;
+}
+
 // The exact set of a sequence of n keys: its first eh and its last et keys.
 __host__ __device__ inline void exact_range(int n_sink, int n_window, int n, int& eh, int& et) {
   eh = n_sink < n ? n_sink : n;
@@ -93,6 +119,7 @@ enum KernelId {
   kKTransposeW = 0,
   kKProject,
   kKChunkSort,
+  kKChunkInsert,
   kKQhash,
   kKDecode,
   kKNumKernels
@@ -109,6 +136,7 @@ enum CheckBit : uint32_t {
   kChkEntry = 4u,          // a bucket entry >= the chunk's length
   kChkSlot = 8u,           // an attention workgroup's unit or slot out of range
   kChkSortCode = 16u,      // a key code >= 2^K in the sort
+  kChkInsert = 32u,        // an insert: a code >= 2^K or a bucket end outside the chunk's entries
 };
 #ifdef LSH_CHECKED
 extern uint32_t* g_check;   // device word of the checked build (null: no checks)

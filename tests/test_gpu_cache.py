@@ -192,6 +192,56 @@ def test_update_equals_fresh_build():
         assert torch.equal(r1[k], r2[k]), k
 
 
+def test_insert_equals_fresh_build():
+    # appends of at most 256 keys onto built tables are inserted into their
+    # chunks: one key, 256 keys, up to a chunk boundary, into an empty chunk,
+    # across a chunk boundary (with rebuilds in between).  After every step
+    # the tables are those a fresh build over the same keys writes, bit for
+    # bit, and the decodes agree bit for bit
+    cfg = GROWTH[0][0]
+    schedule = [2500, 2501, 2757, 3000, 3072, 3073, 3100, 3200, 3400, 4096, 4097, 4353]
+    say(f"case insert equals fresh build schedule={schedule}")
+    lsh = _lsh()
+    dev = torch.device("cuda:0")
+    data = workloads.generate(cfg)
+    keys, vals = data["keys"].to(dev), data["values"].to(dev)
+    W = data["W"].to(dev).contiguous()
+    q = data["q"][0].to(dev).contiguous()
+    ck = torch.full_like(keys, float("nan"))
+    cv = torch.full_like(vals, float("nan"))
+    tb = lsh.alloc_tables(ck, cfg.K, cfg.L, stride=1024, return_codes=True)
+    for n in schedule:
+        n0 = tb["n"]
+        ck[:, :, n0:n] = keys[:, :, n0:n]
+        cv[:, :, n0:n] = vals[:, :, n0:n]
+        lsh.update_tables(ck, W, tb, n, cfg.K, cfg.L)
+        fresh = lsh.build_tables(keys[:, :, :n].contiguous(), W, cfg.K, cfg.L, stride=1024, return_codes=True)
+        torch.cuda.synchronize()
+        nj = lsh.lsh_num_chunks(n, 1024)
+        assert torch.equal(tb["indices"][..., :n], fresh["indices"]), n
+        assert torch.equal(tb["codes"][..., :n], fresh["codes"]), n
+        assert torch.equal(tb["offsets"][:, :, :, :nj], fresh["offsets"]), n
+        r1 = lsh.decode_attention(q, ck, cv, W, tb, cfg.K, cfg.L, cfg.T, sm_scale=cfg.scale)
+        r2 = lsh.decode_attention(q, keys[:, :, :n].contiguous(), vals[:, :, :n].contiguous(), W, fresh, cfg.K,
+                                  cfg.L, cfg.T, sm_scale=cfg.scale)
+        torch.cuda.synchronize()
+        for k in ("out", "lse", "nsel"):
+            assert torch.equal(r1[k], r2[k]), (n, k)
+        say(f"[{cfg.name}] n={n} ({n - n0} keys {'inserted' if 0 < n0 and n - n0 <= 256 else 'by rebuild'}) "
+            f"tables and decode equal a fresh build")
+
+
+def test_ragged_insert():
+    # per-sequence lengths far apart, so the bounds do not settle the choice
+    # and each sequence takes it: in one call some insert (1 and 256 keys),
+    # one stays, one is rebuilt; tables and decodes checked against the oracle
+    cfg = workloads.Config("cache-ragged-insert", B=3, Hq=8, Hkv=2, N=5000, d=128, K=9, L=16, T=2, dtype="bf16",
+                           planted=4, a=0.8, offset="per_head", seed=41)
+    say("case ragged insert")
+    schedule = [[1000, 2500, 300], [1001, 2501, 300], [1257, 2502, 1300], [1300, 2700, 1301], [1301, 3072, 1557]]
+    grow(cfg, schedule, stride=1024, n_sink=2, n_window=64)
+
+
 def test_full_size_decode_steps_128k():
     # the 128K GQA-8 workload as a cache: built over all but the last 8 keys,
     # then 8 decode steps that each append one key and decode (hybrid: 4

@@ -57,7 +57,8 @@ for name, run in cases:
 cfg = workloads.Config("checked-ragged", B=3, Hq=8, Hkv=2, N=5000, d=128, K=8, L=20, T=2, dtype="bf16",
                        planted=4, a=0.8, offset="per_head", seed=36)
 say("case checked ragged growth with per-head W")
-C.grow(cfg, [[1000, 0, 300], [3000, 2500, 1025], [5000, 5000, 4097]], stride=1024, n_sink=2, n_window=100,
+C.grow(cfg, [[1000, 0, 300], [1001, 0, 301], [3000, 2500, 1025], [3001, 2756, 1025], [5000, 5000, 4097]],
+       stride=1024, n_sink=2, n_window=100,
        W_heads=workloads.per_head_projections(cfg, seed=1036))
 torch.cuda.synchronize()
 say("  violation bits", int(word.item()))
