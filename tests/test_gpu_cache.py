@@ -231,6 +231,44 @@ def test_insert_equals_fresh_build():
             f"tables and decode equal a fresh build")
 
 
+def test_insert_odd_pitch():
+    # a cache whose capacity is odd (3001 keys), so most tables' rows start
+    # off a 16-byte boundary and the insertion stages and writes them with
+    # 2-byte accesses; appends up to, into and across the 1536 chunk
+    # boundary; the tables and decodes equal a fresh build's bit for bit
+    cfg = workloads.Config("insert-odd-pitch", B=1, Hq=6, Hkv=2, N=3001, d=128, K=9, L=12, T=2, dtype="bf16",
+                           planted=3, a=0.8, offset="per_head", seed=42)
+    schedule = [1000, 1001, 1257, 1500, 1536, 1537, 1600, 1601]
+    say(f"case insert odd pitch schedule={schedule}")
+    lsh = _lsh()
+    dev = torch.device("cuda:0")
+    data = workloads.generate(cfg)
+    keys, vals = data["keys"].to(dev), data["values"].to(dev)
+    W = data["W"].to(dev).contiguous()
+    q = data["q"][0].to(dev).contiguous()
+    ck = torch.full_like(keys, float("nan"))
+    cv = torch.full_like(vals, float("nan"))
+    tb = lsh.alloc_tables(ck, cfg.K, cfg.L, stride=512, return_codes=True)
+    for n in schedule:
+        n0 = tb["n"]
+        ck[:, :, n0:n] = keys[:, :, n0:n]
+        cv[:, :, n0:n] = vals[:, :, n0:n]
+        lsh.update_tables(ck, W, tb, n, cfg.K, cfg.L)
+        fresh = lsh.build_tables(keys[:, :, :n].contiguous(), W, cfg.K, cfg.L, stride=512, return_codes=True)
+        torch.cuda.synchronize()
+        nj = lsh.lsh_num_chunks(n, 512)
+        assert torch.equal(tb["indices"][..., :n], fresh["indices"]), n
+        assert torch.equal(tb["codes"][..., :n], fresh["codes"]), n
+        assert torch.equal(tb["offsets"][:, :, :, :nj], fresh["offsets"]), n
+        r1 = lsh.decode_attention(q, ck, cv, W, tb, cfg.K, cfg.L, cfg.T, sm_scale=cfg.scale)
+        r2 = lsh.decode_attention(q, keys[:, :, :n].contiguous(), vals[:, :, :n].contiguous(), W, fresh, cfg.K,
+                                  cfg.L, cfg.T, sm_scale=cfg.scale)
+        torch.cuda.synchronize()
+        for k in ("out", "lse", "nsel"):
+            assert torch.equal(r1[k], r2[k]), (n, k)
+        say(f"[{cfg.name}] n={n} tables and decode equal a fresh build")
+
+
 def test_ragged_insert():
     # per-sequence lengths far apart, so the bounds do not settle the choice
     # and each sequence takes it: in one call some insert (1 and 256 keys),
