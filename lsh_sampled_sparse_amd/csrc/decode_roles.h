@@ -379,8 +379,11 @@ __device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned 
   // segment of bucket qcode_l inside this chunk, in blocks, for table l = tid
   int nblk = 0;
   if (tid < p.L && clen > 0) {
-    const int qc = p.qcodes[static_cast<size_t>(bh) * p.L + tid];
-    LSH_PCHECK(p, qc < nb, kChkQueryCode);
+    // (the query hash writes codes below 2^K; the mask keeps any other value
+    // inside the chunk's bucket starts, and the checked build reports it)
+    const int qraw = p.qcodes[static_cast<size_t>(bh) * p.L + tid];
+    LSH_PCHECK(p, qraw < nb, kChkQueryCode);
+    const int qc = qraw & (nb - 1);
     const size_t row = static_cast<size_t>(u) * p.L + tid;
     const uint16_t* op = p.offsets + (row * p.nJP + J) * nb + qc;
     LSH_PCHECK(p, static_cast<int>(op[0]) <= (qc + 1 < nb ? static_cast<int>(op[1]) : clen) &&
@@ -626,7 +629,26 @@ __device__ inline void fold_heads(const FusedParams& p, int bh0, int f, int F, u
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   __syncthreads();
   LSH_STAMP(p, 8);
-  // column block 0's first batch of slot values
+  // the max / sum of every (head, slot) pair (nh * np <= kMergeMaxPairs = 8
+  // per thread) and the first batch of the heads' chunk selection counts go
+  // out first, loaded by the threads that hold them; then column block 0's
+  // first batch of slot values.  The max / sum and counts are then waited for
+  // alone (loads complete in order), and the slot values stay in flight
+  // through the barrier and the weights below, until the sums need them
+  static_assert(kMergeMaxPairs <= 8 * kFusedThreads, "one batch of max / sum loads");
+  float2 ml[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int i = tid + q * kFusedThreads;
+    const float* ps = p.partials + (static_cast<size_t>(bh0 + f + F * (i / np)) * np + i % np) * kPartialStride;
+    ml[q] = i < nh * np ? *reinterpret_cast<const float2*>(ps + kHeadDim) : make_float2(0.f, 0.f);
+  }
+  int cv[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int i = tid + q * kFusedThreads;
+    cv[q] = i < nh * p.nJ ? p.chunk_nsel[static_cast<size_t>(bh0 + f + F * (i / p.nJ)) * p.nJ + i % p.nJ] : 0;
+  }
   const int c0 = R > 1 ? tid % C : tid;
   const int r0 = R > 1 ? tid / C : 0;
   const bool live0 = c0 < C && r0 < R;
@@ -637,27 +659,21 @@ __device__ inline void fold_heads(const FusedParams& p, int bh0, int f, int F, u
   float4 x[kFoldRows];
 #pragma unroll
   for (int i = 0; i < kFoldRows; ++i) x[i] = base0[static_cast<size_t>(min(r0 + i * R, np - 1)) * kRowQ];
-  // max / sum of every (head, slot) pair and the heads' chunk selection
-  // counts: loads with clamped indices issue together, eight per thread at a time
-  for (int i0 = 0; i0 < nh * np; i0 += 8 * kFusedThreads) {
-    float2 ml[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int i = min(i0 + tid + q * kFusedThreads, nh * np - 1);
-      const float* ps = p.partials + (static_cast<size_t>(bh0 + f + F * (i / np)) * np + i % np) * kPartialStride;
-      ml[q] = *reinterpret_cast<const float2*>(ps + kHeadDim);
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int i = i0 + tid + q * kFusedThreads;
-      if (i < nh * np) {
-        s.m[i] = ml[q].x;
-        s.l[i] = ml[q].y;
-      }
+  for (int q = 0; q < 8; ++q) {
+    const int i = tid + q * kFusedThreads;
+    if (i < nh * np) {
+      s.m[i] = ml[q].x;
+      s.l[i] = ml[q].y;
     }
   }
-  for (int i0 = 0; i0 < nh * p.nJ; i0 += 8 * kFusedThreads) {
-    int cv[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int i = tid + q * kFusedThreads;
+    if (i < nh * p.nJ) atomicAdd(&s.nsel[i / p.nJ], cv[q]);
+  }
+  // the rest of the counts (more than 2048 (head, chunk) pairs)
+  for (int i0 = 8 * kFusedThreads; i0 < nh * p.nJ; i0 += 8 * kFusedThreads) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int i = min(i0 + tid + q * kFusedThreads, nh * p.nJ - 1);
