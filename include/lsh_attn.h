@@ -168,7 +168,13 @@ lsh_status lsh_build_tables(const void* keys, const void* W,
  * sequence has the chunks from the one holding key old_b to the one holding
  * key new_b - 1 rebuilt from their keys.  The scalars bound the arrays:
  * n_old <= old_b <= new_b <= n_new, with device values clamped into that
- * range (the launch covers the chunks of keys n_old .. n_new - 1).  0 <= n_old <= n_new <= n_cap and
+ * range (the launch covers the chunks of keys n_old .. n_new - 1).  Each
+ * sequence's choice is taken on the device from its own lengths; the host
+ * leaves the rebuild kernels out only when the bounds settle it for every
+ * sequence (0 < n_old, n_new - n_old <= 256), so a step captured in a graph
+ * with bounds that close runs the insertion alone, and one with wider bounds
+ * also launches the rebuild kernels, whose workgroups then return at once
+ * for the sequences that insert.  0 <= n_old <= n_new <= n_cap and
  * w_per_head in {0, 1}, else LSH_ERR_INVALID_ARG; n_old == n_new launches
  * nothing.  Size limits as for lsh_build_tables with N = n_cap.
  * lsh_build_tables(.., N, ..) is this call with n_old = 0, n_new = n_cap = N,
