@@ -604,7 +604,7 @@ def main():
         del cgraphs
         log(f"centred plant: {cms:.4f} ms, selected {centred['selected_frac_of_keys']}")
 
-    decode_hybrid_steady = append_decode = None
+    decode_hybrid_steady = append_decode = decode_per_head_w = decode_ragged = None
     if full:
         # the hybrid decode: the exact sink + window set runs as extra
         # attention workgroups, the selection leaves those keys out
@@ -620,6 +620,47 @@ def main():
             "exact_kv_bytes": int(B * Hkv * n_exact * 2 * d * esz),
             "kernels": {k: v["avg_us"] for k, v in hk.items()},
         }
+
+        # one SimHash projection per kv head (W [Hkv, d, L*K]): tables built
+        # with kv head g's W[g], query head h hashed with W[h / G]
+        c0 = copies[0]
+        Wh = workloads.per_head_projections(cfg, seed=cfg.seed + 1000, device=dev).contiguous()
+        aux_off, aux_idx = torch.empty_like(c0["offsets"]), torch.empty_like(c0["indices"])
+        lsh.lsh_update_tables(c0["keys"], Wh, K, L, stride, 0, N, aux_off, aux_idx, None, c0["bws"])
+
+        def decode_ph(c):
+            lsh.lsh_decode_attention_cached(c0["q"], c0["keys"], c0["values"], Wh, aux_idx, aux_off, N, K, L, T,
+                                            stride, cfg.scale, 0, 0, c0["out"], c0["lse"], c0["nsel"], None, None,
+                                            c0["dws"])
+        decode_ph(c0)
+        ptimes = kernel_times(decode_ph, args.steps)
+        ph_ms = sum(ptimes[k][0] for k in DECODE_KERNELS) / args.steps
+        decode_per_head_w = {"kernel_sum_ms": round(ph_ms, 5), "qh_per_s": round(qh / (ph_ms * 1e-3), 1),
+                             "kernels": {k: v["avg_us"] for k, v in kernel_table(ptimes, {}).items()}}
+
+        # ragged lengths (batches only): sequence b holds N - (b mod 4) N / 8
+        # keys, its tables built over those keys (per-sequence lengths on the
+        # device), and the decode attends each sequence's own keys
+        if B > 1:
+            lens = [N - (b % 4) * (N // 8) for b in range(B)]
+            lens_t = torch.tensor(lens, dtype=torch.int32, device=dev)
+            zeros_t = torch.zeros_like(lens_t)
+            lsh.lsh_update_tables(c0["keys"], c0["W"], K, L, stride, 0, N, aux_off, aux_idx, None, c0["bws"],
+                                  old_lens=zeros_t, new_lens=lens_t)
+
+            def decode_rg(c):
+                lsh.lsh_decode_attention_cached(c0["q"], c0["keys"], c0["values"], c0["W"], aux_idx, aux_off, N, K,
+                                                L, T, stride, cfg.scale, 0, 0, c0["out"], c0["lse"], c0["nsel"],
+                                                None, None, c0["dws"], seq_lens=lens_t)
+            decode_rg(c0)
+            rtimes = kernel_times(decode_rg, args.steps)
+            rg_ms = sum(rtimes[k][0] for k in DECODE_KERNELS) / args.steps
+            decode_ragged = {"lens": sorted(set(lens), reverse=True), "kernel_sum_ms": round(rg_ms, 5),
+                             "qh_per_s": round(qh / (rg_ms * 1e-3), 1),
+                             "keys_per_s": round(sum(lens) * Hkv / (rg_ms * 1e-3), 1),
+                             "kernels": {k: v["avg_us"] for k, v in kernel_table(rtimes, {}).items()}}
+        del aux_off, aux_idx
+        torch.cuda.synchronize()
 
         # multi-step decode over a growing cache: each step appends one key
         # (inserted into the chunk it falls into) and runs the hybrid decode
@@ -688,6 +729,8 @@ def main():
             "centred_plant": centred,
             "decode_hybrid_steady": decode_hybrid_steady,
             "append_decode_steady": append_decode,
+            "decode_per_head_w": decode_per_head_w,
+            "decode_ragged": decode_ragged,
         },
     }
 
