@@ -97,26 +97,44 @@ __global__ __launch_bounds__(256) void qhash_kernel(const typename T::storage* _
     if (lane == 0) lnu_samples[j] = g;
     return;
   }
-  // a workgroup hashes hpb heads: 16 with one shared W, or the G heads of
-  // one (sequence, kv head) with a W per kv head
-  const int hpb = w_head_stride ? G : kQHeads;
-  const int h0 = blockIdx.y * hpb;
+  // a workgroup hashes up to 16 heads: 16 consecutive ones with one shared
+  // W; with a W per kv head, the G heads of kv head g in each of 16 / G
+  // consecutive sequences (they all hash with W[g]).  head_of(hh) is the
+  // head of slot hh, or -1
+  int Hq = 0, Bq = 0, spb = 0, gw = 0, b0 = 0;         // per-head W: the workgroup's kv head and sequences
+  if (w_head_stride) {
+    Hq = G * Hkv;
+    Bq = BH / Hq;
+    spb = kQHeads / G;
+    const int nbb = (Bq + spb - 1) / spb;
+    gw = static_cast<int>(blockIdx.y) / nbb;
+    b0 = (static_cast<int>(blockIdx.y) % nbb) * spb;
+  }
+  auto head_of = [&](int hh) {
+    if (!w_head_stride) {
+      const int h = static_cast<int>(blockIdx.y) * kQHeads + hh;
+      return hh < kQHeads && h < BH ? h : -1;
+    }
+    const int b = b0 + hh / G;
+    return hh < spb * G && b < Bq ? b * Hq + gw * G + hh % G : -1;
+  };
   if (K == 0) {
-    for (int e = blockIdx.x * 256 + tid; e < hpb * L; e += gridDim.x * 256) {
-      const int h = h0 + e / L;
-      if (h < BH) qcodes[static_cast<size_t>(h) * L + e % L] = 0;
+    for (int e = blockIdx.x * 256 + tid; e < kQHeads * L; e += gridDim.x * 256) {
+      const int h = head_of(e / L);
+      if (h >= 0) qcodes[static_cast<size_t>(h) * L + e % L] = 0;
     }
     return;
   }
-  W += static_cast<size_t>((h0 / G) % Hkv) * w_head_stride;
+  W += static_cast<size_t>(gw) * w_head_stride;
   const int tpw = 64 / K;               // whole tables per workgroup
   const int l0 = blockIdx.x * tpw;
   {
     // 16 heads x 128 dims: thread t takes 8 consecutive dims of head t / 16
     // in one (bf16) or two (fp32) 16-byte loads
     const int hh = tid >> 4, c8 = (tid & 15) * 8;
-    const bool okh = hh < hpb && h0 + hh < BH;
-    const typename T::storage* src = q + static_cast<size_t>(okh ? h0 + hh : 0) * kHeadDim + c8;
+    const int hq = head_of(hh);
+    const bool okh = hq >= 0;
+    const typename T::storage* src = q + static_cast<size_t>(okh ? hq : 0) * kHeadDim + c8;
     float v[8];
     if constexpr (sizeof(typename T::storage) == 2) {
       const u32x4_t w4 = *reinterpret_cast<const u32x4_t*>(src);
@@ -172,8 +190,8 @@ __global__ __launch_bounds__(256) void qhash_kernel(const typename T::storage* _
   __syncthreads();
   for (int e = tid; e < kQHeads * tpw; e += 256) {
     const int hh = e / tpw, t = e % tpw;
-    const int l = l0 + t, h = h0 + hh;
-    if (hh < hpb && h < BH && l < L) {
+    const int l = l0 + t, h = head_of(hh);
+    if (h >= 0 && l < L) {
       uint32_t code = 0;
       for (int b = 0; b < K; ++b) code |= static_cast<uint32_t>(sgn[hh][t * K + b]) << b;
       qcodes[static_cast<size_t>(h) * L + l] = static_cast<uint16_t>(code);
@@ -462,8 +480,10 @@ static hipError_t launch_qhash(const DecodeArgs& a, int nsync, int kid, hipStrea
   using S = typename T::storage;
   const int BH = a.B * a.Hq;
   const int G = a.Hq / a.Hkv;
-  const int hpb = a.w_heads > 1 ? G : kQHeads;          // heads per qhash workgroup
-  const int head_blocks = (BH + hpb - 1) / hpb;
+  // workgroups of heads: 16 consecutive heads each with one W; with a W per
+  // kv head, one per (kv head, 16 / G consecutive sequences)
+  const int spb = kQHeads / G;
+  const int head_blocks = a.w_heads > 1 ? a.Hkv * ((a.B + spb - 1) / spb) : (BH + kQHeads - 1) / kQHeads;
   const size_t w_head_stride = a.w_heads > 1 ? static_cast<size_t>(kHeadDim) * a.L * a.K : 0;
   const int tpw = a.K > 0 ? 64 / a.K : 256;
   const int xblocks = (a.L + tpw - 1) / tpw;
