@@ -476,7 +476,8 @@ __global__ __launch_bounds__(kFusedThreads, 2) void decode_bf16_kernel(FusedPara
   __shared__ __attribute__((aligned(16))) unsigned char smem[kFusedLdsBytes];
   const DecodeRole r = decode_role(p, blockIdx.x);
   if (r.count) {
-    count_role(p, r.J, r.bh, smem);
+    if (p.count_heads > 1) count_role_heads(p, r.J, r.bh, smem);
+    else count_role(p, r.J, r.bh, smem);
     return;
   }
   attend_bf16_role<GW>(p, r.slot, r.u, smem);

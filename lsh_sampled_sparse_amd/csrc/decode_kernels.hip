@@ -464,7 +464,8 @@ __global__ __launch_bounds__(kFusedThreads) void decode_f32_kernel(FusedParams p
   __shared__ __attribute__((aligned(16))) unsigned char smem[cmax(sizeof(AttendF32Lds<GM>), kRolesLdsBytes)];
   const DecodeRole r = decode_role(p, blockIdx.x);
   if (r.count) {
-    count_role(p, r.J, r.bh, smem);
+    if (p.count_heads > 1) count_role_heads(p, r.J, r.bh, smem);
+    else count_role(p, r.J, r.bh, smem);
     return;
   }
   attend_f32_role<GM>(p, r.slot, r.u, smem);
@@ -547,7 +548,19 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   // counters: ready [U][nJ], arrive_unit [U]
   p.ready = a.sync;
   p.arrive_unit = p.ready + U * a.nJ;
-  p.n_count_wg = BH * a.nJ;
+  // count workgroups cover count_heads query heads of one unit (a divisor
+  // of G): the fewest that fit one round of resident workgroups, within the
+  // LDS for the heads' byte counters and segments
+  int hc = 1;
+  while (BH / hc * a.nJ > kResidentWG) {
+    int nx = hc + 1;
+    while (nx <= p.G && p.G % nx != 0) ++nx;
+    if (nx > p.G || nx * a.L > kCountSegs || (nx << a.stride_log2) > kCountCounterBytes) break;
+    hc = nx;
+  }
+  if (a.L > kCountSegs || (1 << a.stride_log2) > kCountCounterBytes) return hipErrorInvalidValue;
+  p.count_heads = hc;
+  p.n_count_wg = BH / hc * a.nJ;
   p.n_exact_wg = U * a.nexact;
   p.n_attend_wg = U * a.nsplit;
   // a fold keeps the (head, slot) pairs of its heads in LDS

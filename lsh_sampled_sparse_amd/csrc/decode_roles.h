@@ -130,10 +130,10 @@ __device__ __forceinline__ int arrive(int32_t* ctr, int* val_lds) {
 
 // This workgroup's stores are complete; thread 0 then adds 1 to *ctr
 // without waiting for the add to return (a workgroup that only signals).
-__device__ __forceinline__ void signal(int32_t* ctr) {
+__device__ __forceinline__ void signal(int32_t* ctr, int add = 1) {
   wait_vmem();
   __syncthreads();
-  if (threadIdx.x == 0) (void)__hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) (void)__hip_atomic_fetch_add(ctr, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // --------------------------------------------------------------------------
@@ -163,6 +163,7 @@ struct FusedParams {
   int npart;
   int n_count_wg, n_exact_wg, n_attend_wg;
   int unit_group;              // units whose splits are dispatched interleaved (decode_role)
+  int count_heads;             // query heads of one unit per count workgroup (divides G)
   float scale;
 #ifdef LSH_TRACE
   unsigned long long* trace;   // [grid][16] phase timestamps (trace builds only)
@@ -190,7 +191,8 @@ struct FusedParams {
 __host__ __device__ inline int fused_sync_words(int U, int nJ) { return U * nJ + U; }
 
 // What workgroup `wid` of the decode launch does.  The grid holds every
-// count workgroup first (chunk by chunk, one per query head), then the
+// count workgroup first (chunk by chunk, one per count_heads query heads of
+// a unit), then the
 // attention workgroups of the units, a group of R units at a time
 // (R = unit_group): within a group, the context splits of its units, split
 // 0 of every unit of the group, then split 1, and so on, then the exact-set
@@ -219,12 +221,12 @@ struct DecodeRole {
 
 __device__ inline DecodeRole decode_role(const FusedParams& p, int wid) {
   DecodeRole r;
-  const int BH = p.B * p.Hq;
+  const int HB = p.B * p.Hq / p.count_heads;                 // count workgroups per chunk
   r.count = wid < p.n_count_wg;
-  r.J = wid / BH;
-  r.bh = wid % BH;
+  r.J = wid / HB;
+  r.bh = (wid % HB) * p.count_heads;                         // the first of its count_heads heads
   if (r.count) {
-    r.u = r.bh / p.G;   // the head's unit (bh / G = b * Hkv + h / G)
+    r.u = r.bh / p.G;   // the heads' unit (bh / G = b * Hkv + h / G)
     r.slot = 0;
     return r;
   }
@@ -345,18 +347,28 @@ constexpr int kCountInflight = 16;
 
 constexpr int kSegMapRows = 512;   // walks of up to 512 x 64 blocks use the segment map
 
+// A count workgroup walks the segments of count_heads (hc) query heads of one
+// unit: segment hh * L + l is head hh's bucket in table l.
+constexpr int kCountSegs = 1024;                 // hc * L <= kCountSegs
+constexpr int kCountCounterBytes = 32 << 10;     // byte counters: hc << stride_log2 <= this
+constexpr int kSegsPerThread = kCountSegs / kFusedThreads;
+constexpr int kCountRankShift = 21;              // scan word: blocks (low 21 bits), non-empty rank (high 11)
+
 struct CountLds {                  // laid out after the byte counters
-  long long fb[256];               // first block of each table's segment
+  long long fb[kCountSegs];        // first block of each segment
   uint64_t starts[kSegMapRows];    // segment map: bit v & 63 of row v >> 6 marks a segment's first block
   int pre[kSegMapRows + 1];        // segment map: set bits in the rows before each row
-  short lo[256], hi[256];          // segment [lo, hi) in entries from 8 * fb
-  int segv[257];                   // exclusive scan of block counts
-  uint8_t seglist[256];            // segment map: the non-empty tables, in order
+  short lo[kCountSegs], hi[kCountSegs];   // segment [lo, hi) in entries from 8 * fb
+  int segv[kCountSegs + 1];        // exclusive scan of block counts
+  uint16_t seglist[kCountSegs];    // segment map: the non-empty segments, in order
+  uint8_t head[kCountSegs];        // the segment's head (0 .. hc - 1)
   uint32_t spare[64];              // trace builds: keeps the traced loads alive
-  uint32_t wtot[kFusedThreads / 64];
+  uint32_t wtot[kSegsPerThread][kFusedThreads / 64];   // scan: per row of segments and wave
+  int hsel[16][kFusedThreads / 64];   // selected keys per head and wave
   int flag;
 };
 
+// One query head per workgroup: thread l takes table l (L <= 255).
 __device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned char* smem) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = bh / p.Hq, h = bh % p.Hq;
@@ -409,11 +421,11 @@ __device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned 
     const uint32_t v = __shfl_up(incl, o);
     if (lane >= o) incl += v;
   }
-  if (lane == 63) s.wtot[wave] = incl;
+  if (lane == 63) s.wtot[0][wave] = incl;
   __syncthreads();
   {
     uint32_t wbase = 0;
-    for (int w = 0; w < wave; ++w) wbase += s.wtot[w];
+    for (int w = 0; w < wave; ++w) wbase += s.wtot[0][w];
     incl += wbase;
     s.segv[tid + 1] = static_cast<int>(incl & 0xffffffu);
     if (tid == 0) s.segv[0] = 0;
@@ -445,10 +457,10 @@ __device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned 
       const int v = __shfl_up(x, o);
       if (lane >= o) x += v;
     }
-    if (lane == 63) s.wtot[wave] = static_cast<uint32_t>(x);
+    if (lane == 63) s.wtot[0][wave] = static_cast<uint32_t>(x);
     __syncthreads();
     int wb = 0;
-    for (int w = 0; w < wave; ++w) wb += static_cast<int>(s.wtot[w]);
+    for (int w = 0; w < wave; ++w) wb += static_cast<int>(s.wtot[0][w]);
     x += wb;
     if (r0 < nrows) s.pre[r0] = x - c0 - c1;
     if (r0 + 1 < nrows) s.pre[r0 + 1] = x - c1;
@@ -569,15 +581,289 @@ __device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned 
     for (int i = tid; i < cfull; i += kFusedThreads) dst[i] = c8[i];
   }
   mysel = wave_sum_int(mysel);
-  if (lane == 0) s.wtot[wave] = mysel;
+  if (lane == 0) s.wtot[0][wave] = mysel;
   __syncthreads();
   if (tid == 0) {
     int t = 0;
-    for (int w = 0; w < kW; ++w) t += s.wtot[w];
+    for (int w = 0; w < kW; ++w) t += s.wtot[0][w];
     st_agent(p.chunk_nsel + static_cast<size_t>(bh) * p.nJ + J, t);
   }
   LSH_STAMP(p, 3);
   signal(p.ready + u * p.nJ + J);
+}
+
+// Several query heads of one unit per workgroup (count_heads > 1): segment
+// hh * L + l, of up to kCountSegs, is head hh's bucket in table l; the heads
+// keep their own byte counters and bitmask words.
+__device__ inline void count_role_heads(const FusedParams& p, int J, int bh0, unsigned char* smem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hc = p.count_heads;
+  const int S = hc * p.L;                                                // segments
+  const int b = bh0 / p.Hq, h0 = bh0 % p.Hq;
+  const int u = b * p.Hkv + h0 / p.G;
+  const int nb = 1 << p.K;
+  const int sl = p.stride_log2;
+  const int cbeg = J << sl;
+  const int cwp = 1 << (sl - 2);                                         // counter words per head
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(smem);                     // [hc][cwp]: one byte per key of the chunk
+  CountLds& s = *reinterpret_cast<CountLds*>(smem + (static_cast<size_t>(hc) << sl));
+  const int Nb = seq_len_of(p.seq_lens, b, p.N);
+  const int cfull = min(1 << sl, p.N - cbeg);
+  const int clen = max(0, min(1 << sl, Nb - cbeg));
+  const int cwords = (cfull + 3) >> 2;
+  int exact_head, exact_tail;
+  exact_range(p.n_sink, p.n_window, Nb, exact_head, exact_tail);
+
+  LSH_STAMP(p, 0);
+  for (int i = tid; i < hc * cwp; i += kFusedThreads) cnt[i] = 0;
+
+  // the segment of head hh's bucket in table l inside this chunk, in blocks:
+  // thread t takes segment t of each row of 256 (with one head, thread l
+  // takes table l); the query codes, then the bucket bounds, each set of
+  // loads in flight together
+  int qraw[kSegsPerThread];
+#pragma unroll
+  for (int k = 0; k < kSegsPerThread; ++k) {
+    const int sg = tid + k * kFusedThreads;
+    qraw[k] = 0;
+    if (sg < S && clen > 0) qraw[k] = p.qcodes[static_cast<size_t>(bh0 + sg / p.L) * p.L + sg % p.L];
+  }
+  uint32_t own[kSegsPerThread];
+#pragma unroll
+  for (int k = 0; k < kSegsPerThread; ++k) {
+    const int sg = tid + k * kFusedThreads;
+    int nblk = 0;
+    if (sg < S && clen > 0) {
+      const int l = sg % p.L;
+      // (the query hash writes codes below 2^K; the mask keeps any other value
+      // inside the chunk's bucket starts, and the checked build reports it)
+      LSH_PCHECK(p, qraw[k] < nb, kChkQueryCode);
+      const int qc = qraw[k] & (nb - 1);
+      const size_t row = static_cast<size_t>(u) * p.L + l;
+      const uint16_t* op = p.offsets + (row * p.nJP + J) * nb + qc;
+      LSH_PCHECK(p, static_cast<int>(op[0]) <= (qc + 1 < nb ? static_cast<int>(op[1]) : clen) &&
+                        (qc + 1 < nb ? static_cast<int>(op[1]) : static_cast<int>(op[0])) <= clen,
+                 kChkSegment);
+      // clamped into the chunk: tables of another stride cannot send the walk out of it
+      const int s0 = min(static_cast<int>(op[0]), clen);
+      const int e0 = qc + 1 < nb ? min(static_cast<int>(op[1]), clen) : clen;
+      const size_t first = row * p.P + cbeg + s0;      // element index of the segment's first entry
+      const int lo = static_cast<int>(first & 7);
+      const int len = max(e0 - s0, 0);
+      nblk = len > 0 ? (lo + len + 7) >> 3 : 0;
+      s.fb[sg] = static_cast<long long>(first >> 3);
+      s.lo[sg] = static_cast<short>(lo);
+      s.hi[sg] = static_cast<short>(lo + len);
+      s.head[sg] = static_cast<uint8_t>(sg / p.L);
+    }
+    // scan word: the block count, and 1 in the rank field when non-empty
+    own[k] = static_cast<uint32_t>(nblk) + (nblk > 0 ? (1u << kCountRankShift) : 0u);
+  }
+  // one scan per row of 256 segments gives the block offsets and the rank of
+  // each non-empty segment among them; the rows follow each other
+  const int rows = (S + kFusedThreads - 1) / kFusedThreads;   // rows holding segments (one with one head)
+  uint32_t incl[kSegsPerThread];
+#pragma unroll
+  for (int k = 0; k < kSegsPerThread; ++k) incl[k] = own[k];
+#pragma unroll
+  for (int k = 0; k < kSegsPerThread; ++k) {
+    if (k < rows) {
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_up(incl[k], o);
+        if (lane >= o) incl[k] += v;
+      }
+      if (lane == 63) s.wtot[k][wave] = incl[k];
+    }
+  }
+  __syncthreads();
+  {
+    constexpr uint32_t kBlocks = (1u << kCountRankShift) - 1u;
+    uint32_t row_base = 0;                           // segments of the rows before
+#pragma unroll
+    for (int k = 0; k < kSegsPerThread; ++k) {
+      if (k >= rows) break;
+      uint32_t before = 0, row_tot = 0;
+      for (int w = 0; w < kFusedThreads / 64; ++w) {
+        if (w < wave) before += s.wtot[k][w];
+        row_tot += s.wtot[k][w];
+      }
+      const int sg = tid + k * kFusedThreads;
+      const uint32_t x = row_base + before + incl[k] - own[k];   // exclusive, at segment sg
+      if (sg < S) s.segv[sg] = static_cast<int>(x & kBlocks);
+      if (sg < S && (own[k] & kBlocks) > 0) s.seglist[x >> kCountRankShift] = static_cast<uint16_t>(sg);
+      row_base += row_tot;
+    }
+    if (tid == 0) s.segv[S] = static_cast<int>(row_base & kBlocks);
+  }
+  __syncthreads();
+  LSH_STAMP(p, 1);
+
+  const int total = s.segv[S];
+  // segment map (walks of at most kSegMapRows rows of 64 blocks): the
+  // segment of block v is seglist[(set bits of starts before v) - 1]
+  const int nrows = (total + 63) >> 6;
+  const bool mapped = nrows <= kSegMapRows;
+  if (mapped) {
+    for (int r = tid; r < nrows; r += kFusedThreads) s.starts[r] = 0ull;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kSegsPerThread; ++k) {
+      const int sg = tid + k * kFusedThreads;
+      if (sg < S && (own[k] & ((1u << kCountRankShift) - 1u)) > 0) {
+        const int v = s.segv[sg];
+        atomicOr(reinterpret_cast<unsigned long long*>(&s.starts[v >> 6]), 1ull << (v & 63));
+      }
+    }
+    __syncthreads();
+    // exclusive scan of the rows' bit counts (two rows per thread)
+    const int r0 = 2 * tid;
+    const int c0 = r0 < nrows ? __popcll(s.starts[r0]) : 0;
+    const int c1 = r0 + 1 < nrows ? __popcll(s.starts[r0 + 1]) : 0;
+    int x = c0 + c1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(x, o);
+      if (lane >= o) x += v;
+    }
+    if (lane == 63) s.wtot[0][wave] = static_cast<uint32_t>(x);
+    __syncthreads();
+    int wb = 0;
+    for (int w = 0; w < wave; ++w) wb += static_cast<int>(s.wtot[0][w]);
+    x += wb;
+    if (r0 < nrows) s.pre[r0] = x - c0 - c1;
+    if (r0 + 1 < nrows) s.pre[r0 + 1] = x - c1;
+    __syncthreads();
+  }
+  constexpr int kW = kFusedThreads / 64;
+  const int per = ((total + kW - 1) / kW + 63) & ~63;
+  const int wstart = wave * per, wend = min(total, wstart + per);
+  const u32x4_t* ib = reinterpret_cast<const u32x4_t*>(p.indices);
+  LSH_STAMP(p, 4);
+  for (int w0 = wstart; w0 < wend; w0 += 64 * kCountInflight) {
+    const int v0 = w0 + lane;
+    // rows of 64 blocks this wave still has (wave-uniform): the unrolled
+    // steps below skip the others, so short walks cost little
+    const int nk = min(kCountInflight, (wend - w0 + 63) >> 6);
+    u32x4_t blk[kCountInflight];
+    int lo[kCountInflight], hi[kCountInflight], cb[kCountInflight];
+    // the segment of each block (past the wave's range: of its last block):
+    // from the segment map, or else by binary searches over the scan
+    int sg[kCountInflight];
+    if (mapped) {
+#pragma unroll
+      for (int k = 0; k < kCountInflight; ++k) {
+        if (k < nk) {
+          const int v = min(v0 + 64 * k, wend - 1);
+          const uint64_t below = s.starts[v >> 6] & ((2ull << (v & 63)) - 1ull);
+          sg[k] = s.seglist[s.pre[v >> 6] + __popcll(below) - 1];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kCountInflight; ++k) sg[k] = 0;
+#pragma unroll
+      for (int step = kCountSegs / 2; step > 0; step >>= 1) {
+        int sv[kCountInflight];
+#pragma unroll
+        for (int k = 0; k < kCountInflight; ++k)
+          if (k < nk) sv[k] = s.segv[min(sg[k] + step, S)];
+#pragma unroll
+        for (int k = 0; k < kCountInflight; ++k) {
+          const int c = sg[k] + step;
+          if (k < nk) sg[k] = (c < S && sv[k] <= min(v0 + 64 * k, wend - 1)) ? c : sg[k];
+        }
+      }
+    }
+    if (w0 == wstart) LSH_STAMP(p, 5);
+    // blocks past the wave's range load its last block again and take no entry
+#pragma unroll
+    for (int k = 0; k < kCountInflight; ++k) {
+      if (k < nk) {
+        const int v = v0 + 64 * k;
+        const bool in = v < wend;
+        const int l = sg[k];
+        const int i = min(v, wend - 1) - s.segv[l];
+        blk[k] = ib[s.fb[l] + i];
+        lo[k] = in ? s.lo[l] - 8 * i : 8;
+        hi[k] = in ? s.hi[l] - 8 * i : 0;
+        cb[k] = s.head[l] * cwp;                   // the segment's head's counters
+      }
+    }
+#ifdef LSH_TRACE
+    if (w0 == wstart) {   // trace builds: the first row's blocks have arrived
+      uint32_t z = 0;
+#pragma unroll
+      for (int k = 0; k < kCountInflight; ++k)
+        if (k < nk) z ^= blk[k][0];
+      if (z == 0x9e3779b9u) s.spare[lane] = z;
+      LSH_STAMP(p, 6);
+    }
+#endif
+    // one LDS add per entry, without branches.  A key is masked into the
+    // chunk's range (the counter array holds one byte per position of a full
+    // chunk), so no access can leave the array whatever the table holds; an
+    // entry outside its segment adds 0.  Keys past the chunk's length (in a
+    // table of another layout) count positions the selection never reads.
+    const uint32_t kmask = (1u << sl) - 1u;
+#pragma unroll
+    for (int k = 0; k < kCountInflight; ++k) {
+      if (k < nk) {
+        const uint32_t inseg = (0xffu << max(lo[k], 0)) & (0xffu >> (8 - min(max(hi[k], 0), 8)));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          LSH_PCHECK(p, !((inseg >> e) & 1u) || ((blk[k][e >> 1] >> (16 * (e & 1))) & 0xffffu) <
+                            static_cast<uint32_t>(clen), kChkEntry);
+          const uint32_t key = (blk[k][e >> 1] >> (16 * (e & 1))) & kmask;
+          const uint32_t inc = ((inseg >> e) & 1u) << ((key & 3u) * 8u);
+          __hip_atomic_fetch_add(&cnt[cb[k] + (key >> 2)], inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      }
+    }
+  }
+  LSH_STAMP(p, 7);
+  __syncthreads();
+  LSH_STAMP(p, 2);
+
+  const int Nw = (p.N + 31) >> 5;
+  const int nwords = (cfull + 31) >> 5;
+  for (int hh = 0; hh < hc; ++hh) {
+    const uint32_t* ch = cnt + hh * cwp;
+    const int bh = bh0 + hh;
+    int mysel = 0;
+    for (int w = tid; w < nwords; w += kFusedThreads) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int wi = w * 8 + j;
+        const uint32_t c4 = wi < cwords ? ch[wi] : 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int key = w * 32 + j * 4 + k;
+          const int n = cbeg + key;
+          const bool ex = n < exact_head || n >= Nb - exact_tail;
+          if (key < clen && !ex && static_cast<int>((c4 >> (8 * k)) & 0xffu) >= p.T) m |= 1u << (j * 4 + k);
+        }
+      }
+      st_agent(p.bitmask + static_cast<size_t>(bh) * Nw + (cbeg >> 5) + w, m);
+      mysel += __builtin_popcount(m);
+    }
+    if (p.counts) {
+      const uint8_t* c8 = reinterpret_cast<const uint8_t*>(ch);
+      uint8_t* dst = p.counts + static_cast<size_t>(bh) * p.N + cbeg;
+      for (int i = tid; i < cfull; i += kFusedThreads) dst[i] = c8[i];
+    }
+    mysel = wave_sum_int(mysel);
+    if (lane == 0) s.hsel[hh][wave] = mysel;
+  }
+  __syncthreads();
+  if (tid < hc) {
+    int t = 0;
+    for (int w = 0; w < kW; ++w) t += s.hsel[tid][w];
+    st_agent(p.chunk_nsel + static_cast<size_t>(bh0 + tid) * p.nJ + J, t);
+  }
+  LSH_STAMP(p, 3);
+  signal(p.ready + u * p.nJ + J, hc);
 }
 
 // --------------------------------------------------------------------------
@@ -810,6 +1096,6 @@ __device__ inline void finish_slot(const FusedParams& p, int u, int slot, unsign
 
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 // LDS the count and merge roles use (the attention roles add theirs)
-constexpr size_t kRolesLdsBytes = cmax((static_cast<size_t>(1) << 13) + sizeof(CountLds), sizeof(MergeLds));
+constexpr size_t kRolesLdsBytes = cmax(static_cast<size_t>(kCountCounterBytes) + sizeof(CountLds), sizeof(MergeLds));
 
 }  // namespace lsh

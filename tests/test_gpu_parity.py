@@ -242,13 +242,20 @@ def test_hybrid_parity(cfg, n_sink, n_window, stride):
     check_case(cfg, data, stride=stride, n_sink=n_sink, n_window=n_window)
 
 
-# more count workgroups (query heads x key chunks) than one round of resident
-# workgroups (512): counting takes several rounds before attention starts
+# more (query head, key chunk) pairs than one round of resident workgroups
+# (512): a count workgroup then takes several heads of one unit (2, 3 or 4
+# here), or counting takes several rounds
 MANY_ROUNDS = [
     (workloads.Config("rounds-bf16", B=3, Hq=12, Hkv=3, N=6000, d=128, K=8, L=16, T=2, dtype="bf16",
                       planted=4, a=0.8, offset="per_unit", seed=41), 4, 300),
     (workloads.Config("rounds-f32", B=2, Hq=16, Hkv=2, N=4200, d=128, K=7, L=12, T=2, dtype="f32",
                       planted=3, a=0.8, offset="per_head", seed=42), 0, 0),
+    # 1536 (head, chunk) pairs: each count workgroup takes the 4 heads of a unit
+    (workloads.Config("rounds-4heads", B=8, Hq=16, Hkv=4, N=3000, d=128, K=8, L=12, T=2, dtype="bf16",
+                      planted=3, a=0.8, offset="per_head", seed=43), 2, 100),
+    # GQA 3: each count workgroup takes the 3 heads of a unit
+    (workloads.Config("rounds-gqa3", B=4, Hq=12, Hkv=4, N=4000, d=128, K=9, L=10, T=1, dtype="bf16",
+                      planted=3, a=0.8, offset="per_unit", seed=44), 0, 0),
 ]
 
 
