@@ -221,16 +221,35 @@ struct DecodeRole {
 
 __device__ inline DecodeRole decode_role(const FusedParams& p, int wid) {
   DecodeRole r;
-  const int HB = p.B * p.Hq / p.count_heads;                 // count workgroups per chunk
+  const int U = p.B * p.Hkv;
   r.count = wid < p.n_count_wg;
-  r.J = wid / HB;
-  r.bh = (wid % HB) * p.count_heads;                         // the first of its count_heads heads
   if (r.count) {
-    r.u = r.bh / p.G;   // the heads' unit (bh / G = b * Hkv + h / G)
+    // (unit, chunk) pairs in chunk-major order, pair = J * U + u, each with
+    // Gh = G / count_heads workgroups; pairs in blocks of 8 so that workgroup
+    // w of a block runs on XCD w mod 8 with all Gh workgroups of its pair
+    // (the heads of a unit often probe the same bucket, whose entries the
+    // XCD's L2 then serves after the first read), the last P mod 8 pairs
+    // one after another
+    const int Gh = p.G / p.count_heads;
+    const int P8 = (U * p.nJ) & ~7;
+    int pair, s;
+    if (wid < P8 * Gh) {
+      const int y = wid >> 3;
+      pair = (y / Gh) * 8 + (wid & 7);
+      s = y % Gh;
+    } else {
+      const int k = wid - P8 * Gh;
+      pair = P8 + k / Gh;
+      s = k % Gh;
+    }
+    r.J = pair / U;
+    r.u = pair - r.J * U;
+    r.bh = r.u * p.G + s * p.count_heads;                    // the first of its count_heads heads
     r.slot = 0;
     return r;
   }
-  const int U = p.B * p.Hkv;
+  r.J = 0;
+  r.bh = 0;
   const int per_unit = p.nexact + p.nsplit;
   const int k = wid - p.n_count_wg;
   const int grp = k / (p.unit_group * per_unit);            // group of units
