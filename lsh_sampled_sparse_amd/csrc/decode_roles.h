@@ -373,14 +373,22 @@ constexpr int kCountCounterBytes = 32 << 10;     // byte counters: hc << stride_
 constexpr int kSegsPerThread = kCountSegs / kFusedThreads;
 constexpr int kCountRankShift = 21;              // scan word: blocks (low 21 bits), non-empty rank (high 11)
 
-struct CountLds {                  // laid out after the byte counters
-  long long fb[kCountSegs];        // first block of each segment
+// A segment as the walk reads it, one 16-byte LDS read per block: its first
+// block (low 56 bits; its head, 0 .. hc - 1, in the top 8), the exclusive
+// scan of the block counts at it, and its entries [lo, hi) counted from the
+// first block's first entry.
+struct __attribute__((aligned(16))) SegInfo {
+  long long fb;
+  int v;
+  short lo, hi;
+};
+constexpr long long kSegBlockMask = (1ll << 56) - 1;
+
+struct CountLds {                  // laid out after the byte counters (a multiple of 256 bytes)
+  SegInfo seg[kCountSegs + 1];     // the segments; seg[S].v = the total block count
   uint64_t starts[kSegMapRows];    // segment map: bit v & 63 of row v >> 6 marks a segment's first block
   int pre[kSegMapRows + 1];        // segment map: set bits in the rows before each row
-  short lo[kCountSegs], hi[kCountSegs];   // segment [lo, hi) in entries from 8 * fb
-  int segv[kCountSegs + 1];        // exclusive scan of block counts
   uint16_t seglist[kCountSegs];    // segment map: the non-empty segments, in order
-  uint8_t head[kCountSegs];        // the segment's head (0 .. hc - 1)
   uint32_t spare[64];              // trace builds: keeps the traced loads alive
   uint32_t wtot[kSegsPerThread][kFusedThreads / 64];   // scan: per row of segments and wave
   int hsel[16][kFusedThreads / 64];   // selected keys per head and wave
@@ -427,9 +435,9 @@ __device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned 
     const int lo = static_cast<int>(first & 7);
     const int len = max(e0 - s0, 0);
     nblk = len > 0 ? (lo + len + 7) >> 3 : 0;
-    s.fb[tid] = static_cast<long long>(first >> 3);
-    s.lo[tid] = static_cast<short>(lo);
-    s.hi[tid] = static_cast<short>(lo + len);
+    s.seg[tid].fb = static_cast<long long>(first >> 3);
+    s.seg[tid].lo = static_cast<short>(lo);
+    s.seg[tid].hi = static_cast<short>(lo + len);
   }
   // one scan gives the block offsets (low 24 bits) and the rank of each
   // non-empty segment among them (high 8 bits)
@@ -446,14 +454,16 @@ __device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned 
     uint32_t wbase = 0;
     for (int w = 0; w < wave; ++w) wbase += s.wtot[0][w];
     incl += wbase;
-    s.segv[tid + 1] = static_cast<int>(incl & 0xffffffu);
-    if (tid == 0) s.segv[0] = 0;
+    s.seg[tid + 1].v = static_cast<int>(incl & 0xffffffu);
+    if (tid == 0) s.seg[0].v = 0;
     if (nblk > 0) s.seglist[(incl - own) >> 24] = static_cast<uint8_t>(tid);
   }
   __syncthreads();
   LSH_STAMP(p, 1);
 
-  const int total = s.segv[p.L];
+  // the walk's bounds are wave-uniform (scalar), so the steps below need no
+  // per-lane branches
+  const int total = __builtin_amdgcn_readfirstlane(s.seg[p.L].v);
   // segment map (walks of at most kSegMapRows rows of 64 blocks): the
   // segment of block v is seglist[(set bits of starts before v) - 1]
   const int nrows = (total + 63) >> 6;
@@ -462,7 +472,7 @@ __device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned 
     for (int r = tid; r < nrows; r += kFusedThreads) s.starts[r] = 0ull;
     __syncthreads();
     if (nblk > 0) {
-      const int v = s.segv[tid];
+      const int v = s.seg[tid].v;
       atomicOr(reinterpret_cast<unsigned long long*>(&s.starts[v >> 6]), 1ull << (v & 63));
     }
     __syncthreads();
@@ -487,13 +497,15 @@ __device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned 
   }
   constexpr int kW = kFusedThreads / 64;
   const int per = ((total + kW - 1) / kW + 63) & ~63;
-  const int wstart = wave * per, wend = min(total, wstart + per);
+  const int wstart = __builtin_amdgcn_readfirstlane(wave) * per, wend = min(total, wstart + per);
   const u32x4_t* ib = reinterpret_cast<const u32x4_t*>(p.indices);
   LSH_STAMP(p, 4);
   for (int w0 = wstart; w0 < wend; w0 += 64 * kCountInflight) {
     const int v0 = w0 + lane;
-    // rows of 64 blocks this wave still has (wave-uniform): the unrolled
-    // steps below skip the others, so short walks cost little
+    // rows of 64 blocks this wave still has (wave-uniform).  The segment
+    // lookups and the loads run for every row, straight-line, so that they
+    // issue back to back (a step behind a branch waits for the loads before
+    // it); only the counting skips the rows past nk
     const int nk = min(kCountInflight, (wend - w0 + 63) >> 6);
     u32x4_t blk[kCountInflight];
     int lo[kCountInflight], hi[kCountInflight];
@@ -503,11 +515,9 @@ __device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned 
     if (mapped) {
 #pragma unroll
       for (int k = 0; k < kCountInflight; ++k) {
-        if (k < nk) {
-          const int v = min(v0 + 64 * k, wend - 1);
-          const uint64_t below = s.starts[v >> 6] & ((2ull << (v & 63)) - 1ull);
-          sg[k] = s.seglist[s.pre[v >> 6] + __popcll(below) - 1];
-        }
+        const int v = min(v0 + 64 * k, wend - 1);
+        const uint64_t below = s.starts[v >> 6] & ((2ull << (v & 63)) - 1ull);
+        sg[k] = s.seglist[s.pre[v >> 6] + __popcll(below) - 1];
       }
     } else {
 #pragma unroll
@@ -517,11 +527,11 @@ __device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned 
         int sv[kCountInflight];
 #pragma unroll
         for (int k = 0; k < kCountInflight; ++k)
-          if (k < nk) sv[k] = s.segv[min(sg[k] + step, 256)];
+          sv[k] = s.seg[min(sg[k] + step, 256)].v;
 #pragma unroll
         for (int k = 0; k < kCountInflight; ++k) {
           const int c = sg[k] + step;
-          if (k < nk) sg[k] = (c < p.L && sv[k] <= min(v0 + 64 * k, wend - 1)) ? c : sg[k];
+          sg[k] = (c < p.L && sv[k] <= min(v0 + 64 * k, wend - 1)) ? c : sg[k];
         }
       }
     }
@@ -529,15 +539,13 @@ __device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned 
     // blocks past the wave's range load its last block again and take no entry
 #pragma unroll
     for (int k = 0; k < kCountInflight; ++k) {
-      if (k < nk) {
-        const int v = v0 + 64 * k;
-        const bool in = v < wend;
-        const int l = sg[k];
-        const int i = min(v, wend - 1) - s.segv[l];
-        blk[k] = ib[s.fb[l] + i];
-        lo[k] = in ? s.lo[l] - 8 * i : 8;
-        hi[k] = in ? s.hi[l] - 8 * i : 0;
-      }
+      const int v = v0 + 64 * k;
+      const bool in = v < wend;
+      const SegInfo si = s.seg[sg[k]];
+      const int i = min(v, wend - 1) - si.v;
+      blk[k] = ib[si.fb + i];
+      lo[k] = in ? si.lo - 8 * i : 8;
+      hi[k] = in ? si.hi - 8 * i : 0;
     }
 #ifdef LSH_TRACE
     if (w0 == wstart) {   // trace builds: the first row's blocks have arrived
@@ -670,10 +678,9 @@ __device__ inline void count_role_heads(const FusedParams& p, int J, int bh0, un
       const int lo = static_cast<int>(first & 7);
       const int len = max(e0 - s0, 0);
       nblk = len > 0 ? (lo + len + 7) >> 3 : 0;
-      s.fb[sg] = static_cast<long long>(first >> 3);
-      s.lo[sg] = static_cast<short>(lo);
-      s.hi[sg] = static_cast<short>(lo + len);
-      s.head[sg] = static_cast<uint8_t>(sg / p.L);
+      s.seg[sg].fb = static_cast<long long>(first >> 3) | (static_cast<long long>(sg / p.L) << 56);
+      s.seg[sg].lo = static_cast<short>(lo);
+      s.seg[sg].hi = static_cast<short>(lo + len);
     }
     // scan word: the block count, and 1 in the rank field when non-empty
     own[k] = static_cast<uint32_t>(nblk) + (nblk > 0 ? (1u << kCountRankShift) : 0u);
@@ -709,16 +716,18 @@ __device__ inline void count_role_heads(const FusedParams& p, int J, int bh0, un
       }
       const int sg = tid + k * kFusedThreads;
       const uint32_t x = row_base + before + incl[k] - own[k];   // exclusive, at segment sg
-      if (sg < S) s.segv[sg] = static_cast<int>(x & kBlocks);
+      if (sg < S) s.seg[sg].v = static_cast<int>(x & kBlocks);
       if (sg < S && (own[k] & kBlocks) > 0) s.seglist[x >> kCountRankShift] = static_cast<uint16_t>(sg);
       row_base += row_tot;
     }
-    if (tid == 0) s.segv[S] = static_cast<int>(row_base & kBlocks);
+    if (tid == 0) s.seg[S].v = static_cast<int>(row_base & kBlocks);
   }
   __syncthreads();
   LSH_STAMP(p, 1);
 
-  const int total = s.segv[S];
+  // the walk's bounds are wave-uniform (scalar), so the steps below need no
+  // per-lane branches
+  const int total = __builtin_amdgcn_readfirstlane(s.seg[S].v);
   // segment map (walks of at most kSegMapRows rows of 64 blocks): the
   // segment of block v is seglist[(set bits of starts before v) - 1]
   const int nrows = (total + 63) >> 6;
@@ -730,7 +739,7 @@ __device__ inline void count_role_heads(const FusedParams& p, int J, int bh0, un
     for (int k = 0; k < kSegsPerThread; ++k) {
       const int sg = tid + k * kFusedThreads;
       if (sg < S && (own[k] & ((1u << kCountRankShift) - 1u)) > 0) {
-        const int v = s.segv[sg];
+        const int v = s.seg[sg].v;
         atomicOr(reinterpret_cast<unsigned long long*>(&s.starts[v >> 6]), 1ull << (v & 63));
       }
     }
@@ -756,13 +765,15 @@ __device__ inline void count_role_heads(const FusedParams& p, int J, int bh0, un
   }
   constexpr int kW = kFusedThreads / 64;
   const int per = ((total + kW - 1) / kW + 63) & ~63;
-  const int wstart = wave * per, wend = min(total, wstart + per);
+  const int wstart = __builtin_amdgcn_readfirstlane(wave) * per, wend = min(total, wstart + per);
   const u32x4_t* ib = reinterpret_cast<const u32x4_t*>(p.indices);
   LSH_STAMP(p, 4);
   for (int w0 = wstart; w0 < wend; w0 += 64 * kCountInflight) {
     const int v0 = w0 + lane;
-    // rows of 64 blocks this wave still has (wave-uniform): the unrolled
-    // steps below skip the others, so short walks cost little
+    // rows of 64 blocks this wave still has (wave-uniform).  The segment
+    // lookups and the loads run for every row, straight-line, so that they
+    // issue back to back (a step behind a branch waits for the loads before
+    // it); only the counting skips the rows past nk
     const int nk = min(kCountInflight, (wend - w0 + 63) >> 6);
     u32x4_t blk[kCountInflight];
     int lo[kCountInflight], hi[kCountInflight], cb[kCountInflight];
@@ -772,11 +783,9 @@ __device__ inline void count_role_heads(const FusedParams& p, int J, int bh0, un
     if (mapped) {
 #pragma unroll
       for (int k = 0; k < kCountInflight; ++k) {
-        if (k < nk) {
-          const int v = min(v0 + 64 * k, wend - 1);
-          const uint64_t below = s.starts[v >> 6] & ((2ull << (v & 63)) - 1ull);
-          sg[k] = s.seglist[s.pre[v >> 6] + __popcll(below) - 1];
-        }
+        const int v = min(v0 + 64 * k, wend - 1);
+        const uint64_t below = s.starts[v >> 6] & ((2ull << (v & 63)) - 1ull);
+        sg[k] = s.seglist[s.pre[v >> 6] + __popcll(below) - 1];
       }
     } else {
 #pragma unroll
@@ -786,11 +795,11 @@ __device__ inline void count_role_heads(const FusedParams& p, int J, int bh0, un
         int sv[kCountInflight];
 #pragma unroll
         for (int k = 0; k < kCountInflight; ++k)
-          if (k < nk) sv[k] = s.segv[min(sg[k] + step, S)];
+          sv[k] = s.seg[min(sg[k] + step, S)].v;
 #pragma unroll
         for (int k = 0; k < kCountInflight; ++k) {
           const int c = sg[k] + step;
-          if (k < nk) sg[k] = (c < S && sv[k] <= min(v0 + 64 * k, wend - 1)) ? c : sg[k];
+          sg[k] = (c < S && sv[k] <= min(v0 + 64 * k, wend - 1)) ? c : sg[k];
         }
       }
     }
@@ -798,16 +807,14 @@ __device__ inline void count_role_heads(const FusedParams& p, int J, int bh0, un
     // blocks past the wave's range load its last block again and take no entry
 #pragma unroll
     for (int k = 0; k < kCountInflight; ++k) {
-      if (k < nk) {
-        const int v = v0 + 64 * k;
-        const bool in = v < wend;
-        const int l = sg[k];
-        const int i = min(v, wend - 1) - s.segv[l];
-        blk[k] = ib[s.fb[l] + i];
-        lo[k] = in ? s.lo[l] - 8 * i : 8;
-        hi[k] = in ? s.hi[l] - 8 * i : 0;
-        cb[k] = s.head[l] * cwp;                   // the segment's head's counters
-      }
+      const int v = v0 + 64 * k;
+      const bool in = v < wend;
+      const SegInfo si = s.seg[sg[k]];
+      const int i = min(v, wend - 1) - si.v;
+      blk[k] = ib[(si.fb & kSegBlockMask) + i];
+      lo[k] = in ? si.lo - 8 * i : 8;
+      hi[k] = in ? si.hi - 8 * i : 0;
+      cb[k] = static_cast<int>(si.fb >> 56) * cwp;   // the segment's head's counters
     }
 #ifdef LSH_TRACE
     if (w0 == wstart) {   // trace builds: the first row's blocks have arrived
