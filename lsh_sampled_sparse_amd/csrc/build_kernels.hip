@@ -469,10 +469,20 @@ __global__ __launch_bounds__(NTHR, NTHR >= 256 ? 4 : 1) void chunk_sort_kernel(
     __syncthreads();
     scan_counters<NTHR>(cnt, wave_tot);
     __syncthreads();
+    // the ranks' counter words, eight reads in flight at a time: the empty
+    // asm makes the addresses be recomputed per group rather than kept live
+    // (registers for occupancy), and it orders the groups, so one per
+    // element would make every read wait for the one before
+    static_assert(E % 8 == 0, "rank reads in groups of 8");
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-      asm volatile("" : "+v"(e[i]));   // recompute the address rather than keep it live
-      old[i] += *cword(e[i]);
+    for (int i0 = 0; i0 < E; i0 += 8) {
+#pragma unroll
+      for (int i = i0; i < i0 + 8; ++i) asm volatile("" : "+v"(e[i]));
+      uint32_t rk[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rk[i] = *cword(e[i0 + i]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) old[i0 + i] += rk[i];
     }
     __syncthreads();                            // every rank is read: buf may overwrite the counters
     // old: byte offset of the element's position in the unpadded order; the
