@@ -440,31 +440,40 @@ __device__ __forceinline__ void attend_bf16_role(const FusedParams& p, int s, in
 #pragma unroll
     for (int i = 0; i < 4; ++i) wacc[(wave * 16 + 4 * g4 + i) * kHeadDim + 16 * t + sl] = O[t][i];
   __syncthreads();
-  for (int e = tid; e < G * kHeadDim; e += 256) {
-    const int hh = e / kHeadDim, d = e % kHeadDim;
+  // G <= 4 GW heads: at most 2 GW elements of the G x 128 states per thread.
+  // Without branches, so that every LDS read is in flight at once: a wave
+  // that took no key of a head has max -inf and weight 0 (its state is 0)
+#pragma unroll
+  for (int k = 0; k < 2 * GW; ++k) {
+    const int e = tid + 256 * k;
+    const bool live = e < G * kHeadDim;
+    const int hh = live ? e / kHeadDim : 0, d = e % kHeadDim;
+    float mw[kWaves];
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, A.ep_m[w][hh]);
+    for (int w = 0; w < kWaves; ++w) {
+      mw[w] = A.ep_m[w][hh];
+      M = fmaxf(M, mw[w]);
+    }
     float Acc = 0.f, Lm = 0.f;
-    if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        if (A.ep_m[w][hh] == -INFINITY) continue;
-        const float f = __expf(A.ep_m[w][hh] - M);
-        Acc = fmaf(wacc[(w * 16 + hh) * kHeadDim + d], f, Acc);
-        Lm = fmaf(A.ep_l[w][hh], f, Lm);
-      }
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = mw[w] == -INFINITY ? 0.f : __expf(mw[w] - M);   // all -inf when M is
+      Acc = fmaf(wacc[(w * 16 + hh) * kHeadDim + d], f, Acc);
+      Lm = fmaf(A.ep_l[w][hh], f, Lm);
     }
     if (!ok) {   // a wait gave up: poison this partial
       Acc = __builtin_nanf("");
       M = 0.f;
       Lm = 1.f;
     }
-    float* dst = p.partials + (static_cast<size_t>(bh0 + hh) * npart + s) * kPartialStride;
-    st_agent(dst + d, Acc);
-    if (d == 0) {
-      st_agent(dst + kHeadDim, M);
-      st_agent(dst + kHeadDim + 1, Lm);
+    if (live) {
+      float* dst = p.partials + (static_cast<size_t>(bh0 + hh) * npart + s) * kPartialStride;
+      st_agent(dst + d, Acc);
+      if (d == 0) {
+        st_agent(dst + kHeadDim, M);
+        st_agent(dst + kHeadDim + 1, Lm);
+      }
     }
   }
 }
