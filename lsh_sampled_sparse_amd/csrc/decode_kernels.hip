@@ -128,6 +128,20 @@ __global__ __launch_bounds__(256) void qhash_kernel(const typename T::storage* _
   W += static_cast<size_t>(gw) * w_head_stride;
   const int tpw = 64 / K;               // whole tables per workgroup
   const int l0 = blockIdx.x * tpw;
+  // this lane's column of W over the wave's 32 dims, loaded first: the loads
+  // do not depend on q, so they are in flight with q's
+  const int LK = L * K;
+  const int col = l0 * K + lane;
+  const bool colv = lane < tpw * K && col < LK;
+  float w[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const size_t at = static_cast<size_t>(32 * wave + i) * LK + (colv ? col : 0);
+    if constexpr (sizeof(typename T::storage) == 2)
+      w[i] = bf16_to_f32(W[at]);   // (converted once the loads arrive)
+    else
+      w[i] = W[at];
+  }
   {
     // 16 heads x 128 dims: thread t takes 8 consecutive dims of head t / 16
     // in one (bf16) or two (fp32) 16-byte loads
@@ -155,18 +169,6 @@ __global__ __launch_bounds__(256) void qhash_kernel(const typename T::storage* _
     for (int k = 0; k < 8; ++k) qs[hh][c8 + k] = okh ? v[k] : 0.f;
   }
   __syncthreads();
-  const int LK = L * K;
-  const int col = l0 * K + lane;
-  const bool colv = lane < tpw * K && col < LK;
-  float w[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const size_t at = static_cast<size_t>(32 * wave + i) * LK + (colv ? col : 0);
-    if constexpr (sizeof(typename T::storage) == 2)
-      w[i] = bf16_to_f32(W[at]);
-    else
-      w[i] = W[at];
-  }
 #pragma unroll
   for (int hh = 0; hh < kQHeads; ++hh) {
     const floatx4_t* qv = reinterpret_cast<const floatx4_t*>(&qs[hh][32 * wave]);
