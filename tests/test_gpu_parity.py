@@ -179,6 +179,36 @@ def test_k0_is_exact_attention():
         assert int(r["nsel"][0, h]) == cfg.N
 
 
+# K = 0 puts every key of a chunk in the one probed bucket, so a count
+# workgroup walks L * stride / 8 blocks per head: past 512 rows of 64 blocks
+# the walk finds each block's segment by binary search instead of the
+# segment map.  One head per count workgroup (128 (head, chunk) pairs), and
+# two (640 pairs: more than one round of resident workgroups).
+K0_LONG = [
+    workloads.Config("k0-long", B=1, Hq=8, Hkv=2, N=9000, d=128, K=0, L=40, T=2, dtype="bf16",
+                     planted=4, a=0.8, offset="per_head", seed=22),
+    workloads.Config("k0-long-2heads", B=8, Hq=16, Hkv=2, N=40000, d=128, K=0, L=40, T=2, dtype="bf16",
+                     planted=4, a=0.8, offset="per_head", seed=23),
+]
+
+
+@pytest.mark.parametrize("cfg", K0_LONG, ids=[c.name for c in K0_LONG])
+def test_k0_long_walks(cfg):
+    say(f"case {cfg.name}")
+    data = workloads.generate(cfg)
+    units = [(0, 0), (cfg.B - 1, cfg.Hkv - 1)]
+    tb, r = check_case(cfg, data, units=units)
+    keys = data["keys"].float().numpy()
+    vals = data["values"].float().numpy()
+    q = data["q"][0].float().numpy()
+    for b, g in units:
+        for h in range(g * cfg.G, (g + 1) * cfg.G):
+            ex, lse = O.exact_attention(q[b, h], keys[b, g], vals[b, g], cfg.scale)
+            out = to_np(r["out"][b, h])
+            assert np.linalg.norm(out - ex) / np.linalg.norm(ex) <= PAR.OUT_RTOL
+            assert int(r["nsel"][b, h]) == cfg.N
+
+
 def test_deterministic():
     cfg = SMALL[2]
     say("case determinism")
