@@ -395,6 +395,22 @@ struct CountLds {                  // laid out after the byte counters (a multip
   int flag;
 };
 
+// The bits of a bitmask word whose keys may be selected, for the word whose
+// first key is k0: keys below kend (the sequence's keys in the chunk), at or
+// above exact_head and below tail_start (outside the exact set).  The same
+// for every head, so it is formed once per word.
+__device__ __forceinline__ uint32_t bits_below(int x) { return x <= 0 ? 0u : (x >= 32 ? ~0u : (1u << x) - 1u); }
+__device__ __forceinline__ uint32_t selectable_bits(int k0, int kend, int exact_head, int tail_start) {
+  return bits_below(kend - k0) & ~bits_below(exact_head - k0) & bits_below(tail_start - k0);
+}
+// Bit k set when byte k of c4 (a key's collision count) is at least T.
+__device__ __forceinline__ uint32_t counts_at_least(uint32_t c4, int T) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r |= static_cast<int>((c4 >> (8 * k)) & 0xffu) >= T ? (1u << k) : 0u;
+  return r;
+}
+
 // One query head per workgroup: thread l takes table l (L <= 255).
 __device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned char* smem) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -590,15 +606,9 @@ __device__ inline void count_role(const FusedParams& p, int J, int bh, unsigned 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int wi = w * 8 + j;
-      const uint32_t c4 = wi < cwords ? cnt[wi] : 0u;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int key = w * 32 + j * 4 + k;
-        const int n = cbeg + key;
-        const bool ex = n < exact_head || n >= Nb - exact_tail;
-        if (key < clen && !ex && static_cast<int>((c4 >> (8 * k)) & 0xffu) >= p.T) m |= 1u << (j * 4 + k);
-      }
+      m |= counts_at_least(wi < cwords ? cnt[wi] : 0u, p.T) << (4 * j);
     }
+    m &= selectable_bits(cbeg + 32 * w, cbeg + clen, exact_head, Nb - exact_tail);
     st_agent(p.bitmask + static_cast<size_t>(bh) * Nw + (cbeg >> 5) + w, m);
     mysel += __builtin_popcount(m);
   }
@@ -648,12 +658,26 @@ __device__ inline void count_role_heads(const FusedParams& p, int J, int bh0, un
   // thread t takes segment t of each row of 256 (with one head, thread l
   // takes table l); the query codes, then the bucket bounds, each set of
   // loads in flight together
+  // (every load below is issued, from a clamped address where the segment
+  // does not exist, so that each set is in flight at once: a load behind a
+  // branch waits for the ones before it)
   int qraw[kSegsPerThread];
 #pragma unroll
   for (int k = 0; k < kSegsPerThread; ++k) {
-    const int sg = tid + k * kFusedThreads;
-    qraw[k] = 0;
-    if (sg < S && clen > 0) qraw[k] = p.qcodes[static_cast<size_t>(bh0 + sg / p.L) * p.L + sg % p.L];
+    const int sg = min(tid + k * kFusedThreads, S - 1);
+    qraw[k] = p.qcodes[static_cast<size_t>(bh0 + sg / p.L) * p.L + sg % p.L];
+  }
+  int ob0[kSegsPerThread], ob1[kSegsPerThread];   // the bucket's first entry, and the next bucket's
+#pragma unroll
+  for (int k = 0; k < kSegsPerThread; ++k) {
+    const int sg = min(tid + k * kFusedThreads, S - 1);
+    // (the query hash writes codes below 2^K; the mask keeps any other value
+    // inside the chunk's bucket starts, and the checked build reports it)
+    const int qc = qraw[k] & (nb - 1);
+    const size_t row = static_cast<size_t>(u) * p.L + sg % p.L;
+    const uint16_t* op = p.offsets + (row * p.nJP + J) * nb + qc;
+    ob0[k] = op[0];
+    ob1[k] = op[qc + 1 < nb ? 1 : 0];
   }
   uint32_t own[kSegsPerThread];
 #pragma unroll
@@ -662,18 +686,14 @@ __device__ inline void count_role_heads(const FusedParams& p, int J, int bh0, un
     int nblk = 0;
     if (sg < S && clen > 0) {
       const int l = sg % p.L;
-      // (the query hash writes codes below 2^K; the mask keeps any other value
-      // inside the chunk's bucket starts, and the checked build reports it)
       LSH_PCHECK(p, qraw[k] < nb, kChkQueryCode);
       const int qc = qraw[k] & (nb - 1);
       const size_t row = static_cast<size_t>(u) * p.L + l;
-      const uint16_t* op = p.offsets + (row * p.nJP + J) * nb + qc;
-      LSH_PCHECK(p, static_cast<int>(op[0]) <= (qc + 1 < nb ? static_cast<int>(op[1]) : clen) &&
-                        (qc + 1 < nb ? static_cast<int>(op[1]) : static_cast<int>(op[0])) <= clen,
+      LSH_PCHECK(p, ob0[k] <= (qc + 1 < nb ? ob1[k] : clen) && (qc + 1 < nb ? ob1[k] : ob0[k]) <= clen,
                  kChkSegment);
       // clamped into the chunk: tables of another stride cannot send the walk out of it
-      const int s0 = min(static_cast<int>(op[0]), clen);
-      const int e0 = qc + 1 < nb ? min(static_cast<int>(op[1]), clen) : clen;
+      const int s0 = min(ob0[k], clen);
+      const int e0 = qc + 1 < nb ? min(ob1[k], clen) : clen;
       const size_t first = row * p.P + cbeg + s0;      // element index of the segment's first entry
       const int lo = static_cast<int>(first & 7);
       const int len = max(e0 - s0, 0);
@@ -862,15 +882,9 @@ __device__ inline void count_role_heads(const FusedParams& p, int J, int bh0, un
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int wi = w * 8 + j;
-        const uint32_t c4 = wi < cwords ? ch[wi] : 0u;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int key = w * 32 + j * 4 + k;
-          const int n = cbeg + key;
-          const bool ex = n < exact_head || n >= Nb - exact_tail;
-          if (key < clen && !ex && static_cast<int>((c4 >> (8 * k)) & 0xffu) >= p.T) m |= 1u << (j * 4 + k);
-        }
+        m |= counts_at_least(wi < cwords ? ch[wi] : 0u, p.T) << (4 * j);
       }
+      m &= selectable_bits(cbeg + 32 * w, cbeg + clen, exact_head, Nb - exact_tail);
       st_agent(p.bitmask + static_cast<size_t>(bh) * Nw + (cbeg >> 5) + w, m);
       mysel += __builtin_popcount(m);
     }
