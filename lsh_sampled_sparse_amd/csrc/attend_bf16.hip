@@ -18,11 +18,13 @@
 // Stegun 4.4.46) and the hardware log2 keep it to ~35 instructions per pair.
 // The four waves' (max, sum, acc) states are merged through LDS into one
 // partial per query head and split, for the log-sum-exp merge that follows.
-// Workgroups past the context splits take the hybrid decode's exact set
-// (for a sequence of n keys, keys [0, exact_head) and [n - exact_tail, n),
-// counted 0 .. ne - 1 across both ranges), a piece of exact_len keys each:
-// every key is taken for every head of the group and weighted 1 (u = 1),
-// which is plain softmax attention on the same tiles.
+// The hybrid decode's exact set (for a sequence of n keys, keys
+// [0, exact_head) and [n - exact_tail, n)) is taken by the context splits
+// that hold it: such a key goes to every head of the group with weight 1
+// (ln u = 0), so the split's softmax covers its sampled keys and its exact
+// keys together, which equals the log-sum-exp merge of the two parts (the
+// count role leaves exact keys out of the bitmask).  bf16 launches have no
+// exact-set workgroups.
 #include <math.h>
 
 #include "decode_roles.h"
@@ -37,6 +39,7 @@ constexpr int kWaves = 4;
 constexpr int kTile = 32;         // keys per tile (the K extent of one MFMA 16x16x32)
 constexpr int kRingN = 128;       // per-wave ring of compacted keys
 constexpr int kVRow = 136;        // LDS row of one V row: 128 dims + 8 pad (272 B)
+constexpr int kExactKey = static_cast<int>(0x80000000u);   // ring entry flag: a key of the exact set
 constexpr int kBlock = 512;       // keys whose mask words are fetched together
 constexpr float kPiF = 3.14159265358979323846f;
 constexpr float kLnUFloorF = -69.07755278982137f;   // ln(1e-30)
@@ -145,13 +148,12 @@ struct AttendLds {
 };
 constexpr size_t kFusedLdsBytes = cmax(sizeof(AttendLds), kRolesLdsBytes);
 
-// The attention role: partial slot s (a context split, or past nsplit a
-// piece of the exact set) of unit u.  GW = number of 64-lane mask words per
+// The attention role: partial slot s (a context split) of unit u.  GW = number of 64-lane mask words per
 // head and 512-key block that a lane holds: the G heads' 16 words per block
 // are spread over GW loads.
 template <int GW>
 __device__ __forceinline__ void attend_bf16_role(const FusedParams& p, int s, int u, unsigned char* smem) {
-  LSH_PCHECK(p, u < p.B * p.Hkv && s < p.npart, kChkSlot);
+  LSH_PCHECK(p, u < p.B * p.Hkv && s < p.nsplit, kChkSlot);
   AttendLds& A = *reinterpret_cast<AttendLds*>(smem);
   LSH_STAMP(p, 0);
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(p.q);
@@ -160,7 +162,7 @@ __device__ __forceinline__ void attend_bf16_role(const FusedParams& p, int s, in
   const uint32_t* bitmask = p.bitmask;
   const int Hq = p.Hq, Hkv = p.Hkv, N = p.N, P = p.P, K = p.K, Tth = p.T;
   const float scale = p.scale;
-  const int split_len = p.split_len, nsplit = p.nsplit, exact_len = p.exact_len;
+  const int split_len = p.split_len;
   const int npart = p.npart;
   float4* tab4 = A.tab4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -172,13 +174,11 @@ __device__ __forceinline__ void attend_bf16_role(const FusedParams& p, int s, in
   const uint16_t* kb = keys + static_cast<size_t>(u) * P * kHeadDim;
   const uint16_t* vb = values + static_cast<size_t>(u) * P * kHeadDim;
   const bool k0 = (K == 0);
-  const bool exact = s >= nsplit;          // a piece of the exact set
-  const bool nolnu = k0 || exact;
+  const bool nolnu = k0;
   // this sequence's keys and exact set
   const int Nb = seq_len_of(p.seq_lens, b, N);
   int exact_head, exact_tail;
   exact_range(p.n_sink, p.n_window, Nb, exact_head, exact_tail);
-  const int ne = exact_head + exact_tail;
   const uint16_t gmask = static_cast<uint16_t>((1u << G) - 1u);
   const float TKln2 = static_cast<float>(Tth * K) * 0.69314718055994531f;
 
@@ -202,11 +202,10 @@ __device__ __forceinline__ void attend_bf16_role(const FusedParams& p, int s, in
   LnuFetch lf;
   lnu_fetch(p, nolnu, lf);
 
-  // this wave's range: keys of the context split, or exact-set positions
-  const int plen = exact ? exact_len : split_len;
-  const int sb = exact ? (s - nsplit) * exact_len : s * split_len;
-  const int se = min(exact ? ne : Nb, sb + plen);
-  const int wq = plen / kWaves;
+  // this wave's range: its quarter of the context split's keys
+  const int sb = s * split_len;
+  const int se = min(Nb, sb + split_len);
+  const int wq = split_len / kWaves;
   const int wb = min(se, sb + wave * wq), we = min(se, sb + (wave + 1) * wq);
 
   int* ridx = A.ring_idx[wave];
@@ -219,7 +218,7 @@ __device__ __forceinline__ void attend_bf16_role(const FusedParams& p, int s, in
   // workgroups of every query head of the group); a wait that does not end
   // leaves a NaN partial
   bool ok = true;
-  if (!exact && sb < se) {
+  if (sb < se) {
     const int j0 = sb >> p.stride_log2, j1 = (se - 1) >> p.stride_log2;
     ok = wait_counters(p.ready + u * p.nJ + j0, j1 - j0 + 1, G, &A.flag);
   }
@@ -238,32 +237,12 @@ __device__ __forceinline__ void attend_bf16_role(const FusedParams& p, int s, in
   };
   int blk = wb;                        // next window to compact
   int blk_loaded = wb;                 // block start of mw
-  if (!exact) {
-    load_block(wb, mw);
-    load_block(wb + kBlock, mw_next);
-  }
+  load_block(wb, mw);
+  load_block(wb + kBlock, mw_next);
 
   int rhead = 0, rcnt = 0;
   // compact windows of 64 keys until a full tile is queued or the range ends
   auto fill = [&]() {
-    if (exact) {
-      // every position of the range, all heads; the lanes that take one are
-      // lanes 0 .. count - 1, so a lane's ring slot follows from its index
-      while (rcnt < kTile && blk < we) {
-        const int i = blk + lane;
-        const bool any = i < we;
-        const uint64_t bal = ballot(any);
-        if (any) {
-          const int e = (rhead + rcnt + lane) & (kRingN - 1);
-          ridx[e] = i < exact_head ? i : i + (Nb - ne);
-          rhm[e] = gmask;
-        }
-        rcnt += __builtin_popcountll(bal);
-        blk += 64;
-      }
-      __builtin_amdgcn_wave_barrier();
-      return;
-    }
     while (rcnt < kTile && blk < we) {
       if (blk >= blk_loaded + kBlock) {
         blk_loaded += kBlock;
@@ -281,11 +260,15 @@ __device__ __forceinline__ void attend_bf16_role(const FusedParams& p, int s, in
           hm |= static_cast<int>((w >> (lane & 31)) & 1u) << (4 * k + hq);
         }
       const int n = blk + lane;
+      // a key of the exact set (never in the bitmask): every head, ln u = 0,
+      // marked in bit 31 of its ring entry
+      const bool ex = n < exact_head || n >= Nb - exact_tail;
+      hm = ex ? static_cast<int>(gmask) : hm;
       const bool any = n < we && hm != 0;
       const uint64_t bal = ballot(any);
       if (any) {
         const int e = (rhead + rcnt + mbcnt(bal)) & (kRingN - 1);
-        ridx[e] = n;
+        ridx[e] = ex ? (n | kExactKey) : n;
         rhm[e] = static_cast<uint16_t>(hm);
       }
       rcnt += __builtin_popcountll(bal);
@@ -300,19 +283,23 @@ __device__ __forceinline__ void attend_bf16_role(const FusedParams& p, int s, in
   Frag<BF16> Kf[2];
   u32x4_t vr[8];
   int hmk[2];
+  bool exk[2];
   auto issue = [&](int nt) {
 #pragma unroll
     for (int gp = 0; gp < 2; ++gp) {
       const int slot = 16 * gp + sl;
       const int e = (rhead + (slot < nt ? slot : 0)) & (kRingN - 1);
+      const int r = ridx[e];
       hmk[gp] = slot < nt ? static_cast<int>(rhm[e]) : 0;
-      Kf[gp].load_interleaved_nt(kb + static_cast<size_t>(ridx[e]) * kHeadDim + g4 * 8);
+      exk[gp] = r < 0;                               // kExactKey: an exact-set key
+      Kf[gp].load_interleaved_nt(kb + static_cast<size_t>(r & ~kExactKey) * kHeadDim + g4 * 8);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = g4 + 4 * j;
       const int e = (rhead + (row < nt ? row : 0)) & (kRingN - 1);
-      vr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + static_cast<size_t>(ridx[e]) * kHeadDim + sl * 8));
+      vr[j] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(vb + static_cast<size_t>(ridx[e] & ~kExactKey) * kHeadDim + sl * 8));
     }
   };
 
@@ -349,6 +336,7 @@ __device__ __forceinline__ void attend_bf16_role(const FusedParams& p, int s, in
     const float rk0 = ks0 > 0.f ? __builtin_amdgcn_rsqf(ks0) : 0.f;
     const float rk1 = ks1 > 0.f ? __builtin_amdgcn_rsqf(ks1) : 0.f;
     const int hm0 = hmk[0], hm1 = hmk[1];
+    const bool ex0 = exk[0], ex1 = exk[1];
 
     // retire the tile from the ring, queue the next one and start its loads
     rhead = (rhead + nt) & (kRingN - 1);
@@ -364,8 +352,8 @@ __device__ __forceinline__ void attend_bf16_role(const FusedParams& p, int s, in
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float x0 = S0[i], x1 = S1[i];
-      const float u0 = nolnu ? 0.f : lnu_of_cos(x0 * rq[i] * rk0, tab4, TKln2);
-      const float u1 = nolnu ? 0.f : lnu_of_cos(x1 * rq[i] * rk1, tab4, TKln2);
+      const float u0 = nolnu || ex0 ? 0.f : lnu_of_cos(x0 * rq[i] * rk0, tab4, TKln2);
+      const float u1 = nolnu || ex1 ? 0.f : lnu_of_cos(x1 * rq[i] * rk1, tab4, TKln2);
       const int hh = 4 * g4 + i;
       const bool ok = hh < G;
       lg[0][i] = (ok && ((hm0 >> hh) & 1)) ? fmaf(scale, x0, -u0) : -INFINITY;
@@ -478,8 +466,8 @@ __device__ __forceinline__ void attend_bf16_role(const FusedParams& p, int s, in
   }
 }
 
-// The one-launch decode for bf16 K/V: count, exact and attend workgroups,
-// unit by unit (decode_role).
+// The one-launch decode for bf16 K/V: count and attend workgroups, unit by
+// unit (decode_role).
 template <int GW>
 __global__ __launch_bounds__(kFusedThreads, 2) void decode_bf16_kernel(FusedParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kFusedLdsBytes];

@@ -4,7 +4,8 @@
 //
 // One grid holds, in this order of workgroup id,
 //   count    workgroups: one per (key chunk, query head), the selection bitmask
-//   exact    workgroups: the hybrid decode's exact set, in pieces
+//   exact    workgroups: the hybrid decode's exact set, in pieces (fp32 launches;
+//            in bf16 launches the context splits take the exact keys)
 //   attend   workgroups: one per (context split, sequence, kv head)
 // An attend workgroup waits, by polling a counter in the workspace, for the
 // count workgroups of its split's chunks, all of LOWER id.  Workgroups of a

@@ -434,6 +434,9 @@ static lsh_status decode_cached(const void* q, const void* keys, const void* val
   const int ne128 = (ne + 127) / 128 * 128;
   a.exact_len = std::max({128, (per_piece + 127) / 128 * 128, std::min(ne128, w.split_len / 8 / 128 * 128)});
   a.nexact = (ne + a.exact_len - 1) / a.exact_len;
+  // bf16: the context splits take the exact set's keys themselves (every
+  // head, ln u = 0), so no piece waits in the tail of the launch
+  if (dtype == 1) a.nexact = 0;
   return hip_status(lsh::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
