@@ -23,8 +23,7 @@
 // that hold it: such a key goes to every head of the group with weight 1
 // (ln u = 0), so the split's softmax covers its sampled keys and its exact
 // keys together, which equals the log-sum-exp merge of the two parts (the
-// count role leaves exact keys out of the bitmask).  bf16 launches have no
-// exact-set workgroups.
+// count role leaves exact keys out of the bitmask).
 #include <math.h>
 
 #include "decode_roles.h"
@@ -39,7 +38,6 @@ constexpr int kWaves = 4;
 constexpr int kTile = 32;         // keys per tile (the K extent of one MFMA 16x16x32)
 constexpr int kRingN = 128;       // per-wave ring of compacted keys
 constexpr int kVRow = 136;        // LDS row of one V row: 128 dims + 8 pad (272 B)
-constexpr int kExactKey = static_cast<int>(0x80000000u);   // ring entry flag: a key of the exact set
 constexpr int kBlock = 512;       // keys whose mask words are fetched together
 constexpr float kPiF = 3.14159265358979323846f;
 constexpr float kLnUFloorF = -69.07755278982137f;   // ln(1e-30)
@@ -484,7 +482,7 @@ __global__ __launch_bounds__(kFusedThreads, 2) void decode_bf16_kernel(FusedPara
 }
 
 hipError_t launch_decode_bf16(const FusedParams& p, int kid, hipStream_t stream) {
-  const dim3 grid(p.n_count_wg + p.n_exact_wg + p.n_attend_wg);
+  const dim3 grid(p.n_count_wg + p.n_attend_wg);
   if (p.G <= 4) return launch(kid, decode_bf16_kernel<1>, grid, dim3(kFusedThreads), 0, stream, p);
   if (p.G <= 8) return launch(kid, decode_bf16_kernel<2>, grid, dim3(kFusedThreads), 0, stream, p);
   return launch(kid, decode_bf16_kernel<4>, grid, dim3(kFusedThreads), 0, stream, p);

@@ -12,9 +12,9 @@
 //           LDS byte counters and the selection bitmask (count >= T); per
 //           (context split, sequence, kv head) the union of the group's
 //           selections, ballot compaction, gathered K/V rows, q.k, 1/u
-//           weights, online softmax in fp32 and P.V, written as one partial
-//           state per query head (and the hybrid decode's exact set, in
-//           pieces, with unit weights); the log-sum-exp merges of those
+//           weights, online softmax in fp32 and P.V (the hybrid decode's
+//           exact keys with every head and unit weights), written as one
+//           partial state per query head; the log-sum-exp merges of those
 //           partials (the stable merge MAC-Attention also uses,
 //           "MAC-Attention" README, "How It Works") run in the last
 //           workgroups to finish.  The bf16 grid is in attend_bf16.hip, the
@@ -244,7 +244,7 @@ struct AttendF32Lds {
 
 template <int GM>
 __device__ __forceinline__ void attend_f32_role(const FusedParams& p, int s, int u, unsigned char* smem) {
-  LSH_PCHECK(p, u < p.B * p.Hkv && s < p.npart, kChkSlot);
+  LSH_PCHECK(p, u < p.B * p.Hkv && s < p.nsplit, kChkSlot);
   AttendF32Lds<GM>& A = *reinterpret_cast<AttendF32Lds<GM>*>(smem);
   const float* __restrict__ q = static_cast<const float*>(p.q);
   const float* __restrict__ keys = static_cast<const float*>(p.keys);
@@ -259,18 +259,15 @@ __device__ __forceinline__ void attend_f32_role(const FusedParams& p, int s, int
   const float* kb = keys + static_cast<size_t>(u) * p.P * kHeadDim;
   const float* vb = values + static_cast<size_t>(u) * p.P * kHeadDim;
   const bool k0 = (K == 0);
-  const bool exact = s >= p.nsplit;     // a piece of the exact set (all heads, u = 1)
-  const bool nolnu = k0 || exact;
+  const bool nolnu = k0;
   const int Nb = seq_len_of(p.seq_lens, b, N);
   int exact_head, exact_tail;
   exact_range(p.n_sink, p.n_window, Nb, exact_head, exact_tail);
-  const int ne = exact_head + exact_tail;
   const float TK = static_cast<float>(p.T * K);
 
-  const int plen = exact ? p.exact_len : p.split_len;
-  const int sb = exact ? (s - p.nsplit) * p.exact_len : s * p.split_len;
-  const int se = min(exact ? ne : Nb, sb + plen);
-  const int wq = plen / 4;
+  const int sb = s * p.split_len;
+  const int se = min(Nb, sb + p.split_len);
+  const int wq = p.split_len / 4;
   const int wb = min(se, sb + wave * wq), we = min(se, sb + (wave + 1) * wq);
 
   // query fragments: lane holds head (lane & 15), dims [32 (lane >> 4), +32)
@@ -283,7 +280,7 @@ __device__ __forceinline__ void attend_f32_role(const FusedParams& p, int s, int
   lnu_fetch(p, nolnu, lf);
   // the split's selection must be complete
   bool ok = true;
-  if (!exact && sb < se) {
+  if (sb < se) {
     const int j0 = sb >> p.stride_log2, j1 = (se - 1) >> p.stride_log2;
     ok = wait_counters(p.ready + u * p.nJ + j0, j1 - j0 + 1, G, &A.flag);
   }
@@ -311,7 +308,9 @@ __device__ __forceinline__ void attend_f32_role(const FusedParams& p, int s, int
   auto process_tile = [&](int ntile) {
     const bool has = slot < ntile;
     const int e = (head + (has ? slot : 0)) & (kRing - 1);
-    const int idx = A.sidx[wave][e];
+    const int rix = A.sidx[wave][e];
+    const int idx = rix & ~kExactKey;
+    const bool exk = rix < 0;          // a key of the exact set: ln u = 0
     const int hmk = has ? static_cast<int>(A.shm[wave][e]) : 0;
     Frag<F32> Kf;
     Kf.load(kb + static_cast<size_t>(idx) * kHeadDim + grp * 32, true);
@@ -337,7 +336,7 @@ __device__ __forceinline__ void attend_f32_role(const FusedParams& p, int s, int
         const float x = sc[i];
         const float nn = A.qn[hh] * kn;
         const float cs = nn > 0.f ? x / nn : 0.f;
-        logit = scale * x - (nolnu ? 0.f : log_inclusion(cs, A.tab, TK));
+        logit = scale * x - (nolnu || exk ? 0.f : log_inclusion(cs, A.tab, TK));
       }
       const float mt = row16_max(logit);
       const float mnew = fmaxf(m_run[i], mt);
@@ -373,26 +372,25 @@ __device__ __forceinline__ void attend_f32_role(const FusedParams& p, int s, int
   };
 
   for (int blk = wb; blk < we; blk += 64) {
-    const int i = blk + lane;           // key, or position in the exact set
-    int n = i, hm = 0;
-    if (exact) {
-      n = i < exact_head ? i : i + (Nb - ne);
-      hm = (1 << G) - 1;
-    } else {
-      const int w0 = blk >> 5;
-      for (int hh = 0; hh < G; ++hh) {
-        const uint32_t* bm = p.bitmask + static_cast<size_t>(bh0 + hh) * Nw;
-        const uint32_t lo = ld_agent(bm + w0);
-        const uint32_t hi = (w0 + 1 < Nw) ? ld_agent(bm + w0 + 1) : 0u;
-        const uint32_t word = lane < 32 ? lo : hi;
-        hm |= static_cast<int>((word >> (lane & 31)) & 1u) << hh;
-      }
+    const int n = blk + lane;
+    int hm = 0;
+    const int w0 = blk >> 5;
+    for (int hh = 0; hh < G; ++hh) {
+      const uint32_t* bm = p.bitmask + static_cast<size_t>(bh0 + hh) * Nw;
+      const uint32_t lo = ld_agent(bm + w0);
+      const uint32_t hi = (w0 + 1 < Nw) ? ld_agent(bm + w0 + 1) : 0u;
+      const uint32_t word = lane < 32 ? lo : hi;
+      hm |= static_cast<int>((word >> (lane & 31)) & 1u) << hh;
     }
-    const bool any = (i < we) && hm != 0;
+    // a key of the exact set (never in the bitmask): every head, ln u = 0,
+    // marked in bit 31 of its ring entry
+    const bool ex = n < exact_head || n >= Nb - exact_tail;
+    hm = ex ? (1 << G) - 1 : hm;
+    const bool any = (n < we) && hm != 0;
     const uint64_t bal = ballot(any);
     if (any) {
       const int e = (head + cnt + mbcnt(bal)) & (kRing - 1);
-      A.sidx[wave][e] = n;
+      A.sidx[wave][e] = ex ? (n | kExactKey) : n;
       A.shm[wave][e] = static_cast<uint16_t>(hm);
     }
     cnt += __builtin_popcountll(bal);
@@ -543,9 +541,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.nsplit = a.nsplit;
   p.n_sink = a.n_sink;
   p.n_window = a.n_window;
-  p.exact_len = a.exact_len;
-  p.nexact = a.nexact;
-  p.npart = a.nsplit + a.nexact;
+  p.npart = a.nsplit;
   p.scale = a.scale;
   // counters: ready [U][nJ], arrive_unit [U]
   p.ready = a.sync;
@@ -563,7 +559,6 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.L > kCountSegs || (1 << a.stride_log2) > kCountCounterBytes) return hipErrorInvalidValue;
   p.count_heads = hc;
   p.n_count_wg = BH / hc * a.nJ;
-  p.n_exact_wg = U * a.nexact;
   p.n_attend_wg = U * a.nsplit;
   // a fold keeps the (head, slot) pairs of its heads in LDS
   const int F = p.G < p.npart ? p.G : p.npart;
@@ -577,7 +572,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = (a.dtype == 1) ? launch_qhash<BF16>(a, nsync, kq, stream) : launch_qhash<F32>(a, nsync, kq, stream);
   if (e != hipSuccess) return e;
   if (a.dtype == 1) return launch_decode_bf16(p, kd, stream);
-  const dim3 grid(p.n_count_wg + p.n_exact_wg + p.n_attend_wg);
+  const dim3 grid(p.n_count_wg + p.n_attend_wg);
   if (p.G <= 4) return launch(kd, decode_f32_kernel<4>, grid, dim3(kFusedThreads), 0, stream, p);
   if (p.G <= 8) return launch(kd, decode_f32_kernel<8>, grid, dim3(kFusedThreads), 0, stream, p);
   return launch(kd, decode_f32_kernel<16>, grid, dim3(kFusedThreads), 0, stream, p);

@@ -4,8 +4,6 @@
 //
 // One grid holds, in this order of workgroup id,
 //   count    workgroups: one per (key chunk, query head), the selection bitmask
-//   exact    workgroups: the hybrid decode's exact set, in pieces (fp32 launches;
-//            in bf16 launches the context splits take the exact keys)
 //   attend   workgroups: one per (context split, sequence, kv head)
 // An attend workgroup waits, by polling a counter in the workspace, for the
 // count workgroups of its split's chunks, all of LOWER id.  Workgroups of a
@@ -26,7 +24,7 @@
 // Fences in every workgroup are avoided: an L2 write-back or invalidate per
 // workgroup costs far more than these few coherent accesses.
 //
-// The merge: each attend / exact workgroup writes one partial state (acc,
+// The merge: each attend workgroup writes one partial state (acc,
 // max, sum) per query head of its group; the last workgroups of a (sequence,
 // kv head) to finish fold them into the outputs (finish_slot).  Folds run in
 // slot order, whoever runs them, so the result is deterministic.
@@ -42,6 +40,9 @@
 namespace lsh {
 
 constexpr int kFusedThreads = 256;         // every role runs 4 waves
+// An attention role's ring entry: the key index, with this bit set for a key
+// of the hybrid decode's exact set (every head of the group, ln u = 0)
+constexpr int kExactKey = static_cast<int>(0x80000000u);
 constexpr int kSpinLimit = 1 << 18;        // polls before a wait gives up (a fraction of a second)
 
 // --------------------------------------------------------------------------
@@ -160,9 +161,9 @@ struct FusedParams {
   uint8_t* counts;             // optional [BH][N]
   int B, Hq, Hkv, G, N, P, K, L, T;
   int stride_log2, nJ, nJP;
-  int split_len, nsplit, n_sink, n_window, exact_len, nexact;
+  int split_len, nsplit, n_sink, n_window;
   int npart;
-  int n_count_wg, n_exact_wg, n_attend_wg;
+  int n_count_wg, n_attend_wg;
   int unit_group;              // units whose splits are dispatched interleaved (decode_role)
   int count_heads;             // query heads of one unit per count workgroup (divides G)
   float scale;
@@ -196,13 +197,11 @@ __host__ __device__ inline int fused_sync_words(int U, int nJ) { return U * nJ +
 // a unit), then the
 // attention workgroups of the units, a group of R units at a time
 // (R = unit_group): within a group, the context splits of its units, split
-// 0 of every unit of the group, then split 1, and so on, then the exact-set
-// pieces of its units.  Attention workgroups that take the later slots of a
-// CU stream more slowly while the earlier ones run, so this gives every unit
-// of a group its share of early and late slots and the units end together,
-// instead of the last-dispatched unit ending last; the short exact-set
-// pieces fill slots in the group's tail (ahead of the splits they took early
-// slots from them: 2 us more per hybrid decode at 128K).
+// 0 of every unit of the group, then split 1, and so on.  Attention
+// workgroups that take the later slots of a CU stream more slowly while the
+// earlier ones run, so this gives every unit of a group its share of early
+// and late slots and the units end together, instead of the last-dispatched
+// unit ending last.
 // Progress: count workgroups come before every attention workgroup and never
 // wait; a unit's finishers wait only for workgroups of their own unit, and
 // only the R units of the group being dispatched can still have workgroups
@@ -217,7 +216,7 @@ struct DecodeRole {
   bool count;
   int u;
   int J, bh;       // count: key chunk and query head
-  int slot;        // attention: context split (< nsplit) or exact-set piece
+  int slot;        // attention: context split
 };
 
 __device__ inline DecodeRole decode_role(const FusedParams& p, int wid) {
@@ -251,20 +250,13 @@ __device__ inline DecodeRole decode_role(const FusedParams& p, int wid) {
   }
   r.J = 0;
   r.bh = 0;
-  const int per_unit = p.nexact + p.nsplit;
   const int k = wid - p.n_count_wg;
-  const int grp = k / (p.unit_group * per_unit);            // group of units
+  const int grp = k / (p.unit_group * p.nsplit);            // group of units
   const int u0 = grp * p.unit_group;
   const int R = min(p.unit_group, U - u0);                   // units in this group
-  const int i = k - u0 * per_unit;                           // position in the group
-  if (i < R * p.nsplit) {                                    // splits, split by split
-    r.u = u0 + i % R;
-    r.slot = i / R;
-  } else {                                                   // exact-set pieces, unit by unit
-    const int e = i - R * p.nsplit;
-    r.u = u0 + e / max(p.nexact, 1);
-    r.slot = p.nsplit + e % max(p.nexact, 1);
-  }
+  const int i = k - u0 * p.nsplit;                           // position in the group
+  r.u = u0 + i % R;                                          // splits, split by split
+  r.slot = i / R;
   return r;
 }
 
@@ -910,7 +902,7 @@ __device__ inline void count_role_heads(const FusedParams& p, int J, int bh0, un
 // --------------------------------------------------------------------------
 // Merge
 //
-// Every attend / exact workgroup of unit u writes its partial slot and then
+// Every attend workgroup of unit u writes its partial slot and then
 // arrives at the unit's counter.  The last F = min(G, npart) arrivals are
 // the finishers: finisher f waits until all npart slots have arrived and
 // folds the slots of heads f, f + F, ... into out / lse / nsel.  Attend

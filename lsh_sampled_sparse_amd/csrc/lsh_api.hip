@@ -99,10 +99,9 @@ DecodeLayout decode_layout(int B, int Hq, int Hkv, int N, int L, const Geometry&
   w.lnu = off;        off = align_up(off + lsh::kLnuSamples * sizeof(double));
   // partial slots: nsplit <= min(ceil(N / 256), ceil(kResidentWG / units)), a bound
   // that grows with N, so the workspace size at a cache's capacity covers
-  // every shorter length; plus the exact set's pieces
+  // every shorter length
   const long long slots = std::max<long long>(
-      w.nsplit, std::min((static_cast<long long>(N) + 255) / 256, (lsh::kResidentWG - 1 + units) / units)) +
-      lsh::kMaxExactSplits;
+      w.nsplit, std::min((static_cast<long long>(N) + 255) / 256, (lsh::kResidentWG - 1 + units) / units));
   w.partials = off;
   off = align_up(off + BH * static_cast<size_t>(slots) * lsh::kPartialStride * sizeof(float));
   // counters of the decode launch: per (unit, chunk) and per unit
@@ -422,21 +421,8 @@ static lsh_status decode_cached(const void* q, const void* keys, const void* val
   // the no-alloc path takes no timing events: the pool of events grows while
   // a timing window is open
   a.timed = !noalloc;
-  // the exact set goes to the attention kernel as extra workgroups over
-  // pieces of up to an eighth of a context split (short next to the splits,
-  // so they add no round of workgroups at the end, yet not so many that
-  // they crowd long splits out of their slots), at least 128 keys (one
-  // 32-key tile per wave), at most kMaxExactSplits of them, sized for the
-  // longest sequence (a sequence's exact set, min(n, n_sink + n_window)
-  // keys, grows with its length n)
-  const int ne = static_cast<int>(std::min<long long>(N, static_cast<long long>(n_sink) + n_window));
-  const int per_piece = (ne + lsh::kMaxExactSplits - 1) / lsh::kMaxExactSplits;
-  const int ne128 = (ne + 127) / 128 * 128;
-  a.exact_len = std::max({128, (per_piece + 127) / 128 * 128, std::min(ne128, w.split_len / 8 / 128 * 128)});
-  a.nexact = (ne + a.exact_len - 1) / a.exact_len;
-  // bf16: the context splits take the exact set's keys themselves (every
-  // head, ln u = 0), so no piece waits in the tail of the launch
-  if (dtype == 1) a.nexact = 0;
+  // (the context splits take the exact set's keys themselves: every head of
+  // the group, ln u = 0)
   return hip_status(lsh::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 

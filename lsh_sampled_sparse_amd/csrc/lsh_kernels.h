@@ -45,7 +45,7 @@ struct DecodeArgs {
   uint32_t* bitmask;     // [B*Hq][Nw]
   int32_t* chunk_nsel;   // [B*Hq][nJ]
   double* lnu_samples;   // [kLnuSamples] the ln-u correction g at theta_t = t pi / (2 kLnuTable)
-  float* partials;       // [B*Hq][nsplit + nexact][130]
+  float* partials;       // [B*Hq][nsplit][kPartialStride]
   int32_t* sync;         // the decode launch's counters (zeroed by the query-hash launch)
   float* out;            // [B*Hq][128]
   float* lse;            // optional [B*Hq]
@@ -61,7 +61,6 @@ struct DecodeArgs {
   // exact set of sequence b (length n): keys [0, eh) and [n - et, n) with
   // eh = min(n_sink, n), et = min(n_window, n - eh)
   int n_sink, n_window;
-  int exact_len, nexact;       // the exact set in nexact pieces of exact_len keys, one workgroup each
   bool timed;                  // false: the launches never take timing events (no allocation)
 };
 
@@ -112,7 +111,6 @@ constexpr int kLnuSamples = 2 * kLnuTable + 1;
 // cache line holds two workgroups' partials.
 constexpr int kResidentWG = 512;   // decode workgroups resident at once: about two per CU on 256 CUs
 constexpr int kPartialStride = 160;
-constexpr int kMaxExactSplits = 16;   // partial slots per head reserved for the exact set
 
 // Kernel kinds, in launch order; names for the timing interface.
 enum KernelId {

@@ -156,10 +156,11 @@ static void decode_rejects() {
   EXPECT(lsh_decode_attention_noalloc(nullptr, kFake, kFake, kFake, kFake16, kFake16, 1, 4, 1, 4096, 4096, nullptr,
                                       128, 8, 32, 2, 4096, 0.08f, LSH_BF16, 0, 0, 0, kFakeF, nullptr, nullptr,
                                       nullptr, nullptr, nullptr) == LSH_ERR_INVALID_ARG);
-  EXPECT(lsh_decode_workspace_size(512, 16, 1, 256, 128, 8, 32, 256) > LSH_NOALLOC_SCRATCH_BYTES);
-  EXPECT(lsh_decode_attention_noalloc(kFake, kFake, kFake, kFake, kFake16, kFake16, 512, 16, 1, 256, 256, nullptr,
-                                      128, 8, 32, 2, 256, 0.08f, LSH_BF16, 0, 0, 0, kFakeF, nullptr, nullptr,
-                                      nullptr, nullptr, nullptr) == LSH_ERR_WORKSPACE);
+  // 8192 query heads over 64K keys: their bitmask words alone are 64 MiB
+  EXPECT(lsh_decode_workspace_size(512, 16, 1, 65536, 128, 8, 32, 8192) > LSH_NOALLOC_SCRATCH_BYTES);
+  EXPECT(lsh_decode_attention_noalloc(kFake, kFake, kFake, kFake, kFake16, kFake16, 512, 16, 1, 65536, 65536,
+                                      nullptr, 128, 8, 32, 2, 8192, 0.08f, LSH_BF16, 0, 0, 0, kFakeF, nullptr,
+                                      nullptr, nullptr, nullptr, nullptr) == LSH_ERR_WORKSPACE);
 }
 
 static void timing_window() {

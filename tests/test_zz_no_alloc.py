@@ -94,23 +94,24 @@ def test_noalloc_matches_cached_twice():
 
 
 def test_noalloc_refuses_oversize():
-    # 512 sequences of 16 query heads need more workspace (86 MiB, mostly
-    # per-head partial results) than the 64 MiB scratch: refused before any
-    # launch, outputs untouched
+    # 512 sequences of 16 query heads over 64K keys need more workspace
+    # than the 64 MiB scratch (their bitmask words alone are 64 MiB):
+    # refused before any launch, outputs untouched (the inputs are never
+    # read, so they are left uninitialised)
     import lsh_sampled_sparse_amd as lsh
     lsh.lib()
     dev = torch.device("cuda:0")
-    B, Hq, Hkv, N, K, L = 512, 16, 1, 256, 8, 32
-    assert lsh.lsh_decode_workspace_size(B, Hq, Hkv, N, 128, K, L, 256) > lsh.NOALLOC_SCRATCH_BYTES
+    B, Hq, Hkv, N, K, L, stride = 512, 16, 1, 65536, 8, 32, 8192
+    assert lsh.lsh_decode_workspace_size(B, Hq, Hkv, N, 128, K, L, stride) > lsh.NOALLOC_SCRATCH_BYTES
     say("case noalloc oversize")
     q = torch.zeros(B, Hq, 128, dtype=torch.bfloat16, device=dev)
-    keys = torch.zeros(B, Hkv, N, 128, dtype=torch.bfloat16, device=dev)
+    keys = torch.empty(B, Hkv, N, 128, dtype=torch.bfloat16, device=dev)
     W = torch.zeros(128, L * K, dtype=torch.bfloat16, device=dev)
-    idx = torch.zeros(B, Hkv, L, N, dtype=torch.int16, device=dev)
-    offs = torch.zeros(B, Hkv, L, 1, 1 << K, dtype=torch.int16, device=dev)
+    idx = torch.empty(B, Hkv, L, N, dtype=torch.int16, device=dev)
+    offs = torch.empty(B, Hkv, L, N // stride, 1 << K, dtype=torch.int16, device=dev)
     out = torch.full((B, Hq, 128), 7.0, device=dev)
     with pytest.raises(lsh.LshError) as ei:
-        lsh.lsh_decode_attention_noalloc(q, keys, keys, W, idx, offs, N, K, L, 2, 256, 0.1, 0, 0, out)
+        lsh.lsh_decode_attention_noalloc(q, keys, keys, W, idx, offs, N, K, L, 2, stride, 0.1, 0, 0, out)
     assert ei.value.status == lsh.LSH_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
