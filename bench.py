@@ -244,6 +244,21 @@ def ingest_pmc(d, kind, workload):
                        f"{avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_LDS_IDX_ACTIVE']:.3f}")
     if "SQ_INSTS_VALU" in avg and avg.get("SQ_INSTS_MFMA"):
         derived.append(f"- VALU instructions per MFMA instruction: {avg['SQ_INSTS_VALU'] / avg['SQ_INSTS_MFMA']:.2f}")
+    if avg.get("SQ_BUSY_CYCLES"):
+        # summed over the 32 shader engines (8 XCDs x 4): cycles of one engine
+        cyc = avg["SQ_BUSY_CYCLES"] / 32.0
+        derived.append(f"- cycles per launch: {cyc:.4g} (SQ_BUSY_CYCLES over the 32 shader engines), "
+                       f"{cyc / dur / 1e9:.2f} GHz over the mean launch duration")
+        for k, what in (("SQ_LDS_IDX_ACTIVE", "LDS active"), ("SQ_LDS_BANK_CONFLICT", "LDS bank-conflict")):
+            if k in avg:
+                derived.append(f"- {what} cycles per CU: {avg[k] / 256:.4g} = {avg[k] / 256 / cyc:.1%} of the launch "
+                               f"({avg[k] / 256 / cyc * dur * 1e6:.1f} µs), over 256 CUs")
+    if avg.get("SQ_WAVE_CYCLES") and "SQ_WAIT_ANY" in avg:
+        derived.append(f"- wave-cycles spent waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES): "
+                       f"{avg['SQ_WAIT_ANY'] / avg['SQ_WAVE_CYCLES']:.1%}")
+    if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg:
+        h, m = avg["TCC_HIT_sum"], avg["TCC_MISS_sum"]
+        derived.append(f"- L2 hit rate: {h / (h + m):.1%} of {h + m:.4g} requests")
     if derived:
         lines += ["", "Derived:", ""] + derived
     path = os.path.join(ROOT, "profiles", f"pmc_{kind}_{workload}.md")
