@@ -33,6 +33,22 @@ def test_every_declared_symbol_is_exported():
     assert sorted(lsh.EXPORTS) == names
 
 
+def test_library_resolves_its_own_symbols():
+    """Every kernel the library launches has its host-side stub in the
+    library: no symbol of its own namespace is left undefined (a kernel
+    template whose host pass fails substitution quietly loses its stub, and
+    a lazily bound library would only fail at that kernel's launch)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", "-C", lsh.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    own = [ln for ln in out.splitlines() if "lsh::" in ln]
+    assert not own, "undefined library symbols:\n" + "\n".join(own[:10])
+
+
 def test_status_strings():
     for s in range(5):
         assert lsh.lsh_status_string(s).startswith("LSH_")
